@@ -1,0 +1,248 @@
+"""Benchmark of the SmoothQuant W8A8 linear path (+ bf16 LoRA) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole path over one batch of the workload, for
+every input group: calibrate the per-channel maxima, compute the smoothing
+vector and fold it into INT8 weights, quantize the activations per token,
+run the INT8 GEMM with its dequant epilogue for every projection, and add the
+bf16 LoRA delta. The default workload is the Llama-3-8B projection set at
+M=2048 tokens. Inputs are seeded synthetic tensors, resident in HBM before the
+timed region starts.
+
+Output: one JSON line. `value` is GEMM INT8 tera-operations per second of the
+whole step (2*M*N*K summed over the projections, divided by the step time).
+HIP events around every kernel launch (on the stream the kernels run on) give
+per-stage times and the GEMM's own rate, reported as its roofline fraction
+against the MI355X dense INT8 MFMA peak. The CPU oracle is timed on a bounded
+sample of the same step (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, 5.0 POP/s
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
+DEFAULT_WORKLOAD = "llama3_8b_proj_m2048"
+GEMM_KERNEL_SRC = os.path.join(ROOT, "w8a8_smoothquant_int8_amd", "csrc", "k_gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic_llama3_8b_proj_m2048.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=128,
+                    help="activation rows per input in the CPU-oracle sample")
+    return ap.parse_args()
+
+
+def kernel_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per GEMM launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE runs, if they
+    were taken on the current GEMM source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        m = re.match(r"\s*([a-z_]+)\s*:\s*(\S+)", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("gemm_source_sha256_16") != kernel_hash(GEMM_KERNEL_SRC):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timeline:
+    """HIP events recorded on the launch stream between kernel calls."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []
+
+    def mark(self, tag):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.marks.append((tag, e))
+
+    def durations(self):
+        out = {}
+        for (tag, e0), (_, e1) in zip(self.marks, self.marks[1:]):
+            if tag is None:
+                continue
+            out.setdefault(tag, []).append(e0.elapsed_time(e1))
+        return out
+
+
+def setup(wl, torch):
+    from w8a8_smoothquant_int8_amd.pipeline import LinearGroup
+    groups = []
+    for inp, _K in wl.inputs:
+        rows = wl.group_rows(inp)
+        loras = {p: tuple(t.cuda() for t in wl.lora(p)) for p in rows} if wl.lora_rank else {}
+        g = LinearGroup(wl.w_group(inp).cuda(), rows, wl.alpha, wl.out_dtype, wl.M, lora=loras)
+        groups.append((inp, g, wl.x(inp).cuda(), wl.x_cal(inp).cuda()))
+    torch.cuda.synchronize()
+    return groups
+
+
+def run_step(groups, tl=None):
+    mark = tl.mark if tl is not None else (lambda tag: None)
+    for inp, g, X, Xc in groups:
+        mark("calibrate")
+        g.calibrate(Xc)
+    for inp, g, X, Xc in groups:
+        mark("smooth_fold")
+        g.fold()
+    for inp, g, X, Xc in groups:
+        mark("quant")
+        g.quantize(X)
+        for p in g.rows:
+            mark("gemm")
+            g.gemm(p)
+            mark("lora")
+            g.apply_lora(p, X)
+    mark(None)
+
+
+def cpu_baseline(wl, rows_per_input: int):
+    """The oracle as it stands, on a bounded sample of one step: weights are
+    folded in full; the activation path (quantize, INT8 GEMM, dequant, LoRA)
+    runs on `rows_per_input` rows of each input and is scaled to all M rows."""
+    import numpy as np
+    import oracle.sq_oracle as O
+    from threadpoolctl import threadpool_info
+
+    t_fixed = 0.0
+    t_rows = 0.0
+    m = min(rows_per_input, wl.M)
+    for inp, _K in wl.inputs:
+        X = wl.x(inp).float().numpy()[:m]
+        Xc = wl.x_cal(inp).float().numpy()
+        W = wl.w_group(inp).float().numpy()
+        rows = wl.group_rows(inp)
+        t0 = time.perf_counter()
+        act_max = O.calibrate_absmax(Xc)
+        s = O.smoothing_scale(act_max, O.weight_absmax(W), wl.alpha)
+        wq, wsc = O.fold_and_quantize_weights(W, s)
+        t1 = time.perf_counter()
+        xq, a = O.quantize_per_token(X, s)
+        for p, (r0, r1) in rows.items():
+            y = O.dequantize(O.int8_gemm(xq, wq[r0:r1]), a, wsc[r0:r1], wl.out_dtype)
+            if wl.lora_rank:
+                A, B = wl.lora(p)
+                O.lora_apply(y, X, wl.dtype, A.float().numpy(), B.float().numpy(), 1.0, wl.out_dtype)
+        t2 = time.perf_counter()
+        t_fixed += t1 - t0
+        t_rows += t2 - t1
+    step_s = t_fixed + t_rows * (wl.M / m)
+    threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    return {
+        "value": wl.gemm_ops() / step_s / 1e12,
+        "unit": "TOPS",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"one step of {wl.name}: weights calibrated/smoothed/folded in full "
+                   f"({t_fixed:.1f} s); quantize+GEMM+dequant+LoRA on {m} of {wl.M} rows per input "
+                   f"({t_rows:.1f} s) scaled x{wl.M / m:g}; numpy oracle, BLAS threads={threads}"),
+        "step_s": step_s,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from synth.workloads import get_workload
+    import w8a8_smoothquant_int8_amd as sq
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if not sq.sq_query_support(0):
+        raise SystemExit("device 0 is not gfx950")
+    wl = get_workload(args.workload)
+    groups = setup(wl, torch)
+    for _ in range(args.warmup):
+        run_step(groups)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` steps, synchronized on both sides.
+    tl = Timeline(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(groups, tl)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    ops = wl.gemm_ops()
+    value = ops * args.steps / elapsed / 1e12
+    d = tl.durations()
+    stage_ms = {k: sum(v) / args.steps for k, v in d.items()}
+    gemm_launches = len(d.get("gemm", []))
+    gemm_avg_ms = sum(d["gemm"]) / gemm_launches
+    gemm_ops_per_launch = ops / len([p for p in wl.projections])
+    gemm_tops = gemm_ops_per_launch / (gemm_avg_ms * 1e-3) / 1e12
+    traffic = stored_traffic()
+
+    quant_bytes = sum((2 if wl.dtype != "f32" else 4) * wl.M * K + wl.M * K + 4 * wl.M
+                      for _i, K in wl.inputs)
+    line = {
+        "metric": "W8A8 GEMM+LoRA INT8 TOPS and % of MI355X INT8 MFMA peak (1 GPU)",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "M": wl.M, "act_dtype": wl.dtype, "out_dtype": wl.out_dtype,
+                   "alpha": wl.alpha, "lora_rank": wl.lora_rank,
+                   "projections": {p.name: [p.N, wl.K_of(p.input)] for p in wl.projections},
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "k_w8a8_gemm", "achieved": round(gemm_tops, 1),
+                     "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                     "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+                     "traffic": traffic},
+        "stages_ms_per_step": {k: round(v, 4) for k, v in stage_ms.items()},
+        "gemm_avg_launch_ms": round(gemm_avg_ms, 5),
+        "quant_gbs": round(quant_bytes / (stage_ms["quant"] * 1e-3) / 1e9, 1),
+        "value_pct_of_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2),
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(wl, args.cpu_rows)
+        cb.pop("step_s")
+        cb["value"] = round(cb["value"], 6)
+        line["cpu_baseline"] = cb
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * sq.h - C ABI of libsq, the SmoothQuant W8A8 linear-layer hot path for
+ * AMD Instinct MI355X (gfx950), with a bf16 LoRA delta.
+ *
+ * What the calls compute (sources are cited per call):
+ *   [SQ]   "SmoothQuant" explainer (ozercemkelahmet.com/tools/smoothquant),
+ *          "How it works" Steps 2-7, "A short Python sketch",
+ *          "Calibration in practice".
+ *   [LoRA] TensorRT-LLM issue #12703, "LoRA support for W8A8 SmoothQuant
+ *          (SmoothQuantAttention / SmoothQuantLinear)", section "Pitch".
+ *   [GRP]  TensorRT-LLM PR #17521, "Add FP8 LoRA support for B200",
+ *          "Description" (per-request adapters, eager and graph replay).
+ *
+ * Conventions shared by every call.
+ *  - Layouts are row-major. X is [M, K] (tokens x input channels) with a row
+ *    stride ldx in elements; W is [N, K] (output x input channels, the
+ *    nn.Linear convention); Y is [M, N] with row stride ldy.
+ *  - Every pointer except `act_max`, `s`, `a_scale`, `w_scale` and the segment
+ *    tables must be 16-byte aligned; K, N and every ld must be multiples of
+ *    16 elements. M may be any value >= 0; M == 0 returns SQ_OK and launches
+ *    nothing.
+ *  - Ownership: the caller owns every buffer. The library never allocates,
+ *    frees or keeps a pointer after a call returns.
+ *  - Execution: each call validates its arguments on the host, then enqueues
+ *    kernels on `stream` (a hipStream_t passed as void*; NULL means the null
+ *    stream) and returns without synchronising. No call reads device memory
+ *    on the host, so every call may be captured into a HIP graph. Faults that
+ *    only the device can detect surface at the caller's next synchronisation.
+ *  - Errors: argument errors are detected before any HIP call and returned as
+ *    a negative sq_status; nothing is enqueued in that case. A device that is
+ *    not gfx950 gives SQ_ERR_UNSUPPORTED_ARCH (with one warning on stderr per
+ *    process). Results are deterministic: two runs on the same inputs give
+ *    bitwise identical outputs.
+ *  - NaN and Inf inputs are outside the contract.
+ */
+#ifndef SQ_H
+#define SQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SQ_OK = 0,
+  SQ_ERR_INVALID_ARG = -1,       /* null pointer, negative or zero size, bad enum, alpha out of [0,1] */
+  SQ_ERR_UNSUPPORTED_DTYPE = -2, /* dtype not allowed for this argument */
+  SQ_ERR_MISALIGNED = -3,        /* pointer not 16-byte aligned, or K/N/ld not a multiple of 16 */
+  SQ_ERR_UNSUPPORTED_ARCH = -4,  /* current device is not gfx950 (or no device) */
+  SQ_ERR_WORKSPACE = -5,         /* workspace missing or smaller than required */
+  SQ_ERR_HIP = -6                /* a HIP runtime call failed (launch error) */
+} sq_status;
+
+typedef enum { SQ_F32 = 0, SQ_F16 = 1, SQ_BF16 = 2 } sq_dtype;
+
+typedef enum {
+  SQ_ACT_PER_TOKEN_DYNAMIC = 0,  /* one scale per row, computed from the row ([SQ] Step 6) */
+  SQ_ACT_PER_TENSOR_STATIC = 1   /* one scale for the tensor, fixed by calibration ([SQ] Step 6) */
+} sq_act_mode;
+
+/* Largest LoRA rank the LoRA calls accept. */
+#define SQ_MAX_LORA_RANK 64
+
+/* Capability query ([GRP]: gate on what the library was compiled for).
+ * Sets *supported to 1 if `device` is a gfx950 device this library has code
+ * for, else 0. Returns SQ_OK, SQ_ERR_INVALID_ARG (null pointer) or SQ_ERR_HIP
+ * (device query failed; *supported is set to 0). */
+int sq_query_support(int device, int* supported);
+
+/* Static string naming a status code. Never NULL. */
+const char* sq_status_string(int status);
+
+/* [SQ] Step 4 / "Calibration in practice": running per-channel absmax.
+ * act_max[k] = max(act_max[k], max_m |X[m, k]|) for m < M.
+ * X: [M, K] of dtype xt (f32, f16 or bf16), row stride ldx.
+ * act_max: [K] fp32, device, in/out. The caller zero-fills it before the first
+ * batch; later batches keep raising it. The maximum is exact and independent
+ * of the order rows are visited. */
+int sq_calibrate_absmax(const void* X, int xt, int64_t M, int64_t K, int64_t ldx,
+                        float* act_max, void* stream);
+
+/* [SQ] Step 3 and the sketch's smooth_layer: smoothing scale.
+ * w_max[k] = max_n |W[n, k]|; with a = max(act_max[k], 1e-5) and
+ * w = max(w_max[k], 1e-5) (fp64 constants), s[k] = fp32(max(a^alpha /
+ * w^(1-alpha), 1e-5)) evaluated in fp64 (square roots when alpha == 0.5).
+ * W: [N, K] dtype wt, row stride ldw. alpha in [0, 1].
+ * s_out: [K] fp32, device, written. */
+int sq_smooth_scale(const float* act_max, const void* W, int wt, int64_t N, int64_t K,
+                    int64_t ldw, double alpha, float* s_out, void* stream);
+
+/* [SQ] Step 5 (multiply weight columns by s) and Step 6 (per-output-channel
+ * INT8): W_s[n, k] = fp32(W[n, k] * s[k]); w_scale[n] = max_k |W_s[n, k]| / 127
+ * (fp32); Wq[n, k] = clamp(rne(fp32(W_s[n, k] / w_scale[n])), -127, 127). A row
+ * whose absmax is 0 gets w_scale 0 and codes 0. s == NULL means s = 1.
+ * Wq: [N, K] int8, contiguous (row stride K). w_scale: [N] fp32. */
+int sq_fold_quant_weights(const void* W, int wt, int64_t N, int64_t K, int64_t ldw,
+                          const float* s, int8_t* Wq, float* w_scale, void* stream);
+
+/* sq_smooth_scale followed by sq_fold_quant_weights on the same stream.
+ * Projections that read the same input (Q/K/V, or gate/up) share one s: pass
+ * their weights stacked as one [N_total, K] matrix. */
+int sq_smooth_fold(const float* act_max, const void* W, int wt, int64_t N, int64_t K,
+                   int64_t ldw, double alpha, float* s_out, int8_t* Wq, float* w_scale,
+                   void* stream);
+
+/* [SQ] Step 6, static variant: one per-tensor activation scale from
+ * calibration maxima: a_scale[0] = max_k fp32(act_max[k] / s[k]) / 127 (fp32),
+ * the per-tensor absmax of the smoothed calibration batch over 127.
+ * s == NULL means s = 1. a_scale: [1] fp32, device, written. */
+int sq_static_act_scale(const float* act_max, const float* s, int64_t K, float* a_scale,
+                        void* stream);
+
+/* [SQ] Step 5 (divide the layer input by s) and Step 6 (INT8 activations).
+ * x_s[m, k] = fp32(X[m, k] / s[k]) (IEEE division result; s == NULL: x_s = X).
+ * Dynamic: a_scale[m] = max_k |x_s[m, k]| / 127 (fp32), written ([M]).
+ * Static:  a_scale[0] is read ([1]); values beyond it clip.
+ * Xq[m, k] = clamp(rne(fp32(x_s[m, k] / a_scale)), -127, 127); a zero scale
+ * gives codes 0. Xq: [M, K] int8, contiguous (row stride K). */
+int sq_quant_per_token(const void* X, int xt, int64_t M, int64_t K, int64_t ldx,
+                       const float* s, int mode, int8_t* Xq, float* a_scale, void* stream);
+
+/* [SQ] Step 7: INT8 x INT8 -> INT32 GEMM with the dequant epilogue.
+ * acc[m, n] = sum_k Xq[m, k] * Wq[n, k] (exact INT32: |acc| <= K * 127^2);
+ * Y[m, n] = yt((fp32(acc) * a_scale[m]) * w_scale[n]), one RNE rounding to yt.
+ * Xq: [M, K], Wq: [N, K], both int8 contiguous. a_scale: [M] (dynamic) or [1]
+ * (static, mode = SQ_ACT_PER_TENSOR_STATIC). w_scale: [N]. Y: [M, N] of
+ * dtype yt (bf16, f16 or f32), row stride ldy. */
+int sq_w8a8_gemm(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
+                 const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
+                 int64_t ldy, void* stream);
+
+/* The same GEMM with the raw INT32 accumulators as output ([M, N] contiguous),
+ * for checking the integer products on their own. */
+int sq_w8a8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, int64_t K,
+                     int32_t* acc, void* stream);
+
+/* Bytes of device workspace the LoRA calls need for M rows of K channels and
+ * ranks up to max_rank (fp32 partial sums of the rank-r intermediate). */
+size_t sq_lora_workspace_bytes(int64_t M, int64_t K, int max_rank);
+
+/* [LoRA] Pitch: the low-rank path runs after the INT8 GEMM in bf16 and is
+ * added to the dequantized output:
+ *   T[m, i] = bf16(sum_k bf16(X[m, k]) * A[i, k])      (fp32 accumulation)
+ *   Y[m, n] = yt(fp32(Y[m, n]) + scale * sum_i T[m, i] * B[n, i])
+ * X is the layer's original (unsmoothed) input, dtype xt. A: [r, K] bf16
+ * contiguous; B: [N, r] bf16 contiguous; 1 <= r <= SQ_MAX_LORA_RANK, r a
+ * multiple of 8. Y: [M, N] dtype yt, row stride ldy, updated in place.
+ * ws: device workspace of at least sq_lora_workspace_bytes(M, K, r) bytes. */
+int sq_lora_apply(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* A,
+                  const void* B, int r, float scale, void* Y, int yt, int64_t N, int64_t ldy,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* [LoRA] + [GRP]: one adapter per request. Rows [seg_start[g], seg_start[g+1])
+ * of X and Y form request g (0 <= g < num_segments) and use adapter
+ * seg_adapter[g]; -1 means no adapter (those rows of Y are not touched).
+ * Device tables: seg_start [num_segments+1] int32, non-decreasing, from 0 to
+ * M; seg_adapter [num_segments] int32; A_ptrs / B_ptrs [num_adapters] device
+ * pointers to each adapter's A [r_a, K] and B [N, r_a] (bf16, contiguous,
+ * 16-byte aligned); ranks [num_adapters] int32, each a multiple of 8 in
+ * [8, max_rank]. The host never reads these tables; an out-of-contract table
+ * is undefined behaviour. max_rank <= SQ_MAX_LORA_RANK bounds every rank and
+ * sizes the workspace: sq_lora_workspace_bytes(M, K, max_rank). */
+int sq_lora_apply_segmented(const void* X, int xt, int64_t M, int64_t K, int64_t ldx,
+                            int num_segments, const int32_t* seg_start,
+                            const int32_t* seg_adapter, int num_adapters,
+                            const void* const* A_ptrs, const void* const* B_ptrs,
+                            const int32_t* ranks, int max_rank, float scale, void* Y, int yt,
+                            int64_t N, int64_t ldy, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SQ_H */

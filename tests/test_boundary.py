@@ -1,0 +1,211 @@
+"""The C-ABI boundary of libsq, without a GPU.
+
+Argument validation runs on the host before any HIP call, so invalid calls can
+be checked with fake, never-dereferenced pointer values. Nothing here launches
+a kernel.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import w8a8_smoothquant_int8_amd as sq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sq.h")
+
+P = ctypes.c_void_p(0x10000)        # 16-byte aligned fake device pointer
+P4 = ctypes.c_void_p(0x10004)       # 4-byte aligned, not 16
+NULL = None
+S = None                            # stream
+
+
+@pytest.fixture(scope="module")
+def L():
+    return sq.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(sq_\w+)\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(sq.SIGNATURES)
+
+
+def test_status_strings(L):
+    for code in range(0, -7, -1):
+        assert sq.status_string(code).startswith("SQ_")
+    assert "unknown" in sq.status_string(17)
+
+
+def test_query_support_rejects_null(L):
+    assert L.sq_query_support(0, None) == sq.SQ_ERR_INVALID_ARG
+
+
+def _env_run(code: str, env_extra: dict) -> subprocess.CompletedProcess:
+    env = dict(os.environ, **env_extra)
+    return subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                          cwd=ROOT, timeout=120)
+
+
+def test_arch_gate_forced_unsupported_warns_once():
+    code = (
+        "import ctypes, w8a8_smoothquant_int8_amd as sq\n"
+        "L = sq.lib(); P = ctypes.c_void_p(0x10000)\n"
+        "out = ctypes.c_int(7)\n"
+        "assert L.sq_query_support(0, ctypes.byref(out)) == 0 and out.value == 0\n"
+        "for _ in range(3):\n"
+        "    rc = L.sq_quant_per_token(P, sq.SQ_BF16, 4, 64, 64, None, 0, P, P, None)\n"
+        "    assert rc == sq.SQ_ERR_UNSUPPORTED_ARCH, rc\n"
+        "print('done')\n")
+    r = _env_run(code, {"SQ_FORCE_ARCH": "gfx942"})
+    assert r.returncode == 0, r.stderr
+    assert r.stderr.count("not gfx950") == 1
+    assert "done" in r.stdout
+
+
+def test_arch_gate_forced_supported_query():
+    code = ("import ctypes, w8a8_smoothquant_int8_amd as sq\n"
+            "out = ctypes.c_int(0)\n"
+            "assert sq.lib().sq_query_support(0, ctypes.byref(out)) == 0 and out.value == 1\n")
+    r = _env_run(code, {"SQ_FORCE_ARCH": "gfx950"})
+    assert r.returncode == 0, r.stderr
+
+
+# ---------------------------------------------------------------------------
+# Validation: each call rejects bad arguments before touching the device.
+# ---------------------------------------------------------------------------
+def test_calibrate_validation(L):
+    f = L.sq_calibrate_absmax
+    assert f(NULL, sq.SQ_BF16, 4, 64, 64, P, S) == sq.SQ_ERR_INVALID_ARG
+    assert f(P, 7, 4, 64, 64, P, S) == sq.SQ_ERR_UNSUPPORTED_DTYPE
+    assert f(P, sq.SQ_BF16, -1, 64, 64, P, S) == sq.SQ_ERR_INVALID_ARG
+    assert f(P, sq.SQ_BF16, 4, 0, 64, P, S) == sq.SQ_ERR_INVALID_ARG
+    assert f(P, sq.SQ_BF16, 4, 64, 32, P, S) == sq.SQ_ERR_INVALID_ARG       # ld < K
+    assert f(P, sq.SQ_BF16, 4, 40, 48, P, S) == sq.SQ_ERR_MISALIGNED        # K % 16
+    assert f(P, sq.SQ_BF16, 4, 64, 72, P, S) == sq.SQ_ERR_MISALIGNED        # ld % 16
+    assert f(P4, sq.SQ_BF16, 4, 64, 64, P, S) == sq.SQ_ERR_MISALIGNED
+    assert f(P, sq.SQ_BF16, 4, 64, 64, NULL, S) == sq.SQ_ERR_INVALID_ARG
+    assert f(P, sq.SQ_BF16, 4, 65536, 65536, P, S) == sq.SQ_ERR_INVALID_ARG  # K > 32768
+    assert f(P, sq.SQ_BF16, 0, 64, 64, P, S) == sq.SQ_OK                    # M = 0: no-op
+
+
+def test_smooth_validation(L):
+    f = L.sq_smooth_scale
+    assert f(P, P, sq.SQ_BF16, 8, 64, 64, -0.1, P, S) == sq.SQ_ERR_INVALID_ARG
+    assert f(P, P, sq.SQ_BF16, 8, 64, 64, 1.5, P, S) == sq.SQ_ERR_INVALID_ARG
+    assert f(P, P, sq.SQ_BF16, 8, 64, 64, float("nan"), P, S) == sq.SQ_ERR_INVALID_ARG
+    assert f(NULL, P, sq.SQ_BF16, 8, 64, 64, 0.5, P, S) == sq.SQ_ERR_INVALID_ARG
+    assert f(P, P, sq.SQ_BF16, 0, 64, 64, 0.5, P, S) == sq.SQ_ERR_INVALID_ARG   # N >= 1
+    g = L.sq_smooth_fold
+    assert g(P, P, sq.SQ_BF16, 8, 64, 64, 0.5, P, NULL, P, S) == sq.SQ_ERR_INVALID_ARG
+    assert g(P, P, sq.SQ_BF16, 8, 64, 64, 0.5, P, P4, P, S) == sq.SQ_ERR_MISALIGNED
+    h = L.sq_fold_quant_weights
+    assert h(P, sq.SQ_F16, 8, 64, 64, NULL, NULL, P, S) == sq.SQ_ERR_INVALID_ARG
+    assert h(P, sq.SQ_F16, 8, 64, 64, NULL, P4, P, S) == sq.SQ_ERR_MISALIGNED
+    assert L.sq_static_act_scale(NULL, NULL, 64, P, S) == sq.SQ_ERR_INVALID_ARG
+    assert L.sq_static_act_scale(P, NULL, 0, P, S) == sq.SQ_ERR_INVALID_ARG
+
+
+def test_quant_validation(L):
+    f = L.sq_quant_per_token
+    assert f(P, sq.SQ_BF16, 4, 64, 64, NULL, 5, P, P, S) == sq.SQ_ERR_INVALID_ARG     # mode
+    assert f(P, sq.SQ_BF16, 4, 64, 64, NULL, 0, NULL, P, S) == sq.SQ_ERR_INVALID_ARG
+    assert f(P, sq.SQ_BF16, 4, 64, 64, NULL, 0, P, NULL, S) == sq.SQ_ERR_INVALID_ARG
+    assert f(P, sq.SQ_BF16, 4, 64, 64, NULL, 0, P4, P, S) == sq.SQ_ERR_MISALIGNED
+    assert f(P, sq.SQ_BF16, 0, 64, 64, NULL, 0, P, P, S) == sq.SQ_OK
+
+
+def test_gemm_validation(L):
+    f = L.sq_w8a8_gemm
+    args = lambda **kw: [kw.get(k, v) for k, v in dict(
+        xq=P, wq=P, a=P, mode=0, w=P, M=4, N=64, K=64, Y=P, yt=sq.SQ_BF16, ldy=64, st=S).items()]
+    assert f(*args()) != sq.SQ_ERR_INVALID_ARG
+    assert f(*args(xq=NULL)) == sq.SQ_ERR_INVALID_ARG
+    assert f(*args(N=40, ldy=48)) == sq.SQ_ERR_MISALIGNED
+    assert f(*args(K=40)) == sq.SQ_ERR_MISALIGNED
+    assert f(*args(ldy=32)) == sq.SQ_ERR_INVALID_ARG
+    assert f(*args(yt=9)) == sq.SQ_ERR_UNSUPPORTED_DTYPE
+    assert f(*args(mode=3)) == sq.SQ_ERR_INVALID_ARG
+    assert f(*args(Y=P4)) == sq.SQ_ERR_MISALIGNED
+    assert f(*args(M=0)) == sq.SQ_OK
+    g = L.sq_w8a8_gemm_i32
+    assert g(P, P, 4, 64, 64, NULL, S) == sq.SQ_ERR_INVALID_ARG
+    assert g(P, P, 4, 64, 64, P4, S) == sq.SQ_ERR_MISALIGNED
+
+
+def test_lora_validation(L):
+    ws = L.sq_lora_workspace_bytes(64, 256, 16)
+    assert ws > 0
+    f = L.sq_lora_apply
+    ok = [P, sq.SQ_BF16, 64, 256, 256, P, P, 16, 1.0, P, sq.SQ_BF16, 128, 128, P, ws, S]
+
+    def call(**kw):
+        a = list(ok)
+        for i, k in enumerate(["X", "xt", "M", "K", "ldx", "A", "B", "r", "scale", "Y", "yt", "N",
+                               "ldy", "ws", "wsb", "st"]):
+            if k in kw:
+                a[i] = kw[k]
+        return f(*a)
+    assert call(r=0) == sq.SQ_ERR_INVALID_ARG
+    assert call(r=72) == sq.SQ_ERR_INVALID_ARG
+    assert call(r=12) == sq.SQ_ERR_MISALIGNED
+    assert call(A=NULL) == sq.SQ_ERR_INVALID_ARG
+    assert call(wsb=ws - 1) == sq.SQ_ERR_WORKSPACE
+    assert call(ws=NULL) == sq.SQ_ERR_WORKSPACE
+    assert call(scale=float("inf")) == sq.SQ_ERR_INVALID_ARG
+    assert call(M=0, ws=NULL, wsb=0) == sq.SQ_OK
+    g = L.sq_lora_apply_segmented
+    seg = [P, sq.SQ_BF16, 64, 256, 256, 4, P, P, 3, P, P, P, 64, 1.0, P, sq.SQ_BF16, 128, 128, P,
+           L.sq_lora_workspace_bytes(64, 256, 64), S]
+    bad = list(seg); bad[6] = NULL
+    assert g(*bad) == sq.SQ_ERR_INVALID_ARG
+    bad = list(seg); bad[12] = 128
+    assert g(*bad) == sq.SQ_ERR_INVALID_ARG
+    bad = list(seg); bad[19] = 16
+    assert g(*bad) == sq.SQ_ERR_WORKSPACE
+    bad = list(seg); bad[5] = 0
+    assert g(*bad) == sq.SQ_OK                      # no segments: no-op
+
+
+def test_lora_workspace_grows_with_rank(L):
+    assert L.sq_lora_workspace_bytes(2048, 4096, 64) == 4 * L.sq_lora_workspace_bytes(2048, 4096, 16)
+    assert L.sq_lora_workspace_bytes(0, 4096, 16) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(sq, "_lib", None)
+    monkeypatch.setattr(sq, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(sq.LibraryNotBuilt):
+        sq.lib()
+
+
+# ---------------------------------------------------------------------------
+# Host-side check of the exact-division identity the quant kernels rely on:
+# RN32(RN64(x * RN64(1/d))) == RN32(x / d) for fp32 x, d.
+# ---------------------------------------------------------------------------
+def test_fp64_reciprocal_division_identity():
+    rng = np.random.default_rng(0)
+    F = np.float32
+    n = 400000
+    x = (rng.standard_normal(n) * np.exp(rng.uniform(-20, 20, n))).astype(F)
+    d = np.exp(rng.uniform(-20, 20, n)).astype(F)
+    # adversarial: x close to (k + 1/2) * d, the ties of the final integer rounding
+    k = rng.integers(-127, 127, n) + 0.5
+    d2 = np.exp(rng.uniform(-12, 2, n)).astype(F)
+    x2 = (k * d2.astype(np.float64)).astype(F)
+    x2 = np.nextafter(x2, np.where(rng.random(n) < 0.5, -np.inf, np.inf).astype(F))
+    for a, b in ((x, d), (x2, d2)):
+        ref = a / b
+        got = (a.astype(np.float64) * (1.0 / b.astype(np.float64))).astype(F)
+        assert np.array_equal(got, ref)

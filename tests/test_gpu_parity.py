@@ -1,0 +1,360 @@
+"""HIP path vs the CPU oracle, stage by stage, on the same seeded inputs (GPU).
+
+Bars: INT8 codes, INT32 accumulators, maxima, scales: bit-exact. Dequantized
+bf16/fp16/fp32 outputs: bit-exact (the kernels use the oracle's operation
+order; the stated tolerance of 1 ulp / 1e-3 is not needed). LoRA-added
+outputs: |gpu - oracle| <= 2e-2 |oracle| + 2e-2 rms(oracle) elementwise.
+Every stage gets the oracle's inputs for that stage, so a difference upstream
+cannot cascade.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.sq_oracle as O
+import w8a8_smoothquant_int8_amd as sq
+from synth.workloads import cast_to
+
+pytestmark = pytest.mark.gpu
+F32 = np.float32
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    assert sq.sq_query_support(0), "device 0 is not gfx950"
+    torch.manual_seed(0)
+
+
+def npf(t):
+    return t.detach().float().cpu().numpy()
+
+
+def dev(x, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x)) if isinstance(x, np.ndarray) else x
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def acts(rng, M, K, dtype, n_out=3, factor=50.0, ld=None, sigma=1.0):
+    """Random N(0, sigma) matrix with outlier columns, as a (possibly strided) device tensor,
+    and its exact fp32 values."""
+    x = (rng.standard_normal((M, K)) * sigma).astype(F32)
+    cols = rng.choice(K, size=min(n_out, K), replace=False)
+    x[:, cols] *= factor
+    t = cast_to(x, dtype)
+    if ld is not None and ld > K:
+        wide = torch.zeros(M, ld, dtype=t.dtype)
+        wide[:, :K] = t
+        return wide.cuda()[:, :K], t.float().numpy()
+    return t.cuda(), t.float().numpy()
+
+
+def bits_equal(a, b):
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+# ---------------------------------------------------------------------------
+# Calibration absmax
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("M,K,ld", [(1, 16, 16), (37, 272, 288), (300, 1040, 1040), (2048, 4096, 4096)])
+def test_calibrate_absmax(dtype, M, K, ld):
+    rng = np.random.default_rng(M * 7 + K)
+    x1, x1n = acts(rng, M, K, dtype, ld=ld)
+    x2, x2n = acts(rng, max(M // 2, 1), K, dtype, factor=80.0)
+    am = torch.zeros(K, dtype=torch.float32, device="cuda")
+    sq.sq_calibrate_absmax(x1, am)
+    sq.sq_calibrate_absmax(x2, am)
+    ref = O.calibrate_absmax(x2n, O.calibrate_absmax(x1n))
+    assert bits_equal(npf(am), ref)
+
+
+# ---------------------------------------------------------------------------
+# Smoothing scale
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("alpha", [0.5, 0.8, 0.0, 1.0, 0.3])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_smooth_scale(alpha, dtype):
+    rng = np.random.default_rng(11)
+    K, N = 4096, 640
+    am = np.exp(rng.uniform(np.log(0.3), np.log(400), K)).astype(F32)
+    am[:3] = 0.0                                    # dead channels hit the 1e-5 clamp
+    w = cast_to(rng.normal(0, 0.02, (N, K)).astype(F32), dtype)
+    s = torch.empty(K, dtype=torch.float32, device="cuda")
+    sq.sq_smooth_scale(dev(am), w.cuda(), alpha, s)
+    ref = O.smoothing_scale(am, O.weight_absmax(w.float().numpy()), alpha)
+    got = npf(s)
+    if alpha in (0.5, 0.0, 1.0):
+        assert bits_equal(got, ref)                 # sqrt / exact-power forms
+    else:
+        # fp64 pow on both sides, one rounding to fp32: agree except when the
+        # exact value straddles an fp32 rounding boundary; never beyond 1 ulp.
+        ulps = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+        assert ulps.max() <= 1 and np.count_nonzero(ulps) <= 2, np.count_nonzero(ulps)
+
+
+# ---------------------------------------------------------------------------
+# Fold + per-output-channel weight quantization
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("N,K,ld", [(1, 16, 16), (16, 272, 288), (300, 4096, 4096), (33, 14336, 14336),
+                                    (24, 28672, 28672), (40, 20480, 20480), (17, 5120, 5136)])
+def test_fold_quant_weights(dtype, N, K, ld):
+    rng = np.random.default_rng(N + K)
+    w, wn = acts(rng, N, K, dtype, n_out=0, ld=ld, sigma=0.02)
+    if N > 2:
+        w[1].zero_()
+        wn[1] = 0.0
+    s = np.exp(rng.uniform(-2, 3, K)).astype(F32)
+    Wq = torch.empty(N, K, dtype=torch.int8, device="cuda")
+    ws = torch.empty(N, dtype=torch.float32, device="cuda")
+    sq.sq_fold_quant_weights(w, dev(s), Wq, ws)
+    rq, rs = O.fold_and_quantize_weights(wn, s)
+    assert bits_equal(npf(ws), rs)
+    assert bits_equal(Wq.cpu().numpy(), rq)
+
+
+# ---------------------------------------------------------------------------
+# Activation quantization (smoothing divide + per-token / per-tensor)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("M,K,ld", [(1, 16, 16), (5, 48, 64), (300, 256, 256), (130, 4096, 4112),
+                                    (64, 5120, 5120), (70, 14336, 14336), (9, 20480, 20480),
+                                    (40, 28672, 28672)])
+@pytest.mark.parametrize("smooth", [True, False])
+def test_quant_dynamic(dtype, M, K, ld, smooth):
+    rng = np.random.default_rng(M * 3 + K)
+    x, xn = acts(rng, M, K, dtype, ld=ld)
+    if M > 3:
+        x[2].zero_()
+        xn[2] = 0.0
+    s = np.exp(rng.uniform(-1, 2, K)).astype(F32) if smooth else None
+    Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+    a = torch.empty(M, dtype=torch.float32, device="cuda")
+    sq.sq_quant_per_token(x, dev(s) if smooth else None, Xq, a)
+    rq, ra = O.quantize_per_token(xn, s)
+    assert bits_equal(npf(a), ra)
+    assert bits_equal(Xq.cpu().numpy(), rq)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("M,K", [(7, 272), (256, 5120), (64, 20480)])
+def test_quant_static_with_clipping(dtype, M, K):
+    rng = np.random.default_rng(5 + K)
+    xc, xcn = acts(rng, 64, K, dtype, factor=60.0)
+    x, xn = acts(rng, M, K, dtype, factor=60.0)
+    x[0, 0] = 1e3                                   # beyond the calibrated range: clips
+    xn[0, 0] = x[0, 0].float().item()
+    s = np.exp(rng.uniform(-1, 2, K)).astype(F32)
+    am = torch.zeros(K, dtype=torch.float32, device="cuda")
+    sq.sq_calibrate_absmax(xc, am)
+    a = torch.empty(1, dtype=torch.float32, device="cuda")
+    sq.sq_static_act_scale(am, dev(s), a)
+    ra = O.static_activation_scale(O.calibrate_absmax(xcn), s)
+    assert npf(a)[0] == ra
+    Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+    sq.sq_quant_per_token(x, dev(s), Xq, a, mode="static")
+    rq, clipped = O.quantize_per_tensor_static(xn, s, ra)
+    assert clipped >= 1
+    assert bits_equal(Xq.cpu().numpy(), rq)
+
+
+def test_quant_division_vectors_and_ties():
+    # [2.25, 1.125] -> [127, 63] and [3.75, 1.875] -> [127, 64] (IEEE division,
+    # half to even), padded to K = 16; and the hand-worked 4x4 example's ties.
+    x = np.zeros((2, 16), F32)
+    x[0, :2] = [2.25, 1.125]
+    x[1, :2] = [3.75, 1.875]
+    Xq = torch.empty(2, 16, dtype=torch.int8, device="cuda")
+    a = torch.empty(2, dtype=torch.float32, device="cuda")
+    sq.sq_quant_per_token(dev(x), None, Xq, a)
+    assert Xq.cpu().numpy()[:, :2].tolist() == [[127, 63], [127, 64]]
+    X44 = np.zeros((4, 16), F32)
+    X44[:, :4] = [[254, 0.3125, -1.75, 0.03125], [-256, 4, 3, -0.5], [64, -1, 16, 1],
+                  [-32, 0.5, -1, 0.75]]
+    s = np.ones(16, F32)
+    s[:4] = [32, 2, 8, 1]
+    Xq = torch.empty(4, 16, dtype=torch.int8, device="cuda")
+    a = torch.empty(4, dtype=torch.float32, device="cuda")
+    sq.sq_quant_per_token(dev(X44), dev(s), Xq, a)
+    assert Xq.cpu().numpy()[:, :4].tolist() == [[127, 2, -4, 0], [-127, 32, 6, -8],
+                                                 [127, -32, 127, 64], [-127, 32, -16, 95]]
+
+
+# ---------------------------------------------------------------------------
+# INT8 GEMM
+# ---------------------------------------------------------------------------
+GEMM_SHAPES = [(1, 16, 16), (17, 48, 80), (130, 272, 400), (300, 144, 1040), (257, 1024, 4096),
+               (64, 5120, 5120), (129, 384, 14336)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_i32(M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    wq = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    acc = torch.empty(M, N, dtype=torch.int32, device="cuda")
+    sq.sq_w8a8_gemm_i32(dev(xq), dev(wq), acc)
+    assert np.array_equal(acc.cpu().numpy(), O.int8_gemm(xq, wq))
+
+
+def test_gemm_i32_extreme_magnitude():
+    K = 28672
+    xq = np.full((40, K), 127, np.int8)
+    xq[1::2] = -127
+    wq = np.full((48, K), 127, np.int8)
+    wq[::3, ::2] = -127
+    acc = torch.empty(40, 48, dtype=torch.int32, device="cuda")
+    sq.sq_w8a8_gemm_i32(dev(xq), dev(wq), acc)
+    ref = O.int8_gemm(xq, wq)
+    assert ref.max() == K * 127 * 127
+    assert np.array_equal(acc.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("mode", ["dynamic", "static"])
+@pytest.mark.parametrize("M,N,K", [(33, 48, 272), (300, 1024, 4096), (64, 20480, 5120)])
+def test_gemm_dequant(out, mode, M, N, K):
+    rng = np.random.default_rng(M * N + K)
+    xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    wq = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    a = rng.uniform(1e-3, 5e-2, M if mode == "dynamic" else 1).astype(F32)
+    w = rng.uniform(1e-5, 1e-3, N).astype(F32)
+    ldy = N + (16 if N < 1000 else 0)
+    Yw = torch.zeros(M, ldy, dtype=DT[out], device="cuda")
+    Y = Yw[:, :N]
+    sq.sq_w8a8_gemm(dev(xq), dev(wq), dev(a), dev(w), Y, mode=mode)
+    ref = O.dequantize(O.int8_gemm(xq, wq), a if mode == "dynamic" else a[0], w, out)
+    got = Y.cpu()
+    got = got.float().numpy() if out != "f16" else got.numpy()
+    assert bits_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# LoRA
+# ---------------------------------------------------------------------------
+def lora_close(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref ** 2)) if ref.size else 0.0
+    err = np.abs(got - ref)
+    ok = err <= 2e-2 * np.abs(ref) + 2e-2 * rms
+    return bool(ok.all()), float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+
+
+def lora_inputs(rng, M, K, N, r, xdt, ydt):
+    x, xn = acts(rng, M, K, xdt, factor=20.0)
+    a = cast_to(rng.normal(0, 0.01, (r, K)).astype(F32), "bf16")
+    b = cast_to(rng.normal(0, 0.01, (N, r)).astype(F32), "bf16")
+    y = cast_to(rng.normal(0, 0.5, (M, N)).astype(F32), ydt)
+    return x, xn, a, b, y
+
+
+@pytest.mark.parametrize("r", [8, 16, 64])
+@pytest.mark.parametrize("xdt,ydt", [("bf16", "bf16"), ("f32", "bf16"), ("f16", "f16"), ("bf16", "f32")])
+@pytest.mark.parametrize("M,K,N", [(1, 16, 16), (33, 272, 144), (300, 4096, 1024), (70, 14336, 64)])
+def test_lora_apply(r, xdt, ydt, M, K, N):
+    rng = np.random.default_rng(r + M + K + N)
+    x, xn, a, b, y = lora_inputs(rng, M, K, N, r, xdt, ydt)
+    Y = y.cuda()
+    ws = torch.empty(sq.sq_lora_workspace_bytes(M, K, r), dtype=torch.uint8, device="cuda")
+    sq.sq_lora_apply(x, a.cuda(), b.cuda(), Y, ws, scale=1.0)
+    yn = y.float().numpy() if ydt != "f16" else y.numpy()
+    ref = O.lora_apply(yn, xn, xdt, a.float().numpy(), b.float().numpy(), 1.0, ydt)
+    ok, rel = lora_close(Y.cpu().float().numpy(), ref)
+    assert ok, rel
+
+
+def test_lora_zero_b_leaves_output_bitwise():
+    rng = np.random.default_rng(3)
+    x, xn, a, b, y = lora_inputs(rng, 64, 512, 256, 16, "bf16", "bf16")
+    Y = y.cuda()
+    ws = torch.empty(sq.sq_lora_workspace_bytes(64, 512, 16), dtype=torch.uint8, device="cuda")
+    sq.sq_lora_apply(x, a.cuda(), torch.zeros_like(b).cuda(), Y, ws)
+    assert torch.equal(Y.cpu(), y)
+
+
+def make_segments(rng, M, n_adapters, ranks, with_none=True):
+    cuts = np.sort(rng.choice(np.arange(1, M), size=min(M - 1, 9), replace=False))
+    seg_start = np.concatenate([[0], cuts, [M]]).astype(np.int32)
+    S = len(seg_start) - 1
+    seg_adapter = rng.integers(0, n_adapters, S).astype(np.int32)
+    if with_none:
+        seg_adapter[rng.integers(0, S)] = -1
+    return seg_start, seg_adapter
+
+
+@pytest.mark.parametrize("M,K,N", [(97, 272, 144), (700, 4096, 1024)])
+@pytest.mark.parametrize("ydt", ["bf16", "f32"])
+def test_lora_segmented(M, K, N, ydt):
+    rng = np.random.default_rng(M + K)
+    ranks = [8, 16, 64, 16]
+    x, xn = acts(rng, M, K, "bf16", factor=20.0)
+    As = [cast_to(rng.normal(0, 0.01, (r, K)).astype(F32), "bf16") for r in ranks]
+    Bs = [cast_to(rng.normal(0, 0.01, (N, r)).astype(F32), "bf16") for r in ranks]
+    seg_start, seg_adapter = make_segments(rng, M, len(ranks), ranks)
+    y = cast_to(rng.normal(0, 0.5, (M, N)).astype(F32), ydt)
+    Ad = [t.cuda() for t in As]
+    Bd = [t.cuda() for t in Bs]
+    Y = y.cuda()
+    ws = torch.empty(sq.sq_lora_workspace_bytes(M, K, 64), dtype=torch.uint8, device="cuda")
+    sq.sq_lora_apply_segmented(x, dev(seg_start), dev(seg_adapter), sq.pointer_table(Ad, "cuda"),
+                               sq.pointer_table(Bd, "cuda"), dev(np.array(ranks, np.int32)), 64, Y, ws)
+    ref = O.lora_apply_segmented(y.float().numpy(), xn, "bf16", seg_start, seg_adapter,
+                                 [t.float().numpy() for t in As], [t.float().numpy() for t in Bs],
+                                 1.0, ydt)
+    got = Y.cpu().float().numpy()
+    ok, rel = lora_close(got, ref)
+    assert ok, rel
+    for g in np.nonzero(seg_adapter < 0)[0]:        # requests without adapter: untouched
+        r0, r1 = seg_start[g], seg_start[g + 1]
+        assert torch.equal(Y[r0:r1].cpu(), y[r0:r1])
+
+
+def test_lora_segmented_single_adapter_equals_single():
+    rng = np.random.default_rng(9)
+    M, K, N, r = 300, 1024, 256, 16
+    x, xn, a, b, y = lora_inputs(rng, M, K, N, r, "bf16", "bf16")
+    seg_start = np.array([0, 10, 11, 150, 300], np.int32)
+    seg_adapter = np.zeros(4, np.int32)
+    Y1 = y.cuda()
+    Y2 = y.cuda()
+    ws = torch.empty(sq.sq_lora_workspace_bytes(M, K, r), dtype=torch.uint8, device="cuda")
+    sq.sq_lora_apply(x, a.cuda(), b.cuda(), Y1, ws)
+    Ad, Bd = a.cuda(), b.cuda()
+    sq.sq_lora_apply_segmented(x, dev(seg_start), dev(seg_adapter), sq.pointer_table([Ad], "cuda"),
+                               sq.pointer_table([Bd], "cuda"), dev(np.array([r], np.int32)), r, Y2, ws)
+    assert torch.equal(Y1, Y2)
+
+
+# ---------------------------------------------------------------------------
+# Determinism
+# ---------------------------------------------------------------------------
+def test_repeat_runs_are_bitwise_identical():
+    rng = np.random.default_rng(21)
+    M, K, N, r = 513, 4096, 1024, 16
+    x, xn, a, b, y = lora_inputs(rng, M, K, N, r, "bf16", "bf16")
+    w = cast_to(rng.normal(0, 0.02, (N, K)).astype(F32), "bf16").cuda()
+    outs = []
+    for _ in range(2):
+        am = torch.zeros(K, dtype=torch.float32, device="cuda")
+        s = torch.empty(K, dtype=torch.float32, device="cuda")
+        Wq = torch.empty(N, K, dtype=torch.int8, device="cuda")
+        wsc = torch.empty(N, dtype=torch.float32, device="cuda")
+        Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+        asc = torch.empty(M, dtype=torch.float32, device="cuda")
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(sq.sq_lora_workspace_bytes(M, K, r), dtype=torch.uint8, device="cuda")
+        sq.sq_calibrate_absmax(x, am)
+        sq.sq_smooth_fold(am, w, 0.5, s, Wq, wsc)
+        sq.sq_quant_per_token(x, s, Xq, asc)
+        sq.sq_w8a8_gemm(Xq, Wq, asc, wsc, Y)
+        sq.sq_lora_apply(x, a.cuda(), b.cuda(), Y, ws)
+        outs.append([t.cpu() for t in (am, s, Wq, wsc, Xq, asc, Y)])
+    for t1, t2 in zip(*outs):
+        assert torch.equal(t1, t2)

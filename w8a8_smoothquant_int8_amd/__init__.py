@@ -1,0 +1,217 @@
+"""Python binding of libsq, the SmoothQuant W8A8 linear path on MI355X (gfx950).
+
+Every function has the name of the C entry point it calls (include/sq.h) and
+only marshals arguments: torch tensors become device pointers, shapes and
+row strides; the stream is torch's current stream unless one is given. All
+computation happens in the HIP kernels of libsq.so. If the library is not
+built, importing this package still works, but the first call raises
+LibraryNotBuilt: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsq.so")
+
+SQ_OK = 0
+SQ_ERR_INVALID_ARG = -1
+SQ_ERR_UNSUPPORTED_DTYPE = -2
+SQ_ERR_MISALIGNED = -3
+SQ_ERR_UNSUPPORTED_ARCH = -4
+SQ_ERR_WORKSPACE = -5
+SQ_ERR_HIP = -6
+
+SQ_F32, SQ_F16, SQ_BF16 = 0, 1, 2
+SQ_ACT_PER_TOKEN_DYNAMIC, SQ_ACT_PER_TENSOR_STATIC = 0, 1
+SQ_MAX_LORA_RANK = 64
+
+MODES = {"dynamic": SQ_ACT_PER_TOKEN_DYNAMIC, "static": SQ_ACT_PER_TENSOR_STATIC}
+_DT = {torch.float32: SQ_F32, torch.float16: SQ_F16, torch.bfloat16: SQ_BF16}
+
+# Every exported symbol and its C signature.
+_c_int, _c_i64, _vp, _c_f, _c_d, _c_sz = (ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_float, ctypes.c_double, ctypes.c_size_t)
+SIGNATURES = {
+    "sq_query_support": (_c_int, [_c_int, ctypes.POINTER(_c_int)]),
+    "sq_status_string": (ctypes.c_char_p, [_c_int]),
+    "sq_calibrate_absmax": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp]),
+    "sq_smooth_scale": (_c_int, [_vp, _vp, _c_int, _c_i64, _c_i64, _c_i64, _c_d, _vp, _vp]),
+    "sq_fold_quant_weights": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp]),
+    "sq_smooth_fold": (_c_int, [_vp, _vp, _c_int, _c_i64, _c_i64, _c_i64, _c_d, _vp, _vp, _vp, _vp]),
+    "sq_static_act_scale": (_c_int, [_vp, _vp, _c_i64, _vp, _vp]),
+    "sq_quant_per_token": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _c_int, _vp, _vp, _vp]),
+    "sq_w8a8_gemm": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_int,
+                              _c_i64, _vp]),
+    "sq_w8a8_gemm_i32": (_c_int, [_vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp]),
+    "sq_lora_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_int]),
+    "sq_lora_apply": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int, _c_f, _vp,
+                               _c_int, _c_i64, _c_i64, _vp, _c_sz, _vp]),
+    "sq_lora_apply_segmented": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp,
+                                         _c_int, _vp, _vp, _vp, _c_int, _c_f, _vp, _c_int, _c_i64,
+                                         _c_i64, _vp, _c_sz, _vp]),
+}
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class SQError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsq.so (once). Raises LibraryNotBuilt if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryNotBuilt(
+                f"{LIB_PATH} is missing: build it with `python -m w8a8_smoothquant_int8_amd.build` "
+                "(there is no non-HIP fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().sq_status_string(int(status)).decode()
+
+
+def _check(fn: str, st: int) -> None:
+    if st != SQ_OK:
+        raise SQError(fn, st)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+# ---------------------------------------------------------------------------
+def sq_query_support(device: int = 0) -> bool:
+    out = ctypes.c_int(0)
+    _check("sq_query_support", lib().sq_query_support(int(device), ctypes.byref(out)))
+    return bool(out.value)
+
+
+def sq_calibrate_absmax(X: torch.Tensor, act_max: torch.Tensor, stream=None) -> None:
+    M, K = X.shape
+    _check("sq_calibrate_absmax", lib().sq_calibrate_absmax(
+        _ptr(X), _dt(X), M, K, _ld(X), _ptr(act_max), _stream(stream)))
+
+
+def sq_smooth_scale(act_max: torch.Tensor, W: torch.Tensor, alpha: float, s_out: torch.Tensor,
+                    stream=None) -> None:
+    N, K = W.shape
+    _check("sq_smooth_scale", lib().sq_smooth_scale(
+        _ptr(act_max), _ptr(W), _dt(W), N, K, _ld(W), float(alpha), _ptr(s_out), _stream(stream)))
+
+
+def sq_fold_quant_weights(W: torch.Tensor, s: Optional[torch.Tensor], Wq: torch.Tensor,
+                          w_scale: torch.Tensor, stream=None) -> None:
+    N, K = W.shape
+    _check("sq_fold_quant_weights", lib().sq_fold_quant_weights(
+        _ptr(W), _dt(W), N, K, _ld(W), _ptr(s), _ptr(Wq), _ptr(w_scale), _stream(stream)))
+
+
+def sq_smooth_fold(act_max: torch.Tensor, W: torch.Tensor, alpha: float, s_out: torch.Tensor,
+                   Wq: torch.Tensor, w_scale: torch.Tensor, stream=None) -> None:
+    N, K = W.shape
+    _check("sq_smooth_fold", lib().sq_smooth_fold(
+        _ptr(act_max), _ptr(W), _dt(W), N, K, _ld(W), float(alpha), _ptr(s_out), _ptr(Wq),
+        _ptr(w_scale), _stream(stream)))
+
+
+def sq_static_act_scale(act_max: torch.Tensor, s: Optional[torch.Tensor], a_scale: torch.Tensor,
+                        stream=None) -> None:
+    _check("sq_static_act_scale", lib().sq_static_act_scale(
+        _ptr(act_max), _ptr(s), act_max.numel(), _ptr(a_scale), _stream(stream)))
+
+
+def sq_quant_per_token(X: torch.Tensor, s: Optional[torch.Tensor], Xq: torch.Tensor,
+                       a_scale: torch.Tensor, mode: str = "dynamic", stream=None) -> None:
+    M, K = X.shape
+    _check("sq_quant_per_token", lib().sq_quant_per_token(
+        _ptr(X), _dt(X), M, K, _ld(X), _ptr(s), MODES[mode], _ptr(Xq), _ptr(a_scale),
+        _stream(stream)))
+
+
+def sq_w8a8_gemm(Xq: torch.Tensor, Wq: torch.Tensor, a_scale: torch.Tensor, w_scale: torch.Tensor,
+                 Y: torch.Tensor, mode: str = "dynamic", stream=None) -> None:
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    _check("sq_w8a8_gemm", lib().sq_w8a8_gemm(
+        _ptr(Xq), _ptr(Wq), _ptr(a_scale), MODES[mode], _ptr(w_scale), M, N, K, _ptr(Y), _dt(Y),
+        _ld(Y), _stream(stream)))
+
+
+def sq_w8a8_gemm_i32(Xq: torch.Tensor, Wq: torch.Tensor, acc: torch.Tensor, stream=None) -> None:
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    _check("sq_w8a8_gemm_i32", lib().sq_w8a8_gemm_i32(
+        _ptr(Xq), _ptr(Wq), M, N, K, _ptr(acc), _stream(stream)))
+
+
+def sq_lora_workspace_bytes(M: int, K: int, max_rank: int) -> int:
+    return int(lib().sq_lora_workspace_bytes(int(M), int(K), int(max_rank)))
+
+
+def sq_lora_apply(X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, Y: torch.Tensor,
+                  ws: torch.Tensor, scale: float = 1.0, stream=None) -> None:
+    M, K = X.shape
+    r = A.shape[0]
+    N = Y.shape[1]
+    _check("sq_lora_apply", lib().sq_lora_apply(
+        _ptr(X), _dt(X), M, K, _ld(X), _ptr(A), _ptr(B), r, float(scale), _ptr(Y), _dt(Y), N,
+        _ld(Y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def sq_lora_apply_segmented(X: torch.Tensor, seg_start: torch.Tensor, seg_adapter: torch.Tensor,
+                            A_ptrs: torch.Tensor, B_ptrs: torch.Tensor, ranks: torch.Tensor,
+                            max_rank: int, Y: torch.Tensor, ws: torch.Tensor, scale: float = 1.0,
+                            stream=None) -> None:
+    """seg_start/seg_adapter/ranks: int32 device tensors; A_ptrs/B_ptrs: int64 device tensors
+    holding each adapter's data_ptr()."""
+    M, K = X.shape
+    N = Y.shape[1]
+    _check("sq_lora_apply_segmented", lib().sq_lora_apply_segmented(
+        _ptr(X), _dt(X), M, K, _ld(X), seg_adapter.numel(), _ptr(seg_start), _ptr(seg_adapter),
+        ranks.numel(), _ptr(A_ptrs), _ptr(B_ptrs), _ptr(ranks), int(max_rank), float(scale),
+        _ptr(Y), _dt(Y), N, _ld(Y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def pointer_table(tensors: Sequence[torch.Tensor], device) -> torch.Tensor:
+    """Device int64 tensor of the tensors' data pointers (for the segmented call)."""
+    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)

@@ -1,0 +1,361 @@
+// LoRA delta in bf16, added to the dequantized INT8 GEMM output ([LoRA]
+// Pitch), for one adapter or one adapter per request segment ([GRP]).
+//
+//   shrink:  P[s, m, i] = sum_{k in split s} bf16(X[m, k]) * A[i, k]   (fp32)
+//   expand:  T[m, i]    = bf16(sum_s P[s, m, i])        (fixed order of s)
+//            Y[m, n]    = out(fp32(Y[m, n]) + scale * sum_i T[m, i] * B[n, i])
+//
+// Both are dense contractions and run on the gfx950 bf16 matrix instruction
+// V_MFMA_F32_16X16X32_BF16. The shrink reads X once and is HBM-bound; with
+// only M/16 row tiles it splits K into S slices so enough waves stream X, and
+// writes fp32 partial sums to the caller's workspace. There is no atomic: the
+// expand sums the S partials in a fixed order, so results are reproducible
+// bit for bit. The expand's traffic is the read-modify-write of Y; it computes
+// the transposed product (B rows as the first operand) so every lane owns 4
+// consecutive columns of one row of Y (8-byte accesses for bf16).
+//
+// Segments: each 16-row tile finds the requests that overlap it by binary
+// search in seg_start, and runs the MFMAs once per overlapping request with
+// the rows of other requests zeroed, so each row picks up only its own
+// adapter's product. Rows of requests without an adapter (-1) are not written.
+#include "sq_internal.h"
+
+namespace sq {
+
+constexpr int kLoraThreads = 256;
+
+__device__ __forceinline__ v8bf bits_to_v8bf(uint4 u) { return __builtin_bit_cast(v8bf, u); }
+
+// 8 elements of X at p as bf16 bits (RNE for f32/f16 inputs).
+template <int XT>
+__device__ __forceinline__ uint4 load8_as_bf16(const char* p) {
+  if constexpr (XT == SQ_BF16) {
+    return *(const uint4*)p;
+  } else {
+    float v[8];
+    load8_f32<XT>(p, v);
+    uint4 u;
+    u.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+    u.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    u.z = f32_to_bf16_bits(v[4]) | (f32_to_bf16_bits(v[5]) << 16);
+    u.w = f32_to_bf16_bits(v[6]) | (f32_to_bf16_bits(v[7]) << 16);
+    return u;
+  }
+}
+
+// Largest g with seg_start[g] <= m (segments are non-decreasing, seg_start[0] = 0).
+__device__ __forceinline__ int find_segment(const int32_t* seg_start, int nseg, int m) {
+  int lo = 0, hi = nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seg_start[mid] <= m) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct LoraArgs {
+  // single adapter
+  const unsigned short* A;   // [r, K] bf16
+  const unsigned short* B;   // [N, r] bf16
+  int r;
+  // segmented
+  const int32_t* seg_start;
+  const int32_t* seg_adapter;
+  int nseg;
+  const void* const* A_ptrs;
+  const void* const* B_ptrs;
+  const int32_t* ranks;
+};
+
+// grid: (ceil(M / 64), S); 4 waves, each a 16-row tile of its K slice.
+template <int XT, bool SEG>
+__global__ void __launch_bounds__(kLoraThreads)
+k_lora_shrink(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, LoraArgs la, int R,
+              int kchunk, float* __restrict__ P) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int m0 = blockIdx.x * 64 + wave * 16;
+  if (m0 >= M) return;
+  const int s = blockIdx.y;
+  const int ks = s * kchunk;
+  const int ke = ks + kchunk < K ? ks + kchunk : K;
+  const int lrow = lane & 15, kg = lane >> 4;
+  const int my_m = m0 + lrow;
+  const int NT = (R + 15) / 16;
+
+  v4f acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = v4f{0, 0, 0, 0};
+
+  int g0 = 0, g1 = 0;
+  if constexpr (SEG) {
+    g0 = find_segment(la.seg_start, la.nseg, m0);
+    g1 = g0;
+    const int mend = m0 + 16 < M ? m0 + 16 : M;
+    while (g1 + 1 < la.nseg && la.seg_start[g1 + 1] < mend) ++g1;
+  }
+
+  for (int k = ks; k < ke; k += 32) {
+    const int kk = k + kg * 8;
+    const bool kin = kk < ke;
+    uint4 xu = make_uint4(0, 0, 0, 0);
+    if (kin && my_m < M) xu = load8_as_bf16<XT>(X + (int64_t)my_m * ldx_bytes + (int64_t)kk * DtSize<XT>::v);
+    if constexpr (!SEG) {
+      const v8bf xf = bits_to_v8bf(xu);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < NT) {
+          const int i = t * 16 + lrow;
+          uint4 au = make_uint4(0, 0, 0, 0);
+          if (kin && i < la.r) au = *(const uint4*)(la.A + (int64_t)i * K + kk);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, bits_to_v8bf(au), acc[t], 0, 0, 0);
+        }
+      }
+    } else {
+      for (int g = g0; g <= g1; ++g) {
+        const int ad = la.seg_adapter[g];
+        if (ad < 0) continue;
+        const int ra = la.ranks[ad];
+        const unsigned short* Ag = (const unsigned short*)la.A_ptrs[ad];
+        const bool mine = my_m >= la.seg_start[g] && my_m < la.seg_start[g + 1];
+        const v8bf xf = bits_to_v8bf(mine ? xu : make_uint4(0, 0, 0, 0));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t < NT) {
+            const int i = t * 16 + lrow;
+            uint4 au = make_uint4(0, 0, 0, 0);
+            if (kin && i < ra) au = *(const uint4*)(Ag + (int64_t)i * K + kk);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, bits_to_v8bf(au), acc[t], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // Output register j of a 16x16 tile holds row 4*(lane/16) + j, column lane%16.
+  float* Ps = P + (int64_t)s * M * R;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (t < NT) {
+      const int i = t * 16 + lrow;
+      if (i < R) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int m = m0 + kg * 4 + j;
+          if (m < M) Ps[(int64_t)m * R + i] = acc[t][j];
+        }
+      }
+    }
+  }
+}
+
+template <int YT>
+__device__ __forceinline__ void rmw4(void* Y, int64_t off, float scale, const v4f& d) {
+  if constexpr (YT == SQ_F32) {
+    float4* p = (float4*)((float*)Y + off);
+    float4 y = *p;
+    y.x = y.x + scale * d[0]; y.y = y.y + scale * d[1];
+    y.z = y.z + scale * d[2]; y.w = y.w + scale * d[3];
+    *p = y;
+  } else {
+    uint2* p = (uint2*)((unsigned short*)Y + off);
+    uint2 u = *p;
+    uint32_t h[4] = {u.x & 0xFFFFu, u.x >> 16, u.y & 0xFFFFu, u.y >> 16};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float y = YT == SQ_BF16 ? bf16_bits_to_f32(h[j]) : f16_bits_to_f32(h[j]);
+      y = y + scale * d[j];
+      o[j] = YT == SQ_BF16 ? f32_to_bf16_bits(y) : f32_to_f16_bits(y);
+    }
+    u.x = o[0] | (o[1] << 16);
+    u.y = o[2] | (o[3] << 16);
+    *p = u;
+  }
+}
+
+// grid: (ceil(M / 16), ceil(N / (4 * 64 * chunks_per_wave))); 4 waves, each
+// owns the block's 16 rows and `chunks_per_wave` column chunks of 64.
+template <int YT, bool SEG>
+__global__ void __launch_bounds__(kLoraThreads)
+k_lora_expand(const float* __restrict__ P, int S, int R, int M, int N, LoraArgs la, float scale,
+              void* __restrict__ Y, int64_t ldy, int chunks_per_wave) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int m0 = blockIdx.x * 16;
+  const int lrow = lane & 15, kg = lane >> 4;
+  const int my_m = m0 + lrow;
+  const int KS = (R + 31) / 32;        // rank steps of 32 (R <= 64)
+
+  // T operand: T[my_m, ks*32 + kg*8 .. +8] = bf16(sum_s P[s, m, .]), fixed order.
+  uint4 tu[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int k = ks * 32 + kg * 8;
+    if (ks < KS && k < R && my_m < M) {
+      float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int s = 0; s < S; ++s) {
+        const float4* p = (const float4*)(P + ((int64_t)s * M + my_m) * R + k);
+        const float4 a = p[0], b = p[1];
+        t[0] += a.x; t[1] += a.y; t[2] += a.z; t[3] += a.w;
+        t[4] += b.x; t[5] += b.y; t[6] += b.z; t[7] += b.w;
+      }
+      tu[ks].x = f32_to_bf16_bits(t[0]) | (f32_to_bf16_bits(t[1]) << 16);
+      tu[ks].y = f32_to_bf16_bits(t[2]) | (f32_to_bf16_bits(t[3]) << 16);
+      tu[ks].z = f32_to_bf16_bits(t[4]) | (f32_to_bf16_bits(t[5]) << 16);
+      tu[ks].w = f32_to_bf16_bits(t[6]) | (f32_to_bf16_bits(t[7]) << 16);
+    }
+  }
+
+  int g0 = 0, g1 = 0;
+  bool row_has_adapter = !SEG;
+  if constexpr (SEG) {
+    g0 = find_segment(la.seg_start, la.nseg, m0 < M ? m0 : M - 1);
+    g1 = g0;
+    const int mend = m0 + 16 < M ? m0 + 16 : M;
+    while (g1 + 1 < la.nseg && la.seg_start[g1 + 1] < mend) ++g1;
+    for (int g = g0; g <= g1; ++g)
+      if (la.seg_adapter[g] >= 0 && my_m >= la.seg_start[g] && my_m < la.seg_start[g + 1])
+        row_has_adapter = true;
+  }
+
+  const int n_chunks = (N + 63) / 64;
+  const int cbase = (blockIdx.y * 4 + wave) * chunks_per_wave;
+  for (int cc = 0; cc < chunks_per_wave; ++cc) {
+    const int chunk = cbase + cc;
+    if (chunk >= n_chunks) break;
+    const int nb = chunk * 64;
+    v4f acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = v4f{0, 0, 0, 0};
+
+    auto accumulate = [&](const unsigned short* Bm, int r, const uint4* tsel) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (ks < KS) {
+          const int k = ks * 32 + kg * 8;
+          const v8bf tf = bits_to_v8bf(tsel[ks]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int n = nb + t * 16 + lrow;
+            uint4 bu = make_uint4(0, 0, 0, 0);
+            if (n < N && k < r) bu = *(const uint4*)(Bm + (int64_t)n * r + k);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_v8bf(bu), tf, acc[t], 0, 0, 0);
+          }
+        }
+      }
+    };
+    if constexpr (!SEG) {
+      accumulate(la.B, la.r, tu);
+    } else {
+      for (int g = g0; g <= g1; ++g) {
+        const int ad = la.seg_adapter[g];
+        if (ad < 0) continue;
+        const bool mine = my_m >= la.seg_start[g] && my_m < la.seg_start[g + 1];
+        uint4 ts[2];
+        ts[0] = mine ? tu[0] : make_uint4(0, 0, 0, 0);
+        ts[1] = mine ? tu[1] : make_uint4(0, 0, 0, 0);
+        accumulate((const unsigned short*)la.B_ptrs[ad], la.ranks[ad], ts);
+      }
+    }
+
+    // Transposed product: register j of tile t holds column nb + 16t + 4*kg + j,
+    // row my_m.
+    if (my_m < M && row_has_adapter) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int n = nb + t * 16 + kg * 4;
+        if (n < N) rmw4<YT>(Y, (int64_t)my_m * ldy + n, scale, acc[t]);
+      }
+    }
+  }
+}
+
+// Split of K for the shrink: enough (row tile, slice) pairs to fill the chip.
+static void lora_split(int64_t M, int64_t K, int* S, int* kchunk) {
+  const int64_t m_tiles = (M + 15) / 16;
+  int64_t s = (2048 + m_tiles - 1) / (m_tiles > 0 ? m_tiles : 1);
+  int64_t smax = K / 256;
+  if (smax < 1) smax = 1;
+  if (s > smax) s = smax;
+  if (s > 16) s = 16;
+  if (s < 1) s = 1;
+  int64_t kc = (K + s - 1) / s;
+  kc = (kc + 31) / 32 * 32;
+  *kchunk = (int)kc;
+  *S = (int)((K + kc - 1) / kc);
+}
+
+size_t lora_ws_bytes(int64_t M, int64_t K, int R) {
+  int S, kc;
+  lora_split(M, K, &S, &kc);
+  return (size_t)S * (size_t)M * (size_t)R * sizeof(float);
+}
+
+template <int XT, int YT, bool SEG>
+static int launch_lora_t(const void* X, int64_t M, int64_t K, int64_t ldx, const LoraArgs& la, int R,
+                         float scale, void* Y, int64_t N, int64_t ldy, void* ws, hipStream_t st) {
+  int S, kc;
+  lora_split(M, K, &S, &kc);
+  float* P = (float*)ws;
+  dim3 g1((unsigned)((M + 63) / 64), (unsigned)S);
+  k_lora_shrink<XT, SEG><<<g1, kLoraThreads, 0, st>>>((const char*)X, ldx * DtSize<XT>::v, (int)M,
+                                                      (int)K, la, R, kc, P);
+  SQ_LAUNCH_CHECK();
+  const int64_t m_tiles = (M + 15) / 16;
+  const int64_t n_chunks = (N + 63) / 64;
+  int64_t cpw = (m_tiles * n_chunks + 8191) / 8192;   // aim for ~8192 waves
+  if (cpw < 1) cpw = 1;
+  dim3 g2((unsigned)m_tiles, (unsigned)((n_chunks + 4 * cpw - 1) / (4 * cpw)));
+  k_lora_expand<YT, SEG><<<g2, kLoraThreads, 0, st>>>(P, S, R, (int)M, (int)N, la, scale, Y, ldy,
+                                                      (int)cpw);
+  SQ_LAUNCH_CHECK();
+  return SQ_OK;
+}
+
+template <bool SEG>
+static int launch_lora_any(const void* X, int xt, int64_t M, int64_t K, int64_t ldx,
+                           const LoraArgs& la, int R, float scale, void* Y, int yt, int64_t N,
+                           int64_t ldy, void* ws, hipStream_t st) {
+#define SQ_LORA_Y(XT)                                                                              \
+  switch (yt) {                                                                                    \
+    case SQ_F32: return launch_lora_t<XT, SQ_F32, SEG>(X, M, K, ldx, la, R, scale, Y, N, ldy, ws, st); \
+    case SQ_F16: return launch_lora_t<XT, SQ_F16, SEG>(X, M, K, ldx, la, R, scale, Y, N, ldy, ws, st); \
+    default:     return launch_lora_t<XT, SQ_BF16, SEG>(X, M, K, ldx, la, R, scale, Y, N, ldy, ws, st); \
+  }
+  switch (xt) {
+    case SQ_F32: SQ_LORA_Y(SQ_F32)
+    case SQ_F16: SQ_LORA_Y(SQ_F16)
+    default:     SQ_LORA_Y(SQ_BF16)
+  }
+#undef SQ_LORA_Y
+}
+
+int launch_lora(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* A,
+                const void* B, int r, float scale, void* Y, int yt, int64_t N, int64_t ldy,
+                void* ws, hipStream_t st) {
+  if (M == 0) return SQ_OK;
+  LoraArgs la{};
+  la.A = (const unsigned short*)A;
+  la.B = (const unsigned short*)B;
+  la.r = r;
+  return launch_lora_any<false>(X, xt, M, K, ldx, la, r, scale, Y, yt, N, ldy, ws, st);
+}
+
+int launch_lora_segmented(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, int nseg,
+                          const int32_t* seg_start, const int32_t* seg_adapter,
+                          const void* const* A_ptrs, const void* const* B_ptrs,
+                          const int32_t* ranks, int max_rank, float scale, void* Y, int yt,
+                          int64_t N, int64_t ldy, void* ws, hipStream_t st) {
+  if (M == 0 || nseg == 0) return SQ_OK;
+  LoraArgs la{};
+  la.seg_start = seg_start;
+  la.seg_adapter = seg_adapter;
+  la.nseg = nseg;
+  la.A_ptrs = A_ptrs;
+  la.B_ptrs = B_ptrs;
+  la.ranks = ranks;
+  return launch_lora_any<true>(X, xt, M, K, ldx, la, max_rank, scale, Y, yt, N, ldy, ws, st);
+}
+
+}  // namespace sq

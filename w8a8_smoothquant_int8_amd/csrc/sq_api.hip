@@ -1,0 +1,304 @@
+// C ABI of libsq: argument validation, the architecture gate, dispatch.
+//
+// Validation runs on the host before any HIP call, so an invalid call never
+// enqueues work and can be tested without a GPU. The architecture gate
+// follows the capability-query pattern of TensorRT-LLM PR #17521
+// ("Description": gate on what the binary was compiled for, reject other
+// devices, warn once instead of failing deep inside a kernel).
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "sq_internal.h"
+
+namespace sq {
+int launch_colmax(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, float* out, hipStream_t st);
+int launch_fill(float* p, int64_t n, float v, hipStream_t st);
+int launch_smooth_scale(const float* act_max, float* s_inout, int64_t K, double alpha, hipStream_t st);
+int launch_static_scale(const float* act_max, const float* s, int64_t K, float* a_scale, hipStream_t st);
+int launch_fold_quant(const void* W, int wt, int64_t N, int64_t K, int64_t ldw, const float* s,
+                      int8_t* Wq, float* w_scale, hipStream_t st);
+int launch_quant_act(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const float* s,
+                     int mode, int8_t* Xq, float* a_scale, hipStream_t st);
+int launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
+                const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
+                int64_t ldy, hipStream_t st);
+int launch_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, int64_t K,
+                    int32_t* acc, hipStream_t st);
+size_t lora_ws_bytes(int64_t M, int64_t K, int R);
+int launch_lora(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* A,
+                const void* B, int r, float scale, void* Y, int yt, int64_t N, int64_t ldy,
+                void* ws, hipStream_t st);
+int launch_lora_segmented(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, int nseg,
+                          const int32_t* seg_start, const int32_t* seg_adapter,
+                          const void* const* A_ptrs, const void* const* B_ptrs,
+                          const int32_t* ranks, int max_rank, float scale, void* Y, int yt,
+                          int64_t N, int64_t ldy, void* ws, hipStream_t st);
+}  // namespace sq
+
+namespace {
+
+constexpr int64_t kMaxK = 32768;     // row kernels hold a whole row in registers
+constexpr int64_t kMaxDim = (1LL << 31) - 1;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+bool valid_dtype(int t) { return t == SQ_F32 || t == SQ_F16 || t == SQ_BF16; }
+bool valid_mode(int m) { return m == SQ_ACT_PER_TOKEN_DYNAMIC || m == SQ_ACT_PER_TENSOR_STATIC; }
+
+#define SQ_REQUIRE(cond, err) \
+  do {                        \
+    if (!(cond)) return (err); \
+  } while (0)
+
+// Shape rules shared by calls that read an [rows, K] matrix with stride ld.
+int check_matrix(const void* p, int dt, int64_t rows, int64_t K, int64_t ld) {
+  SQ_REQUIRE(p != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(valid_dtype(dt), SQ_ERR_UNSUPPORTED_DTYPE);
+  SQ_REQUIRE(rows >= 0 && rows <= kMaxDim, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(K >= 1 && K <= kMaxK, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(ld >= K, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(K % 16 == 0 && ld % 16 == 0 && aligned16(p), SQ_ERR_MISALIGNED);
+  return SQ_OK;
+}
+
+// Architecture gate: the library carries gfx950 code only.
+std::atomic<int> g_arch_cache[64];   // 0 unknown, 1 supported, 2 unsupported
+std::atomic<bool> g_warned{false};
+
+int arch_of_device(int device, int* supported) {
+  *supported = 0;
+  const char* forced = std::getenv("SQ_FORCE_ARCH");
+  if (forced != nullptr && forced[0] != '\0') {
+    *supported = std::strncmp(forced, "gfx950", 6) == 0;
+    return SQ_OK;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return SQ_ERR_HIP;
+  *supported = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  return SQ_OK;
+}
+
+int gate() {
+  int dev = 0;
+  int supported = 0;
+  bool known = false;
+  const char* forced = std::getenv("SQ_FORCE_ARCH");
+  if (forced != nullptr && forced[0] != '\0') {
+    arch_of_device(0, &supported);
+    known = true;
+  } else if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    int c = g_arch_cache[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+      if (arch_of_device(dev, &supported) == SQ_OK) {
+        g_arch_cache[dev].store(supported ? 1 : 2, std::memory_order_relaxed);
+        known = true;
+      }
+    } else {
+      supported = c == 1;
+      known = true;
+    }
+  } else {
+    (void)hipGetLastError();   // clear the sticky error of a failed device query
+  }
+  if (known && supported) return SQ_OK;
+  if (!g_warned.exchange(true)) {
+    std::fprintf(stderr,
+                 "libsq: the current device is not gfx950 (or no HIP device is present); "
+                 "SmoothQuant kernels are unavailable and calls return SQ_ERR_UNSUPPORTED_ARCH\n");
+  }
+  return SQ_ERR_UNSUPPORTED_ARCH;
+}
+
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+}  // namespace
+
+extern "C" {
+
+const char* sq_status_string(int st) {
+  switch (st) {
+    case SQ_OK: return "SQ_OK";
+    case SQ_ERR_INVALID_ARG: return "SQ_ERR_INVALID_ARG: null pointer, bad size or bad argument";
+    case SQ_ERR_UNSUPPORTED_DTYPE: return "SQ_ERR_UNSUPPORTED_DTYPE: dtype not allowed here";
+    case SQ_ERR_MISALIGNED: return "SQ_ERR_MISALIGNED: pointer not 16-byte aligned or K/N/ld not a multiple of 16";
+    case SQ_ERR_UNSUPPORTED_ARCH: return "SQ_ERR_UNSUPPORTED_ARCH: current device is not gfx950";
+    case SQ_ERR_WORKSPACE: return "SQ_ERR_WORKSPACE: workspace missing or too small";
+    case SQ_ERR_HIP: return "SQ_ERR_HIP: a HIP runtime call failed";
+    default: return "unknown sq_status";
+  }
+}
+
+int sq_query_support(int device, int* supported) {
+  SQ_REQUIRE(supported != nullptr, SQ_ERR_INVALID_ARG);
+  *supported = 0;
+  SQ_REQUIRE(device >= 0, SQ_ERR_INVALID_ARG);
+  const int rc = arch_of_device(device, supported);
+  if (rc != SQ_OK) (void)hipGetLastError();
+  return rc;
+}
+
+int sq_calibrate_absmax(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, float* act_max,
+                        void* stream) {
+  int rc = check_matrix(X, xt, M, K, ldx);
+  if (rc != SQ_OK) return rc;
+  SQ_REQUIRE(act_max != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(aligned4(act_max), SQ_ERR_MISALIGNED);
+  if (M == 0) return SQ_OK;
+  if ((rc = gate()) != SQ_OK) return rc;
+  return sq::launch_colmax(X, xt, M, K, ldx, act_max, as_stream(stream));
+}
+
+int sq_smooth_scale(const float* act_max, const void* W, int wt, int64_t N, int64_t K, int64_t ldw,
+                    double alpha, float* s_out, void* stream) {
+  int rc = check_matrix(W, wt, N, K, ldw);
+  if (rc != SQ_OK) return rc;
+  SQ_REQUIRE(N >= 1, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(act_max != nullptr && s_out != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(aligned4(act_max) && aligned4(s_out), SQ_ERR_MISALIGNED);
+  SQ_REQUIRE(std::isfinite(alpha) && alpha >= 0.0 && alpha <= 1.0, SQ_ERR_INVALID_ARG);
+  if ((rc = gate()) != SQ_OK) return rc;
+  hipStream_t st = as_stream(stream);
+  // w_max accumulates in s_out, which the scale kernel then turns into s.
+  if ((rc = sq::launch_fill(s_out, K, 0.0f, st)) != SQ_OK) return rc;
+  if ((rc = sq::launch_colmax(W, wt, N, K, ldw, s_out, st)) != SQ_OK) return rc;
+  return sq::launch_smooth_scale(act_max, s_out, K, alpha, st);
+}
+
+int sq_fold_quant_weights(const void* W, int wt, int64_t N, int64_t K, int64_t ldw, const float* s,
+                          int8_t* Wq, float* w_scale, void* stream) {
+  int rc = check_matrix(W, wt, N, K, ldw);
+  if (rc != SQ_OK) return rc;
+  SQ_REQUIRE(N >= 1, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(Wq != nullptr && w_scale != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(aligned16(Wq) && aligned4(w_scale) && (s == nullptr || aligned4(s)), SQ_ERR_MISALIGNED);
+  if ((rc = gate()) != SQ_OK) return rc;
+  return sq::launch_fold_quant(W, wt, N, K, ldw, s, Wq, w_scale, as_stream(stream));
+}
+
+int sq_smooth_fold(const float* act_max, const void* W, int wt, int64_t N, int64_t K, int64_t ldw,
+                   double alpha, float* s_out, int8_t* Wq, float* w_scale, void* stream) {
+  int rc = check_matrix(W, wt, N, K, ldw);
+  if (rc != SQ_OK) return rc;
+  SQ_REQUIRE(Wq != nullptr && w_scale != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(aligned16(Wq) && aligned4(w_scale), SQ_ERR_MISALIGNED);
+  if ((rc = sq_smooth_scale(act_max, W, wt, N, K, ldw, alpha, s_out, stream)) != SQ_OK) return rc;
+  return sq::launch_fold_quant(W, wt, N, K, ldw, s_out, Wq, w_scale, as_stream(stream));
+}
+
+int sq_static_act_scale(const float* act_max, const float* s, int64_t K, float* a_scale, void* stream) {
+  SQ_REQUIRE(act_max != nullptr && a_scale != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(K >= 1 && K <= kMaxDim, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(aligned4(act_max) && aligned4(a_scale) && (s == nullptr || aligned4(s)), SQ_ERR_MISALIGNED);
+  int rc = gate();
+  if (rc != SQ_OK) return rc;
+  return sq::launch_static_scale(act_max, s, K, a_scale, as_stream(stream));
+}
+
+int sq_quant_per_token(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const float* s,
+                       int mode, int8_t* Xq, float* a_scale, void* stream) {
+  int rc = check_matrix(X, xt, M, K, ldx);
+  if (rc != SQ_OK) return rc;
+  SQ_REQUIRE(valid_mode(mode), SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(Xq != nullptr && a_scale != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(aligned16(Xq) && aligned4(a_scale) && (s == nullptr || aligned4(s)), SQ_ERR_MISALIGNED);
+  if (M == 0) return SQ_OK;
+  if ((rc = gate()) != SQ_OK) return rc;
+  return sq::launch_quant_act(X, xt, M, K, ldx, s, mode, Xq, a_scale, as_stream(stream));
+}
+
+static int check_gemm(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, int64_t K) {
+  SQ_REQUIRE(Xq != nullptr && Wq != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(M >= 0 && M <= kMaxDim && N >= 1 && N <= kMaxDim, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(K >= 1 && K <= kMaxK, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(K % 16 == 0 && N % 16 == 0 && aligned16(Xq) && aligned16(Wq), SQ_ERR_MISALIGNED);
+  return SQ_OK;
+}
+
+int sq_w8a8_gemm(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
+                 const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt, int64_t ldy,
+                 void* stream) {
+  int rc = check_gemm(Xq, Wq, M, N, K);
+  if (rc != SQ_OK) return rc;
+  SQ_REQUIRE(valid_mode(mode), SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(a_scale != nullptr && w_scale != nullptr && Y != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(valid_dtype(yt), SQ_ERR_UNSUPPORTED_DTYPE);
+  SQ_REQUIRE(ldy >= N, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(ldy % 16 == 0 && aligned16(Y) && aligned4(a_scale) && aligned4(w_scale), SQ_ERR_MISALIGNED);
+  if (M == 0) return SQ_OK;
+  if ((rc = gate()) != SQ_OK) return rc;
+  return sq::launch_gemm(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, as_stream(stream));
+}
+
+int sq_w8a8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, int64_t K,
+                     int32_t* acc, void* stream) {
+  int rc = check_gemm(Xq, Wq, M, N, K);
+  if (rc != SQ_OK) return rc;
+  SQ_REQUIRE(acc != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(aligned16(acc), SQ_ERR_MISALIGNED);
+  if (M == 0) return SQ_OK;
+  if ((rc = gate()) != SQ_OK) return rc;
+  return sq::launch_gemm_i32(Xq, Wq, M, N, K, acc, as_stream(stream));
+}
+
+size_t sq_lora_workspace_bytes(int64_t M, int64_t K, int max_rank) {
+  if (M <= 0 || K <= 0 || max_rank <= 0) return 0;
+  return sq::lora_ws_bytes(M, K, max_rank);
+}
+
+static int check_lora_common(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, void* Y,
+                             int yt, int64_t N, int64_t ldy, int rank, float scale) {
+  int rc = check_matrix(X, xt, M, K, ldx);
+  if (rc != SQ_OK) return rc;
+  SQ_REQUIRE(Y != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(valid_dtype(yt), SQ_ERR_UNSUPPORTED_DTYPE);
+  SQ_REQUIRE(N >= 1 && N <= kMaxDim && ldy >= N, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(N % 16 == 0 && ldy % 16 == 0 && aligned16(Y), SQ_ERR_MISALIGNED);
+  SQ_REQUIRE(rank >= 1 && rank <= SQ_MAX_LORA_RANK, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(rank % 8 == 0, SQ_ERR_MISALIGNED);
+  SQ_REQUIRE(std::isfinite(scale), SQ_ERR_INVALID_ARG);
+  return SQ_OK;
+}
+
+int sq_lora_apply(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* A,
+                  const void* B, int r, float scale, void* Y, int yt, int64_t N, int64_t ldy,
+                  void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_lora_common(X, xt, M, K, ldx, Y, yt, N, ldy, r, scale);
+  if (rc != SQ_OK) return rc;
+  SQ_REQUIRE(A != nullptr && B != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(aligned16(A) && aligned16(B), SQ_ERR_MISALIGNED);
+  if (M == 0) return SQ_OK;
+  const size_t need = sq_lora_workspace_bytes(M, K, r);
+  SQ_REQUIRE(ws != nullptr && ws_bytes >= need, SQ_ERR_WORKSPACE);
+  SQ_REQUIRE(aligned16(ws), SQ_ERR_MISALIGNED);
+  if ((rc = gate()) != SQ_OK) return rc;
+  return sq::launch_lora(X, xt, M, K, ldx, A, B, r, scale, Y, yt, N, ldy, ws, as_stream(stream));
+}
+
+int sq_lora_apply_segmented(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, int num_segments,
+                            const int32_t* seg_start, const int32_t* seg_adapter, int num_adapters,
+                            const void* const* A_ptrs, const void* const* B_ptrs,
+                            const int32_t* ranks, int max_rank, float scale, void* Y, int yt,
+                            int64_t N, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_lora_common(X, xt, M, K, ldx, Y, yt, N, ldy, max_rank, scale);
+  if (rc != SQ_OK) return rc;
+  SQ_REQUIRE(num_segments >= 0 && num_adapters >= 1, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(seg_start != nullptr && seg_adapter != nullptr && A_ptrs != nullptr &&
+                 B_ptrs != nullptr && ranks != nullptr,
+             SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(aligned4(seg_start) && aligned4(seg_adapter) && aligned4(ranks) &&
+                 ((uintptr_t)A_ptrs & 7u) == 0 && ((uintptr_t)B_ptrs & 7u) == 0,
+             SQ_ERR_MISALIGNED);
+  if (M == 0 || num_segments == 0) return SQ_OK;
+  const size_t need = sq_lora_workspace_bytes(M, K, max_rank);
+  SQ_REQUIRE(ws != nullptr && ws_bytes >= need, SQ_ERR_WORKSPACE);
+  SQ_REQUIRE(aligned16(ws), SQ_ERR_MISALIGNED);
+  if ((rc = gate()) != SQ_OK) return rc;
+  return sq::launch_lora_segmented(X, xt, M, K, ldx, num_segments, seg_start, seg_adapter, A_ptrs,
+                                   B_ptrs, ranks, max_rank, scale, Y, yt, N, ldy, ws,
+                                   as_stream(stream));
+}
+
+}  // extern "C"

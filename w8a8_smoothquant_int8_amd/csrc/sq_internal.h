@@ -1,0 +1,129 @@
+// Internal helpers for the libsq HIP kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sq.h"
+
+namespace sq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned short v8u16 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// 16-bit storage formats. bf16 -> fp32 is exact (the bf16 bits are the top
+// half of the fp32 word); fp16 -> fp32 is exact. fp32 -> bf16/fp16 round to
+// nearest, ties to even.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  _Float16 h = __builtin_bit_cast(_Float16, (unsigned short)b);
+  return (float)h;
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);   // finite inputs only
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  // Without the empty register barrier the compiler folds a preceding fp32
+  // multiply into one mixed-precision FMA that rounds only once, straight to
+  // fp16; the path's semantics are an fp32 rounding followed by an fp16 one.
+  asm volatile("" : "+v"(f));
+  _Float16 h = (_Float16)f;          // v_cvt_f16_f32: round to nearest even
+  return (uint32_t)__builtin_bit_cast(unsigned short, h);
+}
+
+// Load 8 consecutive elements of dtype DT starting at p (16-byte aligned for
+// 16-bit types; fp32 uses two 16-byte loads) and widen them to fp32.
+template <int DT>
+__device__ __forceinline__ void load8_f32(const void* p, float* out) {
+  if constexpr (DT == SQ_F32) {
+    const float4* q = (const float4*)p;
+    float4 a = q[0], b = q[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  } else {
+    uint4 v = *(const uint4*)p;
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == SQ_BF16) {
+        out[2 * i] = __uint_as_float(w[i] << 16);
+        out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      } else {
+        out[2 * i] = f16_bits_to_f32(w[i] & 0xFFFFu);
+        out[2 * i + 1] = f16_bits_to_f32(w[i] >> 16);
+      }
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float load1_f32(const void* p) {
+  if constexpr (DT == SQ_F32) return *(const float*)p;
+  else if constexpr (DT == SQ_BF16) return bf16_bits_to_f32(*(const unsigned short*)p);
+  else return f16_bits_to_f32(*(const unsigned short*)p);
+}
+
+template <int DT> struct DtSize { static constexpr int v = (DT == SQ_F32) ? 4 : 2; };
+
+// ---------------------------------------------------------------------------
+// Correctly rounded fp32 quotient through an fp64 reciprocal.
+//
+// For fp32 x and d (d > 0) whose quotient is in the normal fp32 range, and
+// rd = RN64(1/d):  RN32(RN64(x * rd)) == RN32(x / d).
+// Why: write x = X 2^a and d = D 2^c with integers |X| < 2^24, D < 2^24, and
+// an fp32 rounding midpoint m = A 2^b with A odd and 2^24 <= A < 2^25. The
+// odd part of A*D is at least A >= 2^24 while |X| < 2^24, so x != m*d; and
+// x - m*d is a multiple of 2^min(a, b+c), hence at least that large. Both
+// cases put the exact quotient x/d more than 2^-49 (relative) away from every
+// midpoint. The fp64 product x * rd carries two roundings, a relative error
+// below 2^-52, so it lies strictly between the same two midpoints as x/d and
+// rounds to the same fp32 value. Cost: three VALU ops (widen, multiply,
+// narrow) per element instead of the dozen of an IEEE fp32 division.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float div_rn(float x, double rd) {
+  return (float)((double)x * rd);
+}
+
+// Round half to even, clamp to [-127, 127], as an int.
+__device__ __forceinline__ int quant_code(float q) {
+  float r = __builtin_rintf(q);
+  r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
+         ((uint32_t)(d & 0xFF) << 24);
+}
+
+// Max over a wave64 (all lanes get the result). Max is exact and order-free.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// Atomic max for non-negative floats through their bit patterns (the order of
+// non-negative IEEE floats equals the order of their bit patterns).
+__device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
+  atomicMax((unsigned int*)p, __float_as_uint(v));
+}
+
+}  // namespace sq
+
+// Host-side launch helpers.
+#define SQ_LAUNCH_CHECK()                               \
+  do {                                                  \
+    if (hipGetLastError() != hipSuccess) return SQ_ERR_HIP; \
+  } while (0)
