@@ -3,25 +3,41 @@
 //   Y[m, n]   = out((fp32(acc) * a_scale[m]) * w_scale[n])
 //
 // Both operands are K-contiguous ([M, K] and [N, K]), the layout the gfx950
-// INT8 matrix instruction V_MFMA_I32_32X32X32_I8 wants for both of its inputs:
-// each lane supplies 16 consecutive k-bytes of one row. Tiles of both
-// operands are staged through LDS with 16-byte global loads, double-buffered
-// so the next K-tile is in flight while the current one feeds the MFMAs.
+// INT8 matrix instruction V_MFMA_I32_32X32X32_I8 wants for both inputs: each
+// lane supplies 16 consecutive k-bytes of one row, lanes 0-31 and 32-63 the
+// two 16-byte halves of a 32-byte k step.
 //
-// LDS layout: a tile row holds BK = 128 bytes = 8 chunks of 16 bytes; chunk c
-// of row r is stored at chunk position c ^ (r & 7). The MFMA operand read has
-// 32 lanes reading the same logical chunk of 32 consecutive rows; the XOR
-// spreads any 8 consecutive rows over all 8 chunk positions (all 32 banks),
-// so the 16-byte reads are free of bank conflicts, and the 8 lanes that fill
-// one row on the store side also hit 8 distinct positions.
+// Main kernel (K a multiple of 128): block tile BM x BN, K-tile 128 bytes,
+// 2-stage LDS ring filled straight from global memory by
+// GLOBAL_LOAD_LDS_DWORDX4 (no register staging). One wave instruction moves
+// 1 KB = 8 tile rows into consecutive LDS; each lane picks which 16-byte chunk
+// of its row to fetch so that the tile lands XOR-swizzled (swz below) and the
+// MFMA operand reads are free of bank conflicts. Tiles are assigned XCD by
+// XCD: the hardware deals workgroups round-robin to the 8 XCDs, so block b
+// runs on XCD b % 8; each XCD gets a contiguous run of the tile order, which
+// walks patches of 8 tile rows column by column, so the blocks an XCD runs at
+// once share operand panels in its L2.
+//
+// Generic kernel (any K multiple of 16): 128 x 128 tiles staged through
+// registers, zero-filling the K tail.
+#include <cstdlib>
+#include <cstring>
+
 #include "sq_internal.h"
 
 namespace sq {
 
-constexpr int kBM = 128, kBN = 128, kBK = 128;   // block tile (bytes along K)
-constexpr int kGemmThreads = 256;                // 4 waves, 2 x 2, 64 x 64 each
-
 enum OutKind { OUT_I32 = 0, OUT_BF16 = 1, OUT_F16 = 2, OUT_F32 = 3 };
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS position of 16-byte chunk c of tile row r (rows are 128 bytes). gfx950
+// LDS has 64 banks (256 bytes); a 16-byte read serves 16 lanes per cycle. The
+// MFMA operand read has 16 lanes reading the same logical chunk of 16
+// consecutive rows: even rows share bank half 0, odd rows half 1, and
+// c ^ ((r >> 1) & 7) gives the 8 even (and the 8 odd) rows 8 distinct chunk
+// positions, so the 16 lanes cover all 64 banks once.
+__device__ __forceinline__ int swz(int r, int c) { return (c ^ ((r >> 1) & 7)) << 4; }
 
 template <int OUT>
 __device__ __forceinline__ void store_out(void* Y, int64_t ldy, int64_t m, int64_t n, int acc,
@@ -36,28 +52,223 @@ __device__ __forceinline__ void store_out(void* Y, int64_t ldy, int64_t m, int64
   }
 }
 
-template <int OUT, bool STATIC_A>
-__global__ void __launch_bounds__(kGemmThreads)
-k_w8a8_gemm(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+// Map a block to its (tile_m, tile_n), grouping tiles by XCD. Returns false
+// for padding blocks beyond the last tile.
+// Within the tile order, tiles go in groups of kGroupM tile rows: a group
+// walks its kGroupM x tiles_n patch column by column, so the 32 blocks an XCD
+// runs at once cover about 8 x 4 tiles and share 8 A panels and 4 B panels.
+constexpr int kGroupM = 8;
+__device__ __forceinline__ bool xcd_tile(int tiles_m, int tiles, int& tm, int& tn) {
+  const int per = (tiles + 7) / 8;
+  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (t >= tiles) return false;
+  const int tiles_n = tiles / tiles_m;
+  const int group = t / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gsize = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+  const int in = t - group * kGroupM * tiles_n;
+  tm = first_m + in % gsize;
+  tn = in / gsize;
+  return true;
+}
+
+constexpr int kBK = 128;          // K-tile in bytes
+
+// Epilogue shared by both kernels: acc[i][j] is the 32x32 MFMA tile at rows
+// row0 + 32 i, columns col0 + 32 j. Output register q of a 32x32 tile holds
+// row 8*(q/4) + 4*(lane/32) + q%4 and column lane%32.
+template <int OUT, bool STATIC_A, int TM, int TN>
+__device__ __forceinline__ void epilogue(const v16i (&acc)[TM][TN], int row0, int col0, int M, int N,
+                                         const float* __restrict__ a_scale,
+                                         const float* __restrict__ w_scale, void* __restrict__ Y,
+                                         int64_t ldy) {
+  const int lane = threadIdx.x & 63;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const float as_static = (STATIC_A && OUT != OUT_I32) ? a_scale[0] : 0.0f;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int n = col0 + j * 32 + lrow;
+    if (n >= N) continue;
+    const float ws = OUT != OUT_I32 ? w_scale[n] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = row0 + i * 32 + 8 * (q >> 2) + 4 * lhalf + (q & 3);
+        if (m < M) {
+          const float as = OUT == OUT_I32 ? 0.0f : (STATIC_A ? as_static : a_scale[m]);
+          store_out<OUT>(Y, ldy, m, n, acc[i][j][q], as, ws);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Main kernel, K % 128 == 0. WM x WN waves; each wave owns a (BM/WM) x (BN/WN)
+// sub-tile of 32x32 MFMA tiles. The MFMA operand fragments are double-buffered
+// in registers: the LDS reads for k-step s+1 are in flight while the MFMAs of
+// k-step s run.
+//   SCHED 1: scheduling hints interleave one LDS read after each MFMA, and the
+//            barrier closes each K-tile.
+//   SCHED 4: the barrier sits before the last k-step's MFMAs, which then cover
+//            the first fragment reads of the next K-tile.
+// The barrier carries no memory fence (a fence would also wait for the direct
+// loads just issued for the tile after next): each wave waits for its own
+// direct loads of the next tile (vmcnt) and its reads of this tile (lgkmcnt),
+// then all waves meet.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int OUT, bool STATIC_A, int SCHED>
+__global__ void __launch_bounds__(WM * WN * 64)
+k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
             const float* __restrict__ a_scale, const float* __restrict__ w_scale, int M, int N,
             int K, void* __restrict__ Y, int64_t ldy) {
-  __shared__ __attribute__((aligned(16))) char sA[2][kBM * kBK];
-  __shared__ __attribute__((aligned(16))) char sB[2][kBN * kBK];
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+  constexpr int STAGE = (BM + BN) * kBK;            // bytes per LDS stage
+  constexpr int IA = BM / 8 / NW, IB = BN / 8 / NW; // 1 KB direct loads per wave per stage
+  constexpr int KS = kBK / 32;                      // MFMA k-steps per K-tile
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must split over waves");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles = tiles_m * ((N + BN - 1) / BN);
+  int tm, tn;
+  if (!xcd_tile(tiles_m, tiles, tm, tn)) return;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int lane = threadIdx.x & 63;
+  // wave index as a scalar: the LDS destination of a direct load must be uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane >> 3, lp = lane & 7;
+
+  // 32-bit per-lane source offsets (operands < 4 GiB; checked by the host).
+  // Load instruction q of this wave moves tile rows 8 (wave + NW q) + 0..7;
+  // lane l fetches the chunk that belongs at position l & 7 of row l / 8.
+  // Rows past M or N read the last valid row; their results are never stored.
+  uint32_t offA[IA], offB[IB];
+#pragma unroll
+  for (int q = 0; q < IA; ++q) {
+    const int r = 8 * (wave + NW * q) + lr;
+    int g = m0 + r; g = g < M ? g : M - 1;
+    offA[q] = (uint32_t)g * (uint32_t)K + (uint32_t)swz(r, lp);
+  }
+#pragma unroll
+  for (int q = 0; q < IB; ++q) {
+    const int r = 8 * (wave + NW * q) + lr;
+    int g = n0 + r; g = g < N ? g : N - 1;
+    offB[q] = (uint32_t)g * (uint32_t)K + (uint32_t)swz(r, lp);
+  }
+
+  auto issue = [&](int kt, int stage) {
+    char* sa = smem + stage * STAGE;
+    char* sb = sa + BM * kBK;
+    const int8_t* a0 = A + kt * kBK;
+    const int8_t* b0 = B + kt * kBK;
+#pragma unroll
+    for (int q = 0; q < IA; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(a0 + offA[q]),
+                                       (lds_ptr_t)(sa + 1024 * (wave + NW * q)), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < IB; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(b0 + offB[q]),
+                                       (lds_ptr_t)(sb + 1024 * (wave + NW * q)), 16, 0, 0);
+  };
+
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  int rowA[TM], rowB[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) rowA[i] = wm * (BM / WM) + i * 32 + lrow;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) rowB[j] = wn * (BN / WN) + j * 32 + lrow;
+
+  auto load_frags = [&](const char* sa, int ks, v4i* fa, v4i* fb) {
+    const char* sb = sa + BM * kBK;
+    const int c = ks * 2 + lhalf;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[i] = *(const v4i*)(sa + rowA[i] * kBK + swz(rowA[i], c));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[j] = *(const v4i*)(sb + rowB[j] * kBK + swz(rowB[j], c));
+  };
+
+  v16i acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v16i{};
+
+  const int nk = K / kBK;
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+
+  v4i fa[2][TM], fb[2][TN];
+  load_frags(smem, 0, fa[0], fb[0]);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int stage = kt & 1;
+    const char* sa = smem + stage * STAGE;
+    if (kt + 1 < nk) issue(kt + 1, stage ^ 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < KS) load_frags(sa, ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
+      if (SCHED == 4 && ks + 1 == KS) {
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_barrier();
+        if (kt + 1 < nk) load_frags(smem + (stage ^ 1) * STAGE, 0, fa[cur ^ 1], fb[cur ^ 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+      if constexpr (SCHED == 1) {
+        constexpr int NR = TM + TN;
+#pragma unroll
+        for (int u = 0; u < NR; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - NR, 0);
+      }
+    }
+    if constexpr (SCHED != 4) {
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      __builtin_amdgcn_s_barrier();
+      if (kt + 1 < nk) load_frags(smem + (stage ^ 1) * STAGE, 0, fa[0], fb[0]);
+    }
+  }
+
+  epilogue<OUT, STATIC_A, TM, TN>(acc, m0 + wm * (BM / WM), n0 + wn * (BN / WN), M, N, a_scale,
+                                  w_scale, Y, ldy);
+}
+
+// ---------------------------------------------------------------------------
+// Generic kernel: any K % 16 == 0; 128 x 128 tiles staged through registers.
+// ---------------------------------------------------------------------------
+constexpr int kGBM = 128, kGBN = 128;
+constexpr int kGemmThreads = 256;   // 4 waves, 2 x 2, 64 x 64 each
+
+template <int OUT, bool STATIC_A>
+__global__ void __launch_bounds__(kGemmThreads)
+k_gemm_generic(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+               const float* __restrict__ a_scale, const float* __restrict__ w_scale, int M, int N,
+               int K, void* __restrict__ Y, int64_t ldy) {
+  __shared__ __attribute__((aligned(16))) char sA[2][kGBM * kBK];
+  __shared__ __attribute__((aligned(16))) char sB[2][kGBN * kBK];
+
+  const int tiles_m = (M + kGBM - 1) / kGBM;
+  const int tiles = tiles_m * ((N + kGBN - 1) / kGBN);
+  int tm, tn;
+  if (!xcd_tile(tiles_m, tiles, tm, tn)) return;
+  const int m0 = tm * kGBM, n0 = tn * kGBN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // Tile order: consecutive blocks walk down M within a column of N tiles, so
-  // blocks running at the same time share their Wq tile through L2.
-  const int tiles_m = (M + kBM - 1) / kBM;
-  const int bm = blockIdx.x % tiles_m;
-  const int bn = blockIdx.x / tiles_m;
-  const int m0 = bm * kBM, n0 = bn * kBN;
-
-  // Global -> LDS: 1024 chunks of 16 bytes per operand tile, 4 per thread.
-  // Thread t moves chunks t + 256 i: row = id / 8, chunk = id % 8.
   const int64_t ldk = K;
   const int nk = (K + kBK - 1) / kBK;
   uint4 ra[4], rb[4];
@@ -85,7 +296,7 @@ k_w8a8_gemm(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
     for (int i = 0; i < 4; ++i) {
       const int id = tid + i * kGemmThreads;
       const int r = id >> 3, c = id & 7;
-      const int off = r * kBK + ((c ^ (r & 7)) << 4);
+      const int off = r * kBK + swz(r, c);
       *(uint4*)(&sA[buf][off]) = ra[i];
       *(uint4*)(&sB[buf][off]) = rb[i];
     }
@@ -101,8 +312,8 @@ k_w8a8_gemm(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
   sstore(0);
   __syncthreads();
 
-  const int lrow = lane & 31;       // row within a 32-row MFMA operand
-  const int lhalf = lane >> 5;      // which 16-byte half of a 32-byte k step
+  const int lrow = lane & 31;
+  const int lhalf = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) gload(kt + 1);
@@ -113,12 +324,12 @@ k_w8a8_gemm(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = wm * 64 + i * 32 + lrow;
-        fa[i] = *(const v4i*)(&sA[buf][r * kBK + ((c ^ (r & 7)) << 4)]);
+        fa[i] = *(const v4i*)(&sA[buf][r * kBK + swz(r, c)]);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int r = wn * 64 + j * 32 + lrow;
-        fb[j] = *(const v4i*)(&sB[buf][r * kBK + ((c ^ (r & 7)) << 4)]);
+        fb[j] = *(const v4i*)(&sB[buf][r * kBK + swz(r, c)]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -130,34 +341,58 @@ k_w8a8_gemm(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
     __syncthreads();
   }
 
-  // Epilogue. Output register q of a 32x32 tile holds row 8*(q/4) + 4*(lane/32)
-  // + q%4 and column lane%32.
-  const float as_static = STATIC_A && OUT != OUT_I32 ? a_scale[0] : 0.0f;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + lrow;
-    if (n >= N) continue;
-    const float ws = OUT != OUT_I32 ? w_scale[n] : 0.0f;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (q >> 2) + 4 * lhalf + (q & 3);
-        if (m < M) {
-          const float as = OUT == OUT_I32 ? 0.0f : (STATIC_A ? as_static : a_scale[m]);
-          store_out<OUT>(Y, ldy, m, n, acc[i][j][q], as, ws);
-        }
-      }
-    }
+  epilogue<OUT, STATIC_A, 2, 2>(acc, m0 + wm * 64, n0 + wn * 64, M, N, a_scale, w_scale, Y, ldy);
+}
+
+// ---------------------------------------------------------------------------
+// Host side: pick a kernel and tile for the shape.
+// ---------------------------------------------------------------------------
+// Tile configurations (measured on MI355X over the workload shapes):
+//   CFG_256: 256x256 tiles, 8 waves of 128x64, SCHED 1 - best once there are
+//            at least ~1.75 tiles per CU (256x256 tiles read the least L2 data
+//            per operation);
+//   CFG_128: 128x128 tiles, 4 waves of 64x64, SCHED 4 - best for fewer tiles
+//            (keeps all 256 CUs busy at M = 2048 and for small M).
+enum TileCfg { CFG_GENERIC = 0, CFG_256 = 1, CFG_128 = 2 };
+
+static int pick_cfg(int64_t M, int64_t N, int64_t K) {
+  if (K % kBK != 0 || M * K >= (1LL << 32) || N * K >= (1LL << 32)) return CFG_GENERIC;
+  // Tuning override: SQ_GEMM_TILE=0|1|2 forces a configuration.
+  const char* e = std::getenv("SQ_GEMM_TILE");
+  if (e && *e) {
+    const int o = std::atoi(e);
+    if (o >= 0 && o <= 2) return o;
   }
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  return t256 >= 448 ? CFG_256 : CFG_128;
+}
+
+template <int BM, int BN, int WM, int WN, int OUT, bool STATIC_A, int SCHED>
+static int launch_pipe(const int8_t* Xq, const int8_t* Wq, const float* a_scale, const float* w_scale,
+                       int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t blocks = (tiles + 7) / 8 * 8;
+  k_gemm_pipe<BM, BN, WM, WN, OUT, STATIC_A, SCHED><<<(unsigned)blocks, WM * WN * 64, 0, st>>>(
+      Xq, Wq, a_scale, w_scale, (int)M, (int)N, (int)K, Y, ldy);
+  SQ_LAUNCH_CHECK();
+  return SQ_OK;
 }
 
 template <int OUT, bool STATIC_A>
 static int launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* a_scale,
                          const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y,
                          int64_t ldy, hipStream_t st) {
-  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-  k_w8a8_gemm<OUT, STATIC_A><<<(unsigned)tiles, kGemmThreads, 0, st>>>(
+  switch (pick_cfg(M, N, K)) {
+    case CFG_256:
+      return launch_pipe<256, 256, 2, 4, OUT, STATIC_A, 1>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, st);
+    case CFG_128:
+      return launch_pipe<128, 128, 2, 2, OUT, STATIC_A, 4>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, st);
+    default:
+      break;
+  }
+  const int64_t tiles = ((M + kGBM - 1) / kGBM) * ((N + kGBN - 1) / kGBN);
+  const int64_t blocks = (tiles + 7) / 8 * 8;
+  k_gemm_generic<OUT, STATIC_A><<<(unsigned)blocks, kGemmThreads, 0, st>>>(
       Xq, Wq, a_scale, w_scale, (int)M, (int)N, (int)K, Y, ldy);
   SQ_LAUNCH_CHECK();
   return SQ_OK;
