@@ -34,7 +34,7 @@ INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, 5.0 POP/s
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 DEFAULT_WORKLOAD = "llama3_8b_proj_m2048"
 GEMM_KERNEL_SRC = os.path.join(ROOT, "w8a8_smoothquant_int8_amd", "csrc", "k_gemm.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic_llama3_8b_proj_m2048.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_{tile}_hbm_traffic_llama3_8b_proj_m2048.txt")
 
 
 def parse():
@@ -54,13 +54,14 @@ def kernel_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def stored_traffic():
-    """HBM bytes per GEMM launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE runs, if they
-    were taken on the current GEMM source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def stored_traffic(tile: str):
+    """HBM bytes per launch of the dominant GEMM kernel from the rocprofv3
+    FETCH_SIZE/WRITE_SIZE runs, if they were taken on the current GEMM source."""
+    path = TRAFFIC_FILE.format(tile=tile)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         m = re.match(r"\s*([a-z_]+)\s*:\s*(\S+)", line)
         if m:
             kv[m.group(1)] = m.group(2)
@@ -79,18 +80,22 @@ class Timeline:
         self.torch = torch
         self.marks = []
 
-    def mark(self, tag):
+    def mark(self, tag, group=None):
         e = self.torch.cuda.Event(enable_timing=True)
         e.record()
-        self.marks.append((tag, e))
+        self.marks.append((tag, group, e))
 
     def durations(self):
-        out = {}
-        for (tag, e0), (_, e1) in zip(self.marks, self.marks[1:]):
+        """{tag: [ms, ...]} and {group: [ms, ...]} for the GEMM launches."""
+        out, gemm = {}, {}
+        for (tag, grp, e0), (_, _, e1) in zip(self.marks, self.marks[1:]):
             if tag is None:
                 continue
-            out.setdefault(tag, []).append(e0.elapsed_time(e1))
-        return out
+            ms = e0.elapsed_time(e1)
+            out.setdefault(tag, []).append(ms)
+            if tag == "gemm":
+                gemm.setdefault(grp, []).append(ms)
+        return out, gemm
 
 
 def setup(wl, torch):
@@ -106,7 +111,8 @@ def setup(wl, torch):
 
 
 def run_step(groups, tl=None):
-    mark = tl.mark if tl is not None else (lambda tag: None)
+    """One pass of the whole path over one batch, every input group."""
+    mark = tl.mark if tl is not None else (lambda tag, **kw: None)
     for inp, g, X, Xc in groups:
         mark("calibrate")
         g.calibrate(Xc)
@@ -116,12 +122,24 @@ def run_step(groups, tl=None):
     for inp, g, X, Xc in groups:
         mark("quant")
         g.quantize(X)
-        for p in g.rows:
-            mark("gemm")
-            g.gemm(p)
-            mark("lora")
-            g.apply_lora(p, X)
+        if g.fused:
+            mark("lora_shrink")
+            g.lora_shrink(X)
+            mark("gemm", group=inp)
+            g.gemm_all_lora()
+        else:
+            mark("gemm", group=inp)
+            g.gemm_all()
     mark(None)
+
+
+def gemm_tile(M: int, N: int, K: int) -> str:
+    """The tile configuration libsq picks for an INT8 GEMM of this shape (the
+    library's rule: 256x256 tiles when there are at least 448 of them, else
+    128x128; K not a multiple of 128 takes the generic kernel)."""
+    if K % 128:
+        return "generic"
+    return "256x256" if ((M + 255) // 256) * ((N + 255) // 256) >= 448 else "128x128"
 
 
 def cpu_baseline(wl, rows_per_input: int):
@@ -200,13 +218,26 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     ops = wl.gemm_ops()
     value = ops * args.steps / elapsed / 1e12
-    d = tl.durations()
+    d, gemm_by_group = tl.durations()
     stage_ms = {k: sum(v) / args.steps for k, v in d.items()}
-    gemm_launches = len(d.get("gemm", []))
-    gemm_avg_ms = sum(d["gemm"]) / gemm_launches
-    gemm_ops_per_launch = ops / len([p for p in wl.projections])
-    gemm_tops = gemm_ops_per_launch / (gemm_avg_ms * 1e-3) / 1e12
-    traffic = stored_traffic()
+    # GEMM launches grouped by the kernel instantiation they run (tile config);
+    # the dominant kernel is the one with the most time.
+    by_kernel = {}
+    for inp, _K in wl.inputs:
+        Ntot = sum(p.N for p in wl.group(inp))
+        K = wl.K_of(inp)
+        cfg = gemm_tile(wl.M, Ntot, K)
+        k = by_kernel.setdefault(cfg, {"ms": [], "ops": 0.0, "launches": 0})
+        k["ms"] += gemm_by_group[inp]
+        k["ops"] += 2.0 * wl.M * Ntot * K * len(gemm_by_group[inp])
+        k["launches"] += len(gemm_by_group[inp])
+    dom = max(by_kernel, key=lambda c: sum(by_kernel[c]["ms"]))
+    kd = by_kernel[dom]
+    gemm_avg_ms = sum(kd["ms"]) / kd["launches"]
+    gemm_tops = (kd["ops"] / kd["launches"]) / (gemm_avg_ms * 1e-3) / 1e12
+    gemm_all_tops = sum(k["ops"] for k in by_kernel.values()) / \
+        (sum(sum(k["ms"]) for k in by_kernel.values()) * 1e-3) / 1e12
+    traffic = stored_traffic(dom)
 
     quant_bytes = sum((2 if wl.dtype != "f32" else 4) * wl.M * K + wl.M * K + 4 * wl.M
                       for _i, K in wl.inputs)
@@ -227,12 +258,15 @@ def main():
                    "alpha": wl.alpha, "lora_rank": wl.lora_rank,
                    "projections": {p.name: [p.N, wl.K_of(p.input)] for p in wl.projections},
                    "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "k_w8a8_gemm", "achieved": round(gemm_tops, 1),
-                     "peak": INT8_PEAK_TOPS, "unit": "TOPS",
-                     "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": traffic},
+        "roofline": {"bound": "mfma",
+                     "kernel": f"k_gemm_pipe {dom} tiles, LoRA epilogue" if any(
+                         g.fused for _i, g, _x, _c in groups) else f"k_gemm_pipe {dom} tiles",
+                     "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                     "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": traffic,
+                     "launches_per_step": kd["launches"] // args.steps,
+                     "avg_launch_ms": round(gemm_avg_ms, 5)},
         "stages_ms_per_step": {k: round(v, 4) for k, v in stage_ms.items()},
-        "gemm_avg_launch_ms": round(gemm_avg_ms, 5),
+        "gemm_all_launches_tops": round(gemm_all_tops, 1),
         "quant_gbs": round(quant_bytes / (stage_ms["quant"] * 1e-3) / 1e9, 1),
         "value_pct_of_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2),
     }

@@ -17,8 +17,8 @@
  *    nn.Linear convention); Y is [M, N] with row stride ldy.
  *  - Every pointer except `act_max`, `s`, `a_scale`, `w_scale` and the segment
  *    tables must be 16-byte aligned; K, N and every ld must be multiples of
- *    16 elements. M may be any value >= 0; M == 0 returns SQ_OK and launches
- *    nothing.
+ *    16 elements; K <= 32768. M may be any value >= 0; M == 0 returns SQ_OK
+ *    and launches nothing.
  *  - Ownership: the caller owns every buffer. The library never allocates,
  *    frees or keeps a pointer after a call returns.
  *  - Execution: each call validates its arguments on the host, then enqueues
@@ -61,7 +61,7 @@ typedef enum {
 } sq_act_mode;
 
 /* Largest LoRA rank the LoRA calls accept. */
-#define SQ_MAX_LORA_RANK 64
+#define SQ_MAX_LORA_RANK 128
 
 /* Capability query ([GRP]: gate on what the library was compiled for).
  * Sets *supported to 1 if `device` is a gfx950 device this library has code
@@ -140,12 +140,34 @@ int sq_w8a8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, i
  * ranks up to max_rank (fp32 partial sums of the rank-r intermediate). */
 size_t sq_lora_workspace_bytes(int64_t M, int64_t K, int max_rank);
 
+/* [LoRA] Pitch, first half: the rank-r intermediate of the LoRA path,
+ *   T[m, i] = bf16(sum_k bf16(X[m, k]) * A[i, k])      (fp32 accumulation)
+ * X: [M, K] dtype xt, the layer's original (unsmoothed) input; A: [r, K] bf16
+ * contiguous; 8 <= r <= SQ_MAX_LORA_RANK, r a multiple of 8. Several adapters
+ * that read the same X can be stacked along r. T: [M, r] bf16, row stride ldt
+ * (>= r, a multiple of 8), written. ws: device workspace of at least
+ * sq_lora_workspace_bytes(M, K, r) bytes. */
+int sq_lora_shrink(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* A, int r,
+                   void* T, int64_t ldt, void* ws, size_t ws_bytes, void* stream);
+
+/* [SQ] Step 7 with the [LoRA] delta fused into the GEMM epilogue:
+ *   y[m, n] = yt((fp32(acc) * a_scale[m]) * w_scale[n])      (as sq_w8a8_gemm)
+ *   Y[m, n] = yt(fp32(y[m, n]) + scale * sum_i T[m, i] * B[n, i])
+ * i.e. the same result as sq_w8a8_gemm followed by the expand half of
+ * sq_lora_apply, without a second pass over Y. T: [M, r] bf16 (row stride
+ * ldt >= r, a multiple of 8), e.g. from sq_lora_shrink; B: [N, r] bf16
+ * contiguous; r as for sq_lora_shrink. Other arguments as sq_w8a8_gemm. */
+int sq_w8a8_gemm_lora(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
+                      const float* w_scale, int64_t M, int64_t N, int64_t K, const void* T,
+                      int64_t ldt, const void* B, int r, float scale, void* Y, int yt,
+                      int64_t ldy, void* stream);
+
 /* [LoRA] Pitch: the low-rank path runs after the INT8 GEMM in bf16 and is
  * added to the dequantized output:
  *   T[m, i] = bf16(sum_k bf16(X[m, k]) * A[i, k])      (fp32 accumulation)
  *   Y[m, n] = yt(fp32(Y[m, n]) + scale * sum_i T[m, i] * B[n, i])
  * X is the layer's original (unsmoothed) input, dtype xt. A: [r, K] bf16
- * contiguous; B: [N, r] bf16 contiguous; 1 <= r <= SQ_MAX_LORA_RANK, r a
+ * contiguous; B: [N, r] bf16 contiguous; 8 <= r <= SQ_MAX_LORA_RANK, r a
  * multiple of 8. Y: [M, N] dtype yt, row stride ldy, updated in place.
  * ws: device workspace of at least sq_lora_workspace_bytes(M, K, r) bytes. */
 int sq_lora_apply(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* A,

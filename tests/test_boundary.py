@@ -36,7 +36,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sq.SIGNATURES)
@@ -158,7 +158,7 @@ def test_lora_validation(L):
                 a[i] = kw[k]
         return f(*a)
     assert call(r=0) == sq.SQ_ERR_INVALID_ARG
-    assert call(r=72) == sq.SQ_ERR_INVALID_ARG
+    assert call(r=136) == sq.SQ_ERR_INVALID_ARG
     assert call(r=12) == sq.SQ_ERR_MISALIGNED
     assert call(A=NULL) == sq.SQ_ERR_INVALID_ARG
     assert call(wsb=ws - 1) == sq.SQ_ERR_WORKSPACE
@@ -170,7 +170,7 @@ def test_lora_validation(L):
            L.sq_lora_workspace_bytes(64, 256, 64), S]
     bad = list(seg); bad[6] = NULL
     assert g(*bad) == sq.SQ_ERR_INVALID_ARG
-    bad = list(seg); bad[12] = 128
+    bad = list(seg); bad[12] = 136
     assert g(*bad) == sq.SQ_ERR_INVALID_ARG
     bad = list(seg); bad[19] = 16
     assert g(*bad) == sq.SQ_ERR_WORKSPACE

@@ -358,3 +358,98 @@ def test_repeat_runs_are_bitwise_identical():
         outs.append([t.cpu() for t in (am, s, Wq, wsc, Xq, asc, Y)])
     for t1, t2 in zip(*outs):
         assert torch.equal(t1, t2)
+
+
+# ---------------------------------------------------------------------------
+# Fused path: stacked shrink, LoRA delta in the GEMM epilogue
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("r", [8, 48, 128])
+@pytest.mark.parametrize("xdt", ["bf16", "f32", "f16"])
+@pytest.mark.parametrize("M,K", [(1, 16), (33, 272), (300, 4096)])
+def test_lora_shrink(r, xdt, M, K):
+    rng = np.random.default_rng(r * 7 + M + K)
+    x, xn = acts(rng, M, K, xdt, factor=20.0)
+    a = cast_to(rng.normal(0, 0.01, (r, K)).astype(F32), "bf16")
+    Tw = torch.zeros(M, r + 16, dtype=torch.bfloat16, device="cuda")
+    T = Tw[:, :r]                                   # row stride wider than r
+    ws = torch.empty(sq.sq_lora_workspace_bytes(M, K, r), dtype=torch.uint8, device="cuda")
+    sq.sq_lora_shrink(x, a.cuda(), T, ws)
+    an = a.float().numpy()
+    ref = O.lora_shrink(xn, xdt, an).astype(np.float64)
+    got = T.float().cpu().numpy().astype(np.float64)
+    xb = xn if xdt == "bf16" else O.round_f32_to_bf16(xn)
+    mag = np.abs(xb.astype(np.float64)) @ np.abs(an.astype(np.float64)).T
+    # fp32 accumulation vs fp64, then one bf16 rounding on each side
+    assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 2.0 ** -12 * mag)
+    assert not Tw[:, r:].any()                      # nothing written past r
+
+
+@pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("mode", ["dynamic", "static"])
+@pytest.mark.parametrize("M,N,K,r", [(33, 48, 272, 8), (300, 1024, 4096, 48), (64, 20480, 5120, 16),
+                                     (257, 2048, 4096, 128), (40, 160, 80, 24)])
+def test_gemm_lora(out, mode, M, N, K, r):
+    rng = np.random.default_rng(M + N + K + r)
+    xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    wq = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    a = rng.uniform(1e-3, 5e-2, M if mode == "dynamic" else 1).astype(F32)
+    w = rng.uniform(1e-5, 1e-3, N).astype(F32)
+    t = cast_to(rng.normal(0, 0.5, (M, r)).astype(F32), "bf16")
+    b = cast_to(rng.normal(0, 0.05, (N, r)).astype(F32), "bf16")
+    Tw = torch.zeros(M, r + 8, dtype=torch.bfloat16)
+    Tw[:, :r] = t
+    Y = torch.zeros(M, N, dtype=DT[out], device="cuda")
+    sq.sq_w8a8_gemm_lora(dev(xq), dev(wq), dev(a), dev(w), Tw.cuda()[:, :r], b.cuda(), Y, scale=0.5,
+                         mode=mode)
+    y = O.dequantize(O.int8_gemm(xq, wq), a if mode == "dynamic" else a[0], w, out)
+    ref = O.lora_expand_add(y, t.float().numpy(), b.float().numpy(), 0.5, out)
+    got = Y.cpu()
+    got = got.float().numpy() if out != "f16" else got.numpy()
+    ok, rel = lora_close(got, ref)
+    assert ok, rel
+    # T is given exactly, so the only difference is fp32 vs fp64 summation of r
+    # products: 16-bit outputs are nearly all bit-identical; fp32 outputs (the
+    # oracle adds in fp64 and rounds once) agree to a few fp32 ulps
+    if out == "f32":
+        g64, r64 = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+        assert np.all(np.abs(g64 - r64) <= 2.0 ** -20 * (np.abs(r64) + 0.5 * np.abs(
+            t.float().numpy().astype(np.float64)) @ np.abs(b.float().numpy().astype(np.float64)).T))
+    else:
+        assert np.mean(np.asarray(got) != np.asarray(ref)) < 0.01
+
+
+def test_gemm_lora_zero_b_equals_plain_gemm():
+    rng = np.random.default_rng(77)
+    M, N, K, r = 300, 2048, 4096, 32
+    xq = dev(rng.integers(-127, 128, (M, K)).astype(np.int8))
+    wq = dev(rng.integers(-127, 128, (N, K)).astype(np.int8))
+    a = dev(rng.uniform(1e-3, 5e-2, M).astype(F32))
+    w = dev(rng.uniform(1e-4, 1e-3, N).astype(F32))
+    t = torch.randn(M, r, device="cuda").bfloat16()
+    Y0 = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    Y1 = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    sq.sq_w8a8_gemm(xq, wq, a, w, Y0)
+    sq.sq_w8a8_gemm_lora(xq, wq, a, w, t, torch.zeros(N, r, dtype=torch.bfloat16, device="cuda"), Y1)
+    assert torch.equal(Y0, Y1)
+
+
+def test_fused_group_matches_unfused():
+    from synth.workloads import get_workload
+    from w8a8_smoothquant_int8_amd.pipeline import LinearGroup
+    wl = get_workload("llama3_8b_proj_m2048")
+    inp = "attn_in"
+    X = wl.x(inp).cuda()
+    W = wl.w_group(inp).cuda()
+    rows = wl.group_rows(inp)
+    loras = {p: tuple(t.cuda() for t in wl.lora(p)) for p in rows}
+    out = []
+    for fuse in (True, False):
+        g = LinearGroup(W, rows, wl.alpha, wl.out_dtype, wl.M, lora=loras, fuse=fuse)
+        assert g.fused == fuse
+        g.calibrate(wl.x_cal(inp).cuda())
+        g.fold()
+        out.append({p: t.clone() for p, t in g.forward(X).items()})
+    for p in rows:
+        ok, rel = lora_close(out[0][p].float().cpu().numpy(), out[1][p].float().cpu().numpy())
+        assert ok, (p, rel)
+        assert (out[0][p] != out[1][p]).float().mean().item() < 0.01

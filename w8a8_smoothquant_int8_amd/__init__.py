@@ -28,7 +28,7 @@ SQ_ERR_HIP = -6
 
 SQ_F32, SQ_F16, SQ_BF16 = 0, 1, 2
 SQ_ACT_PER_TOKEN_DYNAMIC, SQ_ACT_PER_TENSOR_STATIC = 0, 1
-SQ_MAX_LORA_RANK = 64
+SQ_MAX_LORA_RANK = 128
 
 MODES = {"dynamic": SQ_ACT_PER_TOKEN_DYNAMIC, "static": SQ_ACT_PER_TENSOR_STATIC}
 _DT = {torch.float32: SQ_F32, torch.float16: SQ_F16, torch.bfloat16: SQ_BF16}
@@ -48,6 +48,10 @@ SIGNATURES = {
     "sq_w8a8_gemm": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_int,
                               _c_i64, _vp]),
     "sq_w8a8_gemm_i32": (_c_int, [_vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp]),
+    "sq_w8a8_gemm_lora": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_i64,
+                                   _vp, _c_int, _c_f, _vp, _c_int, _c_i64, _vp]),
+    "sq_lora_shrink": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _c_int, _vp, _c_i64, _vp,
+                                _c_sz, _vp]),
     "sq_lora_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_int]),
     "sq_lora_apply": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int, _c_f, _vp,
                                _c_int, _c_i64, _c_i64, _vp, _c_sz, _vp]),
@@ -182,6 +186,28 @@ def sq_w8a8_gemm_i32(Xq: torch.Tensor, Wq: torch.Tensor, acc: torch.Tensor, stre
     N = Wq.shape[0]
     _check("sq_w8a8_gemm_i32", lib().sq_w8a8_gemm_i32(
         _ptr(Xq), _ptr(Wq), M, N, K, _ptr(acc), _stream(stream)))
+
+
+def sq_w8a8_gemm_lora(Xq: torch.Tensor, Wq: torch.Tensor, a_scale: torch.Tensor,
+                      w_scale: torch.Tensor, T: torch.Tensor, B: torch.Tensor, Y: torch.Tensor,
+                      scale: float = 1.0, mode: str = "dynamic", stream=None) -> None:
+    """T: [M, r] bf16 (may be a column slice of a wider tensor); B: [N, r] bf16."""
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    r = B.shape[1]
+    _check("sq_w8a8_gemm_lora", lib().sq_w8a8_gemm_lora(
+        _ptr(Xq), _ptr(Wq), _ptr(a_scale), MODES[mode], _ptr(w_scale), M, N, K, _ptr(T), _ld(T),
+        _ptr(B), r, float(scale), _ptr(Y), _dt(Y), _ld(Y), _stream(stream)))
+
+
+def sq_lora_shrink(X: torch.Tensor, A: torch.Tensor, T: torch.Tensor, ws: torch.Tensor,
+                   stream=None) -> None:
+    """T[:, :r] = bf16(bf16(X) A^T) for A [r, K] bf16; T may be wider than r."""
+    M, K = X.shape
+    r = A.shape[0]
+    _check("sq_lora_shrink", lib().sq_lora_shrink(
+        _ptr(X), _dt(X), M, K, _ld(X), _ptr(A), r, _ptr(T), _ld(T), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def sq_lora_workspace_bytes(M: int, K: int, max_rank: int) -> int:

@@ -39,16 +39,37 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // positions, so the 16 lanes cover all 64 banks once.
 __device__ __forceinline__ int swz(int r, int c) { return (c ^ ((r >> 1) & 7)) << 4; }
 
-template <int OUT>
+// Optional LoRA delta added in the epilogue ([LoRA] Pitch): T [M, r] bf16
+// (row stride ldt) and B [N, r] bf16, Y = out(out(y) + scale * T B^T).
+struct LoraEpi {
+  const unsigned short* T;
+  int64_t ldt;
+  const unsigned short* B;
+  int r;
+  float scale;
+};
+
+template <int OUT, bool LORA>
 __device__ __forceinline__ void store_out(void* Y, int64_t ldy, int64_t m, int64_t n, int acc,
-                                          float as, float ws) {
+                                          float as, float ws, float d, float lscale) {
   if constexpr (OUT == OUT_I32) {
     ((int32_t*)Y)[m * ldy + n] = acc;
   } else {
-    const float y = ((float)acc * as) * ws;        // two fp32 roundings, left to right
-    if constexpr (OUT == OUT_F32) ((float*)Y)[m * ldy + n] = y;
-    else if constexpr (OUT == OUT_BF16) ((unsigned short*)Y)[m * ldy + n] = (unsigned short)f32_to_bf16_bits(y);
-    else ((unsigned short*)Y)[m * ldy + n] = (unsigned short)f32_to_f16_bits(y);
+    float y = ((float)acc * as) * ws;              // two fp32 roundings, left to right
+    if constexpr (OUT == OUT_F32) {
+      if constexpr (LORA) y = y + lscale * d;
+      ((float*)Y)[m * ldy + n] = y;
+    } else {
+      uint32_t h = OUT == OUT_BF16 ? f32_to_bf16_bits(y) : f32_to_f16_bits(y);
+      if constexpr (LORA) {
+        // the GEMM output is rounded to the output type first; the delta is
+        // added to that rounded value and the sum rounded again
+        const float yr = OUT == OUT_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+        const float z = yr + lscale * d;
+        h = OUT == OUT_BF16 ? f32_to_bf16_bits(z) : f32_to_f16_bits(z);
+      }
+      ((unsigned short*)Y)[m * ldy + n] = (unsigned short)h;
+    }
   }
 }
 
@@ -76,28 +97,50 @@ constexpr int kBK = 128;          // K-tile in bytes
 
 // Epilogue shared by both kernels: acc[i][j] is the 32x32 MFMA tile at rows
 // row0 + 32 i, columns col0 + 32 j. Output register q of a 32x32 tile holds
-// row 8*(q/4) + 4*(lane/32) + q%4 and column lane%32.
-template <int OUT, bool STATIC_A, int TM, int TN>
+// row 8*(q/4) + 4*(lane/32) + q%4 and column lane%32. With LORA, the rank-r
+// product for the same tile comes from V_MFMA_F32_32X32X16_BF16, whose output
+// has the same layout (T rows in the first operand, B rows in the second), so
+// it lines up register for register with the INT32 accumulators. The MFMAs run
+// in uniform control flow; rows and columns past M and N read clamped
+// (valid) addresses and are never stored.
+template <int OUT, bool STATIC_A, bool LORA, int TM, int TN>
 __device__ __forceinline__ void epilogue(const v16i (&acc)[TM][TN], int row0, int col0, int M, int N,
                                          const float* __restrict__ a_scale,
                                          const float* __restrict__ w_scale, void* __restrict__ Y,
-                                         int64_t ldy) {
+                                         int64_t ldy, const LoraEpi& le) {
   const int lane = threadIdx.x & 63;
   const int lrow = lane & 31, lhalf = lane >> 5;
   const float as_static = (STATIC_A && OUT != OUT_I32) ? a_scale[0] : 0.0f;
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int n = col0 + j * 32 + lrow;
-    if (n >= N) continue;
-    const float ws = OUT != OUT_I32 ? w_scale[n] : 0.0f;
+    const bool n_ok = n < N;
+    const float ws = (OUT != OUT_I32 && n_ok) ? w_scale[n] : 0.0f;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+      v16f d = {};
+      if constexpr (LORA) {
+        const int64_t mr = row0 + i * 32 + lrow < M ? row0 + i * 32 + lrow : M - 1;
+        const int64_t nr = n_ok ? n : N - 1;
+        for (int k0 = 0; k0 < le.r; k0 += 16) {
+          const int k = k0 + 8 * lhalf;
+          uint4 tu = make_uint4(0, 0, 0, 0), bu = make_uint4(0, 0, 0, 0);
+          if (k < le.r) {
+            tu = *(const uint4*)(le.T + mr * le.ldt + k);
+            bu = *(const uint4*)(le.B + nr * le.r + k);
+          }
+          d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, tu),
+                                                      __builtin_bit_cast(v8bf, bu), d, 0, 0, 0);
+        }
+      }
+      if (n_ok) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = row0 + i * 32 + 8 * (q >> 2) + 4 * lhalf + (q & 3);
-        if (m < M) {
-          const float as = OUT == OUT_I32 ? 0.0f : (STATIC_A ? as_static : a_scale[m]);
-          store_out<OUT>(Y, ldy, m, n, acc[i][j][q], as, ws);
+        for (int q = 0; q < 16; ++q) {
+          const int m = row0 + i * 32 + 8 * (q >> 2) + 4 * lhalf + (q & 3);
+          if (m < M) {
+            const float as = OUT == OUT_I32 ? 0.0f : (STATIC_A ? as_static : a_scale[m]);
+            store_out<OUT, LORA>(Y, ldy, m, n, acc[i][j][q], as, ws, d[q], le.scale);
+          }
         }
       }
     }
@@ -118,11 +161,11 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[TM][TN], int row0, in
 // direct loads of the next tile (vmcnt) and its reads of this tile (lgkmcnt),
 // then all waves meet.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int OUT, bool STATIC_A, int SCHED>
+template <int BM, int BN, int WM, int WN, int OUT, bool STATIC_A, int SCHED, bool LORA>
 __global__ void __launch_bounds__(WM * WN * 64)
 k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
             const float* __restrict__ a_scale, const float* __restrict__ w_scale, int M, int N,
-            int K, void* __restrict__ Y, int64_t ldy) {
+            int K, void* __restrict__ Y, int64_t ldy, LoraEpi le) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
   constexpr int STAGE = (BM + BN) * kBK;            // bytes per LDS stage
@@ -240,8 +283,8 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
     }
   }
 
-  epilogue<OUT, STATIC_A, TM, TN>(acc, m0 + wm * (BM / WM), n0 + wn * (BN / WN), M, N, a_scale,
-                                  w_scale, Y, ldy);
+  epilogue<OUT, STATIC_A, LORA, TM, TN>(acc, m0 + wm * (BM / WM), n0 + wn * (BN / WN), M, N,
+                                        a_scale, w_scale, Y, ldy, le);
 }
 
 // ---------------------------------------------------------------------------
@@ -250,11 +293,11 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
 constexpr int kGBM = 128, kGBN = 128;
 constexpr int kGemmThreads = 256;   // 4 waves, 2 x 2, 64 x 64 each
 
-template <int OUT, bool STATIC_A>
+template <int OUT, bool STATIC_A, bool LORA>
 __global__ void __launch_bounds__(kGemmThreads)
 k_gemm_generic(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                const float* __restrict__ a_scale, const float* __restrict__ w_scale, int M, int N,
-               int K, void* __restrict__ Y, int64_t ldy) {
+               int K, void* __restrict__ Y, int64_t ldy, LoraEpi le) {
   __shared__ __attribute__((aligned(16))) char sA[2][kGBM * kBK];
   __shared__ __attribute__((aligned(16))) char sB[2][kGBN * kBK];
 
@@ -341,7 +384,8 @@ k_gemm_generic(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
     __syncthreads();
   }
 
-  epilogue<OUT, STATIC_A, 2, 2>(acc, m0 + wm * 64, n0 + wn * 64, M, N, a_scale, w_scale, Y, ldy);
+  epilogue<OUT, STATIC_A, LORA, 2, 2>(acc, m0 + wm * 64, n0 + wn * 64, M, N, a_scale, w_scale, Y,
+                                      ldy, le);
 }
 
 // ---------------------------------------------------------------------------
@@ -367,56 +411,77 @@ static int pick_cfg(int64_t M, int64_t N, int64_t K) {
   return t256 >= 448 ? CFG_256 : CFG_128;
 }
 
-template <int BM, int BN, int WM, int WN, int OUT, bool STATIC_A, int SCHED>
+template <int BM, int BN, int WM, int WN, int OUT, bool STATIC_A, int SCHED, bool LORA>
 static int launch_pipe(const int8_t* Xq, const int8_t* Wq, const float* a_scale, const float* w_scale,
-                       int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, hipStream_t st) {
+                       int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, const LoraEpi& le,
+                       hipStream_t st) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int64_t blocks = (tiles + 7) / 8 * 8;
-  k_gemm_pipe<BM, BN, WM, WN, OUT, STATIC_A, SCHED><<<(unsigned)blocks, WM * WN * 64, 0, st>>>(
-      Xq, Wq, a_scale, w_scale, (int)M, (int)N, (int)K, Y, ldy);
+  k_gemm_pipe<BM, BN, WM, WN, OUT, STATIC_A, SCHED, LORA><<<(unsigned)blocks, WM * WN * 64, 0, st>>>(
+      Xq, Wq, a_scale, w_scale, (int)M, (int)N, (int)K, Y, ldy, le);
   SQ_LAUNCH_CHECK();
   return SQ_OK;
 }
 
-template <int OUT, bool STATIC_A>
+template <int OUT, bool STATIC_A, bool LORA>
 static int launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* a_scale,
                          const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y,
-                         int64_t ldy, hipStream_t st) {
+                         int64_t ldy, const LoraEpi& le, hipStream_t st) {
   switch (pick_cfg(M, N, K)) {
     case CFG_256:
-      return launch_pipe<256, 256, 2, 4, OUT, STATIC_A, 1>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, st);
+      return launch_pipe<256, 256, 2, 4, OUT, STATIC_A, 1, LORA>(Xq, Wq, a_scale, w_scale, M, N, K, Y,
+                                                                 ldy, le, st);
     case CFG_128:
-      return launch_pipe<128, 128, 2, 2, OUT, STATIC_A, 4>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, st);
+      return launch_pipe<128, 128, 2, 2, OUT, STATIC_A, 4, LORA>(Xq, Wq, a_scale, w_scale, M, N, K, Y,
+                                                                 ldy, le, st);
     default:
       break;
   }
   const int64_t tiles = ((M + kGBM - 1) / kGBM) * ((N + kGBN - 1) / kGBN);
   const int64_t blocks = (tiles + 7) / 8 * 8;
-  k_gemm_generic<OUT, STATIC_A><<<(unsigned)blocks, kGemmThreads, 0, st>>>(
-      Xq, Wq, a_scale, w_scale, (int)M, (int)N, (int)K, Y, ldy);
+  k_gemm_generic<OUT, STATIC_A, LORA><<<(unsigned)blocks, kGemmThreads, 0, st>>>(
+      Xq, Wq, a_scale, w_scale, (int)M, (int)N, (int)K, Y, ldy, le);
   SQ_LAUNCH_CHECK();
   return SQ_OK;
+}
+
+template <bool LORA>
+static int launch_gemm_any(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
+                           const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
+                           int64_t ldy, const LoraEpi& le, hipStream_t st) {
+  if (M == 0) return SQ_OK;
+  const bool stat = mode == SQ_ACT_PER_TENSOR_STATIC;
+#define SQ_GEMM_OUT(O)                                                                               \
+  return stat ? launch_gemm_t<O, true, LORA>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, le, st)      \
+              : launch_gemm_t<O, false, LORA>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, le, st);
+  switch (yt) {
+    case SQ_BF16: SQ_GEMM_OUT(OUT_BF16)
+    case SQ_F16:  SQ_GEMM_OUT(OUT_F16)
+    default:      SQ_GEMM_OUT(OUT_F32)
+  }
+#undef SQ_GEMM_OUT
 }
 
 int launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
                 const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
                 int64_t ldy, hipStream_t st) {
-  if (M == 0) return SQ_OK;
-  const bool stat = mode == SQ_ACT_PER_TENSOR_STATIC;
-  switch (yt) {
-    case SQ_BF16: return stat ? launch_gemm_t<OUT_BF16, true>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, st)
-                              : launch_gemm_t<OUT_BF16, false>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, st);
-    case SQ_F16:  return stat ? launch_gemm_t<OUT_F16, true>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, st)
-                              : launch_gemm_t<OUT_F16, false>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, st);
-    default:      return stat ? launch_gemm_t<OUT_F32, true>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, st)
-                              : launch_gemm_t<OUT_F32, false>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, st);
-  }
+  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f};
+  return launch_gemm_any<false>(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, none, st);
+}
+
+int launch_gemm_lora(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
+                     const float* w_scale, int64_t M, int64_t N, int64_t K, const void* T,
+                     int64_t ldt, const void* B, int r, float scale, void* Y, int yt, int64_t ldy,
+                     hipStream_t st) {
+  const LoraEpi le{(const unsigned short*)T, ldt, (const unsigned short*)B, r, scale};
+  return launch_gemm_any<true>(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, le, st);
 }
 
 int launch_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, int64_t K,
                     int32_t* acc, hipStream_t st) {
   if (M == 0) return SQ_OK;
-  return launch_gemm_t<OUT_I32, false>(Xq, Wq, nullptr, nullptr, M, N, K, acc, N, st);
+  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f};
+  return launch_gemm_t<OUT_I32, false, false>(Xq, Wq, nullptr, nullptr, M, N, K, acc, N, none, st);
 }
 
 }  // namespace sq

@@ -23,6 +23,8 @@
 namespace sq {
 
 constexpr int kLoraThreads = 256;
+constexpr int kMaxRankTiles = SQ_MAX_LORA_RANK / 16;   // rank tiles of 16 in the shrink
+constexpr int kMaxRankSteps = SQ_MAX_LORA_RANK / 32;   // rank steps of 32 in the expand
 
 __device__ __forceinline__ v8bf bits_to_v8bf(uint4 u) { return __builtin_bit_cast(v8bf, u); }
 
@@ -83,9 +85,9 @@ k_lora_shrink(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, LoraA
   const int my_m = m0 + lrow;
   const int NT = (R + 15) / 16;
 
-  v4f acc[4];
+  v4f acc[kMaxRankTiles];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = v4f{0, 0, 0, 0};
+  for (int t = 0; t < kMaxRankTiles; ++t) acc[t] = v4f{0, 0, 0, 0};
 
   int g0 = 0, g1 = 0;
   if constexpr (SEG) {
@@ -103,7 +105,7 @@ k_lora_shrink(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, LoraA
     if constexpr (!SEG) {
       const v8bf xf = bits_to_v8bf(xu);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < kMaxRankTiles; ++t) {
         if (t < NT) {
           const int i = t * 16 + lrow;
           uint4 au = make_uint4(0, 0, 0, 0);
@@ -120,7 +122,7 @@ k_lora_shrink(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, LoraA
         const bool mine = my_m >= la.seg_start[g] && my_m < la.seg_start[g + 1];
         const v8bf xf = bits_to_v8bf(mine ? xu : make_uint4(0, 0, 0, 0));
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < kMaxRankTiles; ++t) {
           if (t < NT) {
             const int i = t * 16 + lrow;
             uint4 au = make_uint4(0, 0, 0, 0);
@@ -135,7 +137,7 @@ k_lora_shrink(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, LoraA
   // Output register j of a 16x16 tile holds row 4*(lane/16) + j, column lane%16.
   float* Ps = P + (int64_t)s * M * R;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < kMaxRankTiles; ++t) {
     if (t < NT) {
       const int i = t * 16 + lrow;
       if (i < R) {
@@ -185,12 +187,13 @@ k_lora_expand(const float* __restrict__ P, int S, int R, int M, int N, LoraArgs 
   const int m0 = blockIdx.x * 16;
   const int lrow = lane & 15, kg = lane >> 4;
   const int my_m = m0 + lrow;
-  const int KS = (R + 31) / 32;        // rank steps of 32 (R <= 64)
+  const int KS = (R + 31) / 32;        // rank steps of 32
 
   // T operand: T[my_m, ks*32 + kg*8 .. +8] = bf16(sum_s P[s, m, .]), fixed order.
-  uint4 tu[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  uint4 tu[kMaxRankSteps];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  for (int ks = 0; ks < kMaxRankSteps; ++ks) {
+    tu[ks] = make_uint4(0, 0, 0, 0);
     const int k = ks * 32 + kg * 8;
     if (ks < KS && k < R && my_m < M) {
       float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -231,7 +234,7 @@ k_lora_expand(const float* __restrict__ P, int S, int R, int M, int N, LoraArgs 
 
     auto accumulate = [&](const unsigned short* Bm, int r, const uint4* tsel) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < kMaxRankSteps; ++ks) {
         if (ks < KS) {
           const int k = ks * 32 + kg * 8;
           const v8bf tf = bits_to_v8bf(tsel[ks]);
@@ -252,9 +255,9 @@ k_lora_expand(const float* __restrict__ P, int S, int R, int M, int N, LoraArgs 
         const int ad = la.seg_adapter[g];
         if (ad < 0) continue;
         const bool mine = my_m >= la.seg_start[g] && my_m < la.seg_start[g + 1];
-        uint4 ts[2];
-        ts[0] = mine ? tu[0] : make_uint4(0, 0, 0, 0);
-        ts[1] = mine ? tu[1] : make_uint4(0, 0, 0, 0);
+        uint4 ts[kMaxRankSteps];
+#pragma unroll
+        for (int ks = 0; ks < kMaxRankSteps; ++ks) ts[ks] = mine ? tu[ks] : make_uint4(0, 0, 0, 0);
         accumulate((const unsigned short*)la.B_ptrs[ad], la.ranks[ad], ts);
       }
     }
@@ -269,6 +272,30 @@ k_lora_expand(const float* __restrict__ P, int S, int R, int M, int N, LoraArgs 
       }
     }
   }
+}
+
+// T[m, i] = bf16(sum_s P[s, m, i]) (fixed order of s) for the fused GEMM
+// epilogue. One thread per 8 consecutive ranks of one row.
+__global__ void __launch_bounds__(256)
+k_lora_reduce(const float* __restrict__ P, int S, int R, int M, unsigned short* __restrict__ T,
+              int64_t ldt) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = R / 8;
+  if (id >= (int64_t)M * per_row) return;
+  const int m = (int)(id / per_row), i = (int)(id % per_row) * 8;
+  float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int s = 0; s < S; ++s) {
+    const float4* p = (const float4*)(P + ((int64_t)s * M + m) * R + i);
+    const float4 a = p[0], b = p[1];
+    t[0] += a.x; t[1] += a.y; t[2] += a.z; t[3] += a.w;
+    t[4] += b.x; t[5] += b.y; t[6] += b.z; t[7] += b.w;
+  }
+  uint4 u;
+  u.x = f32_to_bf16_bits(t[0]) | (f32_to_bf16_bits(t[1]) << 16);
+  u.y = f32_to_bf16_bits(t[2]) | (f32_to_bf16_bits(t[3]) << 16);
+  u.z = f32_to_bf16_bits(t[4]) | (f32_to_bf16_bits(t[5]) << 16);
+  u.w = f32_to_bf16_bits(t[6]) | (f32_to_bf16_bits(t[7]) << 16);
+  *(uint4*)(T + (int64_t)m * ldt + i) = u;
 }
 
 // Split of K for the shrink: enough (row tile, slice) pairs to fill the chip.
@@ -329,6 +356,36 @@ static int launch_lora_any(const void* X, int xt, int64_t M, int64_t K, int64_t 
     default:     SQ_LORA_Y(SQ_BF16)
   }
 #undef SQ_LORA_Y
+}
+
+template <int XT>
+static int launch_shrink_t(const void* X, int64_t M, int64_t K, int64_t ldx, const LoraArgs& la, int R,
+                           unsigned short* T, int64_t ldt, void* ws, hipStream_t st) {
+  int S, kc;
+  lora_split(M, K, &S, &kc);
+  float* P = (float*)ws;
+  dim3 g1((unsigned)((M + 63) / 64), (unsigned)S);
+  k_lora_shrink<XT, false><<<g1, kLoraThreads, 0, st>>>((const char*)X, ldx * DtSize<XT>::v, (int)M,
+                                                        (int)K, la, R, kc, P);
+  SQ_LAUNCH_CHECK();
+  const int64_t threads = M * (R / 8);
+  k_lora_reduce<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(P, S, R, (int)M, T, ldt);
+  SQ_LAUNCH_CHECK();
+  return SQ_OK;
+}
+
+int launch_lora_shrink(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* A,
+                       int r, void* T, int64_t ldt, void* ws, hipStream_t st) {
+  if (M == 0) return SQ_OK;
+  LoraArgs la{};
+  la.A = (const unsigned short*)A;
+  la.r = r;
+  unsigned short* t = (unsigned short*)T;
+  switch (xt) {
+    case SQ_F32: return launch_shrink_t<SQ_F32>(X, M, K, ldx, la, r, t, ldt, ws, st);
+    case SQ_F16: return launch_shrink_t<SQ_F16>(X, M, K, ldx, la, r, t, ldt, ws, st);
+    default:     return launch_shrink_t<SQ_BF16>(X, M, K, ldx, la, r, t, ldt, ws, st);
+  }
 }
 
 int launch_lora(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* A,

@@ -27,6 +27,12 @@ int launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mo
                 int64_t ldy, hipStream_t st);
 int launch_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, int64_t K,
                     int32_t* acc, hipStream_t st);
+int launch_gemm_lora(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
+                     const float* w_scale, int64_t M, int64_t N, int64_t K, const void* T,
+                     int64_t ldt, const void* B, int r, float scale, void* Y, int yt, int64_t ldy,
+                     hipStream_t st);
+int launch_lora_shrink(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* A,
+                       int r, void* T, int64_t ldt, void* ws, hipStream_t st);
 size_t lora_ws_bytes(int64_t M, int64_t K, int R);
 int launch_lora(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* A,
                 const void* B, int r, float scale, void* Y, int yt, int64_t N, int64_t ldy,
@@ -232,6 +238,34 @@ int sq_w8a8_gemm(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int m
   return sq::launch_gemm(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, as_stream(stream));
 }
 
+static int check_rank(int r) {
+  SQ_REQUIRE(r >= 1 && r <= SQ_MAX_LORA_RANK, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(r % 8 == 0, SQ_ERR_MISALIGNED);
+  return SQ_OK;
+}
+
+int sq_w8a8_gemm_lora(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
+                      const float* w_scale, int64_t M, int64_t N, int64_t K, const void* T,
+                      int64_t ldt, const void* B, int r, float scale, void* Y, int yt, int64_t ldy,
+                      void* stream) {
+  int rc = check_gemm(Xq, Wq, M, N, K);
+  if (rc != SQ_OK) return rc;
+  SQ_REQUIRE(valid_mode(mode), SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(a_scale != nullptr && w_scale != nullptr && Y != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(T != nullptr && B != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(valid_dtype(yt), SQ_ERR_UNSUPPORTED_DTYPE);
+  SQ_REQUIRE(ldy >= N, SQ_ERR_INVALID_ARG);
+  if ((rc = check_rank(r)) != SQ_OK) return rc;
+  SQ_REQUIRE(std::isfinite(scale), SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(ldt >= r, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(ldt % 8 == 0 && aligned16(T) && aligned16(B), SQ_ERR_MISALIGNED);
+  SQ_REQUIRE(ldy % 16 == 0 && aligned16(Y) && aligned4(a_scale) && aligned4(w_scale), SQ_ERR_MISALIGNED);
+  if (M == 0) return SQ_OK;
+  if ((rc = gate()) != SQ_OK) return rc;
+  return sq::launch_gemm_lora(Xq, Wq, a_scale, mode, w_scale, M, N, K, T, ldt, B, r, scale, Y, yt,
+                              ldy, as_stream(stream));
+}
+
 int sq_w8a8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, int64_t K,
                      int32_t* acc, void* stream) {
   int rc = check_gemm(Xq, Wq, M, N, K);
@@ -260,6 +294,22 @@ static int check_lora_common(const void* X, int xt, int64_t M, int64_t K, int64_
   SQ_REQUIRE(rank % 8 == 0, SQ_ERR_MISALIGNED);
   SQ_REQUIRE(std::isfinite(scale), SQ_ERR_INVALID_ARG);
   return SQ_OK;
+}
+
+int sq_lora_shrink(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* A, int r,
+                   void* T, int64_t ldt, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_matrix(X, xt, M, K, ldx);
+  if (rc != SQ_OK) return rc;
+  if ((rc = check_rank(r)) != SQ_OK) return rc;
+  SQ_REQUIRE(A != nullptr && T != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(ldt >= r, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(ldt % 8 == 0 && aligned16(A) && aligned16(T), SQ_ERR_MISALIGNED);
+  if (M == 0) return SQ_OK;
+  const size_t need = sq_lora_workspace_bytes(M, K, r);
+  SQ_REQUIRE(ws != nullptr && ws_bytes >= need, SQ_ERR_WORKSPACE);
+  SQ_REQUIRE(aligned16(ws), SQ_ERR_MISALIGNED);
+  if ((rc = gate()) != SQ_OK) return rc;
+  return sq::launch_lora_shrink(X, xt, M, K, ldx, A, r, T, ldt, ws, as_stream(stream));
 }
 
 int sq_lora_apply(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* A,

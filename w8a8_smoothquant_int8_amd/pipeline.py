@@ -1,11 +1,23 @@
 """The SmoothQuant W8A8 linear path for a group of projections sharing one input.
 
-Calibrate -> smooth and fold -> quantize the input -> INT8 GEMM with dequant per
-projection -> bf16 LoRA delta per projection. Projections that read the same
-input (Q/K/V, or gate/up) share one smoothing vector, because the division by
-s is applied to their common input ("SmoothQuant" explainer, "How it works",
-Step 5); their weights are stacked into one [sum N, K] matrix and each GEMM
-runs on its row range at its own shape.
+Calibrate -> smooth and fold -> quantize the input -> INT8 GEMM with dequant ->
+bf16 LoRA delta. Projections that read the same input (Q/K/V, or gate/up)
+share one smoothing vector, because the division by s is applied to their
+common input ("SmoothQuant" explainer, "How it works", Step 5); their weights
+are stacked into one [sum N, K] matrix.
+
+Forward pass (fused, the default): one quantization of the input, one LoRA
+shrink with every projection's A stacked along the rank (X is read once for
+all adapters), and one GEMM over the stacked weights whose epilogue adds the
+LoRA delta. The stacked B is block-diagonal (projection p's rows carry its B
+in its own rank columns and zeros elsewhere), so each output column gets only
+its own adapter's delta, exactly as separate per-projection calls would give.
+Per-projection outputs are column views of one [M, sum N] buffer.
+
+Unfused (fuse=False): one GEMM and one shrink+expand LoRA call per
+projection, the path the fused one is checked against. Per-request
+(segmented) adapters always use the separate segmented call on the column
+views.
 
 This module only sequences calls into libsq and owns the device buffers (all
 allocated once, up front, so the forward pass allocates nothing and can be
@@ -18,9 +30,9 @@ from typing import Dict, List, Optional, Tuple
 
 import torch
 
-from . import (sq_calibrate_absmax, sq_lora_apply, sq_lora_apply_segmented,
-               sq_lora_workspace_bytes, sq_quant_per_token, sq_smooth_fold,
-               sq_static_act_scale, sq_w8a8_gemm)
+from . import (SQ_MAX_LORA_RANK, sq_calibrate_absmax, sq_lora_apply, sq_lora_apply_segmented,
+               sq_lora_shrink, sq_lora_workspace_bytes, sq_quant_per_token, sq_smooth_fold,
+               sq_static_act_scale, sq_w8a8_gemm, sq_w8a8_gemm_lora)
 
 _OUT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
@@ -42,11 +54,12 @@ class LinearGroup:
 
     def __init__(self, W: torch.Tensor, rows: Dict[str, Tuple[int, int]], alpha: float,
                  out_dtype: str, M: int, lora: Optional[Dict[str, Tuple[torch.Tensor, torch.Tensor]]] = None,
-                 seg_lora: Optional[Dict[str, SegmentedLora]] = None, lora_scale: float = 1.0):
+                 seg_lora: Optional[Dict[str, SegmentedLora]] = None, lora_scale: float = 1.0,
+                 fuse: bool = True):
         dev = W.device
         self.W, self.rows, self.alpha, self.M = W, rows, float(alpha), int(M)
         Ntot, K = W.shape
-        self.K = K
+        self.K, self.Ntot = K, Ntot
         self.act_max = torch.zeros(K, dtype=torch.float32, device=dev)
         self.s = torch.empty(K, dtype=torch.float32, device=dev)
         self.Wq = torch.empty(Ntot, K, dtype=torch.int8, device=dev)
@@ -54,12 +67,30 @@ class LinearGroup:
         self.Xq = torch.empty(self.M, K, dtype=torch.int8, device=dev)
         self.a_scale = torch.empty(max(self.M, 1), dtype=torch.float32, device=dev)
         self.static_scale = torch.empty(1, dtype=torch.float32, device=dev)
-        self.Y = {p: torch.empty(self.M, r1 - r0, dtype=_OUT[out_dtype], device=dev)
-                  for p, (r0, r1) in rows.items()}
+        self.Yg = torch.empty(self.M, Ntot, dtype=_OUT[out_dtype], device=dev)
+        self.Y = {p: self.Yg[:, r0:r1] for p, (r0, r1) in rows.items()}
         self.lora = lora or {}
         self.seg_lora = seg_lora or {}
         self.lora_scale = float(lora_scale)
-        ranks = [a.shape[0] for a, _ in self.lora.values()] + [s.max_rank for s in self.seg_lora.values()]
+
+        # Stacked LoRA for the fused path: every projection has an adapter and
+        # the total rank fits one call.
+        r_tot = sum(a.shape[0] for a, _ in self.lora.values())
+        self.fused = bool(fuse and self.lora and set(self.lora) == set(rows)
+                          and r_tot <= SQ_MAX_LORA_RANK)
+        if self.fused:
+            order = list(rows)
+            self.A_stack = torch.cat([self.lora[p][0] for p in order], dim=0).contiguous()
+            self.B_blk = torch.zeros(Ntot, r_tot, dtype=torch.bfloat16, device=dev)
+            c = 0
+            for p in order:
+                A, B = self.lora[p]
+                r0, r1 = rows[p]
+                self.B_blk[r0:r1, c:c + A.shape[0]] = B
+                c += A.shape[0]
+            self.T = torch.empty(self.M, r_tot, dtype=torch.bfloat16, device=dev)
+        ranks = ([r_tot] if self.fused else [a.shape[0] for a, _ in self.lora.values()]) + \
+                [s.max_rank for s in self.seg_lora.values()]
         wsb = sq_lora_workspace_bytes(self.M, K, max(ranks)) if ranks and self.M else 0
         self.ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
 
@@ -74,17 +105,33 @@ class LinearGroup:
         sq_static_act_scale(self.act_max, self.s, self.static_scale)
 
     # -- per batch ----------------------------------------------------------
+    def _a(self, mode: str) -> torch.Tensor:
+        return self.a_scale if mode == "dynamic" else self.static_scale
+
     def quantize(self, X: torch.Tensor, mode: str = "dynamic") -> None:
-        a = self.a_scale if mode == "dynamic" else self.static_scale
-        sq_quant_per_token(X, self.s, self.Xq, a, mode=mode)
+        sq_quant_per_token(X, self.s, self.Xq, self._a(mode), mode=mode)
 
     def gemm(self, proj: str, mode: str = "dynamic") -> torch.Tensor:
+        """One projection's GEMM without LoRA."""
         r0, r1 = self.rows[proj]
-        a = self.a_scale if mode == "dynamic" else self.static_scale
-        sq_w8a8_gemm(self.Xq, self.Wq[r0:r1], a, self.w_scale[r0:r1], self.Y[proj], mode=mode)
+        sq_w8a8_gemm(self.Xq, self.Wq[r0:r1], self._a(mode), self.w_scale[r0:r1], self.Y[proj],
+                     mode=mode)
         return self.Y[proj]
 
+    def gemm_all(self, mode: str = "dynamic") -> None:
+        """All projections' GEMMs as one call over the stacked weights, without LoRA."""
+        sq_w8a8_gemm(self.Xq, self.Wq, self._a(mode), self.w_scale, self.Yg, mode=mode)
+
+    def lora_shrink(self, X: torch.Tensor) -> None:
+        sq_lora_shrink(X, self.A_stack, self.T, self.ws)
+
+    def gemm_all_lora(self, mode: str = "dynamic") -> None:
+        """All projections' GEMMs as one call, each adding its LoRA delta in the epilogue."""
+        sq_w8a8_gemm_lora(self.Xq, self.Wq, self._a(mode), self.w_scale, self.T, self.B_blk,
+                          self.Yg, scale=self.lora_scale, mode=mode)
+
     def apply_lora(self, proj: str, X: torch.Tensor) -> None:
+        """One projection's LoRA delta as a separate shrink + expand call."""
         if proj in self.lora:
             A, B = self.lora[proj]
             sq_lora_apply(X, A, B, self.Y[proj], self.ws, scale=self.lora_scale)
@@ -95,7 +142,15 @@ class LinearGroup:
 
     def forward(self, X: torch.Tensor, mode: str = "dynamic") -> Dict[str, torch.Tensor]:
         self.quantize(X, mode)
-        for p in self.rows:
-            self.gemm(p, mode)
-            self.apply_lora(p, X)
+        if self.fused:
+            self.lora_shrink(X)
+            self.gemm_all_lora(mode)
+        elif self.lora:
+            for p in self.rows:
+                self.gemm(p, mode)
+                self.apply_lora(p, X)
+        else:
+            self.gemm_all(mode)
+            for p in self.seg_lora:
+                self.apply_lora(p, X)
         return self.Y
