@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=128,
                     help="activation rows per input in the CPU-oracle sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the timed region, run one plain device copy of this many MiB "
+                         "(a kernel of known traffic, to scale rocprofv3 byte counters)")
     return ap.parse_args()
 
 
@@ -202,6 +205,13 @@ def main():
         raise SystemExit("device 0 is not gfx950")
     wl = get_workload(args.workload)
     groups = setup(wl, torch)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         run_step(groups)
     torch.cuda.synchronize()

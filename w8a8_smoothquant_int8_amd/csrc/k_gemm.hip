@@ -49,30 +49,6 @@ struct LoraEpi {
   float scale;
 };
 
-template <int OUT, bool LORA>
-__device__ __forceinline__ void store_out(void* Y, int64_t ldy, int64_t m, int64_t n, int acc,
-                                          float as, float ws, float d, float lscale) {
-  if constexpr (OUT == OUT_I32) {
-    ((int32_t*)Y)[m * ldy + n] = acc;
-  } else {
-    float y = ((float)acc * as) * ws;              // two fp32 roundings, left to right
-    if constexpr (OUT == OUT_F32) {
-      if constexpr (LORA) y = y + lscale * d;
-      ((float*)Y)[m * ldy + n] = y;
-    } else {
-      uint32_t h = OUT == OUT_BF16 ? f32_to_bf16_bits(y) : f32_to_f16_bits(y);
-      if constexpr (LORA) {
-        // the GEMM output is rounded to the output type first; the delta is
-        // added to that rounded value and the sum rounded again
-        const float yr = OUT == OUT_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
-        const float z = yr + lscale * d;
-        h = OUT == OUT_BF16 ? f32_to_bf16_bits(z) : f32_to_f16_bits(z);
-      }
-      ((unsigned short*)Y)[m * ldy + n] = (unsigned short)h;
-    }
-  }
-}
-
 // Map a block to its (tile_m, tile_n), grouping tiles by XCD. Returns false
 // for padding blocks beyond the last tile.
 // Within the tile order, tiles go in groups of kGroupM tile rows: a group
@@ -97,50 +73,139 @@ constexpr int kBK = 128;          // K-tile in bytes
 
 // Epilogue shared by both kernels: acc[i][j] is the 32x32 MFMA tile at rows
 // row0 + 32 i, columns col0 + 32 j. Output register q of a 32x32 tile holds
-// row 8*(q/4) + 4*(lane/32) + q%4 and column lane%32. With LORA, the rank-r
-// product for the same tile comes from V_MFMA_F32_32X32X16_BF16, whose output
-// has the same layout (T rows in the first operand, B rows in the second), so
-// it lines up register for register with the INT32 accumulators. The MFMAs run
-// in uniform control flow; rows and columns past M and N read clamped
-// (valid) addresses and are never stored.
-template <int OUT, bool STATIC_A, bool LORA, int TM, int TN>
-__device__ __forceinline__ void epilogue(const v16i (&acc)[TM][TN], int row0, int col0, int M, int N,
+// row 8*(q/4) + 4*(lane/32) + q%4 and column lane%32.
+//
+// With LORA, the rank-r product for the same tile comes from
+// V_MFMA_F32_32X32X16_BF16 (T rows as the first operand, B rows as the
+// second), whose output has that same layout, so it lines up register for
+// register with the INT32 accumulators. When scale is 1 the accumulators are
+// first turned in place into the output-rounded GEMM values, and the bf16
+// MFMAs accumulate T B^T straight onto them: no extra registers, and every
+// fragment of a 32-rank chunk is loaded at once. Other scales keep a separate
+// delta per tile. The MFMAs run in uniform control flow; rows and columns past
+// M and N read clamped (valid) addresses and are never stored.
+template <int OUT>
+__device__ __forceinline__ float round_out(float y) {
+  if constexpr (OUT == OUT_BF16) return bf16_bits_to_f32(f32_to_bf16_bits(y));
+  else if constexpr (OUT == OUT_F16) return f16_bits_to_f32(f32_to_f16_bits(y));
+  else return y;
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_val(void* Y, int64_t ldy, int64_t m, int64_t n, float y) {
+  if constexpr (OUT == OUT_F32) ((float*)Y)[m * ldy + n] = y;
+  else if constexpr (OUT == OUT_BF16) ((unsigned short*)Y)[m * ldy + n] = (unsigned short)f32_to_bf16_bits(y);
+  else ((unsigned short*)Y)[m * ldy + n] = (unsigned short)f32_to_f16_bits(y);
+}
+
+// LORA: 0 none, 1 LoRA delta with scale 1 (accumulated onto y in place),
+// 2 LoRA delta with any scale (separate delta per tile).
+template <int OUT, bool STATIC_A, int LORA, int TM, int TN>
+__device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], int row0, int col0, int M, int N,
                                          const float* __restrict__ a_scale,
                                          const float* __restrict__ w_scale, void* __restrict__ Y,
                                          int64_t ldy, const LoraEpi& le) {
   const int lane = threadIdx.x & 63;
   const int lrow = lane & 31, lhalf = lane >> 5;
   const float as_static = (STATIC_A && OUT != OUT_I32) ? a_scale[0] : 0.0f;
+  if constexpr (LORA == 2 || OUT == OUT_I32) {
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int n = col0 + j * 32 + lrow;
-    const bool n_ok = n < N;
-    const float ws = (OUT != OUT_I32 && n_ok) ? w_scale[n] : 0.0f;
+    for (int j = 0; j < TN; ++j) {
+      const int n = col0 + j * 32 + lrow;
+      const bool n_ok = n < N;
+      const float ws = (OUT != OUT_I32 && n_ok) ? w_scale[n] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      v16f d = {};
-      if constexpr (LORA) {
-        const int64_t mr = row0 + i * 32 + lrow < M ? row0 + i * 32 + lrow : M - 1;
-        const int64_t nr = n_ok ? n : N - 1;
-        for (int k0 = 0; k0 < le.r; k0 += 16) {
-          const int k = k0 + 8 * lhalf;
-          uint4 tu = make_uint4(0, 0, 0, 0), bu = make_uint4(0, 0, 0, 0);
-          if (k < le.r) {
-            tu = *(const uint4*)(le.T + mr * le.ldt + k);
-            bu = *(const uint4*)(le.B + nr * le.r + k);
+      for (int i = 0; i < TM; ++i) {
+        v16f d = {};
+        if constexpr (LORA == 2) {
+          const int64_t mr = row0 + i * 32 + lrow < M ? row0 + i * 32 + lrow : M - 1;
+          const int64_t nr = n_ok ? n : N - 1;
+          for (int k0 = 0; k0 < le.r; k0 += 16) {
+            const int k = k0 + 8 * lhalf;
+            uint4 tu = make_uint4(0, 0, 0, 0), bu = make_uint4(0, 0, 0, 0);
+            if (k < le.r) {
+              tu = *(const uint4*)(le.T + mr * le.ldt + k);
+              bu = *(const uint4*)(le.B + nr * le.r + k);
+            }
+            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, tu),
+                                                        __builtin_bit_cast(v8bf, bu), d, 0, 0, 0);
           }
-          d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, tu),
-                                                      __builtin_bit_cast(v8bf, bu), d, 0, 0, 0);
+        }
+        if (n_ok) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int m = row0 + i * 32 + 8 * (q >> 2) + 4 * lhalf + (q & 3);
+            if (m < M) {
+              if constexpr (OUT == OUT_I32) {
+                ((int32_t*)Y)[(int64_t)m * ldy + n] = acc[i][j][q];
+              } else {
+                const float as = STATIC_A ? as_static : a_scale[m];
+                float y = ((float)acc[i][j][q] * as) * ws;   // two fp32 roundings, left to right
+                if constexpr (LORA == 2) y = round_out<OUT>(y) + le.scale * d[q];
+                store_val<OUT>(Y, ldy, m, n, y);
+              }
+            }
+          }
         }
       }
-      if (n_ok) {
+    }
+  } else if constexpr (OUT != OUT_I32) {
+    // No LoRA, or LoRA with scale 1: y takes over the accumulators' registers
+    // (the float bits are kept in the same vectors); with LoRA, y += T B^T on
+    // the matrix cores; then all stores.
+    // Row-block outer, so only one row block's 16 a_scale values are live.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      float as[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = row0 + i * 32 + 8 * (q >> 2) + 4 * lhalf + (q & 3);
+        as[q] = STATIC_A ? as_static : (m < M ? a_scale[m] : 0.0f);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = col0 + j * 32 + lrow;
+        const float ws = n < N ? w_scale[n] : 0.0f;
+        v16f t;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) t[q] = round_out<OUT>(((float)acc[i][j][q] * as[q]) * ws);
+        acc[i][j] = __builtin_bit_cast(v16i, t);
+      }
+    }
+    for (int k0 = 0; LORA == 1 && k0 < le.r; k0 += 16) {
+      const int k = k0 + 8 * lhalf;
+      const bool kin = k < le.r;
+      uint4 tf[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int64_t mr = row0 + i * 32 + lrow < M ? row0 + i * 32 + lrow : M - 1;
+        tf[i] = kin ? *(const uint4*)(le.T + mr * le.ldt + k) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t nr = col0 + j * 32 + lrow < N ? col0 + j * 32 + lrow : N - 1;
+        bf[j] = kin ? *(const uint4*)(le.B + nr * le.r + k) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_bit_cast(
+              v16i, __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, tf[i]),
+                                                            __builtin_bit_cast(v8bf, bf[j]),
+                                                            __builtin_bit_cast(v16f, acc[i][j]),
+                                                            0, 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = col0 + j * 32 + lrow;
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int m = row0 + i * 32 + 8 * (q >> 2) + 4 * lhalf + (q & 3);
-          if (m < M) {
-            const float as = OUT == OUT_I32 ? 0.0f : (STATIC_A ? as_static : a_scale[m]);
-            store_out<OUT, LORA>(Y, ldy, m, n, acc[i][j][q], as, ws, d[q], le.scale);
-          }
+          if (m < M) store_val<OUT>(Y, ldy, m, n, __builtin_bit_cast(v16f, acc[i][j])[q]);
         }
       }
     }
@@ -161,7 +226,7 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[TM][TN], int row0, in
 // direct loads of the next tile (vmcnt) and its reads of this tile (lgkmcnt),
 // then all waves meet.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int OUT, bool STATIC_A, int SCHED, bool LORA>
+template <int BM, int BN, int WM, int WN, int OUT, bool STATIC_A, int SCHED, int LORA>
 __global__ void __launch_bounds__(WM * WN * 64)
 k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
             const float* __restrict__ a_scale, const float* __restrict__ w_scale, int M, int N,
@@ -293,7 +358,7 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
 constexpr int kGBM = 128, kGBN = 128;
 constexpr int kGemmThreads = 256;   // 4 waves, 2 x 2, 64 x 64 each
 
-template <int OUT, bool STATIC_A, bool LORA>
+template <int OUT, bool STATIC_A, int LORA>
 __global__ void __launch_bounds__(kGemmThreads)
 k_gemm_generic(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                const float* __restrict__ a_scale, const float* __restrict__ w_scale, int M, int N,
@@ -392,12 +457,22 @@ k_gemm_generic(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
 // Host side: pick a kernel and tile for the shape.
 // ---------------------------------------------------------------------------
 // Tile configurations (measured on MI355X over the workload shapes):
-//   CFG_256: 256x256 tiles, 8 waves of 128x64, SCHED 1 - best once there are
-//            at least ~1.75 tiles per CU (256x256 tiles read the least L2 data
-//            per operation);
-//   CFG_128: 128x128 tiles, 4 waves of 64x64, SCHED 4 - best for fewer tiles
-//            (keeps all 256 CUs busy at M = 2048 and for small M).
+//   CFG_256: 256x256 tiles, 8 waves of 128x64, SCHED 1 - the faster one at
+//            full occupancy (256x256 tiles read the least L2 data per op);
+//   CFG_128: 128x128 tiles, 4 waves of 64x64, SCHED 4 - wins when 256x256
+//            tiles would leave CUs idle in the last round or pad small M.
 enum TileCfg { CFG_GENERIC = 0, CFG_256 = 1, CFG_128 = 2 };
+
+// Score of a tile configuration: the share of the launched tile work that is
+// useful (rows and columns padded up to whole tiles, and the last round of
+// tiles over the chip's resident blocks) times the configuration's measured
+// relative throughput at full occupancy.
+static double tile_score(int64_t M, int64_t N, int64_t bm, int64_t bn, int64_t resident, double rate) {
+  const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn, tiles = tm * tn;
+  const int64_t rounds = (tiles + resident - 1) / resident;
+  const double pad = (double)M / (double)(tm * bm) * (double)N / (double)(tn * bn);
+  return rate * pad * (double)tiles / (double)(rounds * resident);
+}
 
 static int pick_cfg(int64_t M, int64_t N, int64_t K) {
   if (K % kBK != 0 || M * K >= (1LL << 32) || N * K >= (1LL << 32)) return CFG_GENERIC;
@@ -407,11 +482,13 @@ static int pick_cfg(int64_t M, int64_t N, int64_t K) {
     const int o = std::atoi(e);
     if (o >= 0 && o <= 2) return o;
   }
-  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  return t256 >= 448 ? CFG_256 : CFG_128;
+  // 256 CUs: one 256x256 block per CU, two 128x128 blocks per CU.
+  const double s256 = tile_score(M, N, 256, 256, 256, 1.0);
+  const double s128 = tile_score(M, N, 128, 128, 512, 0.9);
+  return s256 >= s128 ? CFG_256 : CFG_128;
 }
 
-template <int BM, int BN, int WM, int WN, int OUT, bool STATIC_A, int SCHED, bool LORA>
+template <int BM, int BN, int WM, int WN, int OUT, bool STATIC_A, int SCHED, int LORA>
 static int launch_pipe(const int8_t* Xq, const int8_t* Wq, const float* a_scale, const float* w_scale,
                        int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, const LoraEpi& le,
                        hipStream_t st) {
@@ -423,7 +500,7 @@ static int launch_pipe(const int8_t* Xq, const int8_t* Wq, const float* a_scale,
   return SQ_OK;
 }
 
-template <int OUT, bool STATIC_A, bool LORA>
+template <int OUT, bool STATIC_A, int LORA>
 static int launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* a_scale,
                          const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y,
                          int64_t ldy, const LoraEpi& le, hipStream_t st) {
@@ -445,7 +522,7 @@ static int launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* a_scal
   return SQ_OK;
 }
 
-template <bool LORA>
+template <int LORA>
 static int launch_gemm_any(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
                            const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
                            int64_t ldy, const LoraEpi& le, hipStream_t st) {
@@ -466,7 +543,7 @@ int launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mo
                 const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
                 int64_t ldy, hipStream_t st) {
   const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f};
-  return launch_gemm_any<false>(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, none, st);
+  return launch_gemm_any<0>(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, none, st);
 }
 
 int launch_gemm_lora(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
@@ -474,14 +551,16 @@ int launch_gemm_lora(const int8_t* Xq, const int8_t* Wq, const float* a_scale, i
                      int64_t ldt, const void* B, int r, float scale, void* Y, int yt, int64_t ldy,
                      hipStream_t st) {
   const LoraEpi le{(const unsigned short*)T, ldt, (const unsigned short*)B, r, scale};
-  return launch_gemm_any<true>(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, le, st);
+  if (scale == 1.0f)
+    return launch_gemm_any<1>(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, le, st);
+  return launch_gemm_any<2>(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, le, st);
 }
 
 int launch_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, int64_t K,
                     int32_t* acc, hipStream_t st) {
   if (M == 0) return SQ_OK;
   const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f};
-  return launch_gemm_t<OUT_I32, false, false>(Xq, Wq, nullptr, nullptr, M, N, K, acc, N, none, st);
+  return launch_gemm_t<OUT_I32, false, 0>(Xq, Wq, nullptr, nullptr, M, N, K, acc, N, none, st);
 }
 
 }  // namespace sq
