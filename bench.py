@@ -136,13 +136,25 @@ def run_step(groups, tl=None):
     mark(None)
 
 
+def _tile_score(M, N, bm, bn, resident, rate):
+    tm, tn = -(-M // bm), -(-N // bn)
+    tiles = tm * tn
+    rounds = -(-tiles // resident)
+    pad = (M / (tm * bm)) * (N / (tn * bn))
+    return rate * pad * tiles / (rounds * resident)
+
+
 def gemm_tile(M: int, N: int, K: int) -> str:
     """The tile configuration libsq picks for an INT8 GEMM of this shape (the
-    library's rule: 256x256 tiles when there are at least 448 of them, else
-    128x128; K not a multiple of 128 takes the generic kernel)."""
-    if K % 128:
+    library's rule: the generic kernel when K is not a multiple of 128 or an
+    operand reaches 4 GiB, else the better of 256x256 tiles, one block per CU,
+    and 128x128 tiles, two blocks per CU at 0.9 of the per-tile rate, scored by
+    the fraction of the last round of blocks that does useful work)."""
+    if K % 128 or M * K >= 1 << 32 or N * K >= 1 << 32:
         return "generic"
-    return "256x256" if ((M + 255) // 256) * ((N + 255) // 256) >= 448 else "128x128"
+    s256 = _tile_score(M, N, 256, 256, 256, 1.0)
+    s128 = _tile_score(M, N, 128, 128, 512, 0.9)
+    return "256x256" if s256 >= s128 else "128x128"
 
 
 def cpu_baseline(wl, rows_per_input: int):

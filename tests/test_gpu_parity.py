@@ -363,10 +363,12 @@ def test_repeat_runs_are_bitwise_identical():
 # ---------------------------------------------------------------------------
 # Fused path: stacked shrink, LoRA delta in the GEMM epilogue
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("r", [8, 48, 128])
+@pytest.mark.parametrize("r", [8, 24, 48, 128])
 @pytest.mark.parametrize("xdt", ["bf16", "f32", "f16"])
-@pytest.mark.parametrize("M,K", [(1, 16), (33, 272), (300, 4096)])
+@pytest.mark.parametrize("M,K", [(1, 16), (33, 272), (300, 4096), (2048, 14336), (4096, 4368)])
 def test_lora_shrink(r, xdt, M, K):
+    """Covers one and two row tiles per wave, one and several k-chunks per
+    slice, a K tail inside a chunk and a last rank tile that is partly empty."""
     rng = np.random.default_rng(r * 7 + M + K)
     x, xn = acts(rng, M, K, xdt, factor=20.0)
     a = cast_to(rng.normal(0, 0.01, (r, K)).astype(F32), "bf16")

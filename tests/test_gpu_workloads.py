@@ -76,7 +76,8 @@ def check_group(wl, inp, seed=0):
             segs[p] = sl
             host[p] = (seg, [t.float().numpy() for t in As], [t.float().numpy() for t in Bs])
     Xd = X.cuda()
-    g = LinearGroup(W.cuda(), rows, wl.alpha, wl.out_dtype, wl.M, lora=loras, seg_lora=segs)
+    g = LinearGroup(W.cuda(), rows, wl.alpha, wl.out_dtype, wl.M, lora=loras, seg_lora=segs,
+                    modes=wl.act_modes)
     g.calibrate(Xc.cuda())
     g.fold()
     torch.cuda.synchronize()

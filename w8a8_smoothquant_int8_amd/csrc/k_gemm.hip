@@ -29,8 +29,6 @@ namespace sq {
 
 enum OutKind { OUT_I32 = 0, OUT_BF16 = 1, OUT_F16 = 2, OUT_F32 = 3 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 // LDS position of 16-byte chunk c of tile row r (rows are 128 bytes). gfx950
 // LDS has 64 banks (256 bytes); a 16-byte read serves 16 lanes per cycle. The
 // MFMA operand read has 16 lanes reading the same logical chunk of 16

@@ -7,10 +7,11 @@
 //
 // Both are dense contractions and run on the gfx950 bf16 matrix instruction
 // V_MFMA_F32_16X16X32_BF16. The shrink reads X once and is HBM-bound; with
-// only M/16 row tiles it splits K into S slices so enough waves stream X, and
-// writes fp32 partial sums to the caller's workspace. There is no atomic: the
-// expand sums the S partials in a fixed order, so results are reproducible
-// bit for bit. The expand's traffic is the read-modify-write of Y; it computes
+// few row blocks at small M it splits K into S slices so enough blocks stream
+// X, and writes fp32 partial sums to the caller's workspace. There is no
+// atomic: the expand (or, for the fused GEMM epilogue, a small reduce kernel)
+// sums the S partials in a fixed order, so results are reproducible bit for
+// bit. The expand's traffic is the read-modify-write of Y; it computes
 // the transposed product (B rows as the first operand) so every lane owns 4
 // consecutive columns of one row of Y (8-byte accesses for bf16).
 //
@@ -69,11 +70,125 @@ struct LoraArgs {
   const int32_t* ranks;
 };
 
-// grid: (ceil(M / 64), S); 4 waves, each a 16-row tile of its K slice.
-template <int XT, bool SEG>
+// Single-adapter shrink, written as partial sums P[s] over groups of k-chunks.
+//
+// grid: (ceil(M / (64 * RT)), S). A block has 4 waves; wave w owns RT row
+// tiles of 16 rows (rows m0 + 16 * rt + 0..15), so a block covers 64 * RT
+// rows. The block visits k-chunks c = blockIdx.y, blockIdx.y + S, ... of
+// KC = 32 * KS elements. For each chunk it stages A[0:R, chunk] in LDS once
+// for all its waves (direct global-to-LDS loads) while each wave loads its
+// rows' X for the chunk into registers, all in flight together; then every
+// 16-row rank tile of A is read from LDS once per k-step and multiplied with
+// each of the wave's row tiles.
+//
+// LDS layout of the staged chunk: row i of A at i * KC * 2 bytes, its 16-byte
+// slot p holding k-chunk p ^ (i & 15). Rows are a multiple of 256 bytes long,
+// so the 16 lanes of one fragment read (rows 16t + 0..15, one logical slot)
+// land on 16 distinct 16-byte bank groups: all 64 banks, no conflict.
+//
+// The product is computed transposed (A rows as the first MFMA operand), so a
+// lane's 4 output registers are 4 consecutive ranks of one row: one 16-byte
+// store into P[s, m, i..i+3].
+template <int XT, int KS, int RT, int NT>
 __global__ void __launch_bounds__(kLoraThreads)
-k_lora_shrink(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, LoraArgs la, int R,
-              int kchunk, float* __restrict__ P) {
+k_lora_shrink(const char* __restrict__ X, int64_t ldx_bytes, int M, int K,
+              const unsigned short* __restrict__ A, int R, int S, float* __restrict__ P) {
+  extern __shared__ __attribute__((aligned(1024))) char lds_a[];   // R x KC bf16
+  constexpr int KC = 32 * KS;        // k elements per chunk
+  constexpr int CPR = KC / 8;        // 16-byte slots per staged row (32 or 16)
+  constexpr int RPI = 64 / CPR;      // staged rows per direct load (2 or 4)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lrow = lane & 15, kg = lane >> 4;
+  const int nI = R / RPI;            // direct loads per chunk (R % 8 == 0)
+  const int nchunks = (K + KC - 1) / KC;
+  const int m0 = blockIdx.x * (64 * RT) + wave * (16 * RT);
+
+  // Rows past M read row M - 1; their sums are never stored.
+  const char* xrow[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    int m = m0 + rt * 16 + lrow;
+    m = m < M ? m : M - 1;
+    xrow[rt] = X + (int64_t)m * ldx_bytes;
+  }
+
+  v4f acc[RT][NT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[rt][t] = v4f{0, 0, 0, 0};
+
+#pragma unroll 1
+  for (int c = blockIdx.y; c < nchunks; c += S) {
+    const int kc0 = c * KC;
+    __syncthreads();   // every wave is done reading the previous chunk
+    // A chunk -> LDS. Load j moves staged rows j * RPI .. + RPI - 1; lane l
+    // fills slot l % CPR of row j * RPI + l / CPR with the k-chunk that
+    // belongs there. Slots past K read a valid chunk and are zeroed on use.
+    for (int j = wave; j < nI; j += 4) {
+      const int i = j * RPI + lane / CPR;
+      const int kk = kc0 + ((lane % CPR) ^ (i & 15)) * 8;
+      const int ksrc = kk < K ? kk : K - 8;
+      __builtin_amdgcn_global_load_lds((const void*)(A + (int64_t)i * K + ksrc),
+                                       (lds_ptr_t)(lds_a + 1024 * j), 16, 0, 0);
+    }
+    uint4 xu[RT][KS];
+#pragma unroll
+    for (int u = 0; u < KS; ++u) {
+      const int kk = kc0 + u * 32 + kg * 8;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        xu[rt][u] = kk < K ? load8_as_bf16<XT>(xrow[rt] + (int64_t)kk * DtSize<XT>::v)
+                           : make_uint4(0, 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): the chunk is in LDS
+    __syncthreads();
+
+    // Rank rows past R (the last tile of a rank that is not a multiple of
+    // 16) and slots past K read staged row R - 1 and are replaced by zeros.
+#pragma unroll
+    for (int u = 0; u < KS; ++u) {
+      const int slot = u * 4 + kg;
+      const bool kin = kc0 + slot * 8 < K;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int i = t * 16 + lrow;
+        const int ic = i < R ? i : R - 1;
+        uint4 au = *(const uint4*)(lds_a + ic * (KC * 2) + ((slot ^ (ic & 15)) << 4));
+        if (!(kin && i < R)) au = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_v8bf(au),
+                                                              bits_to_v8bf(xu[rt][u]),
+                                                              acc[rt][t], 0, 0, 0);
+      }
+    }
+  }
+
+  // Register j of rank tile t: rank 16 t + 4 (lane / 16) + j, row lane % 16.
+  float* Ps = P + (int64_t)blockIdx.y * M * R;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int m = m0 + rt * 16 + lrow;
+    if (m >= M) continue;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int i = t * 16 + kg * 4;
+      if (i < R)
+        *(float4*)(Ps + (int64_t)m * R + i) =
+            make_float4(acc[rt][t][0], acc[rt][t][1], acc[rt][t][2], acc[rt][t][3]);
+    }
+  }
+}
+
+// Segmented shrink. grid: (ceil(M / 64), S); 4 waves, each a 16-row tile of
+// its K slice. A fragments come straight from global memory (L2): the
+// adapter can change from one row tile to the next.
+template <int XT>
+__global__ void __launch_bounds__(kLoraThreads)
+k_lora_shrink_seg(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, LoraArgs la, int R,
+                  int kchunk, float* __restrict__ P) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int m0 = blockIdx.x * 64 + wave * 16;
@@ -89,10 +204,9 @@ k_lora_shrink(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, LoraA
 #pragma unroll
   for (int t = 0; t < kMaxRankTiles; ++t) acc[t] = v4f{0, 0, 0, 0};
 
-  int g0 = 0, g1 = 0;
-  if constexpr (SEG) {
-    g0 = find_segment(la.seg_start, la.nseg, m0);
-    g1 = g0;
+  const int g0 = find_segment(la.seg_start, la.nseg, m0);
+  int g1 = g0;
+  {
     const int mend = m0 + 16 < M ? m0 + 16 : M;
     while (g1 + 1 < la.nseg && la.seg_start[g1 + 1] < mend) ++g1;
   }
@@ -102,33 +216,20 @@ k_lora_shrink(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, LoraA
     const bool kin = kk < ke;
     uint4 xu = make_uint4(0, 0, 0, 0);
     if (kin && my_m < M) xu = load8_as_bf16<XT>(X + (int64_t)my_m * ldx_bytes + (int64_t)kk * DtSize<XT>::v);
-    if constexpr (!SEG) {
-      const v8bf xf = bits_to_v8bf(xu);
+    for (int g = g0; g <= g1; ++g) {
+      const int ad = la.seg_adapter[g];
+      if (ad < 0) continue;
+      const int ra = la.ranks[ad];
+      const unsigned short* Ag = (const unsigned short*)la.A_ptrs[ad];
+      const bool mine = my_m >= la.seg_start[g] && my_m < la.seg_start[g + 1];
+      const v8bf xf = bits_to_v8bf(mine ? xu : make_uint4(0, 0, 0, 0));
 #pragma unroll
       for (int t = 0; t < kMaxRankTiles; ++t) {
         if (t < NT) {
           const int i = t * 16 + lrow;
           uint4 au = make_uint4(0, 0, 0, 0);
-          if (kin && i < la.r) au = *(const uint4*)(la.A + (int64_t)i * K + kk);
+          if (kin && i < ra) au = *(const uint4*)(Ag + (int64_t)i * K + kk);
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, bits_to_v8bf(au), acc[t], 0, 0, 0);
-        }
-      }
-    } else {
-      for (int g = g0; g <= g1; ++g) {
-        const int ad = la.seg_adapter[g];
-        if (ad < 0) continue;
-        const int ra = la.ranks[ad];
-        const unsigned short* Ag = (const unsigned short*)la.A_ptrs[ad];
-        const bool mine = my_m >= la.seg_start[g] && my_m < la.seg_start[g + 1];
-        const v8bf xf = bits_to_v8bf(mine ? xu : make_uint4(0, 0, 0, 0));
-#pragma unroll
-        for (int t = 0; t < kMaxRankTiles; ++t) {
-          if (t < NT) {
-            const int i = t * 16 + lrow;
-            uint4 au = make_uint4(0, 0, 0, 0);
-            if (kin && i < ra) au = *(const uint4*)(Ag + (int64_t)i * K + kk);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, bits_to_v8bf(au), acc[t], 0, 0, 0);
-          }
         }
       }
     }
@@ -298,8 +399,39 @@ k_lora_reduce(const float* __restrict__ P, int S, int R, int M, unsigned short* 
   *(uint4*)(T + (int64_t)m * ldt + i) = u;
 }
 
-// Split of K for the shrink: enough (row tile, slice) pairs to fill the chip.
-static void lora_split(int64_t M, int64_t K, int* S, int* kchunk) {
+// Launch plan of the single-adapter shrink. KC = 256 (8 k-steps) when the
+// staged A chunk (R x KC bf16) fits in 32 KB, else 128. Two row tiles per
+// wave (A fragments read from LDS serve 32 rows) unless that leaves fewer
+// than ~512 (row block, chunk) pairs. S slices, each a strided set of J
+// chunks: S <= 32 bounds the partial sums at 32 * M * R fp32.
+struct ShrinkPlan {
+  int ks, rt, nt, S;   // nt: rank tiles of 16, rounded up to 1, 2, 4 or 8
+  int64_t blocks_m;
+};
+
+static ShrinkPlan plan_shrink(int64_t M, int64_t K, int R) {
+  ShrinkPlan p;
+  p.ks = R <= 64 ? 8 : 4;
+  p.nt = R <= 16 ? 1 : R <= 32 ? 2 : R <= 64 ? 4 : 8;
+  const int64_t kc = 32 * p.ks;
+  const int64_t nch = (K + kc - 1) / kc;
+  p.rt = 2;
+  p.blocks_m = (M + 127) / 128;
+  if (p.blocks_m * nch < 512 && M > 64) {
+    p.rt = 1;
+    p.blocks_m = (M + 63) / 64;
+  }
+  int64_t s = (512 + p.blocks_m - 1) / p.blocks_m;
+  if (s > 32) s = 32;
+  if (s > nch) s = nch;
+  const int64_t j = (nch + s - 1) / s;   // chunks per slice
+  p.S = (int)((nch + j - 1) / j);
+  return p;
+}
+
+// Split of K for the segmented shrink: about 2048 (16-row tile, slice) waves,
+// slices of at least 256 and a multiple of 32 elements, at most 16 slices.
+static void seg_split(int64_t M, int64_t K, int* S, int* kchunk) {
   const int64_t m_tiles = (M + 15) / 16;
   int64_t s = (2048 + m_tiles - 1) / (m_tiles > 0 ? m_tiles : 1);
   int64_t smax = K / 256;
@@ -313,21 +445,60 @@ static void lora_split(int64_t M, int64_t K, int* S, int* kchunk) {
   *S = (int)((K + kc - 1) / kc);
 }
 
+// Workspace for any rank up to R, single-adapter or segmented.
 size_t lora_ws_bytes(int64_t M, int64_t K, int R) {
   int S, kc;
-  lora_split(M, K, &S, &kc);
-  return (size_t)S * (size_t)M * (size_t)R * sizeof(float);
+  seg_split(M, K, &S, &kc);
+  int64_t smax = S;
+  const int probe[2] = {R < 64 ? R : 64, R};   // both chunk widths the rank range can use
+  for (int q = 0; q < 2; ++q) {
+    const ShrinkPlan p = plan_shrink(M, K, probe[q]);
+    if (p.S > smax) smax = p.S;
+  }
+  return (size_t)smax * (size_t)M * (size_t)R * sizeof(float);
+}
+
+// Single-adapter shrink into P; returns the number of slices written.
+template <int XT>
+static int launch_shrink_p(const void* X, int64_t M, int64_t K, int64_t ldx, const unsigned short* A,
+                           int R, float* P, hipStream_t st) {
+  const ShrinkPlan p = plan_shrink(M, K, R);
+  const dim3 grid((unsigned)p.blocks_m, (unsigned)p.S);
+  const size_t lds = (size_t)R * 32 * p.ks * 2;
+  const char* x = (const char*)X;
+  const int64_t ldb = ldx * DtSize<XT>::v;
+#define SQ_SHRINK(KS_, NT_)                                                                  \
+  (p.rt == 2 ? k_lora_shrink<XT, KS_, 2, NT_><<<grid, kLoraThreads, lds, st>>>(x, ldb, (int)M, \
+                                                   (int)K, A, R, p.S, P)                      \
+             : k_lora_shrink<XT, KS_, 1, NT_><<<grid, kLoraThreads, lds, st>>>(x, ldb, (int)M, \
+                                                   (int)K, A, R, p.S, P))
+  switch (p.nt) {
+    case 1: SQ_SHRINK(8, 1); break;
+    case 2: SQ_SHRINK(8, 2); break;
+    case 4: SQ_SHRINK(8, 4); break;
+    default: SQ_SHRINK(4, 8); break;
+  }
+#undef SQ_SHRINK
+  return p.S;
+}
+
+template <int XT>
+static int launch_shrink_seg_p(const void* X, int64_t M, int64_t K, int64_t ldx, const LoraArgs& la,
+                               int R, float* P, hipStream_t st) {
+  int S, kc;
+  seg_split(M, K, &S, &kc);
+  dim3 g1((unsigned)((M + 63) / 64), (unsigned)S);
+  k_lora_shrink_seg<XT><<<g1, kLoraThreads, 0, st>>>((const char*)X, ldx * DtSize<XT>::v, (int)M,
+                                                     (int)K, la, R, kc, P);
+  return S;
 }
 
 template <int XT, int YT, bool SEG>
 static int launch_lora_t(const void* X, int64_t M, int64_t K, int64_t ldx, const LoraArgs& la, int R,
                          float scale, void* Y, int64_t N, int64_t ldy, void* ws, hipStream_t st) {
-  int S, kc;
-  lora_split(M, K, &S, &kc);
   float* P = (float*)ws;
-  dim3 g1((unsigned)((M + 63) / 64), (unsigned)S);
-  k_lora_shrink<XT, SEG><<<g1, kLoraThreads, 0, st>>>((const char*)X, ldx * DtSize<XT>::v, (int)M,
-                                                      (int)K, la, R, kc, P);
+  const int S = SEG ? launch_shrink_seg_p<XT>(X, M, K, ldx, la, R, P, st)
+                    : launch_shrink_p<XT>(X, M, K, ldx, la.A, R, P, st);
   SQ_LAUNCH_CHECK();
   const int64_t m_tiles = (M + 15) / 16;
   const int64_t n_chunks = (N + 63) / 64;
@@ -361,12 +532,8 @@ static int launch_lora_any(const void* X, int xt, int64_t M, int64_t K, int64_t 
 template <int XT>
 static int launch_shrink_t(const void* X, int64_t M, int64_t K, int64_t ldx, const LoraArgs& la, int R,
                            unsigned short* T, int64_t ldt, void* ws, hipStream_t st) {
-  int S, kc;
-  lora_split(M, K, &S, &kc);
   float* P = (float*)ws;
-  dim3 g1((unsigned)((M + 63) / 64), (unsigned)S);
-  k_lora_shrink<XT, false><<<g1, kLoraThreads, 0, st>>>((const char*)X, ldx * DtSize<XT>::v, (int)M,
-                                                        (int)K, la, R, kc, P);
+  const int S = launch_shrink_p<XT>(X, M, K, ldx, la.A, R, P, st);
   SQ_LAUNCH_CHECK();
   const int64_t threads = M * (R / 8);
   k_lora_reduce<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(P, S, R, (int)M, T, ldt);

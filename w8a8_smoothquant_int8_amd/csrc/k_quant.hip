@@ -6,20 +6,23 @@
 //   STATIC  (activations, per tensor):     v = fp32(X[m,k] / s[k]); scale given
 //
 // The kernel is HBM-bound: it reads each input element once (16-byte loads)
-// and writes one byte per element. A block owns one row at a time and walks
-// rows with a grid stride; each thread keeps CPT chunks of 8 consecutive
-// channels of the row in registers, so the row is read once, reduced (wave
-// max, then LDS across waves) and quantized from registers. The per-channel
-// fp64 reciprocals 1/s[k] that make the divisions exact (div_rn) are computed
-// once per block and reused for every row the block visits; the next row's
-// input is loaded before the current row is reduced, to keep HBM busy.
+// and writes one byte per element. A block owns RPB rows at a time and walks
+// rows with a grid stride; each thread covers CPT chunks of 8 consecutive
+// channels. The first pass turns the raw row into the smoothed fp32 values v
+// (kept in registers) and their max; the raw registers are then free, so the
+// block's next rows are loaded into them while this row group is reduced
+// (wave max, then LDS across waves: one barrier per group) and quantized from
+// v (at 8 chunks per thread v is recomputed instead, for registers, and the
+// next rows load after the group). The per-channel factors (fp32 s for FOLD, the fp64 reciprocals 1/s that
+// make the divisions exact for the others, see div_rn) are computed once per
+// block, after its first loads are issued, and reused for all its rows.
 #include "sq_internal.h"
 
 namespace sq {
 
 enum QuantKind { Q_FOLD = 0, Q_DYNAMIC = 1, Q_STATIC = 2 };
 
-constexpr int kQuantMaxThreads = 1024;
+constexpr int kQuantMaxThreads = 512;
 
 template <int DT, int CPT>
 struct RowChunks {
@@ -67,7 +70,7 @@ __device__ __forceinline__ void widen8(const uint4* w, float* out) {
 // rows: M (activations) or N (weights). in_ld_bytes: input row stride.
 // s: [K] or null (no smoothing). scale_io: [rows] written (FOLD, DYNAMIC) or
 // [1] read (STATIC). out: [rows, K] int8 contiguous.
-template <int DT, int CPT, int KIND>
+template <int DT, int CPT, int KIND, int RPB>
 __global__ void __launch_bounds__(kQuantMaxThreads)
 k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld_bytes,
              const float* __restrict__ s, float* __restrict__ scale_io, int8_t* __restrict__ out) {
@@ -76,6 +79,20 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int nwaves = T >> 6;
+  const int64_t stride = (int64_t)gridDim.x * RPB;
+
+  // At 8 chunks per thread the registers do not hold v next to the factors:
+  // v is recomputed from the raw row in the second pass, so the next rows are
+  // loaded only after it.
+  constexpr bool kStoreV = CPT <= 4;
+  RowChunks<DT, CPT> raw[RPB];
+  auto load_group = [&](int64_t m0) {
+#pragma unroll
+    for (int r = 0; r < RPB; ++r)
+      if (m0 + r < rows) load_row<DT, CPT>(raw[r], in + (m0 + r) * in_ld_bytes, K, tid, T);
+  };
+  int64_t m0 = (int64_t)blockIdx.x * RPB;
+  if (m0 < rows) load_group(m0);
 
   // Per-channel factor: fp32 s (FOLD multiplies) or fp64 1/s (divisions).
   float sm[CPT][8];
@@ -85,52 +102,226 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
     const int64_t c = tid + (int64_t)j * T;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float sv = (s != nullptr && c * 8 < K) ? s[c * 8 + e] : 1.0f;
+      const float sv = (s != nullptr && c * 8 < K) ? s[c * 8 + e] : 1.0f;
       if constexpr (KIND == Q_FOLD) sm[j][e] = sv;
       else rs[j][e] = 1.0 / (double)sv;      // RN64(1/s), IEEE fp64 division
     }
   }
 
-  double r_static = 0.0;
   float a_static = 0.0f;
+  double r_static = 0.0;
   if constexpr (KIND == Q_STATIC) {
     a_static = scale_io[0];
     r_static = a_static != 0.0f ? 1.0 / (double)a_static : 0.0;
   }
 
-  __shared__ float red[2][kQuantMaxThreads / 64];
-
-  // Rows of up to 2 chunks per thread also prefetch the next row; wider rows
-  // would need more registers than a 1024-thread block can give a thread.
-  constexpr bool kPrefetch = CPT <= 2;
-  RowChunks<DT, CPT> cur, nxt;
-  int64_t m = blockIdx.x;
-  if (kPrefetch && m < rows) load_row<DT, CPT>(cur, in + m * in_ld_bytes, K, tid, T);
+  __shared__ float red[2][RPB][kQuantMaxThreads / 64];
   int parity = 0;
-  for (; m < rows; m += gridDim.x) {
-    const int64_t mn = m + gridDim.x;
-    if (kPrefetch) {
-      if (mn < rows) load_row<DT, CPT>(nxt, in + mn * in_ld_bytes, K, tid, T);
-    } else {
-      load_row<DT, CPT>(cur, in + m * in_ld_bytes, K, tid, T);
-    }
-
-    float v[CPT][8];
-    float amax = 0.0f;
+  for (; m0 < rows; m0 += stride) {
+    if (!kStoreV && m0 != (int64_t)blockIdx.x * RPB) load_group(m0);
+    auto smooth = [&](const float x, int j, int e) -> float {
+      if constexpr (KIND == Q_FOLD) return x * sm[j][e];   // fp32 multiply
+      else return div_rn(x, rs[j][e]);                     // fp32(x / s), exact
+    };
+    // pass 1: smoothed values and their row max
+    float v[RPB][kStoreV ? CPT : 1][8];
+    float amax[RPB];
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int64_t c = tid + (int64_t)j * T;
-      float x[8];
-      widen8<DT>(cur.w[j], x);
+    for (int r = 0; r < RPB; ++r) {
+      amax[r] = 0.0f;
+      if (m0 + r < rows) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float t;
-        if constexpr (KIND == Q_FOLD) t = x[e] * sm[j][e];     // fp32 multiply
-        else t = div_rn(x[e], rs[j][e]);                      // fp32(x / s), exact
-        v[j][e] = t;
-        if (c * 8 < K) amax = __builtin_fmaxf(amax, __builtin_fabsf(t));
+        for (int j = 0; j < CPT; ++j) {
+          const int64_t c = tid + (int64_t)j * T;
+          if (c * 8 < K) {
+            float x[8];
+            widen8<DT>(raw[r].w[j], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float y = smooth(x[e], j, e);
+              if constexpr (kStoreV) v[r][j][e] = y;
+              amax[r] = __builtin_fmaxf(amax[r], __builtin_fabsf(y));
+            }
+          }
+        }
       }
     }
+    // the raw registers are free: load the block's next rows into them
+    if (kStoreV && m0 + stride < rows) load_group(m0 + stride);
+
+    float scale[RPB];
+    double rscale[RPB];
+    if constexpr (KIND == Q_STATIC) {
+#pragma unroll
+      for (int r = 0; r < RPB; ++r) { scale[r] = a_static; rscale[r] = r_static; }
+    } else {
+#pragma unroll
+      for (int r = 0; r < RPB; ++r) {
+        amax[r] = wave_max(amax[r]);
+        if (lane == 0) red[parity][r][wave] = amax[r];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < RPB; ++r) {
+        float a = red[parity][r][0];
+        for (int w = 1; w < nwaves; ++w) a = __builtin_fmaxf(a, red[parity][r][w]);
+        scale[r] = a / 127.0f;                                   // IEEE fp32 division
+        rscale[r] = scale[r] != 0.0f ? 1.0 / (double)scale[r] : 0.0;
+        if (tid == 0 && m0 + r < rows) scale_io[m0 + r] = scale[r];
+      }
+      parity ^= 1;
+    }
+
+    // pass 2: codes from v
+#pragma unroll
+    for (int r = 0; r < RPB; ++r) {
+      if (m0 + r >= rows) break;
+      int8_t* orow = out + (m0 + r) * K;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int64_t c = tid + (int64_t)j * T;
+        if (c * 8 < K) {
+          float y[8];
+          if constexpr (kStoreV) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = v[r][j][e];
+          } else {
+            widen8<DT>(raw[r].w[j], y);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = smooth(y[e], j, e);
+          }
+          int q[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            q[e] = scale[r] != 0.0f ? quant_code(div_rn(y[e], rscale[r])) : 0;
+          uint2 pk;
+          pk.x = pack4_i8(q[0], q[1], q[2], q[3]);
+          pk.y = pack4_i8(q[4], q[5], q[6], q[7]);
+          *(uint2*)(orow + c * 8) = pk;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wave-per-row variant, for rows of at most 4096 channels (CPL <= 8 chunks
+// per lane: the raw row and its smoothed values fit one wave's registers
+// together). Each wave owns whole rows (grid-stride over waves), so the row
+// max is a wave reduction and the kernel has no barrier after its start. The
+// per-channel factors live in LDS, computed once per block: fp32 s for FOLD,
+// fp64 1/s otherwise, laid out so that the 16-byte reads of consecutive lanes
+// are consecutive (no bank conflict). Lane l covers chunks c = l + 64 j
+// (j < CPL) of 8 channels; the next row is loaded into the raw registers as
+// soon as v is formed, so every wave keeps a row in flight.
+// ---------------------------------------------------------------------------
+constexpr int kWaveRowThreads = 512;
+
+template <int DT, int KIND, int CPL>
+struct WaveRowCfg {
+  static constexpr int kWords = DT == SQ_F32 ? 2 : 1;          // 16-byte words per chunk
+  static constexpr int kTabParts = KIND == Q_FOLD ? 2 : 4;     // 16-byte factor words per chunk
+  static_assert(CPL <= 8, "raw row plus v must fit the registers");
+};
+
+template <int DT, int KIND, int CPL>
+__global__ void __launch_bounds__(kWaveRowThreads)
+k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_bytes,
+             const float* __restrict__ s, float* __restrict__ scale_io, int8_t* __restrict__ out) {
+  using Cfg = WaveRowCfg<DT, KIND, CPL>;
+  constexpr int kWords = Cfg::kWords;
+  // factor word p of chunk c at tab[p * 64 * CPL + c]
+  __shared__ uint4 tab[Cfg::kTabParts * 64 * CPL];
+  const int nch = K / 8;
+  const int lane = threadIdx.x & 63;
+  const int wpb = blockDim.x >> 6;
+  const int64_t nw = (int64_t)gridDim.x * wpb;
+  int64_t m = (int64_t)blockIdx.x * wpb + (threadIdx.x >> 6);
+
+  // Chunks past the row end (c >= nch) load chunk nch - 1 and read its factors;
+  // their values are zeroed before the max and they are never stored. No
+  // branch in the arithmetic, so loads and LDS reads can be issued early.
+  uint4 raw[CPL][kWords];
+  auto load = [&](int64_t row) {
+    const char* p = in + row * in_ld_bytes;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j < nch ? lane + 64 * j : nch - 1;
+#pragma unroll
+      for (int q = 0; q < kWords; ++q) raw[j][q] = ((const uint4*)(p + (int64_t)c * 8 * DtSize<DT>::v))[q];
+    }
+  };
+  if (m < rows) load(m);
+
+  for (int c = threadIdx.x; c < nch; c += blockDim.x) {
+    float sv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[e] = s != nullptr ? s[c * 8 + e] : 1.0f;
+    if constexpr (KIND == Q_FOLD) {
+      tab[c] = make_uint4(__float_as_uint(sv[0]), __float_as_uint(sv[1]), __float_as_uint(sv[2]),
+                          __float_as_uint(sv[3]));
+      tab[64 * CPL + c] = make_uint4(__float_as_uint(sv[4]), __float_as_uint(sv[5]),
+                                     __float_as_uint(sv[6]), __float_as_uint(sv[7]));
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double r0 = 1.0 / (double)sv[2 * q];       // RN64(1/s), IEEE fp64 division
+        const double r1 = 1.0 / (double)sv[2 * q + 1];
+        const unsigned long long b0 = __double_as_longlong(r0), b1 = __double_as_longlong(r1);
+        tab[q * 64 * CPL + c] = make_uint4((uint32_t)b0, (uint32_t)(b0 >> 32), (uint32_t)b1,
+                                           (uint32_t)(b1 >> 32));
+      }
+    }
+  }
+  __syncthreads();
+
+  // v for chunk j of this lane from its raw 8 values
+  auto smooth8 = [&](int j, float* x) {
+    const int c = lane + 64 * j < nch ? lane + 64 * j : nch - 1;
+    if constexpr (KIND == Q_FOLD) {
+      const uint4 f0 = tab[c], f1 = tab[64 * CPL + c];
+      const float f[8] = {__uint_as_float(f0.x), __uint_as_float(f0.y), __uint_as_float(f0.z),
+                          __uint_as_float(f0.w), __uint_as_float(f1.x), __uint_as_float(f1.y),
+                          __uint_as_float(f1.z), __uint_as_float(f1.w)};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = x[e] * f[e];          // fp32 multiply
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 f = tab[q * 64 * CPL + c];
+        const double r0 = __longlong_as_double(((unsigned long long)f.y << 32) | f.x);
+        const double r1 = __longlong_as_double(((unsigned long long)f.w << 32) | f.z);
+        x[2 * q] = div_rn(x[2 * q], r0);                        // fp32(x / s), exact
+        x[2 * q + 1] = div_rn(x[2 * q + 1], r1);
+      }
+    }
+  };
+
+  float a_static = 0.0f;
+  double r_static = 0.0;
+  if constexpr (KIND == Q_STATIC) {
+    a_static = scale_io[0];
+    r_static = a_static != 0.0f ? 1.0 / (double)a_static : 0.0;
+  }
+
+  for (; m < rows; m += nw) {
+    float v[CPL][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      float x[8];
+      widen8<DT>(raw[j], x);
+      smooth8(j, x);
+      const bool in_row = lane + 64 * j < nch;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[j][e] = x[e];
+        amax = __builtin_fmaxf(amax, in_row ? __builtin_fabsf(x[e]) : 0.0f);
+      }
+      // groups of 4 chunks: their LDS reads issue together, registers stay bounded
+      if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+    if (m + nw < rows) load(m + nw);
 
     float scale;
     double rscale;
@@ -138,65 +329,108 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
       scale = a_static;
       rscale = r_static;
     } else {
-      amax = wave_max(amax);
-      if (lane == 0) red[parity][wave] = amax;
-      __syncthreads();
-      amax = red[parity][0];
-      for (int w = 1; w < nwaves; ++w) amax = __builtin_fmaxf(amax, red[parity][w]);
-      parity ^= 1;
-      scale = amax / 127.0f;                                  // IEEE fp32 division
+      scale = wave_max(amax) / 127.0f;                           // IEEE fp32 division
       rscale = scale != 0.0f ? 1.0 / (double)scale : 0.0;
-      if (tid == 0) scale_io[m] = scale;
+      if (lane == 0) scale_io[m] = scale;
     }
 
     int8_t* orow = out + m * K;
+    // scale == 0 (all-zero row, or a zero static scale): every code is 0
+    const uint32_t keep = scale != 0.0f ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int64_t c = tid + (int64_t)j * T;
-      if (c * 8 < K) {
-        int q[8];
+    for (int j = 0; j < CPL; ++j) {
+      int q[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = scale != 0.0f ? quant_code(div_rn(v[j][e], rscale)) : 0;
-        uint2 pk;
-        pk.x = pack4_i8(q[0], q[1], q[2], q[3]);
-        pk.y = pack4_i8(q[4], q[5], q[6], q[7]);
-        *(uint2*)(orow + c * 8) = pk;
-      }
+      for (int e = 0; e < 8; ++e) q[e] = quant_code(div_rn(v[j][e], rscale));
+      uint2 pk;
+      pk.x = pack4_i8(q[0], q[1], q[2], q[3]) & keep;
+      pk.y = pack4_i8(q[4], q[5], q[6], q[7]) & keep;
+      const int c = lane + 64 * j;
+      if (c < nch) *(uint2*)(orow + c * 8) = pk;
+      if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
-    if (kPrefetch) cur = nxt;
   }
 }
 
-// Pick threads per block T (multiple of 64, <= 1024) and chunks per thread
-// CPT (<= 4) so that T * CPT * 8 >= K, preferring CPT <= 2 (prefetching).
-static void pick_shape(int64_t K, int* T, int* cpt) {
+// Resident blocks of one kernel on the current device (occupancy x CUs),
+// cached per kernel instantiation and device.
+template <typename Tag>
+static int64_t resident_blocks(const void* f, int T) {
+  static int per_cu[16] = {0};
+  static int cus[16] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+  if (per_cu[dev] == 0) {
+    int n = 0, b = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, f, T, 0) != hipSuccess || b <= 0) b = 1;
+    cus[dev] = n;
+    per_cu[dev] = b;
+  }
+  return (int64_t)per_cu[dev] * cus[dev];
+}
+
+template <int DT, int KIND, int CPL>
+static void launch_wave(const char* p, int64_t rows, int64_t K, int64_t ldb, const float* s,
+                        float* scale_io, int8_t* out, hipStream_t st) {
+  auto f = k_quant_wave<DT, KIND, CPL>;
+  constexpr int W = kWaveRowThreads / 64;
+  int64_t grid = (rows + W - 1) / W;
+  const int64_t cap = resident_blocks<WaveRowCfg<DT, KIND, CPL>>((const void*)f, kWaveRowThreads);
+  if (grid > cap) grid = cap;
+  f<<<(unsigned)grid, kWaveRowThreads, 0, st>>>(p, rows, (int)K, ldb, s, scale_io, out);
+}
+
+// Block-per-row-group shape: chunks per thread CPT in {1, 2, 4, 8}, the
+// smallest that lets at most 512 threads cover the row; T = threads, a
+// multiple of 256 (the same number of waves on each of the CU's 4 SIMDs);
+// rows per block iteration RPB = 2 for CPT <= 2, else 1.
+static void pick_shape(int64_t K, int* T, int* cpt, int* rpb) {
   const int64_t chunks = K / 8;
-  int64_t t = (chunks + 1) / 2;
-  t = (t + 63) / 64 * 64;
-  if (t < 64) t = 64;
-  if (t > kQuantMaxThreads) t = kQuantMaxThreads;
+  int c = 1;
+  while (c < 8 && (chunks + c - 1) / c > kQuantMaxThreads) c *= 2;
+  int64_t t = (chunks + c - 1) / c;
+  t = (t + 255) / 256 * 256;
   *T = (int)t;
-  *cpt = (int)((chunks + t - 1) / t);
+  *cpt = c;
+  *rpb = c <= 2 ? 2 : 1;
+}
+
+template <int DT, int CPT, int KIND, int RPB>
+static void launch_shape(const char* p, int64_t rows, int64_t K, int64_t ldb, const float* s,
+                         float* scale_io, int8_t* out, int T, hipStream_t st) {
+  auto f = k_quant_rows<DT, CPT, KIND, RPB>;
+  // One row group per block while the whole problem fits on the chip at once;
+  // beyond that a full wave of blocks, each walking several groups.
+  int64_t grid = (rows + RPB - 1) / RPB;
+  const int64_t cap = resident_blocks<decltype(f)>((const void*)f, T);
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  f<<<(unsigned)grid, T, 0, st>>>(p, rows, K, ldb, s, scale_io, out);
 }
 
 template <int DT, int KIND>
 static int launch_rows_dt(const void* in, int64_t rows, int64_t K, int64_t ld, const float* s,
                           float* scale_io, int8_t* out, hipStream_t st) {
-  int T, cpt;
-  pick_shape(K, &T, &cpt);
-  // At least 4 rows per block, so the per-block reciprocal setup is amortised,
-  // and no more blocks than about 8 waves per SIMD could hold.
-  int64_t grid = (rows + 3) / 4;
-  const int64_t cap = 256LL * (2048 / T);
-  if (grid > cap) grid = cap;
-  if (grid < 1) grid = 1;
   const char* p = (const char*)in;
   const int64_t ldb = ld * DtSize<DT>::v;
+  // wave per row up to K = 4096 (8 chunks per lane)
+  const int64_t lane_chunks = (K / 8 + 63) / 64;
+  if (lane_chunks <= 8) {
+    if (lane_chunks <= 2) launch_wave<DT, KIND, 2>(p, rows, K, ldb, s, scale_io, out, st);
+    else if (lane_chunks <= 4) launch_wave<DT, KIND, 4>(p, rows, K, ldb, s, scale_io, out, st);
+    else launch_wave<DT, KIND, 8>(p, rows, K, ldb, s, scale_io, out, st);
+    SQ_LAUNCH_CHECK();
+    return SQ_OK;
+  }
+  int T, cpt, rpb;
+  pick_shape(K, &T, &cpt, &rpb);
   switch (cpt) {
-    case 1: k_quant_rows<DT, 1, KIND><<<(unsigned)grid, T, 0, st>>>(p, rows, K, ldb, s, scale_io, out); break;
-    case 2: k_quant_rows<DT, 2, KIND><<<(unsigned)grid, T, 0, st>>>(p, rows, K, ldb, s, scale_io, out); break;
-    case 3: k_quant_rows<DT, 3, KIND><<<(unsigned)grid, T, 0, st>>>(p, rows, K, ldb, s, scale_io, out); break;
-    case 4: k_quant_rows<DT, 4, KIND><<<(unsigned)grid, T, 0, st>>>(p, rows, K, ldb, s, scale_io, out); break;
+    case 1: launch_shape<DT, 1, KIND, 2>(p, rows, K, ldb, s, scale_io, out, T, st); break;
+    case 2: launch_shape<DT, 2, KIND, 2>(p, rows, K, ldb, s, scale_io, out, T, st); break;
+    case 4: launch_shape<DT, 4, KIND, 1>(p, rows, K, ldb, s, scale_io, out, T, st); break;
+    case 8: launch_shape<DT, 8, KIND, 1>(p, rows, K, ldb, s, scale_io, out, T, st); break;
     default: return SQ_ERR_INVALID_ARG;   // K > 32768 is rejected by validation
   }
   SQ_LAUNCH_CHECK();

@@ -30,6 +30,7 @@ k_colmax(const char* __restrict__ X, int64_t M, int64_t K, int64_t ldx_bytes, in
   const int64_t r1 = r0 + rows_per_slice < M ? r0 + rows_per_slice : M;
   float mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (col0 < K) {
+#pragma unroll 4
     for (int64_t r = r0 + wave; r < r1; r += kColWavesPerBlock) {
       float v[8];
       load8_f32<DT>(X + r * ldx_bytes + col0 * DtSize<DT>::v, v);
@@ -100,10 +101,12 @@ int launch_colmax(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, floa
                   hipStream_t st) {
   if (M == 0) return SQ_OK;
   const int64_t strips = (K + 511) / 512;
-  // aim for ~2048 blocks; at least 64 rows per slice so each wave loops.
-  int64_t slices = (2048 + strips - 1) / strips;
+  // About 1024 blocks, at least 16 rows per block (4 per wave, whose loads
+  // the unrolled loop keeps in flight together), at most 65535 row slices.
+  int64_t slices = (1024 + strips - 1) / strips;
   int64_t rows = (M + slices - 1) / slices;
-  if (rows < 64) rows = 64;
+  if (rows < 16) rows = 16;
+  if ((M + rows - 1) / rows > 65535) rows = (M + 65534) / 65535;
   slices = (M + rows - 1) / rows;
   dim3 grid((unsigned)strips, (unsigned)slices);
   const int esz = xt == SQ_F32 ? 4 : 2;

@@ -14,6 +14,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned short v8u16 __attribute__((ext_vector_type(8)));
+// LDS address, the destination operand of the direct global-to-LDS load
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kWave = 64;
 

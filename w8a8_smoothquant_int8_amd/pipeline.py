@@ -55,9 +55,10 @@ class LinearGroup:
     def __init__(self, W: torch.Tensor, rows: Dict[str, Tuple[int, int]], alpha: float,
                  out_dtype: str, M: int, lora: Optional[Dict[str, Tuple[torch.Tensor, torch.Tensor]]] = None,
                  seg_lora: Optional[Dict[str, SegmentedLora]] = None, lora_scale: float = 1.0,
-                 fuse: bool = True):
+                 fuse: bool = True, modes: Tuple[str, ...] = ("dynamic",)):
         dev = W.device
         self.W, self.rows, self.alpha, self.M = W, rows, float(alpha), int(M)
+        self.modes = tuple(modes)   # activation modes this group will run
         Ntot, K = W.shape
         self.K, self.Ntot = K, Ntot
         self.act_max = torch.zeros(K, dtype=torch.float32, device=dev)
@@ -102,7 +103,8 @@ class LinearGroup:
 
     def fold(self) -> None:
         sq_smooth_fold(self.act_max, self.W, self.alpha, self.s, self.Wq, self.w_scale)
-        sq_static_act_scale(self.act_max, self.s, self.static_scale)
+        if "static" in self.modes:
+            sq_static_act_scale(self.act_max, self.s, self.static_scale)
 
     # -- per batch ----------------------------------------------------------
     def _a(self, mode: str) -> torch.Tensor:
