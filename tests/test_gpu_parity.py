@@ -103,7 +103,8 @@ def test_smooth_scale(alpha, dtype):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("N,K,ld", [(1, 16, 16), (16, 272, 288), (300, 4096, 4096), (33, 14336, 14336),
-                                    (24, 28672, 28672), (40, 20480, 20480), (17, 5120, 5136)])
+                                    (2100, 14336, 14336), (257, 8192, 8208), (24, 28672, 28672),
+                                    (40, 20480, 20480), (17, 5120, 5136)])
 def test_fold_quant_weights(dtype, N, K, ld):
     rng = np.random.default_rng(N + K)
     w, wn = acts(rng, N, K, dtype, n_out=0, ld=ld, sigma=0.02)
@@ -124,8 +125,8 @@ def test_fold_quant_weights(dtype, N, K, ld):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("M,K,ld", [(1, 16, 16), (5, 48, 64), (300, 256, 256), (130, 4096, 4112),
-                                    (64, 5120, 5120), (70, 14336, 14336), (9, 20480, 20480),
-                                    (40, 28672, 28672)])
+                                    (64, 5120, 5120), (257, 8192, 8208), (70, 14336, 14336),
+                                    (2100, 14336, 14336), (9, 20480, 20480), (40, 28672, 28672)])
 @pytest.mark.parametrize("smooth", [True, False])
 def test_quant_dynamic(dtype, M, K, ld, smooth):
     rng = np.random.default_rng(M * 3 + K)

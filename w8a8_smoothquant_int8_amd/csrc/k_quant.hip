@@ -207,13 +207,14 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
 // ---------------------------------------------------------------------------
 // Wave-per-row variant, for rows of at most 4096 channels (CPL <= 8 chunks
 // per lane: the raw row and its smoothed values fit one wave's registers
-// together). Each wave owns whole rows (grid-stride over waves), so the row
+// together) and, for 16-bit inputs, up to 14336 (the raw row alone fits; v
+// is recomputed in the second pass). Each wave owns whole rows (grid-stride over waves), so the row
 // max is a wave reduction and the kernel has no barrier after its start. The
 // per-channel factors live in LDS, computed once per block: fp32 s for FOLD,
 // fp64 1/s otherwise, laid out so that the 16-byte reads of consecutive lanes
 // are consecutive (no bank conflict). Lane l covers chunks c = l + 64 j
-// (j < CPL) of 8 channels; the next row is loaded into the raw registers as
-// soon as v is formed, so every wave keeps a row in flight.
+// (j < CPL) of 8 channels. When v is kept, the next row is loaded into the
+// raw registers as soon as v is formed; otherwise after the second pass.
 // ---------------------------------------------------------------------------
 constexpr int kWaveRowThreads = 512;
 
@@ -221,7 +222,12 @@ template <int DT, int KIND, int CPL>
 struct WaveRowCfg {
   static constexpr int kWords = DT == SQ_F32 ? 2 : 1;          // 16-byte words per chunk
   static constexpr int kTabParts = KIND == Q_FOLD ? 2 : 4;     // 16-byte factor words per chunk
-  static_assert(CPL <= 8, "raw row plus v must fit the registers");
+  // Up to 8 chunks per lane v is kept next to the raw row; beyond, only the
+  // raw row fits (at most 28 chunks of 16-bit values: 112 registers) and the
+  // second pass recomputes v.
+  static constexpr bool kStoreV = CPL <= 8;
+  static constexpr int kGroup = kStoreV ? 4 : 1;                 // chunks per scheduling group
+  static_assert(CPL * kWords <= 28, "the raw row must fit 112 registers");
 };
 
 template <int DT, int KIND, int CPL>
@@ -230,6 +236,8 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
              const float* __restrict__ s, float* __restrict__ scale_io, int8_t* __restrict__ out) {
   using Cfg = WaveRowCfg<DT, KIND, CPL>;
   constexpr int kWords = Cfg::kWords;
+  constexpr bool kStoreV = Cfg::kStoreV;
+  constexpr int kGroup = Cfg::kGroup;
   // factor word p of chunk c at tab[p * 64 * CPL + c]
   __shared__ uint4 tab[Cfg::kTabParts * 64 * CPL];
   const int nch = K / 8;
@@ -277,7 +285,8 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
 
   // v for chunk j of this lane from its raw 8 values
   auto smooth8 = [&](int j, float* x) {
-    const int c = lane + 64 * j < nch ? lane + 64 * j : nch - 1;
+    int c = lane + 64 * j < nch ? lane + 64 * j : nch - 1;
+    if constexpr (!kStoreV) asm volatile("" : "+v"(c));   // factor reads are redone in pass 2
     if constexpr (KIND == Q_FOLD) {
       const uint4 f0 = tab[c], f1 = tab[64 * CPL + c];
       const float f[8] = {__uint_as_float(f0.x), __uint_as_float(f0.y), __uint_as_float(f0.z),
@@ -305,7 +314,7 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
   }
 
   for (; m < rows; m += nw) {
-    float v[CPL][8];
+    float v[kStoreV ? CPL : 1][8];
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
@@ -315,13 +324,13 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
       const bool in_row = lane + 64 * j < nch;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        v[j][e] = x[e];
+        if constexpr (kStoreV) v[j][e] = x[e];
         amax = __builtin_fmaxf(amax, in_row ? __builtin_fabsf(x[e]) : 0.0f);
       }
-      // groups of 4 chunks: their LDS reads issue together, registers stay bounded
-      if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      // scheduling groups: their LDS reads issue together, registers stay bounded
+      if (j % kGroup == kGroup - 1) __builtin_amdgcn_sched_barrier(0);
     }
-    if (m + nw < rows) load(m + nw);
+    if (kStoreV && m + nw < rows) load(m + nw);
 
     float scale;
     double rscale;
@@ -339,16 +348,30 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
     const uint32_t keep = scale != 0.0f ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
+      float y[8];
+      if constexpr (kStoreV) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = v[j][e];
+      } else {
+        // Opaque to the compiler: otherwise it keeps pass 1's values of all
+        // chunks alive instead of recomputing them here, and spills.
+#pragma unroll
+        for (int q = 0; q < kWords; ++q)
+          asm volatile("" : "+v"(raw[j][q].x), "+v"(raw[j][q].y), "+v"(raw[j][q].z), "+v"(raw[j][q].w));
+        widen8<DT>(raw[j], y);
+        smooth8(j, y);
+      }
       int q[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = quant_code(div_rn(v[j][e], rscale));
+      for (int e = 0; e < 8; ++e) q[e] = quant_code(div_rn(y[e], rscale));
       uint2 pk;
       pk.x = pack4_i8(q[0], q[1], q[2], q[3]) & keep;
       pk.y = pack4_i8(q[4], q[5], q[6], q[7]) & keep;
       const int c = lane + 64 * j;
       if (c < nch) *(uint2*)(orow + c * 8) = pk;
-      if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      if (j % kGroup == kGroup - 1) __builtin_amdgcn_sched_barrier(0);
     }
+    if (!kStoreV && m + nw < rows) load(m + nw);
   }
 }
 
@@ -415,12 +438,22 @@ static int launch_rows_dt(const void* in, int64_t rows, int64_t K, int64_t ld, c
                           float* scale_io, int8_t* out, hipStream_t st) {
   const char* p = (const char*)in;
   const int64_t ldb = ld * DtSize<DT>::v;
-  // wave per row up to K = 4096 (8 chunks per lane)
+  // wave per row up to K = 4096, and for 16-bit inputs up to K = 14336 (8,
+  // resp. 28 chunks per lane)
   const int64_t lane_chunks = (K / 8 + 63) / 64;
-  if (lane_chunks <= 8) {
+  if (lane_chunks <= 8 || (DT != SQ_F32 && lane_chunks <= 28)) {
     if (lane_chunks <= 2) launch_wave<DT, KIND, 2>(p, rows, K, ldb, s, scale_io, out, st);
     else if (lane_chunks <= 4) launch_wave<DT, KIND, 4>(p, rows, K, ldb, s, scale_io, out, st);
-    else launch_wave<DT, KIND, 8>(p, rows, K, ldb, s, scale_io, out, st);
+    else if (lane_chunks <= 8) launch_wave<DT, KIND, 8>(p, rows, K, ldb, s, scale_io, out, st);
+    else if constexpr (DT != SQ_F32) {
+      switch ((lane_chunks + 3) / 4) {
+        case 3: launch_wave<DT, KIND, 12>(p, rows, K, ldb, s, scale_io, out, st); break;
+        case 4: launch_wave<DT, KIND, 16>(p, rows, K, ldb, s, scale_io, out, st); break;
+        case 5: launch_wave<DT, KIND, 20>(p, rows, K, ldb, s, scale_io, out, st); break;
+        case 6: launch_wave<DT, KIND, 24>(p, rows, K, ldb, s, scale_io, out, st); break;
+        default: launch_wave<DT, KIND, 28>(p, rows, K, ldb, s, scale_io, out, st); break;
+      }
+    }
     SQ_LAUNCH_CHECK();
     return SQ_OK;
   }
