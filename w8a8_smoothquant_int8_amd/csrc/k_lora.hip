@@ -376,27 +376,37 @@ k_lora_expand(const float* __restrict__ P, int S, int R, int M, int N, LoraArgs 
 }
 
 // T[m, i] = bf16(sum_s P[s, m, i]) (fixed order of s) for the fused GEMM
-// epilogue. One thread per 8 consecutive ranks of one row.
-__global__ void __launch_bounds__(256)
+// epilogue. One thread per 4 consecutive ranks of one row, 64-thread blocks
+// (enough blocks at small M). The loads of 8 slices are issued together; the
+// sums stay in slice order.
+__global__ void __launch_bounds__(64)
 k_lora_reduce(const float* __restrict__ P, int S, int R, int M, unsigned short* __restrict__ T,
               int64_t ldt) {
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int per_row = R / 8;
+  const int64_t id = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  const int per_row = R / 4;
   if (id >= (int64_t)M * per_row) return;
-  const int m = (int)(id / per_row), i = (int)(id % per_row) * 8;
-  float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int s = 0; s < S; ++s) {
-    const float4* p = (const float4*)(P + ((int64_t)s * M + m) * R + i);
-    const float4 a = p[0], b = p[1];
-    t[0] += a.x; t[1] += a.y; t[2] += a.z; t[3] += a.w;
-    t[4] += b.x; t[5] += b.y; t[6] += b.z; t[7] += b.w;
+  const int m = (int)(id / per_row), i = (int)(id % per_row) * 4;
+  const int64_t slice = (int64_t)M * R;
+  const float* p = P + (int64_t)m * R + i;
+  float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+  int s = 0;
+  for (; s + 8 <= S; s += 8) {
+    float4 a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] = *(const float4*)(p + (s + u) * slice);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      t.x += a[u].x; t.y += a[u].y; t.z += a[u].z; t.w += a[u].w;
+    }
   }
-  uint4 u;
-  u.x = f32_to_bf16_bits(t[0]) | (f32_to_bf16_bits(t[1]) << 16);
-  u.y = f32_to_bf16_bits(t[2]) | (f32_to_bf16_bits(t[3]) << 16);
-  u.z = f32_to_bf16_bits(t[4]) | (f32_to_bf16_bits(t[5]) << 16);
-  u.w = f32_to_bf16_bits(t[6]) | (f32_to_bf16_bits(t[7]) << 16);
-  *(uint4*)(T + (int64_t)m * ldt + i) = u;
+  for (; s < S; ++s) {
+    const float4 a = *(const float4*)(p + s * slice);
+    t.x += a.x; t.y += a.y; t.z += a.z; t.w += a.w;
+  }
+  uint2 u;
+  u.x = f32_to_bf16_bits(t.x) | (f32_to_bf16_bits(t.y) << 16);
+  u.y = f32_to_bf16_bits(t.z) | (f32_to_bf16_bits(t.w) << 16);
+  *(uint2*)(T + (int64_t)m * ldt + i) = u;
 }
 
 // Launch plan of the single-adapter shrink. KC = 256 (8 k-steps) when the
@@ -535,8 +545,8 @@ static int launch_shrink_t(const void* X, int64_t M, int64_t K, int64_t ldx, con
   float* P = (float*)ws;
   const int S = launch_shrink_p<XT>(X, M, K, ldx, la.A, R, P, st);
   SQ_LAUNCH_CHECK();
-  const int64_t threads = M * (R / 8);
-  k_lora_reduce<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(P, S, R, (int)M, T, ldt);
+  const int64_t threads = M * (R / 4);
+  k_lora_reduce<<<(unsigned)((threads + 63) / 64), 64, 0, st>>>(P, S, R, (int)M, T, ldt);
   SQ_LAUNCH_CHECK();
   return SQ_OK;
 }
