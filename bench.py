@@ -204,12 +204,12 @@ def gemm_tile(M: int, N: int, K: int) -> str:
     """The tile configuration libsq picks for an INT8 GEMM of this shape (the
     library's rule: the generic kernel when K is not a multiple of 128 or an
     operand reaches 4 GiB, else the better of 256x256 tiles, one block per CU,
-    and 128x128 tiles, two blocks per CU at 0.9 of the per-tile rate, scored by
+    and 128x128 tiles, two blocks per CU at 0.8 of the per-tile rate, scored by
     the fraction of the last round of blocks that does useful work)."""
     if K % 128 or M * K >= 1 << 32 or N * K >= 1 << 32:
         return "generic"
     s256 = _tile_score(M, N, 256, 256, 256, 1.0)
-    s128 = _tile_score(M, N, 128, 128, 512, 0.9)
+    s128 = _tile_score(M, N, 128, 128, 512, 0.8)
     return "256x256" if s256 >= s128 else "128x128"
 
 

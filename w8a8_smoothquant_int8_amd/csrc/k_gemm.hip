@@ -211,6 +211,194 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], int row0, int col0
 }
 
 // ---------------------------------------------------------------------------
+// LDS-staged epilogue of the main kernel (16-bit or fp32 output; no LoRA, or
+// LoRA with scale 1). The epilogue above is latency-bound when a block runs
+// it alone: one round trip for the scales, one per 16-rank LoRA chunk, and
+// 2-byte output stores scattered over 64-byte row pieces. Here the block's
+// LDS is free once the K loop is done (every wave has consumed its last
+// fragments), so:
+//   1. all waves issue direct global->LDS loads of the block's a_scale and
+//      w_scale slices and of the T and B rows of up to 64 ranks at once;
+//   2. one wait and barrier; the scales and LoRA fragments come from LDS;
+//   3. (more than 64 ranks: the next 64, same way);
+//   4. the rounded outputs go to LDS as a [BM, BN] tile, then every thread
+//      writes 16-byte pieces of whole rows (fp32 outputs are stored from the
+//      registers directly: the fp32 tile would not fit).
+// Values and operation order are those of the epilogue above.
+// ---------------------------------------------------------------------------
+constexpr int kStageRanks = 64;
+
+// Direct global->LDS copy of `count` 4-byte words from src[idx(i)] to dst[i]
+// (one 64-word load per wave instruction), shared by the block's waves.
+template <int NW, typename Idx>
+__device__ __forceinline__ void stage_words(const float* src, char* dst, int count, int wave,
+                                            int lane, Idx idx) {
+  for (int base = wave * 64; base < count; base += NW * 64) {
+    const int i = base + lane;
+    if (i < count)
+      __builtin_amdgcn_global_load_lds((const void*)(src + idx(i)), (lds_ptr_t)(dst + 4 * base), 4,
+                                       0, 0);
+  }
+}
+
+// Direct copy of `rows` rows of `r16` 16-byte chunks each: row i of the LDS
+// tile (packed, r16 chunks per row) from src + row_off(i) (bytes).
+template <int NW, typename RowOff>
+__device__ __forceinline__ void stage_rows(const char* src, char* dst, int rows, int r16, int wave,
+                                           int lane, RowOff row_off) {
+  const int total = rows * r16;
+  for (int base = wave * 64; base < total; base += NW * 64) {
+    const int g = base + lane;
+    if (g < total) {
+      const int row = g / r16, ch = g - row * r16;
+      __builtin_amdgcn_global_load_lds((const void*)(src + row_off(row) + 16 * ch),
+                                       (lds_ptr_t)(dst + 16 * base), 16, 0, 0);
+    }
+  }
+}
+
+template <int OUT, bool STATIC_A, int LORA, int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void epilogue_staged(v16i (&acc)[BM / WM / 32][BN / WN / 32], char* smem,
+                                                int m0, int n0, int wm, int wn, int M, int N,
+                                                const float* __restrict__ a_scale,
+                                                const float* __restrict__ w_scale,
+                                                void* __restrict__ Y, int64_t ldy,
+                                                const LoraEpi& le) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int row0 = wm * (BM / WM), col0 = wn * (BN / WN);   // wave sub-tile within the block
+  // LDS layout: [a_scale BM][w_scale BN] fp32, then T [BM][<=64] and B [BN][<=64] bf16
+  char* s_as = smem;
+  char* s_ws = s_as + 4 * BM;
+  char* s_t = s_ws + 4 * BN;
+  const int rank_pass = le.r < kStageRanks ? le.r : kStageRanks;
+  char* s_b = s_t + 2 * BM * rank_pass;
+
+  auto stage_lora = [&](int k_base) {
+    const int rp = le.r - k_base < kStageRanks ? le.r - k_base : kStageRanks;
+    const int r16 = rp / 8;
+    stage_rows<NW>((const char*)le.T, s_t, BM, r16, wave, lane, [&](int row) -> int64_t {
+      const int64_t m = m0 + row < M ? m0 + row : M - 1;
+      return (m * le.ldt + k_base) * 2;
+    });
+    stage_rows<NW>((const char*)le.B, s_b, BN, r16, wave, lane, [&](int row) -> int64_t {
+      const int64_t n = n0 + row < N ? n0 + row : N - 1;
+      return (n * le.r + k_base) * 2;
+    });
+    return rp;
+  };
+
+  if constexpr (!STATIC_A)
+    stage_words<NW>(a_scale, s_as, BM, wave, lane, [&](int i) { return m0 + i < M ? m0 + i : M - 1; });
+  stage_words<NW>(w_scale, s_ws, BN, wave, lane, [&](int i) { return n0 + i < N ? n0 + i : N - 1; });
+  int rp = 0;
+  if constexpr (LORA == 1) rp = stage_lora(0);
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+
+  // y = out((fp32(acc) * a_scale[m]) * w_scale[n]), in place in the accumulators
+  const float as_static = STATIC_A ? a_scale[0] : 0.0f;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    float as[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // rows 8 g + 4 lhalf + 0..3 of the 32-row tile: 4 consecutive scales
+      const int r = row0 + i * 32 + 8 * g + 4 * lhalf;
+      if constexpr (STATIC_A) {
+        as[4 * g] = as[4 * g + 1] = as[4 * g + 2] = as[4 * g + 3] = as_static;
+      } else {
+        const float4 v = *(const float4*)(s_as + 4 * r);
+        as[4 * g] = v.x; as[4 * g + 1] = v.y; as[4 * g + 2] = v.z; as[4 * g + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const float ws = *(const float*)(s_ws + 4 * (col0 + j * 32 + lrow));
+      v16f t;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) t[q] = round_out<OUT>(((float)acc[i][j][q] * as[q]) * ws);
+      acc[i][j] = __builtin_bit_cast(v16i, t);
+    }
+  }
+
+  if constexpr (LORA == 1) {
+    for (int k_base = 0; k_base < le.r; k_base += kStageRanks) {
+      if (k_base > 0) {
+        __builtin_amdgcn_s_barrier();         // every wave is done with the previous ranks
+        rp = stage_lora(k_base);
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_barrier();
+      }
+      for (int k0 = 0; k0 < rp; k0 += 16) {
+        const int k = k0 + 8 * lhalf;          // rank within this pass
+        const bool kin = k < rp;
+        uint4 tf[TM], bf[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          tf[i] = kin ? *(const uint4*)(s_t + 2 * ((row0 + i * 32 + lrow) * rp + k)) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          bf[j] = kin ? *(const uint4*)(s_b + 2 * ((col0 + j * 32 + lrow) * rp + k)) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_bit_cast(
+                v16i, __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, tf[i]),
+                                                              __builtin_bit_cast(v8bf, bf[j]),
+                                                              __builtin_bit_cast(v16f, acc[i][j]),
+                                                              0, 0, 0));
+      }
+    }
+  }
+
+  if constexpr (OUT == OUT_F32) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + col0 + j * 32 + lrow;
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int m = m0 + row0 + i * 32 + 8 * (q >> 2) + 4 * lhalf + (q & 3);
+          if (m < M) ((float*)Y)[(int64_t)m * ldy + n] = __builtin_bit_cast(v16f, acc[i][j])[q];
+        }
+    }
+  } else {
+    // [BM, BN] tile of output bits in LDS, then whole-row 16-byte stores
+    __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): this wave's LDS reads are done
+    __builtin_amdgcn_s_barrier();
+    unsigned short* s_y = (unsigned short*)smem;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int r = row0 + i * 32 + 8 * (q >> 2) + 4 * lhalf + (q & 3);
+          const float y = __builtin_bit_cast(v16f, acc[i][j])[q];
+          s_y[r * BN + col0 + j * 32 + lrow] =
+              (unsigned short)(OUT == OUT_BF16 ? f32_to_bf16_bits(y) : f32_to_f16_bits(y));
+        }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    constexpr int CPRow = BN / 8;            // 16-byte pieces per tile row
+#pragma unroll 4
+    for (int g = threadIdx.x; g < BM * CPRow; g += NW * 64) {
+      const int r = g / CPRow, c = g - r * CPRow;
+      const int m = m0 + r, n = n0 + 8 * c;
+      if (m < M && n < N)
+        *(uint4*)((unsigned short*)Y + (int64_t)m * ldy + n) = *(const uint4*)(s_y + r * BN + 8 * c);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Main kernel, K % 128 == 0. WM x WN waves; each wave owns a (BM/WM) x (BN/WN)
 // sub-tile of 32x32 MFMA tiles. The MFMA operand fragments are double-buffered
 // in registers: the LDS reads for k-step s+1 are in flight while the MFMAs of
@@ -346,8 +534,12 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
     }
   }
 
-  epilogue<OUT, STATIC_A, LORA, TM, TN>(acc, m0 + wm * (BM / WM), n0 + wn * (BN / WN), M, N,
-                                        a_scale, w_scale, Y, ldy, le);
+  if constexpr (OUT != OUT_I32 && LORA != 2)
+    epilogue_staged<OUT, STATIC_A, LORA, BM, BN, WM, WN>(acc, smem, m0, n0, wm, wn, M, N, a_scale,
+                                                          w_scale, Y, ldy, le);
+  else
+    epilogue<OUT, STATIC_A, LORA, TM, TN>(acc, m0 + wm * (BM / WM), n0 + wn * (BN / WN), M, N,
+                                          a_scale, w_scale, Y, ldy, le);
 }
 
 // ---------------------------------------------------------------------------
@@ -482,7 +674,7 @@ static int pick_cfg(int64_t M, int64_t N, int64_t K) {
   }
   // 256 CUs: one 256x256 block per CU, two 128x128 blocks per CU.
   const double s256 = tile_score(M, N, 256, 256, 256, 1.0);
-  const double s128 = tile_score(M, N, 128, 128, 512, 0.9);
+  const double s128 = tile_score(M, N, 128, 128, 512, 0.8);
   return s256 >= s128 ? CFG_256 : CFG_128;
 }
 
