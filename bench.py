@@ -10,15 +10,15 @@ bf16 LoRA delta. The default workload is the Llama-3-8B projection set at
 M=2048 tokens. Inputs are seeded synthetic tensors, resident in HBM before the
 timed region starts.
 
-The input groups are independent, so a timed step issues every group on its
-own pair of streams (the LoRA shrink beside the quantizer, the GEMM after
-both) and the groups' kernels overlap.
+The input groups are independent, so a timed step issues every group as one
+native call (sq_linear_group_run: calibrate, fold, quantize, LoRA shrink,
+GEMM) on its own stream and the groups' kernels overlap.
 
 Output: one JSON line. `value` is GEMM INT8 tera-operations per second of the
 whole step (2*M*N*K summed over the projections, divided by the step time).
-HIP events recorded on each GEMM's stream around its launch give the GEMM's
-own rate, reported as its roofline fraction against the MI355X dense INT8
-MFMA peak. Per-stage times come from a few extra untimed steps issued in order
+HIP events that the library records on each GEMM's stream right around its
+launch give the GEMM's own rate, reported as its roofline fraction against the
+MI355X dense INT8 MFMA peak. Per-stage times come from a few extra untimed steps issued in order
 on one stream. The CPU oracle is timed on a bounded sample of the same step
 (cpu_baseline).
 """
@@ -45,8 +45,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_{tile}_hbm_traffic_llama3_8b
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=128,
@@ -73,7 +73,7 @@ def stored_traffic(tile: str):
         return None
     kv = {}
     for line in open(path):
-        m = re.match(r"\s*([a-z_]+)\s*:\s*(\S+)", line)
+        m = re.match(r"\s*([a-z0-9_]+)\s*:\s*(\S+)", line)
         if m:
             kv[m.group(1)] = m.group(2)
     if kv.get("gemm_source_sha256_16") != kernel_hash(GEMM_KERNEL_SRC):
@@ -147,49 +147,45 @@ def run_step(groups, tl=None):
 
 
 class Streams:
-    """Two streams per input group. All streams keep the default priority."""
+    """One stream per input group, default priority."""
 
     def __init__(self, torch, n_groups):
         self.torch = torch
         self.main = [torch.cuda.Stream() for _ in range(n_groups)]
-        self.side = [torch.cuda.Stream() for _ in range(n_groups)]
 
 
 def run_step_streams(groups, st, gemm_ev=None):
     """One pass of the whole path over one batch. The input groups are
-    independent: each runs calibrate -> fold -> quantize -> GEMM on its own
-    stream, with the LoRA shrink beside the quantizer on a second stream (both
-    only read X; the GEMM waits for both). The groups' short, latency-bound
-    kernels fill each other's gaps, and a GEMM whose tiles leave CUs idle in
-    its last round shares the chip with the next group's work.
-    gemm_ev: {group: [(start, end), ...]} collects HIP events recorded on the
-    GEMM's stream right around each GEMM launch."""
+    independent: each runs calibrate -> fold -> quantize -> LoRA shrink ->
+    GEMM as one native call (sq_linear_group_run) on its own stream, so the
+    groups' short, latency-bound kernels fill each other's gaps and a GEMM
+    whose tiles leave CUs idle in its last round shares the chip with the next
+    group's work. gemm_ev: {group: [(start, end), ...]} collects HIP events
+    that the library records on the group's stream right around its GEMM."""
     torch = st.torch
     cur = torch.cuda.current_stream()
-    for (inp, g, X, Xc), sm, ss in zip(groups, st.main, st.side):
+    for (inp, g, X, Xc), sm in zip(groups, st.main):
         sm.wait_stream(cur)
-        ss.wait_stream(cur)
-        with torch.cuda.stream(ss):
-            if g.fused:
-                g.lora_shrink(X)
-        with torch.cuda.stream(sm):
-            g.calibrate(Xc)
-            g.fold()
-            g.quantize(X)
-            sm.wait_stream(ss)
-            if gemm_ev is not None:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-            if g.fused:
-                g.gemm_all_lora()
-            else:
-                g.gemm_all()
-            if gemm_ev is not None:
-                e1 = torch.cuda.Event(enable_timing=True)
-                e1.record()
-                gemm_ev.setdefault(inp, []).append((e0, e1))
+        e0 = e1 = None
+        if gemm_ev is not None:
+            e0, e1 = gemm_ev["pool"].pop()
+            gemm_ev.setdefault(inp, []).append((e0, e1))
+        g.run(X, Xc, stream=sm, gemm_begin=e0, gemm_end=e1)
     for sm in st.main:
         cur.wait_stream(sm)
+
+
+def event_pool(torch, n):
+    """n (start, end) pairs of timing events, created up front (a first record
+    creates the underlying HIP event) so the library can record them."""
+    pool = []
+    for _ in range(n):
+        pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        for e in pair:
+            e.record()
+        pool.append(pair)
+    torch.cuda.synchronize()
+    return pool
 
 
 def _tile_score(M, N, bm, bn, resident, rate):
@@ -287,7 +283,7 @@ def main():
 
     # Timed region: exactly `steps` steps, synchronized on both sides. HIP
     # events on each GEMM's stream time the GEMM launches for the roofline.
-    gemm_ev = {}
+    gemm_ev = {"pool": event_pool(torch, args.steps * len(groups))}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -298,6 +294,7 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     ops = wl.gemm_ops()
     value = ops * args.steps / elapsed / 1e12
+    gemm_ev.pop("pool")
     gemm_by_group = {g: [a.elapsed_time(b) for a, b in evs] for g, evs in gemm_ev.items()}
 
     # Per-stage times: a few more steps, untimed, with every launch issued in

@@ -191,6 +191,58 @@ int sq_lora_apply_segmented(const void* X, int xt, int64_t M, int64_t K, int64_t
                             const int32_t* ranks, int max_rank, float scale, void* Y, int yt,
                             int64_t N, int64_t ldy, void* ws, size_t ws_bytes, void* stream);
 
+/* The whole path for one input group ([SQ] "How it works", Steps 4-7, in
+ * order; [LoRA] Pitch): the projections that read the same activations, with
+ * their weights stacked along N and their adapters stacked along r, run as
+ * one call, so a step costs one host call per group instead of one per
+ * kernel. Every pointer and size below has the meaning and the rules it has
+ * in the single-purpose call named beside it. */
+#define SQ_GROUP_CALIBRATE 1  /* act_max := 0, then sq_calibrate_absmax over X_cal */
+#define SQ_GROUP_FOLD 2       /* sq_smooth_fold; static mode: then sq_static_act_scale */
+#define SQ_GROUP_FORWARD 4    /* sq_quant_per_token, sq_lora_shrink (r > 0), then
+                                 sq_w8a8_gemm_lora (r > 0) or sq_w8a8_gemm */
+
+typedef struct {
+  const void* X;          /* [M, K] activations, dtype xt, row stride ldx */
+  int xt;
+  int64_t M, ldx;
+  const void* X_cal;      /* [M_cal, K] calibration batch, dtype xt, stride ld_cal */
+  int64_t M_cal, ld_cal;
+  const void* W;          /* [N, K] stacked weights, dtype wt, row stride ldw */
+  int wt;
+  int64_t N, K, ldw;
+  double alpha;           /* migration strength, 0 <= alpha <= 1 */
+  int mode;               /* sq_act_mode */
+  float* act_max;         /* [K] */
+  float* s;               /* [K] smoothing vector, written by FOLD */
+  int8_t* Wq;             /* [N, K], written by FOLD */
+  float* w_scale;         /* [N], written by FOLD */
+  int8_t* Xq;             /* [M, K], written by FORWARD */
+  float* a_scale;         /* [M] (dynamic: written by FORWARD) or [1] (static: written by FOLD) */
+  const void* A;          /* [r, K] bf16 stacked adapters; r == 0: no LoRA */
+  const void* B;          /* [N, r] bf16 */
+  int r;
+  float lora_scale;
+  void* T;                /* [M, r] bf16, row stride ldt */
+  int64_t ldt;
+  void* workspace;        /* >= sq_lora_workspace_bytes(M, K, r) bytes when r > 0 */
+  size_t workspace_bytes;
+  void* Y;                /* [M, N] dtype yt, row stride ldy */
+  int yt;
+  int64_t ldy;
+} sq_linear_group;
+
+/* Runs the phases selected by `flags` (a nonzero OR of SQ_GROUP_*) for group
+ * `g`, in the order calibrate, fold, forward, all on `stream`. Every phase's
+ * arguments are validated before anything is enqueued; on an argument error
+ * nothing runs. gemm_begin / gemm_end: hipEvent_t handles (as void*) or NULL;
+ * when given, FORWARD records them on `stream` immediately before and after
+ * the GEMM launch (if M > 0), so the caller can time the GEMM alone; a failed
+ * record returns SQ_ERR_HIP. The call
+ * allocates nothing and may be captured into a HIP graph. */
+int sq_linear_group_run(const sq_linear_group* g, int flags, void* stream, void* gemm_begin,
+                        void* gemm_end);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sq.SIGNATURES)
@@ -209,3 +209,74 @@ def test_fp64_reciprocal_division_identity():
         ref = a / b
         got = (a.astype(np.float64) * (1.0 / b.astype(np.float64))).astype(F)
         assert np.array_equal(got, ref)
+
+
+def _group(**over):
+    """An sq_linear_group filled with valid fake pointers and shapes."""
+    d = sq.SqLinearGroup()
+    d.X, d.xt, d.M, d.ldx = 0x10000, sq.SQ_BF16, 64, 256
+    d.X_cal, d.M_cal, d.ld_cal = 0x20000, 64, 256
+    d.W, d.wt, d.N, d.K, d.ldw = 0x30000, sq.SQ_BF16, 128, 256, 256
+    d.alpha, d.mode = 0.5, sq.SQ_ACT_PER_TOKEN_DYNAMIC
+    d.act_max, d.s, d.Wq, d.w_scale = 0x40000, 0x41000, 0x50000, 0x60000
+    d.Xq, d.a_scale = 0x70000, 0x80000
+    d.A, d.B, d.r, d.lora_scale, d.T, d.ldt = 0x90000, 0xA0000, 16, 1.0, 0xB0000, 16
+    d.workspace, d.workspace_bytes = 0xC0000, sq.sq_lora_workspace_bytes(64, 256, 16)
+    d.Y, d.yt, d.ldy = 0xD0000, sq.SQ_BF16, 128
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def _run(L, d, flags=7):
+    return L.sq_linear_group_run(ctypes.byref(d), flags, S, None, None)
+
+
+def test_group_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror of sq_linear_group has the C struct's size and field offsets."""
+    fields = [f for f, _ in sq.SqLinearGroup._fields_]
+    src = tmp_path / "layout.c"
+    body = "".join(f'  printf(" %zu", offsetof(sq_linear_group, {f}));\n' for f in fields)
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n"
+                   f'#include "{HEADER}"\n'
+                   "int main(void) {\n"
+                   '  printf("%zu", sizeof(sq_linear_group));\n'
+                   + body +
+                   '  printf("\\n");\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-o", str(exe), str(src)], check=True)
+    out = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(sq.SqLinearGroup)
+    assert out[1:] == [getattr(sq.SqLinearGroup, f).offset for f in fields]
+
+
+def test_group_validation(L):
+    """Every phase's arguments are checked before anything is enqueued."""
+    E = sq
+    assert L.sq_linear_group_run(None, 7, S, None, None) == E.SQ_ERR_INVALID_ARG
+    assert _run(L, _group(), flags=0) == E.SQ_ERR_INVALID_ARG
+    assert _run(L, _group(), flags=8) == E.SQ_ERR_INVALID_ARG
+    assert _run(L, _group(mode=5)) == E.SQ_ERR_INVALID_ARG
+    # calibrate
+    assert _run(L, _group(X_cal=None), flags=1) == E.SQ_ERR_INVALID_ARG
+    assert _run(L, _group(ld_cal=200), flags=1) == E.SQ_ERR_INVALID_ARG
+    assert _run(L, _group(act_max=0x40002), flags=1) == E.SQ_ERR_MISALIGNED
+    # fold
+    assert _run(L, _group(alpha=1.5), flags=2) == E.SQ_ERR_INVALID_ARG
+    assert _run(L, _group(Wq=0x50004), flags=2) == E.SQ_ERR_MISALIGNED
+    assert _run(L, _group(wt=7), flags=2) == E.SQ_ERR_UNSUPPORTED_DTYPE
+    assert _run(L, _group(K=250, ldx=250, ldw=250, ld_cal=250), flags=2) == E.SQ_ERR_MISALIGNED
+    # forward
+    assert _run(L, _group(N=120, ldy=128), flags=4) == E.SQ_ERR_MISALIGNED
+    assert _run(L, _group(ldy=64), flags=4) == E.SQ_ERR_INVALID_ARG
+    assert _run(L, _group(r=12), flags=4) == E.SQ_ERR_MISALIGNED
+    assert _run(L, _group(r=136), flags=4) == E.SQ_ERR_INVALID_ARG
+    assert _run(L, _group(T=None), flags=4) == E.SQ_ERR_INVALID_ARG
+    assert _run(L, _group(workspace_bytes=16), flags=4) == E.SQ_ERR_WORKSPACE
+    assert _run(L, _group(yt=9), flags=4) == E.SQ_ERR_UNSUPPORTED_DTYPE
+    # a forward-phase error stops the call even when the earlier phases are valid
+    assert _run(L, _group(Y=None), flags=7) == E.SQ_ERR_INVALID_ARG
+    # no LoRA: A, B, T and the workspace are not needed
+    d = _group(r=0, A=None, B=None, T=None, workspace=None, workspace_bytes=0)
+    assert _run(L, d, flags=4) in (E.SQ_OK, E.SQ_ERR_UNSUPPORTED_ARCH)

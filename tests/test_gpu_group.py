@@ -1,0 +1,110 @@
+"""sq_linear_group_run: one native call per input group (GPU).
+
+The call must produce exactly what the single-purpose calls produce in the
+same order (calibrate, smooth + fold, quantize, LoRA shrink, GEMM with the
+LoRA epilogue): every output is compared bit for bit. The single-purpose path
+itself is checked against the oracle in test_gpu_parity.py and
+test_gpu_workloads.py.
+"""
+import pytest
+import torch
+
+import w8a8_smoothquant_int8_amd as sq
+from synth.workloads import get_workload
+from w8a8_smoothquant_int8_amd.pipeline import ALL_PHASES, LinearGroup
+
+pytestmark = pytest.mark.gpu
+
+
+def make_group(wl, inp, lora=True, modes=("dynamic",)):
+    W = wl.w_group(inp).cuda()
+    rows = wl.group_rows(inp)
+    loras = {p: tuple(t.cuda() for t in wl.lora(p)) for p in rows} if (lora and wl.lora_rank) else {}
+    return LinearGroup(W, rows, wl.alpha, wl.out_dtype, wl.M, lora=loras, modes=modes)
+
+
+def outputs(g, mode="dynamic"):
+    a = g.a_scale if mode == "dynamic" else g.static_scale
+    return [t.clone() for t in (g.act_max, g.s, g.Wq, g.w_scale, g.Xq, a, g.Yg)]
+
+
+def separate(g, X, Xc, mode="dynamic"):
+    g.calibrate(Xc)
+    g.fold()
+    g.forward(X, mode)
+    torch.cuda.synchronize()
+    return outputs(g, mode)
+
+
+def assert_same(a, b):
+    for i, (x, y) in enumerate(zip(a, b)):
+        assert torch.equal(x, y), i
+
+
+@pytest.mark.parametrize("inp", ["attn_in", "o_in", "mlp_in", "down_in"])
+def test_group_run_equals_separate_calls(inp):
+    wl = get_workload("llama3_8b_proj_m2048")
+    g = make_group(wl, inp)
+    assert g.fused
+    X, Xc = wl.x(inp).cuda(), wl.x_cal(inp).cuda()
+    ref = separate(g, X, Xc)
+    for t in (g.act_max, g.s, g.Wq, g.w_scale, g.Xq, g.a_scale, g.Yg):
+        t.zero_()
+    g.run(X, Xc)
+    torch.cuda.synchronize()
+    assert_same(outputs(g), ref)
+
+
+def test_group_run_static_mode_and_no_lora():
+    wl = get_workload("opt13b_layer_prefill_m4096")
+    inp = wl.inputs[0][0]
+    g = make_group(wl, inp, lora=False, modes=("static",))
+    X, Xc = wl.x(inp).cuda(), wl.x_cal(inp).cuda()
+    ref = separate(g, X, Xc, mode="static")
+    for t in (g.act_max, g.s, g.Wq, g.w_scale, g.Xq, g.static_scale, g.Yg):
+        t.zero_()
+    g.run(X, Xc, mode="static")
+    torch.cuda.synchronize()
+    assert_same(outputs(g, "static"), ref)
+
+
+def test_group_run_phases_one_by_one_and_events():
+    wl = get_workload("llama3_8b_proj_m2048")
+    g = make_group(wl, "attn_in")
+    X, Xc = wl.x("attn_in").cuda(), wl.x_cal("attn_in").cuda()
+    g.run(X, Xc)
+    torch.cuda.synchronize()
+    ref = outputs(g)
+    g.Yg.zero_()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    for flags in (sq.SQ_GROUP_CALIBRATE, sq.SQ_GROUP_FOLD, sq.SQ_GROUP_FORWARD):
+        g.run(X, Xc, flags=flags, gemm_begin=e0, gemm_end=e1)
+    torch.cuda.synchronize()
+    assert_same(outputs(g), ref)
+    assert e0.elapsed_time(e1) > 0.0
+
+
+def test_group_run_graph_replays_match_eager():
+    """The whole step of a group captured into a HIP graph (fills, not
+    memsets) and replayed several times, with eager work in between."""
+    wl = get_workload("llama3_8b_proj_m2048")
+    g = make_group(wl, "mlp_in")
+    X, Xc = wl.x("mlp_in").cuda(), wl.x_cal("mlp_in").cuda()
+    g.run(X, Xc)
+    torch.cuda.synchronize()
+    ref = outputs(g)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        g.run(X, Xc, flags=ALL_PHASES)
+    for rep in range(3):
+        for t in (g.act_max, g.s, g.Wq, g.Xq, g.Yg):
+            t.fill_(7)
+        tmp = torch.randn(512, 512, device="cuda") @ torch.randn(512, 512, device="cuda")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_same(outputs(g), ref)
+        del tmp

@@ -58,7 +58,24 @@ SIGNATURES = {
     "sq_lora_apply_segmented": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp,
                                          _c_int, _vp, _vp, _vp, _c_int, _c_f, _vp, _c_int, _c_i64,
                                          _c_i64, _vp, _c_sz, _vp]),
+    "sq_linear_group_run": (_c_int, [_vp, _c_int, _vp, _vp, _vp]),
 }
+
+SQ_GROUP_CALIBRATE, SQ_GROUP_FOLD, SQ_GROUP_FORWARD = 1, 2, 4
+
+
+class SqLinearGroup(ctypes.Structure):
+    """Mirror of the C struct sq_linear_group (include/sq.h), field for field."""
+    _fields_ = [
+        ("X", _vp), ("xt", _c_int), ("M", _c_i64), ("ldx", _c_i64),
+        ("X_cal", _vp), ("M_cal", _c_i64), ("ld_cal", _c_i64),
+        ("W", _vp), ("wt", _c_int), ("N", _c_i64), ("K", _c_i64), ("ldw", _c_i64),
+        ("alpha", _c_d), ("mode", _c_int),
+        ("act_max", _vp), ("s", _vp), ("Wq", _vp), ("w_scale", _vp), ("Xq", _vp), ("a_scale", _vp),
+        ("A", _vp), ("B", _vp), ("r", _c_int), ("lora_scale", _c_f), ("T", _vp), ("ldt", _c_i64),
+        ("workspace", _vp), ("workspace_bytes", _c_sz),
+        ("Y", _vp), ("yt", _c_int), ("ldy", _c_i64),
+    ]
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -241,3 +258,43 @@ def sq_lora_apply_segmented(X: torch.Tensor, seg_start: torch.Tensor, seg_adapte
 def pointer_table(tensors: Sequence[torch.Tensor], device) -> torch.Tensor:
     """Device int64 tensor of the tensors' data pointers (for the segmented call)."""
     return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
+
+
+def sq_linear_group_desc(X: torch.Tensor, X_cal: Optional[torch.Tensor], W: torch.Tensor,
+                         alpha: float, mode: str, act_max: torch.Tensor, s: torch.Tensor,
+                         Wq: torch.Tensor, w_scale: torch.Tensor, Xq: torch.Tensor,
+                         a_scale: torch.Tensor, Y: torch.Tensor, A: Optional[torch.Tensor] = None,
+                         B: Optional[torch.Tensor] = None, T: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None,
+                         lora_scale: float = 1.0) -> SqLinearGroup:
+    """Fill an sq_linear_group from tensors. The struct holds raw pointers:
+    the tensors must stay alive (and in place) while it is used."""
+    M, K = X.shape
+    N = W.shape[0]
+    d = SqLinearGroup()
+    d.X, d.xt, d.M, d.ldx = X.data_ptr(), _dt(X), M, _ld(X)
+    if X_cal is not None:
+        d.X_cal, d.M_cal, d.ld_cal = X_cal.data_ptr(), X_cal.shape[0], _ld(X_cal)
+    d.W, d.wt, d.N, d.K, d.ldw = W.data_ptr(), _dt(W), N, K, _ld(W)
+    d.alpha, d.mode = float(alpha), MODES[mode]
+    d.act_max, d.s, d.Wq, d.w_scale = (act_max.data_ptr(), s.data_ptr(), Wq.data_ptr(),
+                                       w_scale.data_ptr())
+    d.Xq, d.a_scale = Xq.data_ptr(), a_scale.data_ptr()
+    if A is not None:
+        d.A, d.B, d.r, d.lora_scale = A.data_ptr(), B.data_ptr(), A.shape[0], float(lora_scale)
+        d.T, d.ldt = T.data_ptr(), _ld(T)
+        d.workspace, d.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    d.Y, d.yt, d.ldy = Y.data_ptr(), _dt(Y), _ld(Y)
+    return d
+
+
+def sq_linear_group_run(desc: SqLinearGroup, flags: int, stream=None, gemm_begin=None,
+                        gemm_end=None) -> None:
+    """gemm_begin / gemm_end: torch.cuda.Event objects (already created, e.g.
+    recorded once) or raw hipEvent_t handles, or None."""
+    def ev(e):
+        if e is None:
+            return None
+        return ctypes.c_void_p(e.cuda_event if hasattr(e, "cuda_event") else int(e))
+    _check("sq_linear_group_run", lib().sq_linear_group_run(
+        ctypes.byref(desc), int(flags), _stream(stream), ev(gemm_begin), ev(gemm_end)))

@@ -351,4 +351,95 @@ int sq_lora_apply_segmented(const void* X, int xt, int64_t M, int64_t K, int64_t
                                    as_stream(stream));
 }
 
+int sq_linear_group_run(const sq_linear_group* g, int flags, void* stream, void* gemm_begin,
+                        void* gemm_end) {
+  SQ_REQUIRE(g != nullptr, SQ_ERR_INVALID_ARG);
+  constexpr int kAll = SQ_GROUP_CALIBRATE | SQ_GROUP_FOLD | SQ_GROUP_FORWARD;
+  SQ_REQUIRE(flags != 0 && (flags & ~kAll) == 0, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(valid_mode(g->mode), SQ_ERR_INVALID_ARG);
+  const bool lora = g->r != 0;
+  const bool is_static = g->mode == SQ_ACT_PER_TENSOR_STATIC;
+  int rc;
+  // 1. validate every selected phase
+  if (flags & SQ_GROUP_CALIBRATE) {
+    if ((rc = check_matrix(g->X_cal, g->xt, g->M_cal, g->K, g->ld_cal)) != SQ_OK) return rc;
+    SQ_REQUIRE(g->act_max != nullptr, SQ_ERR_INVALID_ARG);
+    SQ_REQUIRE(aligned4(g->act_max), SQ_ERR_MISALIGNED);
+  }
+  if (flags & SQ_GROUP_FOLD) {
+    if ((rc = check_matrix(g->W, g->wt, g->N, g->K, g->ldw)) != SQ_OK) return rc;
+    SQ_REQUIRE(g->N >= 1, SQ_ERR_INVALID_ARG);
+    SQ_REQUIRE(g->act_max != nullptr && g->s != nullptr && g->Wq != nullptr && g->w_scale != nullptr,
+               SQ_ERR_INVALID_ARG);
+    SQ_REQUIRE(aligned4(g->act_max) && aligned4(g->s) && aligned16(g->Wq) && aligned4(g->w_scale),
+               SQ_ERR_MISALIGNED);
+    SQ_REQUIRE(std::isfinite(g->alpha) && g->alpha >= 0.0 && g->alpha <= 1.0, SQ_ERR_INVALID_ARG);
+    if (is_static) {
+      SQ_REQUIRE(g->a_scale != nullptr, SQ_ERR_INVALID_ARG);
+      SQ_REQUIRE(aligned4(g->a_scale), SQ_ERR_MISALIGNED);
+    }
+  }
+  if (flags & SQ_GROUP_FORWARD) {
+    if ((rc = check_matrix(g->X, g->xt, g->M, g->K, g->ldx)) != SQ_OK) return rc;
+    SQ_REQUIRE(g->s != nullptr && g->Xq != nullptr && g->a_scale != nullptr, SQ_ERR_INVALID_ARG);
+    SQ_REQUIRE(aligned4(g->s) && aligned16(g->Xq) && aligned4(g->a_scale), SQ_ERR_MISALIGNED);
+    if ((rc = check_gemm(g->Xq, g->Wq, g->M, g->N, g->K)) != SQ_OK) return rc;
+    SQ_REQUIRE(g->w_scale != nullptr && g->Y != nullptr, SQ_ERR_INVALID_ARG);
+    SQ_REQUIRE(valid_dtype(g->yt), SQ_ERR_UNSUPPORTED_DTYPE);
+    SQ_REQUIRE(g->ldy >= g->N, SQ_ERR_INVALID_ARG);
+    SQ_REQUIRE(g->ldy % 16 == 0 && aligned16(g->Y) && aligned4(g->w_scale), SQ_ERR_MISALIGNED);
+    if (lora) {
+      if ((rc = check_rank(g->r)) != SQ_OK) return rc;
+      SQ_REQUIRE(g->A != nullptr && g->B != nullptr && g->T != nullptr, SQ_ERR_INVALID_ARG);
+      SQ_REQUIRE(std::isfinite(g->lora_scale), SQ_ERR_INVALID_ARG);
+      SQ_REQUIRE(g->ldt >= g->r, SQ_ERR_INVALID_ARG);
+      SQ_REQUIRE(g->ldt % 8 == 0 && aligned16(g->A) && aligned16(g->B) && aligned16(g->T),
+                 SQ_ERR_MISALIGNED);
+      if (g->M > 0) {
+        SQ_REQUIRE(g->workspace != nullptr &&
+                       g->workspace_bytes >= sq_lora_workspace_bytes(g->M, g->K, g->r),
+                   SQ_ERR_WORKSPACE);
+        SQ_REQUIRE(aligned16(g->workspace), SQ_ERR_MISALIGNED);
+      }
+    }
+  }
+  if ((rc = gate()) != SQ_OK) return rc;
+  hipStream_t st = as_stream(stream);
+  // 2. launch
+  if (flags & SQ_GROUP_CALIBRATE) {
+    if ((rc = sq::launch_fill(g->act_max, g->K, 0.0f, st)) != SQ_OK) return rc;
+    if (g->M_cal > 0 &&
+        (rc = sq::launch_colmax(g->X_cal, g->xt, g->M_cal, g->K, g->ld_cal, g->act_max, st)) != SQ_OK)
+      return rc;
+  }
+  if (flags & SQ_GROUP_FOLD) {
+    if ((rc = sq::launch_fill(g->s, g->K, 0.0f, st)) != SQ_OK) return rc;
+    if ((rc = sq::launch_colmax(g->W, g->wt, g->N, g->K, g->ldw, g->s, st)) != SQ_OK) return rc;
+    if ((rc = sq::launch_smooth_scale(g->act_max, g->s, g->K, g->alpha, st)) != SQ_OK) return rc;
+    if ((rc = sq::launch_fold_quant(g->W, g->wt, g->N, g->K, g->ldw, g->s, g->Wq, g->w_scale, st)) !=
+        SQ_OK)
+      return rc;
+    if (is_static && (rc = sq::launch_static_scale(g->act_max, g->s, g->K, g->a_scale, st)) != SQ_OK)
+      return rc;
+  }
+  if ((flags & SQ_GROUP_FORWARD) && g->M > 0) {
+    if ((rc = sq::launch_quant_act(g->X, g->xt, g->M, g->K, g->ldx, g->s, g->mode, g->Xq, g->a_scale,
+                                   st)) != SQ_OK)
+      return rc;
+    if (lora && (rc = sq::launch_lora_shrink(g->X, g->xt, g->M, g->K, g->ldx, g->A, g->r, g->T,
+                                             g->ldt, g->workspace, st)) != SQ_OK)
+      return rc;
+    if (gemm_begin != nullptr && hipEventRecord((hipEvent_t)gemm_begin, st) != hipSuccess)
+      return SQ_ERR_HIP;
+    rc = lora ? sq::launch_gemm_lora(g->Xq, g->Wq, g->a_scale, g->mode, g->w_scale, g->M, g->N, g->K,
+                                     g->T, g->ldt, g->B, g->r, g->lora_scale, g->Y, g->yt, g->ldy, st)
+              : sq::launch_gemm(g->Xq, g->Wq, g->a_scale, g->mode, g->w_scale, g->M, g->N, g->K, g->Y,
+                                g->yt, g->ldy, st);
+    if (rc != SQ_OK) return rc;
+    if (gemm_end != nullptr && hipEventRecord((hipEvent_t)gemm_end, st) != hipSuccess)
+      return SQ_ERR_HIP;
+  }
+  return SQ_OK;
+}
+
 }  // extern "C"

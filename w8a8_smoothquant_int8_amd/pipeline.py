@@ -14,6 +14,9 @@ in its own rank columns and zeros elsewhere), so each output column gets only
 its own adapter's delta, exactly as separate per-projection calls would give.
 Per-projection outputs are column views of one [M, sum N] buffer.
 
+run() issues calibrate, fold and the fused forward pass of a group as one
+native call (sq_linear_group_run): the same kernels, one host call.
+
 Unfused (fuse=False): one GEMM and one shrink+expand LoRA call per
 projection, the path the fused one is checked against. Per-request
 (segmented) adapters always use the separate segmented call on the column
@@ -30,9 +33,13 @@ from typing import Dict, List, Optional, Tuple
 
 import torch
 
-from . import (SQ_MAX_LORA_RANK, sq_calibrate_absmax, sq_lora_apply, sq_lora_apply_segmented,
-               sq_lora_shrink, sq_lora_workspace_bytes, sq_quant_per_token, sq_smooth_fold,
-               sq_static_act_scale, sq_w8a8_gemm, sq_w8a8_gemm_lora)
+from . import (SQ_GROUP_CALIBRATE, SQ_GROUP_FOLD, SQ_GROUP_FORWARD, SQ_MAX_LORA_RANK,
+               sq_calibrate_absmax, sq_linear_group_desc, sq_linear_group_run, sq_lora_apply,
+               sq_lora_apply_segmented, sq_lora_shrink, sq_lora_workspace_bytes,
+               sq_quant_per_token, sq_smooth_fold, sq_static_act_scale, sq_w8a8_gemm,
+               sq_w8a8_gemm_lora)
+
+ALL_PHASES = SQ_GROUP_CALIBRATE | SQ_GROUP_FOLD | SQ_GROUP_FORWARD
 
 _OUT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
@@ -141,6 +148,25 @@ class LinearGroup:
             g = self.seg_lora[proj]
             sq_lora_apply_segmented(X, g.seg_start, g.seg_adapter, g.A_ptrs, g.B_ptrs, g.ranks,
                                     g.max_rank, self.Y[proj], self.ws, scale=self.lora_scale)
+
+    # -- one native call per step ---------------------------------------------
+    def run(self, X: torch.Tensor, X_cal: Optional[torch.Tensor], flags: int = ALL_PHASES,
+            mode: str = "dynamic", stream=None, gemm_begin=None, gemm_end=None) -> None:
+        """The selected phases (calibrate, fold, forward) as one sq_linear_group_run
+        call: the same kernels as calibrate() + fold() + forward() on the fused
+        path, launched from native code. Needs the fused LoRA path or no LoRA."""
+        if self.seg_lora or (self.lora and not self.fused):
+            raise ValueError("run() covers the stacked-LoRA (fused) and no-LoRA groups")
+        key = (X.data_ptr(), None if X_cal is None else X_cal.data_ptr(), mode)
+        if getattr(self, "_desc_key", None) != key:
+            lora = dict(A=self.A_stack, B=self.B_blk, T=self.T, workspace=self.ws,
+                        lora_scale=self.lora_scale) if self.fused else {}
+            self._desc = sq_linear_group_desc(X, X_cal, self.W, self.alpha, mode, self.act_max,
+                                              self.s, self.Wq, self.w_scale, self.Xq, self._a(mode),
+                                              self.Yg, **lora)
+            self._desc_inputs = (X, X_cal)      # keep the tensors the pointers refer to alive
+            self._desc_key = key
+        sq_linear_group_run(self._desc, flags, stream, gemm_begin, gemm_end)
 
     def forward(self, X: torch.Tensor, mode: str = "dynamic") -> Dict[str, torch.Tensor]:
         self.quantize(X, mode)
