@@ -205,58 +205,64 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
 }
 
 // ---------------------------------------------------------------------------
-// Wave-per-row variant, for rows of at most 4096 channels (CPL <= 8 chunks
-// per lane: the raw row and its smoothed values fit one wave's registers
-// together) and, for 16-bit inputs, up to 14336 (the raw row alone fits; v
-// is recomputed in the second pass). Each wave owns whole rows (grid-stride over waves), so the row
-// max is a wave reduction and the kernel has no barrier after its start. The
-// per-channel factors live in LDS, computed once per block: fp32 s for FOLD,
-// fp64 1/s otherwise, laid out so that the 16-byte reads of consecutive lanes
-// are consecutive (no bank conflict). Lane l covers chunks c = l + 64 j
-// (j < CPL) of 8 channels. When v is kept, the next row is loaded into the
-// raw registers as soon as v is formed; otherwise after the second pass.
+// Wave-per-row quantizer: WPR = 1, 2 or 4 waves per row (K <= 4096, 8192,
+// 16384 for 16-bit inputs; fp32 inputs up to 4096), each lane covering at
+// most CPL = 8 chunks of 8 channels, so that the raw row share, its smoothed
+// values v and the next row's loads all fit in registers. With one wave per
+// row the row max is a wave reduction and the kernel has no barrier after its
+// start; with 2 or 4 the row's waves meet in LDS, one block barrier per row.
+// The per-channel factors live in LDS, computed once per block: fp32 s for
+// FOLD, fp64 1/s otherwise, laid out so that the 16-byte reads of consecutive
+// lanes are consecutive (no bank conflict). Lane l of the row's wave h covers
+// chunks c = 64 CPL h + l + 64 j (j < CPL); pass 1 forms v and the row max,
+// the raw registers then take the wave's next row while this one is reduced
+// and quantized from v.
 // ---------------------------------------------------------------------------
 constexpr int kWaveRowThreads = 512;
 
-template <int DT, int KIND, int CPL>
+template <int DT, int KIND, int CPL, int WPR>
 struct WaveRowCfg {
   static constexpr int kWords = DT == SQ_F32 ? 2 : 1;          // 16-byte words per chunk
   static constexpr int kTabParts = KIND == Q_FOLD ? 2 : 4;     // 16-byte factor words per chunk
-  // Up to 8 chunks per lane v is kept next to the raw row; beyond, only the
-  // raw row fits (at most 28 chunks of 16-bit values: 112 registers) and the
-  // second pass recomputes v.
-  static constexpr bool kStoreV = CPL <= 8;
-  static constexpr int kGroup = kStoreV ? 4 : 1;                 // chunks per scheduling group
-  static_assert(CPL * kWords <= 28, "the raw row must fit 112 registers");
+  static constexpr int kGroup = 4;                             // chunks per factor-read group
+  static_assert(CPL <= 8, "raw row, v and the next row must fit the registers");
+  static_assert(WPR == 1 || WPR == 2 || WPR == 4, "1, 2 or 4 waves per row");
 };
 
-template <int DT, int KIND, int CPL>
+template <int DT, int KIND, int CPL, int WPR>
 __global__ void __launch_bounds__(kWaveRowThreads)
 k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_bytes,
              const float* __restrict__ s, float* __restrict__ scale_io, int8_t* __restrict__ out) {
-  using Cfg = WaveRowCfg<DT, KIND, CPL>;
+  using Cfg = WaveRowCfg<DT, KIND, CPL, WPR>;
   constexpr int kWords = Cfg::kWords;
-  constexpr bool kStoreV = Cfg::kStoreV;
   constexpr int kGroup = Cfg::kGroup;
-  // factor word p of chunk c at tab[p * 64 * CPL + c]
-  __shared__ uint4 tab[Cfg::kTabParts * 64 * CPL];
+  constexpr int kSpan = 64 * CPL;                  // chunks per wave
+  // factor word p of chunk c at tab[p * kSpan * WPR + c]
+  __shared__ uint4 tab[Cfg::kTabParts * kSpan * WPR];
+  __shared__ float red[2][kWaveRowThreads / 64];
   const int nch = K / 8;
   const int lane = threadIdx.x & 63;
-  const int wpb = blockDim.x >> 6;
-  const int64_t nw = (int64_t)gridDim.x * wpb;
-  int64_t m = (int64_t)blockIdx.x * wpb + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int half = wave % WPR;
+  const int slot = wave / WPR;                     // row slot within the block
+  const int slots = (blockDim.x >> 6) / WPR;
+  const int64_t row_step = (int64_t)gridDim.x * slots;
+  const int64_t iters = (rows + row_step - 1) / row_step;   // the same for every wave
+  int64_t m = (int64_t)blockIdx.x * slots + slot;
+  const int c0 = kSpan * half + lane;              // this lane's first chunk
 
   // Chunks past the row end (c >= nch) load chunk nch - 1 and read its factors;
   // their values are zeroed before the max and they are never stored. No
   // branch in the arithmetic, so loads and LDS reads can be issued early.
   uint4 raw[CPL][kWords];
+  auto chunk = [&](int j) { return c0 + 64 * j < nch ? c0 + 64 * j : nch - 1; };
   auto load = [&](int64_t row) {
     const char* p = in + row * in_ld_bytes;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j < nch ? lane + 64 * j : nch - 1;
 #pragma unroll
-      for (int q = 0; q < kWords; ++q) raw[j][q] = ((const uint4*)(p + (int64_t)c * 8 * DtSize<DT>::v))[q];
+      for (int q = 0; q < kWords; ++q)
+        raw[j][q] = ((const uint4*)(p + (int64_t)chunk(j) * 8 * DtSize<DT>::v))[q];
     }
   };
   if (m < rows) load(m);
@@ -268,27 +274,30 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
     if constexpr (KIND == Q_FOLD) {
       tab[c] = make_uint4(__float_as_uint(sv[0]), __float_as_uint(sv[1]), __float_as_uint(sv[2]),
                           __float_as_uint(sv[3]));
-      tab[64 * CPL + c] = make_uint4(__float_as_uint(sv[4]), __float_as_uint(sv[5]),
-                                     __float_as_uint(sv[6]), __float_as_uint(sv[7]));
+      tab[kSpan * WPR + c] = make_uint4(__float_as_uint(sv[4]), __float_as_uint(sv[5]),
+                                        __float_as_uint(sv[6]), __float_as_uint(sv[7]));
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const double r0 = 1.0 / (double)sv[2 * q];       // RN64(1/s), IEEE fp64 division
         const double r1 = 1.0 / (double)sv[2 * q + 1];
         const unsigned long long b0 = __double_as_longlong(r0), b1 = __double_as_longlong(r1);
-        tab[q * 64 * CPL + c] = make_uint4((uint32_t)b0, (uint32_t)(b0 >> 32), (uint32_t)b1,
-                                           (uint32_t)(b1 >> 32));
+        tab[q * kSpan * WPR + c] = make_uint4((uint32_t)b0, (uint32_t)(b0 >> 32), (uint32_t)b1,
+                                              (uint32_t)(b1 >> 32));
       }
     }
   }
   __syncthreads();
 
-  // v for chunk j of this lane from its raw 8 values
-  auto smooth8 = [&](int j, float* x) {
-    int c = lane + 64 * j < nch ? lane + 64 * j : nch - 1;
-    if constexpr (!kStoreV) asm volatile("" : "+v"(c));   // factor reads are redone in pass 2
+  // v for chunk j of this lane from its raw 8 values. `dep` is a value the
+  // factor reads must wait for (see the pass-1 loop); through it the factor
+  // index is opaque to the compiler, which would otherwise hoist the reads of
+  // all chunks (16 registers each) out of the row loop or to its top, and spill.
+  auto smooth8 = [&](int j, float* x, float dep) {
+    int c = chunk(j);
+    asm volatile("" : "+v"(c) : "v"(dep));
     if constexpr (KIND == Q_FOLD) {
-      const uint4 f0 = tab[c], f1 = tab[64 * CPL + c];
+      const uint4 f0 = tab[c], f1 = tab[kSpan * WPR + c];
       const float f[8] = {__uint_as_float(f0.x), __uint_as_float(f0.y), __uint_as_float(f0.z),
                           __uint_as_float(f0.w), __uint_as_float(f1.x), __uint_as_float(f1.y),
                           __uint_as_float(f1.z), __uint_as_float(f1.w)};
@@ -297,7 +306,7 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 f = tab[q * 64 * CPL + c];
+        const uint4 f = tab[q * kSpan * WPR + c];
         const double r0 = __longlong_as_double(((unsigned long long)f.y << 32) | f.x);
         const double r1 = __longlong_as_double(((unsigned long long)f.w << 32) | f.z);
         x[2 * q] = div_rn(x[2 * q], r0);                        // fp32(x / s), exact
@@ -313,24 +322,36 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
     r_static = a_static != 0.0f ? 1.0 / (double)a_static : 0.0;
   }
 
-  for (; m < rows; m += nw) {
-    float v[kStoreV ? CPL : 1][8];
+  for (int64_t it = 0; it < iters; ++it, m += row_step) {
+    const bool active = m < rows;                 // uniform over the wave pair
+    float v[CPL][8];
     float amax = 0.0f;
+    if (active) {
+      // Chunks in groups of kGroup: a group's factor reads wait for the
+      // previous group's results (registers stay bounded).
+      float dep = 0.0f;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      float x[8];
-      widen8<DT>(raw[j], x);
-      smooth8(j, x);
-      const bool in_row = lane + 64 * j < nch;
+      for (int j = 0; j < CPL; ++j) {
+        if (j % kGroup == 0 && j > 0) dep = v[j - 1][7];
+        float x[8];
+        widen8<DT>(raw[j], x);
+        smooth8(j, x, dep);
+        const bool in_row = c0 + 64 * j < nch;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if constexpr (kStoreV) v[j][e] = x[e];
-        amax = __builtin_fmaxf(amax, in_row ? __builtin_fabsf(x[e]) : 0.0f);
+        for (int e = 0; e < 8; ++e) {
+          v[j][e] = x[e];
+          amax = __builtin_fmaxf(amax, in_row ? __builtin_fabsf(x[e]) : 0.0f);
+        }
       }
-      // scheduling groups: their LDS reads issue together, registers stay bounded
-      if (j % kGroup == kGroup - 1) __builtin_amdgcn_sched_barrier(0);
+      // The next row's loads reuse the raw registers: they must not be
+      // issued before pass 1 is done with them (an opaque zero that depends
+      // on the row max keeps the compiler from hoisting them).
+      if (m + row_step < rows) {
+        int zero;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(zero) : "v"(amax));
+        load(m + row_step + zero);
+      }
     }
-    if (kStoreV && m + nw < rows) load(m + nw);
 
     float scale;
     double rscale;
@@ -338,40 +359,36 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
       scale = a_static;
       rscale = r_static;
     } else {
-      scale = wave_max(amax) / 127.0f;                           // IEEE fp32 division
+      amax = wave_max(amax);
+      if constexpr (WPR > 1) {
+        // the row's waves meet in LDS (double-buffered: one barrier per row)
+        float* r = red[it & 1];
+        if (lane == 0) r[wave] = amax;
+        __syncthreads();
+        amax = r[WPR * slot];
+#pragma unroll
+        for (int w = 1; w < WPR; ++w) amax = __builtin_fmaxf(amax, r[WPR * slot + w]);
+      }
+      scale = amax / 127.0f;                                     // IEEE fp32 division
       rscale = scale != 0.0f ? 1.0 / (double)scale : 0.0;
-      if (lane == 0) scale_io[m] = scale;
+      if (active && half == 0 && lane == 0) scale_io[m] = scale;
     }
+    if (!active) continue;
 
     int8_t* orow = out + m * K;
     // scale == 0 (all-zero row, or a zero static scale): every code is 0
     const uint32_t keep = scale != 0.0f ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      float y[8];
-      if constexpr (kStoreV) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = v[j][e];
-      } else {
-        // Opaque to the compiler: otherwise it keeps pass 1's values of all
-        // chunks alive instead of recomputing them here, and spills.
-#pragma unroll
-        for (int q = 0; q < kWords; ++q)
-          asm volatile("" : "+v"(raw[j][q].x), "+v"(raw[j][q].y), "+v"(raw[j][q].z), "+v"(raw[j][q].w));
-        widen8<DT>(raw[j], y);
-        smooth8(j, y);
-      }
       int q[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = quant_code(div_rn(y[e], rscale));
+      for (int e = 0; e < 8; ++e) q[e] = quant_code(div_rn(v[j][e], rscale));
       uint2 pk;
       pk.x = pack4_i8(q[0], q[1], q[2], q[3]) & keep;
       pk.y = pack4_i8(q[4], q[5], q[6], q[7]) & keep;
-      const int c = lane + 64 * j;
+      const int c = c0 + 64 * j;
       if (c < nch) *(uint2*)(orow + c * 8) = pk;
-      if (j % kGroup == kGroup - 1) __builtin_amdgcn_sched_barrier(0);
     }
-    if (!kStoreV && m + nw < rows) load(m + nw);
   }
 }
 
@@ -394,13 +411,14 @@ static int64_t resident_blocks(const void* f, int T) {
   return (int64_t)per_cu[dev] * cus[dev];
 }
 
-template <int DT, int KIND, int CPL>
+template <int DT, int KIND, int CPL, int WPR>
 static void launch_wave(const char* p, int64_t rows, int64_t K, int64_t ldb, const float* s,
                         float* scale_io, int8_t* out, hipStream_t st) {
-  auto f = k_quant_wave<DT, KIND, CPL>;
-  constexpr int W = kWaveRowThreads / 64;
-  int64_t grid = (rows + W - 1) / W;
-  const int64_t cap = resident_blocks<WaveRowCfg<DT, KIND, CPL>>((const void*)f, kWaveRowThreads);
+  auto f = k_quant_wave<DT, KIND, CPL, WPR>;
+  constexpr int slots = kWaveRowThreads / 64 / WPR;
+  int64_t grid = (rows + slots - 1) / slots;
+  const int64_t cap =
+      resident_blocks<WaveRowCfg<DT, KIND, CPL, WPR>>((const void*)f, kWaveRowThreads);
   if (grid > cap) grid = cap;
   f<<<(unsigned)grid, kWaveRowThreads, 0, st>>>(p, rows, (int)K, ldb, s, scale_io, out);
 }
@@ -421,13 +439,16 @@ static void pick_shape(int64_t K, int* T, int* cpt, int* rpb) {
 }
 
 template <int DT, int CPT, int KIND, int RPB>
+struct RowsTag {};
+
+template <int DT, int CPT, int KIND, int RPB>
 static void launch_shape(const char* p, int64_t rows, int64_t K, int64_t ldb, const float* s,
                          float* scale_io, int8_t* out, int T, hipStream_t st) {
   auto f = k_quant_rows<DT, CPT, KIND, RPB>;
   // One row group per block while the whole problem fits on the chip at once;
   // beyond that a full wave of blocks, each walking several groups.
   int64_t grid = (rows + RPB - 1) / RPB;
-  const int64_t cap = resident_blocks<decltype(f)>((const void*)f, T);
+  const int64_t cap = resident_blocks<RowsTag<DT, CPT, KIND, RPB>>((const void*)f, T);
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
   f<<<(unsigned)grid, T, 0, st>>>(p, rows, K, ldb, s, scale_io, out);
@@ -438,24 +459,32 @@ static int launch_rows_dt(const void* in, int64_t rows, int64_t K, int64_t ld, c
                           float* scale_io, int8_t* out, hipStream_t st) {
   const char* p = (const char*)in;
   const int64_t ldb = ld * DtSize<DT>::v;
-  // wave per row up to K = 4096, and for 16-bit inputs up to K = 14336 (8,
-  // resp. 28 chunks per lane)
+  // waves per row: 1 up to K = 4096 (8 chunks per lane); for 16-bit inputs
+  // 2 up to 8192 and 4 up to 16384
   const int64_t lane_chunks = (K / 8 + 63) / 64;
-  if (lane_chunks <= 8 || (DT != SQ_F32 && lane_chunks <= 28)) {
-    if (lane_chunks <= 2) launch_wave<DT, KIND, 2>(p, rows, K, ldb, s, scale_io, out, st);
-    else if (lane_chunks <= 4) launch_wave<DT, KIND, 4>(p, rows, K, ldb, s, scale_io, out, st);
-    else if (lane_chunks <= 8) launch_wave<DT, KIND, 8>(p, rows, K, ldb, s, scale_io, out, st);
-    else if constexpr (DT != SQ_F32) {
-      switch ((lane_chunks + 3) / 4) {
-        case 3: launch_wave<DT, KIND, 12>(p, rows, K, ldb, s, scale_io, out, st); break;
-        case 4: launch_wave<DT, KIND, 16>(p, rows, K, ldb, s, scale_io, out, st); break;
-        case 5: launch_wave<DT, KIND, 20>(p, rows, K, ldb, s, scale_io, out, st); break;
-        case 6: launch_wave<DT, KIND, 24>(p, rows, K, ldb, s, scale_io, out, st); break;
-        default: launch_wave<DT, KIND, 28>(p, rows, K, ldb, s, scale_io, out, st); break;
-      }
-    }
+  if (lane_chunks <= 8) {
+    if (lane_chunks <= 2) launch_wave<DT, KIND, 2, 1>(p, rows, K, ldb, s, scale_io, out, st);
+    else if (lane_chunks <= 4) launch_wave<DT, KIND, 4, 1>(p, rows, K, ldb, s, scale_io, out, st);
+    else launch_wave<DT, KIND, 8, 1>(p, rows, K, ldb, s, scale_io, out, st);
     SQ_LAUNCH_CHECK();
     return SQ_OK;
+  }
+  if constexpr (DT != SQ_F32) {
+    if (lane_chunks <= 32) {
+      const int wpr = lane_chunks <= 16 ? 2 : 4;
+      const int64_t cpl = (lane_chunks + wpr - 1) / wpr;    // 5 .. 8
+#define SQ_WAVE_CPL(W)                                                                       \
+  switch (cpl) {                                                                             \
+    case 5: launch_wave<DT, KIND, 5, W>(p, rows, K, ldb, s, scale_io, out, st); break;       \
+    case 6: launch_wave<DT, KIND, 6, W>(p, rows, K, ldb, s, scale_io, out, st); break;       \
+    case 7: launch_wave<DT, KIND, 7, W>(p, rows, K, ldb, s, scale_io, out, st); break;       \
+    default: launch_wave<DT, KIND, 8, W>(p, rows, K, ldb, s, scale_io, out, st); break;      \
+  }
+      if (wpr == 2) { SQ_WAVE_CPL(2) } else { SQ_WAVE_CPL(4) }
+#undef SQ_WAVE_CPL
+      SQ_LAUNCH_CHECK();
+      return SQ_OK;
+    }
   }
   int T, cpt, rpb;
   pick_shape(K, &T, &cpt, &rpb);
