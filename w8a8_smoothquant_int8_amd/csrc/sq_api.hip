@@ -16,6 +16,10 @@
 namespace sq {
 int launch_colmax(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, float* out, hipStream_t st);
 int launch_fill(float* p, int64_t n, float v, hipStream_t st);
+int launch_fill2(float* p1, int64_t n1, float* p2, int64_t n2, float v, hipStream_t st);
+int launch_colmax2(const void* X1, int xt1, int64_t M1, int64_t K1, int64_t ld1, float* out1,
+                   const void* X2, int xt2, int64_t M2, int64_t K2, int64_t ld2, float* out2,
+                   hipStream_t st);
 int launch_smooth_scale(const float* act_max, float* s_inout, int64_t K, double alpha, hipStream_t st);
 int launch_static_scale(const float* act_max, const float* s, int64_t K, float* a_scale, hipStream_t st);
 int launch_fold_quant(const void* W, int wt, int64_t N, int64_t K, int64_t ldw, const float* s,
@@ -406,15 +410,23 @@ int sq_linear_group_run(const sq_linear_group* g, int flags, void* stream, void*
   if ((rc = gate()) != SQ_OK) return rc;
   hipStream_t st = as_stream(stream);
   // 2. launch
-  if (flags & SQ_GROUP_CALIBRATE) {
-    if ((rc = sq::launch_fill(g->act_max, g->K, 0.0f, st)) != SQ_OK) return rc;
-    if (g->M_cal > 0 &&
-        (rc = sq::launch_colmax(g->X_cal, g->xt, g->M_cal, g->K, g->ld_cal, g->act_max, st)) != SQ_OK)
+  const bool cal = flags & SQ_GROUP_CALIBRATE, fold = flags & SQ_GROUP_FOLD;
+  if (cal && fold) {
+    // both column maxima (act_max over X_cal, w_max over W, accumulated in s)
+    // from one zero-fill and one two-job column-max launch
+    if ((rc = sq::launch_fill2(g->act_max, g->K, g->s, g->K, 0.0f, st)) != SQ_OK) return rc;
+    if ((rc = sq::launch_colmax2(g->X_cal, g->xt, g->M_cal, g->K, g->ld_cal, g->act_max, g->W,
+                                 g->wt, g->N, g->K, g->ldw, g->s, st)) != SQ_OK)
       return rc;
-  }
-  if (flags & SQ_GROUP_FOLD) {
+  } else if (cal) {
+    if ((rc = sq::launch_fill(g->act_max, g->K, 0.0f, st)) != SQ_OK) return rc;
+    if ((rc = sq::launch_colmax(g->X_cal, g->xt, g->M_cal, g->K, g->ld_cal, g->act_max, st)) != SQ_OK)
+      return rc;
+  } else if (fold) {
     if ((rc = sq::launch_fill(g->s, g->K, 0.0f, st)) != SQ_OK) return rc;
     if ((rc = sq::launch_colmax(g->W, g->wt, g->N, g->K, g->ldw, g->s, st)) != SQ_OK) return rc;
+  }
+  if (fold) {
     if ((rc = sq::launch_smooth_scale(g->act_max, g->s, g->K, g->alpha, st)) != SQ_OK) return rc;
     if ((rc = sq::launch_fold_quant(g->W, g->wt, g->N, g->K, g->ldw, g->s, g->Wq, g->w_scale, st)) !=
         SQ_OK)
