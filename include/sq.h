@@ -121,6 +121,20 @@ int sq_static_act_scale(const float* act_max, const float* s, int64_t K, float* 
 int sq_quant_per_token(const void* X, int xt, int64_t M, int64_t K, int64_t ldx,
                        const float* s, int mode, int8_t* Xq, float* a_scale, void* stream);
 
+/* [SQ] Step 6, static variant, with the clip count that "Calibration in
+ * practice" and the page's closing advice ask to watch: a fixed per-tensor
+ * scale lets values beyond the calibrated range clip, and the share of
+ * clipped codes is the signal that the static scale no longer fits.
+ * Xq exactly as sq_quant_per_token in static mode (a_scale[0] read, [1]).
+ * *clipped += the number of elements whose rounded code rne(x_s / a_scale)
+ * had magnitude above 127 and was clamped (a zero scale clips nothing).
+ * clipped: one device uint64, 8-byte aligned, accumulated (never reset by
+ * this call), so several batches or layers can share one counter; the
+ * caller zeroes it. Count is exact and independent of launch order. */
+int sq_quant_static_clipped(const void* X, int xt, int64_t M, int64_t K, int64_t ldx,
+                            const float* s, const float* a_scale, int8_t* Xq,
+                            unsigned long long* clipped, void* stream);
+
 /* [SQ] Step 7: INT8 x INT8 -> INT32 GEMM with the dequant epilogue.
  * acc[m, n] = sum_k Xq[m, k] * Wq[n, k] (exact INT32: |acc| <= K * 127^2);
  * Y[m, n] = yt((fp32(acc) * a_scale[m]) * w_scale[n]), one RNE rounding to yt.

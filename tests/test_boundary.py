@@ -36,7 +36,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sq.SIGNATURES)
@@ -124,6 +124,19 @@ def test_quant_validation(L):
     assert f(P, sq.SQ_BF16, 4, 64, 64, NULL, 0, P, NULL, S) == sq.SQ_ERR_INVALID_ARG
     assert f(P, sq.SQ_BF16, 4, 64, 64, NULL, 0, P4, P, S) == sq.SQ_ERR_MISALIGNED
     assert f(P, sq.SQ_BF16, 0, 64, 64, NULL, 0, P, P, S) == sq.SQ_OK
+
+
+def test_static_clipped_validation(L):
+    f = L.sq_quant_static_clipped
+    P8 = ctypes.c_void_p(0x10008)
+    assert f(P, sq.SQ_BF16, 4, 64, 64, NULL, P, P, NULL, S) == sq.SQ_ERR_INVALID_ARG    # counter
+    assert f(P, sq.SQ_BF16, 4, 64, 64, NULL, NULL, P, P, S) == sq.SQ_ERR_INVALID_ARG    # scale
+    assert f(P, sq.SQ_BF16, 4, 64, 64, NULL, P, NULL, P, S) == sq.SQ_ERR_INVALID_ARG    # Xq
+    assert f(P, sq.SQ_BF16, 4, 64, 64, NULL, P, P, P4, S) == sq.SQ_ERR_MISALIGNED       # counter % 8
+    assert f(P, sq.SQ_BF16, 4, 64, 64, NULL, P, P4, P, S) == sq.SQ_ERR_MISALIGNED       # Xq % 16
+    assert f(P, sq.SQ_BF16, 4, 40, 48, NULL, P, P, P, S) == sq.SQ_ERR_MISALIGNED        # K % 16
+    assert f(P, 9, 4, 64, 64, NULL, P, P, P, S) == sq.SQ_ERR_UNSUPPORTED_DTYPE
+    assert f(P, sq.SQ_BF16, 0, 64, 64, NULL, P, P, P8, S) == sq.SQ_OK                   # M == 0
 
 
 def test_gemm_validation(L):

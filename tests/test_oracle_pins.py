@@ -458,3 +458,26 @@ def test_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(O, "lora_shrink", lambda x, dt, a: orig_shrink(x, "bf16", a) * 0)
     assert _fails(lambda: test_brute_force_lora(1))
     monkeypatch.setattr(O, "lora_shrink", orig_shrink)
+
+
+def test_static_clip_count_brute_force_ties():
+    """The clip count is the number of codes whose half-to-even rounding leaves
+    [-127, 127] ("SmoothQuant" explainer, "How it works", Step 6, static scale):
+    127.5 and 128.5 round to 128 and clip, 126.5 rounds to 126 and does not."""
+    row = np.array([126.4, 127.4, 127.5, 128.6, -127.5, -127.49, 200.0, -1000.0,
+                    126.5, 0.0, 1.0, -1.0, 127.0, -127.0, 128.5, 3.0], np.float32)
+    x = np.stack([row, -row])
+    q, clipped = O.quantize_per_tensor_static(x, None, np.float32(1.0))
+    by_hand = 0
+    for v in x.ravel():
+        f = float(v)
+        r = round(f)                      # Python rounds half to even
+        by_hand += abs(r) > 127
+    assert clipped == by_hand == 12
+    assert q[0, 2] == 127 and q[0, 4] == -127 and q[0, 8] == 126 and q[0, 14] == 127
+    # with a scale of 2 and s = 4 every value is divided by 8: nothing clips
+    q8, c8 = O.quantize_per_tensor_static(x, np.full(16, 4.0, np.float32), np.float32(2.0))
+    assert c8 == 0 and q8[0, 6] == 25
+    # a zero scale gives zero codes and no clips
+    q0, c0 = O.quantize_per_tensor_static(x, None, np.float32(0.0))
+    assert c0 == 0 and not q0.any()

@@ -45,6 +45,8 @@ SIGNATURES = {
     "sq_smooth_fold": (_c_int, [_vp, _vp, _c_int, _c_i64, _c_i64, _c_i64, _c_d, _vp, _vp, _vp, _vp]),
     "sq_static_act_scale": (_c_int, [_vp, _vp, _c_i64, _vp, _vp]),
     "sq_quant_per_token": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _c_int, _vp, _vp, _vp]),
+    "sq_quant_static_clipped": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp,
+                                         _vp]),
     "sq_w8a8_gemm": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_int,
                               _c_i64, _vp]),
     "sq_w8a8_gemm_i32": (_c_int, [_vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp]),
@@ -186,6 +188,16 @@ def sq_quant_per_token(X: torch.Tensor, s: Optional[torch.Tensor], Xq: torch.Ten
     M, K = X.shape
     _check("sq_quant_per_token", lib().sq_quant_per_token(
         _ptr(X), _dt(X), M, K, _ld(X), _ptr(s), MODES[mode], _ptr(Xq), _ptr(a_scale),
+        _stream(stream)))
+
+
+def sq_quant_static_clipped(X: torch.Tensor, s: Optional[torch.Tensor], a_scale: torch.Tensor,
+                            Xq: torch.Tensor, clipped: torch.Tensor, stream=None) -> None:
+    """Static per-tensor quant; adds the number of clamped codes to clipped
+    (one int64 element on the device, which the caller zeroes)."""
+    M, K = X.shape
+    _check("sq_quant_static_clipped", lib().sq_quant_static_clipped(
+        _ptr(X), _dt(X), M, K, _ld(X), _ptr(s), _ptr(a_scale), _ptr(Xq), _ptr(clipped),
         _stream(stream)))
 
 

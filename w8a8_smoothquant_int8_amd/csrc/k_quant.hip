@@ -20,7 +20,11 @@
 
 namespace sq {
 
-enum QuantKind { Q_FOLD = 0, Q_DYNAMIC = 1, Q_STATIC = 2 };
+// Q_STATIC_CLIP: Q_STATIC that also counts the codes it clamps (a kind of its
+// own, so the plain static kernels carry none of the counting registers).
+enum QuantKind { Q_FOLD = 0, Q_DYNAMIC = 1, Q_STATIC = 2, Q_STATIC_CLIP = 3 };
+template <int KIND>
+constexpr bool kStaticKind = KIND == Q_STATIC || KIND == Q_STATIC_CLIP;
 
 constexpr int kQuantMaxThreads = 512;
 
@@ -73,7 +77,8 @@ __device__ __forceinline__ void widen8(const uint4* w, float* out) {
 template <int DT, int CPT, int KIND, int RPB>
 __global__ void __launch_bounds__(kQuantMaxThreads)
 k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld_bytes,
-             const float* __restrict__ s, float* __restrict__ scale_io, int8_t* __restrict__ out) {
+             const float* __restrict__ s, float* __restrict__ scale_io, int8_t* __restrict__ out,
+             unsigned long long* __restrict__ clip) {
   const int tid = threadIdx.x;
   const int T = blockDim.x;
   const int lane = tid & 63;
@@ -108,9 +113,11 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
     }
   }
 
+  constexpr bool counting = KIND == Q_STATIC_CLIP;   // clipped-code count into *clip
+  int nclip = 0;
   float a_static = 0.0f;
   double r_static = 0.0;
-  if constexpr (KIND == Q_STATIC) {
+  if constexpr (kStaticKind<KIND>) {
     a_static = scale_io[0];
     r_static = a_static != 0.0f ? 1.0 / (double)a_static : 0.0;
   }
@@ -151,7 +158,7 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
 
     float scale[RPB];
     double rscale[RPB];
-    if constexpr (KIND == Q_STATIC) {
+    if constexpr (kStaticKind<KIND>) {
 #pragma unroll
       for (int r = 0; r < RPB; ++r) { scale[r] = a_static; rscale[r] = r_static; }
     } else {
@@ -192,8 +199,12 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
           }
           int q[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            q[e] = scale[r] != 0.0f ? quant_code(div_rn(y[e], rscale[r])) : 0;
+          for (int e = 0; e < 8; ++e) {
+            if constexpr (counting)
+              q[e] = scale[r] != 0.0f ? quant_code_count(div_rn(y[e], rscale[r]), nclip) : 0;
+            else
+              q[e] = scale[r] != 0.0f ? quant_code(div_rn(y[e], rscale[r])) : 0;
+          }
           uint2 pk;
           pk.x = pack4_i8(q[0], q[1], q[2], q[3]);
           pk.y = pack4_i8(q[4], q[5], q[6], q[7]);
@@ -201,6 +212,11 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
         }
       }
     }
+  }
+  if constexpr (counting) {
+    // every lane reaches this point; one atomic per wave
+    const int n = wave_sum(nclip);
+    if ((threadIdx.x & 63) == 0 && n != 0) atomicAdd(clip, (unsigned long long)n);
   }
 }
 
@@ -232,7 +248,8 @@ struct WaveRowCfg {
 template <int DT, int KIND, int CPL, int WPR>
 __global__ void __launch_bounds__(kWaveRowThreads)
 k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_bytes,
-             const float* __restrict__ s, float* __restrict__ scale_io, int8_t* __restrict__ out) {
+             const float* __restrict__ s, float* __restrict__ scale_io, int8_t* __restrict__ out,
+             unsigned long long* __restrict__ clip) {
   using Cfg = WaveRowCfg<DT, KIND, CPL, WPR>;
   constexpr int kWords = Cfg::kWords;
   constexpr int kGroup = Cfg::kGroup;
@@ -315,9 +332,11 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
     }
   };
 
+  constexpr bool counting = KIND == Q_STATIC_CLIP;   // clipped-code count into *clip
+  int nclip = 0;
   float a_static = 0.0f;
   double r_static = 0.0;
-  if constexpr (KIND == Q_STATIC) {
+  if constexpr (kStaticKind<KIND>) {
     a_static = scale_io[0];
     r_static = a_static != 0.0f ? 1.0 / (double)a_static : 0.0;
   }
@@ -355,7 +374,7 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
 
     float scale;
     double rscale;
-    if constexpr (KIND == Q_STATIC) {
+    if constexpr (kStaticKind<KIND>) {
       scale = a_static;
       rscale = r_static;
     } else {
@@ -380,15 +399,28 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
     const uint32_t keep = scale != 0.0f ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
+      const int c = c0 + 64 * j;
       int q[8];
+      if constexpr (counting) {
+        // chunks past the row end hold a clamped re-read of the row: not counted
+        int n = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = quant_code(div_rn(v[j][e], rscale));
+        for (int e = 0; e < 8; ++e) q[e] = quant_code_count(div_rn(v[j][e], rscale), n);
+        nclip += c < nch ? n : 0;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = quant_code(div_rn(v[j][e], rscale));
+      }
       uint2 pk;
       pk.x = pack4_i8(q[0], q[1], q[2], q[3]) & keep;
       pk.y = pack4_i8(q[4], q[5], q[6], q[7]) & keep;
-      const int c = c0 + 64 * j;
       if (c < nch) *(uint2*)(orow + c * 8) = pk;
     }
+  }
+  if constexpr (counting) {
+    // every lane reaches this point; one atomic per wave
+    const int n = wave_sum(nclip);
+    if ((threadIdx.x & 63) == 0 && n != 0) atomicAdd(clip, (unsigned long long)n);
   }
 }
 
@@ -413,14 +445,14 @@ static int64_t resident_blocks(const void* f, int T) {
 
 template <int DT, int KIND, int CPL, int WPR>
 static void launch_wave(const char* p, int64_t rows, int64_t K, int64_t ldb, const float* s,
-                        float* scale_io, int8_t* out, hipStream_t st) {
+                        float* scale_io, int8_t* out, unsigned long long* clip, hipStream_t st) {
   auto f = k_quant_wave<DT, KIND, CPL, WPR>;
   constexpr int slots = kWaveRowThreads / 64 / WPR;
   int64_t grid = (rows + slots - 1) / slots;
   const int64_t cap =
       resident_blocks<WaveRowCfg<DT, KIND, CPL, WPR>>((const void*)f, kWaveRowThreads);
   if (grid > cap) grid = cap;
-  f<<<(unsigned)grid, kWaveRowThreads, 0, st>>>(p, rows, (int)K, ldb, s, scale_io, out);
+  f<<<(unsigned)grid, kWaveRowThreads, 0, st>>>(p, rows, (int)K, ldb, s, scale_io, out, clip);
 }
 
 // Block-per-row-group shape: chunks per thread CPT in {1, 2, 4, 8}, the
@@ -443,7 +475,8 @@ struct RowsTag {};
 
 template <int DT, int CPT, int KIND, int RPB>
 static void launch_shape(const char* p, int64_t rows, int64_t K, int64_t ldb, const float* s,
-                         float* scale_io, int8_t* out, int T, hipStream_t st) {
+                         float* scale_io, int8_t* out, unsigned long long* clip, int T,
+                         hipStream_t st) {
   auto f = k_quant_rows<DT, CPT, KIND, RPB>;
   // One row group per block while the whole problem fits on the chip at once;
   // beyond that a full wave of blocks, each walking several groups.
@@ -451,21 +484,21 @@ static void launch_shape(const char* p, int64_t rows, int64_t K, int64_t ldb, co
   const int64_t cap = resident_blocks<RowsTag<DT, CPT, KIND, RPB>>((const void*)f, T);
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
-  f<<<(unsigned)grid, T, 0, st>>>(p, rows, K, ldb, s, scale_io, out);
+  f<<<(unsigned)grid, T, 0, st>>>(p, rows, K, ldb, s, scale_io, out, clip);
 }
 
 template <int DT, int KIND>
 static int launch_rows_dt(const void* in, int64_t rows, int64_t K, int64_t ld, const float* s,
-                          float* scale_io, int8_t* out, hipStream_t st) {
+                          float* scale_io, int8_t* out, unsigned long long* clip, hipStream_t st) {
   const char* p = (const char*)in;
   const int64_t ldb = ld * DtSize<DT>::v;
   // waves per row: 1 up to K = 4096 (8 chunks per lane); for 16-bit inputs
   // 2 up to 8192 and 4 up to 16384
   const int64_t lane_chunks = (K / 8 + 63) / 64;
   if (lane_chunks <= 8) {
-    if (lane_chunks <= 2) launch_wave<DT, KIND, 2, 1>(p, rows, K, ldb, s, scale_io, out, st);
-    else if (lane_chunks <= 4) launch_wave<DT, KIND, 4, 1>(p, rows, K, ldb, s, scale_io, out, st);
-    else launch_wave<DT, KIND, 8, 1>(p, rows, K, ldb, s, scale_io, out, st);
+    if (lane_chunks <= 2) launch_wave<DT, KIND, 2, 1>(p, rows, K, ldb, s, scale_io, out, clip, st);
+    else if (lane_chunks <= 4) launch_wave<DT, KIND, 4, 1>(p, rows, K, ldb, s, scale_io, out, clip, st);
+    else launch_wave<DT, KIND, 8, 1>(p, rows, K, ldb, s, scale_io, out, clip, st);
     SQ_LAUNCH_CHECK();
     return SQ_OK;
   }
@@ -475,10 +508,10 @@ static int launch_rows_dt(const void* in, int64_t rows, int64_t K, int64_t ld, c
       const int64_t cpl = (lane_chunks + wpr - 1) / wpr;    // 5 .. 8
 #define SQ_WAVE_CPL(W)                                                                       \
   switch (cpl) {                                                                             \
-    case 5: launch_wave<DT, KIND, 5, W>(p, rows, K, ldb, s, scale_io, out, st); break;       \
-    case 6: launch_wave<DT, KIND, 6, W>(p, rows, K, ldb, s, scale_io, out, st); break;       \
-    case 7: launch_wave<DT, KIND, 7, W>(p, rows, K, ldb, s, scale_io, out, st); break;       \
-    default: launch_wave<DT, KIND, 8, W>(p, rows, K, ldb, s, scale_io, out, st); break;      \
+    case 5: launch_wave<DT, KIND, 5, W>(p, rows, K, ldb, s, scale_io, out, clip, st); break;       \
+    case 6: launch_wave<DT, KIND, 6, W>(p, rows, K, ldb, s, scale_io, out, clip, st); break;       \
+    case 7: launch_wave<DT, KIND, 7, W>(p, rows, K, ldb, s, scale_io, out, clip, st); break;       \
+    default: launch_wave<DT, KIND, 8, W>(p, rows, K, ldb, s, scale_io, out, clip, st); break;      \
   }
       if (wpr == 2) { SQ_WAVE_CPL(2) } else { SQ_WAVE_CPL(4) }
 #undef SQ_WAVE_CPL
@@ -489,10 +522,10 @@ static int launch_rows_dt(const void* in, int64_t rows, int64_t K, int64_t ld, c
   int T, cpt, rpb;
   pick_shape(K, &T, &cpt, &rpb);
   switch (cpt) {
-    case 1: launch_shape<DT, 1, KIND, 2>(p, rows, K, ldb, s, scale_io, out, T, st); break;
-    case 2: launch_shape<DT, 2, KIND, 2>(p, rows, K, ldb, s, scale_io, out, T, st); break;
-    case 4: launch_shape<DT, 4, KIND, 1>(p, rows, K, ldb, s, scale_io, out, T, st); break;
-    case 8: launch_shape<DT, 8, KIND, 1>(p, rows, K, ldb, s, scale_io, out, T, st); break;
+    case 1: launch_shape<DT, 1, KIND, 2>(p, rows, K, ldb, s, scale_io, out, clip, T, st); break;
+    case 2: launch_shape<DT, 2, KIND, 2>(p, rows, K, ldb, s, scale_io, out, clip, T, st); break;
+    case 4: launch_shape<DT, 4, KIND, 1>(p, rows, K, ldb, s, scale_io, out, clip, T, st); break;
+    case 8: launch_shape<DT, 8, KIND, 1>(p, rows, K, ldb, s, scale_io, out, clip, T, st); break;
     default: return SQ_ERR_INVALID_ARG;   // K > 32768 is rejected by validation
   }
   SQ_LAUNCH_CHECK();
@@ -501,25 +534,30 @@ static int launch_rows_dt(const void* in, int64_t rows, int64_t K, int64_t ld, c
 
 template <int KIND>
 static int launch_rows(const void* in, int dt, int64_t rows, int64_t K, int64_t ld, const float* s,
-                       float* scale_io, int8_t* out, hipStream_t st) {
+                       float* scale_io, int8_t* out, unsigned long long* clip, hipStream_t st) {
   if (rows == 0) return SQ_OK;
   switch (dt) {
-    case SQ_F32: return launch_rows_dt<SQ_F32, KIND>(in, rows, K, ld, s, scale_io, out, st);
-    case SQ_F16: return launch_rows_dt<SQ_F16, KIND>(in, rows, K, ld, s, scale_io, out, st);
-    default:     return launch_rows_dt<SQ_BF16, KIND>(in, rows, K, ld, s, scale_io, out, st);
+    case SQ_F32: return launch_rows_dt<SQ_F32, KIND>(in, rows, K, ld, s, scale_io, out, clip, st);
+    case SQ_F16: return launch_rows_dt<SQ_F16, KIND>(in, rows, K, ld, s, scale_io, out, clip, st);
+    default:     return launch_rows_dt<SQ_BF16, KIND>(in, rows, K, ld, s, scale_io, out, clip, st);
   }
 }
 
 int launch_fold_quant(const void* W, int wt, int64_t N, int64_t K, int64_t ldw, const float* s,
                       int8_t* Wq, float* w_scale, hipStream_t st) {
-  return launch_rows<Q_FOLD>(W, wt, N, K, ldw, s, w_scale, Wq, st);
+  return launch_rows<Q_FOLD>(W, wt, N, K, ldw, s, w_scale, Wq, nullptr, st);
 }
 
+// clip (static mode only, may be null): device uint64 the number of clamped
+// codes is added to.
 int launch_quant_act(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const float* s,
-                     int mode, int8_t* Xq, float* a_scale, hipStream_t st) {
+                     int mode, int8_t* Xq, float* a_scale, unsigned long long* clip,
+                     hipStream_t st) {
+  if (mode == SQ_ACT_PER_TENSOR_STATIC && clip != nullptr)
+    return launch_rows<Q_STATIC_CLIP>(X, xt, M, K, ldx, s, a_scale, Xq, clip, st);
   if (mode == SQ_ACT_PER_TENSOR_STATIC)
-    return launch_rows<Q_STATIC>(X, xt, M, K, ldx, s, a_scale, Xq, st);
-  return launch_rows<Q_DYNAMIC>(X, xt, M, K, ldx, s, a_scale, Xq, st);
+    return launch_rows<Q_STATIC>(X, xt, M, K, ldx, s, a_scale, Xq, nullptr, st);
+  return launch_rows<Q_DYNAMIC>(X, xt, M, K, ldx, s, a_scale, Xq, nullptr, st);
 }
 
 }  // namespace sq

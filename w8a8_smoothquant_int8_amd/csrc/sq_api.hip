@@ -25,7 +25,7 @@ int launch_static_scale(const float* act_max, const float* s, int64_t K, float* 
 int launch_fold_quant(const void* W, int wt, int64_t N, int64_t K, int64_t ldw, const float* s,
                       int8_t* Wq, float* w_scale, hipStream_t st);
 int launch_quant_act(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const float* s,
-                     int mode, int8_t* Xq, float* a_scale, hipStream_t st);
+                     int mode, int8_t* Xq, float* a_scale, unsigned long long* clip, hipStream_t st);
 int launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
                 const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
                 int64_t ldy, hipStream_t st);
@@ -216,7 +216,23 @@ int sq_quant_per_token(const void* X, int xt, int64_t M, int64_t K, int64_t ldx,
   SQ_REQUIRE(aligned16(Xq) && aligned4(a_scale) && (s == nullptr || aligned4(s)), SQ_ERR_MISALIGNED);
   if (M == 0) return SQ_OK;
   if ((rc = gate()) != SQ_OK) return rc;
-  return sq::launch_quant_act(X, xt, M, K, ldx, s, mode, Xq, a_scale, as_stream(stream));
+  return sq::launch_quant_act(X, xt, M, K, ldx, s, mode, Xq, a_scale, nullptr, as_stream(stream));
+}
+
+int sq_quant_static_clipped(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const float* s,
+                            const float* a_scale, int8_t* Xq, unsigned long long* clipped,
+                            void* stream) {
+  int rc = check_matrix(X, xt, M, K, ldx);
+  if (rc != SQ_OK) return rc;
+  SQ_REQUIRE(Xq != nullptr && a_scale != nullptr && clipped != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(aligned16(Xq) && aligned4(a_scale) && (s == nullptr || aligned4(s)) &&
+                 ((uintptr_t)clipped & 7u) == 0,
+             SQ_ERR_MISALIGNED);
+  if (M == 0) return SQ_OK;
+  if ((rc = gate()) != SQ_OK) return rc;
+  // static mode only reads the scale
+  return sq::launch_quant_act(X, xt, M, K, ldx, s, SQ_ACT_PER_TENSOR_STATIC, Xq,
+                              const_cast<float*>(a_scale), clipped, as_stream(stream));
 }
 
 static int check_gemm(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, int64_t K) {
@@ -436,7 +452,7 @@ int sq_linear_group_run(const sq_linear_group* g, int flags, void* stream, void*
   }
   if ((flags & SQ_GROUP_FORWARD) && g->M > 0) {
     if ((rc = sq::launch_quant_act(g->X, g->xt, g->M, g->K, g->ldx, g->s, g->mode, g->Xq, g->a_scale,
-                                   st)) != SQ_OK)
+                                   nullptr, st)) != SQ_OK)
       return rc;
     if (lora && (rc = sq::launch_lora_shrink(g->X, g->xt, g->M, g->K, g->ldx, g->A, g->r, g->T,
                                              g->ldt, g->workspace, st)) != SQ_OK)

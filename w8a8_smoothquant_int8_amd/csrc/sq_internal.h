@@ -105,6 +105,15 @@ __device__ __forceinline__ int quant_code(float q) {
   return (int)r;
 }
 
+// quant_code, also counting a code whose rounded value lies beyond +-127
+// (the clamp changed it).
+__device__ __forceinline__ int quant_code_count(float q, int& clipped) {
+  float r = __builtin_rintf(q);
+  clipped += __builtin_fabsf(r) > 127.0f;
+  r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
          ((uint32_t)(d & 0xFF) << 24);
@@ -114,6 +123,13 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// Sum over a wave64 (all lanes get the result).
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
   return v;
 }
 

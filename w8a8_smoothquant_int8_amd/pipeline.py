@@ -36,10 +36,15 @@ import torch
 from . import (SQ_GROUP_CALIBRATE, SQ_GROUP_FOLD, SQ_GROUP_FORWARD, SQ_MAX_LORA_RANK,
                sq_calibrate_absmax, sq_linear_group_desc, sq_linear_group_run, sq_lora_apply,
                sq_lora_apply_segmented, sq_lora_shrink, sq_lora_workspace_bytes,
-               sq_quant_per_token, sq_smooth_fold, sq_static_act_scale, sq_w8a8_gemm,
-               sq_w8a8_gemm_lora)
+               sq_quant_per_token, sq_quant_static_clipped, sq_smooth_fold, sq_static_act_scale,
+               sq_w8a8_gemm, sq_w8a8_gemm_lora)
 
 ALL_PHASES = SQ_GROUP_CALIBRATE | SQ_GROUP_FOLD | SQ_GROUP_FORWARD
+
+# Largest share of clipped activation codes the static range check accepts:
+# a few clipped values per million are harmless ("SmoothQuant" explainer,
+# "Calibration in practice"); read here as at most 5 per million.
+MAX_CLIP_RATE = 5e-6
 
 _OUT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
@@ -75,6 +80,8 @@ class LinearGroup:
         self.Xq = torch.empty(self.M, K, dtype=torch.int8, device=dev)
         self.a_scale = torch.empty(max(self.M, 1), dtype=torch.float32, device=dev)
         self.static_scale = torch.empty(1, dtype=torch.float32, device=dev)
+        self.clip_count = torch.zeros(1, dtype=torch.int64, device=dev)   # static mode
+        self.clip_elems = 0                                                # elements counted
         self.Yg = torch.empty(self.M, Ntot, dtype=_OUT[out_dtype], device=dev)
         self.Y = {p: self.Yg[:, r0:r1] for p, (r0, r1) in rows.items()}
         self.lora = lora or {}
@@ -117,8 +124,23 @@ class LinearGroup:
     def _a(self, mode: str) -> torch.Tensor:
         return self.a_scale if mode == "dynamic" else self.static_scale
 
-    def quantize(self, X: torch.Tensor, mode: str = "dynamic") -> None:
-        sq_quant_per_token(X, self.s, self.Xq, self._a(mode), mode=mode)
+    def quantize(self, X: torch.Tensor, mode: str = "dynamic", count_clips: bool = False) -> None:
+        """count_clips (static mode): also add the number of clamped codes to
+        clip_count (device counter, kept across calls until reset_clips)."""
+        if mode == "static" and count_clips:
+            sq_quant_static_clipped(X, self.s, self.static_scale, self.Xq, self.clip_count)
+            self.clip_elems += X.shape[0] * X.shape[1]
+        else:
+            sq_quant_per_token(X, self.s, self.Xq, self._a(mode), mode=mode)
+
+    def reset_clips(self) -> None:
+        self.clip_count.zero_()
+        self.clip_elems = 0
+
+    def clip_rate(self) -> float:
+        """Share of clipped codes over the static batches counted so far (reads
+        the device counter: synchronises with the stream)."""
+        return int(self.clip_count.item()) / self.clip_elems if self.clip_elems else 0.0
 
     def gemm(self, proj: str, mode: str = "dynamic") -> torch.Tensor:
         """One projection's GEMM without LoRA."""
@@ -168,8 +190,25 @@ class LinearGroup:
             self._desc_key = key
         sq_linear_group_run(self._desc, flags, stream, gemm_begin, gemm_end)
 
-    def forward(self, X: torch.Tensor, mode: str = "dynamic") -> Dict[str, torch.Tensor]:
-        self.quantize(X, mode)
+    def forward_static_checked(self, X: torch.Tensor, max_rate: float = MAX_CLIP_RATE
+                               ) -> Tuple[Dict[str, torch.Tensor], float, bool]:
+        """Static-scale forward pass with a range check: the batch is quantized
+        with the calibrated per-tensor scale while its clipped codes are
+        counted; if their share exceeds max_rate the scale no longer covers the
+        batch and the pass is redone with per-token dynamic scales (the more
+        robust variant; "SmoothQuant" explainer, "Calibration in practice").
+        Returns (outputs, clip rate of this batch, fell_back). Reads the
+        counter on the host, so it synchronises once per call."""
+        base, elems = self.clip_count.clone(), X.shape[0] * X.shape[1]
+        Y = self.forward(X, "static", count_clips=True)
+        rate = (int(self.clip_count.item()) - int(base.item())) / elems if elems else 0.0
+        if rate > max_rate:
+            return self.forward(X, "dynamic"), rate, True
+        return Y, rate, False
+
+    def forward(self, X: torch.Tensor, mode: str = "dynamic",
+                count_clips: bool = False) -> Dict[str, torch.Tensor]:
+        self.quantize(X, mode, count_clips)
         if self.fused:
             self.lora_shrink(X)
             self.gemm_all_lora(mode)
