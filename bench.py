@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--no-stages", action="store_true",
                     help="skip the untimed per-stage pass (so a kernel trace of the run covers "
                          "only the warmup and timed steps)")
+    ap.add_argument("--row", choices=sorted(ROWS), default=None,
+                    help="measure one of the widened rows instead of the whole step "
+                         "(one JSON line of its own)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the timed region, run one plain device copy of this many MiB "
                          "(a kernel of known traffic, to scale rocprofv3 byte counters)")
@@ -253,6 +256,73 @@ def cpu_baseline(wl, rows_per_input: int):
     }
 
 
+def time_launches(torch, fn, reps: int, warm: int = 3) -> float:
+    """Average ms of fn() over reps launches on the current stream (HIP events)."""
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def row_f3(args, torch):
+    """Static per-tensor quant with and without the clipped-code counter on the
+    OPT-13B layer inputs at M = 4096 (fp16), and the cost of the range-checked
+    forward pass. Algorithmic bytes per element: the fp16 input read and the
+    INT8 code written (3 bytes)."""
+    from synth.workloads import get_workload
+    from w8a8_smoothquant_int8_amd.pipeline import LinearGroup
+    import w8a8_smoothquant_int8_amd as sq
+    wl = get_workload("opt13b_layer_prefill_m4096")
+    reps = max(args.steps, 10)
+    per_input, best = {}, None
+    for inp, K in wl.inputs:
+        g = LinearGroup(wl.w_group(inp).cuda(), wl.group_rows(inp), wl.alpha, wl.out_dtype, wl.M,
+                        modes=("dynamic", "static"))
+        g.calibrate(wl.x_cal(inp).cuda())
+        g.fold()
+        X = wl.x(inp).cuda()
+        plain = time_launches(torch, lambda: g.quantize(X, "static"), reps)
+        g.reset_clips()
+        clip = time_launches(torch, lambda: g.quantize(X, "static", count_clips=True), reps)
+        rate = g.clip_rate()
+        fwd = time_launches(torch, lambda: g.forward(X, "static"), max(reps // 4, 5))
+        chk = time_launches(torch, lambda: g.forward_static_checked(X, max_rate=1.0),
+                            max(reps // 4, 5))
+        nbytes = 3.0 * wl.M * K
+        per_input[inp] = {"K": K, "plain_us": round(plain * 1e3, 2), "clip_us": round(clip * 1e3, 2),
+                          "plain_gbs": round(nbytes / plain / 1e6, 1),
+                          "clip_gbs": round(nbytes / clip / 1e6, 1),
+                          "counter_overhead_pct": round(100 * (clip / plain - 1), 2),
+                          "clip_rate": rate,
+                          "forward_static_ms": round(fwd, 4),
+                          "forward_static_checked_ms": round(chk, 4)}
+        if best is None or nbytes / clip > best[0]:
+            best = (nbytes / clip, clip, nbytes, inp)
+        del g, X
+        torch.cuda.empty_cache()
+    gbs, ms, nbytes, inp = best
+    return {
+        "row": "f3", "metric": "static per-tensor quant with clip counter, GB/s",
+        "value": round(nbytes / ms / 1e6, 1), "unit": "GB/s",
+        "higher_is_better": True, "dtype": "f16->int8", "data": "synthetic",
+        "config": {"workload": wl.name, "M": wl.M, "reps": reps},
+        "roofline": {"bound": "hbm", "kernel": f"k_quant (STATIC_CLIP) on {inp}",
+                     "achieved": round(nbytes / ms / 1e6, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(ms, 5), "bytes_per_launch": nbytes},
+        "inputs": per_input,
+    }
+
+
+ROWS = {"f3": row_f3}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -260,6 +330,11 @@ def main():
               "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.row:
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        torch.cuda.set_device(0)
+        print(json.dumps(ROWS[args.row](args, torch)))
+        return
     from synth.workloads import get_workload
     import w8a8_smoothquant_int8_amd as sq
 

@@ -178,6 +178,12 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
       }
       parity ^= 1;
     }
+    // Clip counting: rne(fp32(y / scale)) passes 127 exactly when the quotient
+    // reaches 127.5, and the quotient grows with |y|, so a thread whose largest
+    // |y| stays below that clips nothing and skips the count (nearly all do).
+    bool maybe[RPB];
+#pragma unroll
+    for (int r = 0; r < RPB; ++r) maybe[r] = counting && div_rn(amax[r], rscale[r]) >= 127.5f;
 
     // pass 2: codes from v
 #pragma unroll
@@ -199,16 +205,32 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
           }
           int q[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if constexpr (counting)
-              q[e] = scale[r] != 0.0f ? quant_code_count(div_rn(y[e], rscale[r]), nclip) : 0;
-            else
-              q[e] = scale[r] != 0.0f ? quant_code(div_rn(y[e], rscale[r])) : 0;
-          }
+          for (int e = 0; e < 8; ++e) q[e] = scale[r] != 0.0f ? quant_code(div_rn(y[e], rscale[r])) : 0;
           uint2 pk;
           pk.x = pack4_i8(q[0], q[1], q[2], q[3]);
           pk.y = pack4_i8(q[4], q[5], q[6], q[7]);
           *(uint2*)(orow + c * 8) = pk;
+        }
+      }
+      // the rare count: a loop of its own, so the code loop above keeps its registers
+      // (with kStoreV the raw registers already hold the next rows: v is used)
+      if (maybe[r]) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+          const int64_t c = tid + (int64_t)j * T;
+          if (c * 8 < K) {
+            float y[8];
+            if constexpr (kStoreV) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) y[e] = v[r][j][e];
+            } else {
+              widen8<DT>(raw[r].w[j], y);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) y[e] = smooth(y[e], j, e);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) nclip += clips(div_rn(y[e], rscale[r]));
+          }
         }
       }
     }
@@ -397,24 +419,31 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
     int8_t* orow = out + m * K;
     // scale == 0 (all-zero row, or a zero static scale): every code is 0
     const uint32_t keep = scale != 0.0f ? 0xFFFFFFFFu : 0u;
+    // Clip counting: rne(fp32(v / scale)) passes 127 exactly when the quotient
+    // reaches 127.5, and the quotient grows with |v|, so a lane whose largest
+    // in-row |v| stays below that clips nothing and skips the count.
+    const bool maybe = counting && div_rn(amax, rscale) >= 127.5f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = c0 + 64 * j;
       int q[8];
-      if constexpr (counting) {
-        // chunks past the row end hold a clamped re-read of the row: not counted
-        int n = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = quant_code_count(div_rn(v[j][e], rscale), n);
-        nclip += c < nch ? n : 0;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = quant_code(div_rn(v[j][e], rscale));
-      }
+      for (int e = 0; e < 8; ++e) q[e] = quant_code(div_rn(v[j][e], rscale));
       uint2 pk;
       pk.x = pack4_i8(q[0], q[1], q[2], q[3]) & keep;
       pk.y = pack4_i8(q[4], q[5], q[6], q[7]) & keep;
       if (c < nch) *(uint2*)(orow + c * 8) = pk;
+    }
+    // the rare count, in a loop of its own; chunks past the row end hold a
+    // clamped re-read of the row and are not counted
+    if (maybe) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        if (c0 + 64 * j < nch) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) nclip += clips(div_rn(v[j][e], rscale));
+        }
+      }
     }
   }
   if constexpr (counting) {

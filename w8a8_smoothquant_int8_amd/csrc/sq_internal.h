@@ -105,13 +105,9 @@ __device__ __forceinline__ int quant_code(float q) {
   return (int)r;
 }
 
-// quant_code, also counting a code whose rounded value lies beyond +-127
-// (the clamp changed it).
-__device__ __forceinline__ int quant_code_count(float q, int& clipped) {
-  float r = __builtin_rintf(q);
-  clipped += __builtin_fabsf(r) > 127.0f;
-  r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
-  return (int)r;
+// 1 if quant_code(q) clamps: the rounded value lies beyond +-127.
+__device__ __forceinline__ int clips(float q) {
+  return __builtin_fabsf(__builtin_rintf(q)) > 127.0f ? 1 : 0;
 }
 
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
