@@ -40,6 +40,14 @@ Readings of points the pages leave open (each used below):
   R7 a static per-tensor activation scale is max_k(act_max_cal[k] / s[k]) /
      127 from the calibration batch, i.e. the sketch's per-tensor absmax of
      the smoothed calibration activations.
+  R8 the per-layer alpha search ("Calibration in practice": pick the
+     migration strength per layer by how well the quantized layer reproduces
+     its output on calibration data) measures, for each candidate alpha, the
+     squared error of the fp32 dequantized output against the exact
+     unquantized output X W^T on the calibration batch itself (which also
+     supplies the activation maxima), relative to the squared norm of that
+     output. The output is compared before any rounding to a 16-bit output
+     type, so the error is the quantization error alone.
 """
 from __future__ import annotations
 
@@ -302,3 +310,29 @@ def smoothquant_linear(x: np.ndarray, in_dtype: str, w: np.ndarray, x_cal: np.nd
         a, b, sc = lora
         out["y_lora"] = lora_apply(y, x, in_dtype, a, b, sc, out_dtype)
     return out
+
+
+# ----------------------------------------------------------------------------
+# [SQ] "Calibration in practice": per-layer choice of the migration strength.
+# ----------------------------------------------------------------------------
+def alpha_sweep(x_cal: np.ndarray, w: np.ndarray, alphas: Sequence[float],
+                mode: str = "dynamic") -> dict:
+    """R8: for each alpha, run the whole W8A8 path on the calibration batch and
+    measure its output error against the unquantized layer.
+
+    x_cal [M, K] and w [N, K] hold the exact input values (fp32 arrays).
+    Returns err[i] = sum (y_i - y_ref)^2 and ref = sum y_ref^2 (fp64), with
+    y_i the fp32 dequantized output at alphas[i] and y_ref = x_cal w^T in
+    fp64; rel[i] = err[i] / ref; best = the alpha of the smallest rel (the
+    first one on ties).
+    """
+    y_ref = np.asarray(x_cal, np.float64) @ np.asarray(w, np.float64).T
+    ref = float(np.sum(y_ref * y_ref))
+    err = []
+    for a in alphas:
+        r = smoothquant_linear(x_cal, "f32", w, x_cal, float(a), "f32", mode=mode)
+        d = r["y"].astype(np.float64) - y_ref
+        err.append(float(np.sum(d * d)))
+    err = np.array(err, np.float64)
+    rel = err / ref if ref > 0 else np.zeros_like(err)
+    return {"err": err, "ref": ref, "rel": rel, "best": float(alphas[int(np.argmin(rel))])}

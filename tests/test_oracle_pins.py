@@ -481,3 +481,81 @@ def test_static_clip_count_brute_force_ties():
     # a zero scale gives zero codes and no clips
     q0, c0 = O.quantize_per_tensor_static(x, None, np.float32(0.0))
     assert c0 == 0 and not q0.any()
+
+
+# ----------------------------------------------------------------------------
+# Per-layer alpha search (R8)
+# ----------------------------------------------------------------------------
+def _brute_sweep_err(x, w, alpha, mode):
+    """The same error with the pure-Python pipeline and exact rational sums."""
+    from fractions import Fraction
+    xl = [[float(v) for v in row] for row in x]
+    wl = [[float(v) for v in row] for row in w]
+    r = brute.pipeline(xl, wl, xl, alpha, mode=mode, out="f32")
+    err = Fraction(0)
+    ref = Fraction(0)
+    for m in range(len(xl)):
+        for n in range(len(wl)):
+            yr = sum(Fraction(xl[m][k]) * Fraction(wl[n][k]) for k in range(len(xl[0])))
+            d = Fraction(r["y32"][m][n]) - yr
+            err += d * d
+            ref += yr * yr
+    return float(err), float(ref)
+
+
+@pytest.mark.parametrize("mode", ["dynamic", "static"])
+def test_alpha_sweep_matches_brute_force(mode):
+    rng = np.random.default_rng(31)
+    M, K, N = 4, 16, 5
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[:, [3, 11]] *= 40.0
+    w = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    alphas = [0.0, 0.25, 0.5, 0.8, 1.0]
+    sw = O.alpha_sweep(x, w, alphas, mode=mode)
+    for i, a in enumerate(alphas):
+        e, ref = _brute_sweep_err(x, w, a, mode)
+        assert sw["ref"] == pytest.approx(ref, rel=1e-12)
+        assert sw["err"][i] == pytest.approx(e, rel=1e-9), a
+        assert sw["err"][i] > 0
+    assert sw["best"] == alphas[int(np.argmin(sw["rel"]))]
+
+
+@pytest.mark.parametrize("mode", ["dynamic", "static"])
+def test_alpha_sweep_exact_layer_has_zero_error_at_half(mode):
+    """A layer built from integer codes and power-of-two smoothing factors: at
+    alpha = 0.5 the factors come out exactly, every division and scale is exact,
+    the dequantized output equals the exact product and the error is 0. Other
+    alphas give factors that are not powers of two, and nonzero error."""
+    rng = np.random.default_rng(5)
+    M, K, N = 6, 32, 7
+    cx = rng.integers(-100, 101, (M, K))
+    cw = rng.integers(-100, 101, (N, K))
+    cx[np.arange(M), rng.integers(0, K, M)] = 127          # every row reaches 127
+    cw[np.arange(N), rng.integers(0, K, N)] = -127
+    # equal column maxima on both sides: c_k = max |cx[:, k]| = max |cw[:, k]|
+    c = np.maximum(np.abs(cx).max(0), np.abs(cw).max(0))
+    cx[0, :] = np.where(np.abs(cx).max(0) < c, c, cx[0, :])
+    cw[0, :] = np.where(np.abs(cw).max(0) < c, c, cw[0, :])
+    assert np.array_equal(np.abs(cx).max(0), np.abs(cw).max(0))
+    assert (np.abs(cx).max(1) == 127).all() and (np.abs(cw).max(1) == 127).all()
+    sk = np.exp2(rng.integers(-3, 4, K)).astype(np.float64)   # the smoothing factors
+    x = (cx * sk).astype(np.float32)                          # a_k = c_k s_k
+    w = (cw / sk).astype(np.float32)                          # w_k = c_k / s_k
+    sw = O.alpha_sweep(x, w, [0.2, 0.5, 0.9], mode=mode)
+    assert sw["err"][1] == 0.0
+    assert sw["err"][0] > 0 and sw["err"][2] > 0
+    assert sw["best"] == 0.5
+    assert sw["ref"] == float(np.sum((cx.astype(np.float64) @ cw.T.astype(np.float64)) ** 2))
+
+
+def test_alpha_sweep_scale_invariance_at_the_ends():
+    """At alpha 0 and 1 the factors move by exact powers of two when X is scaled
+    by 2, so every code is unchanged and the relative error is identical."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((8, 48)).astype(np.float32)
+    x[:, 5] *= 30
+    w = (rng.standard_normal((16, 48)) * 0.1).astype(np.float32)
+    a = O.alpha_sweep(x, w, [0.0, 1.0])
+    b = O.alpha_sweep(2 * x, w, [0.0, 1.0])
+    assert np.array_equal(b["err"], 4 * a["err"]) and b["ref"] == 4 * a["ref"]
+    assert np.array_equal(a["rel"], b["rel"])
