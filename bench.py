@@ -320,7 +320,68 @@ def row_f3(args, torch):
     }
 
 
-ROWS = {"f3": row_f3}
+def row_f4(args, torch):
+    """Per-layer alpha sweep over the Llama-3-8B projection groups: 21 alphas
+    (0, 0.05, ..., 1) on the 512-row calibration batch, one native call per
+    group. Also times the sweep's largest memory-bound kernel, the weight fold
+    + quant, alone at each group's shape (3 bytes per weight element: 16-bit
+    read, INT8 write)."""
+    from synth.workloads import get_workload
+    import w8a8_smoothquant_int8_amd as sq
+    wl = get_workload(args.workload)
+    alphas = [round(0.05 * i, 2) for i in range(21)]
+    reps = max(min(args.steps, 20), 3)
+    groups, total_ms, best_fold = {}, 0.0, None
+    for inp, K in wl.inputs:
+        X = wl.x_cal(inp).cuda()
+        W = wl.w_group(inp).cuda()
+        M, N = X.shape[0], W.shape[0]
+        ws = torch.empty(sq.sq_alpha_sweep_workspace_bytes(M, N, K), dtype=torch.uint8,
+                         device="cuda")
+        err = torch.empty(len(alphas), 2, dtype=torch.float64, device="cuda")
+        ms = time_launches(torch, lambda: sq.sq_alpha_sweep(X, W, alphas, err, ws), reps, warm=1)
+        host = err.cpu().numpy()
+        rel = host[:, 0] / host[0, 1]
+        ib = int(rel.argmin())
+        # the fold + quant kernel alone, at the sweep's shape
+        s = torch.empty(K, dtype=torch.float32, device="cuda")
+        am = torch.zeros(K, dtype=torch.float32, device="cuda")
+        sq.sq_calibrate_absmax(X, am)
+        sq.sq_smooth_scale(am, W, 0.5, s)
+        Wq = torch.empty(N, K, dtype=torch.int8, device="cuda")
+        wsc = torch.empty(N, dtype=torch.float32, device="cuda")
+        fold_ms = time_launches(torch, lambda: sq.sq_fold_quant_weights(W, s, Wq, wsc), reps * 5)
+        fold_bytes = 3.0 * N * K
+        groups[inp] = {"M_cal": M, "N": N, "K": K, "sweep_ms": round(ms, 4),
+                       "ms_per_alpha": round(ms / len(alphas), 4),
+                       "best_alpha": alphas[ib], "rel_err_best": float(rel[ib]),
+                       "rel_err_at_0.5": float(rel[alphas.index(0.5)]),
+                       "fold_us": round(fold_ms * 1e3, 2),
+                       "fold_gbs": round(fold_bytes / fold_ms / 1e6, 1)}
+        total_ms += ms
+        if best_fold is None or fold_bytes > best_fold[1]:
+            best_fold = (fold_ms, fold_bytes, inp)
+        del X, W, ws, Wq
+        torch.cuda.empty_cache()
+    fold_ms, fold_bytes, finp = best_fold
+    evals = len(alphas) * len(wl.inputs)
+    return {
+        "row": "f4", "metric": "per-layer alpha sweep, layer-alpha evaluations per second",
+        "value": round(evals / (total_ms * 1e-3), 1), "unit": "evaluations/s",
+        "higher_is_better": True, "dtype": wl.dtype + "->int8", "data": "synthetic",
+        "config": {"workload": wl.name, "alphas": len(alphas), "calibration_rows": 512,
+                   "reps": reps},
+        "sweep_ms_all_groups": round(total_ms, 3),
+        "roofline": {"bound": "hbm", "kernel": f"k_quant (FOLD) on the {finp} weights",
+                     "achieved": round(fold_bytes / fold_ms / 1e6, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(fold_bytes / fold_ms / 1e6 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_ms": round(fold_ms, 5),
+                     "bytes_per_launch": fold_bytes},
+        "groups": groups,
+    }
+
+
+ROWS = {"f3": row_f3, "f4": row_f4}
 
 
 def main():

@@ -257,6 +257,35 @@ typedef struct {
 int sq_linear_group_run(const sq_linear_group* g, int flags, void* stream, void* gemm_begin,
                         void* gemm_end);
 
+/* Bytes of device workspace sq_alpha_sweep needs for an [M, K] calibration
+ * batch and [N, K] weights (0 if any size is <= 0). About
+ * 12*M*N + N*K + M*K + 12*K + 4*N + 4*M bytes plus 16 KB. */
+size_t sq_alpha_sweep_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* [SQ] "Calibration in practice": the migration strength alpha is a per-layer
+ * choice, made by how well the quantized layer reproduces its unquantized
+ * output on calibration data. For every alphas[i] this runs the whole path
+ * on X (which also supplies the activation maxima) with the same kernels as
+ * the calls above:
+ *   s = sq_smooth_scale(max_m |X|, W, alphas[i]); Wq, w_scale = fold + quant;
+ *   Xq, a_scale = quant of X (mode: per-token dynamic, or per-tensor static
+ *   from the same maxima); y = fp32 dequant of Xq Wq^T (yt = f32)
+ * and compares y with the unquantized output y_ref = X W^T (exact
+ * products, fp64 sums: within about K * 2^-53 of the exact value):
+ *   err[2 i]     = sum_{m,n} (y[m, n] - y_ref[m, n])^2
+ *   err[2 i + 1] = sum_{m,n} y_ref[m, n]^2
+ * both summed in fp64 in a fixed order (deterministic). err[2i] / err[2i+1]
+ * is the relative squared error at alphas[i]; the best alpha is the smallest.
+ * X: [M, K] dtype xt, row stride ldx; W: [N, K] dtype wt, row stride ldw
+ * (N a multiple of 16). alphas: host array of n_alpha values in [0, 1]
+ * (1 <= n_alpha <= 1024). err: device, [n_alpha, 2] fp64, written.
+ * ws: device workspace, 256-byte aligned, at least
+ * sq_alpha_sweep_workspace_bytes(M, N, K) bytes (SQ_ERR_WORKSPACE if not).
+ * M == 0 writes nothing. */
+int sq_alpha_sweep(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* W,
+                   int wt, int64_t N, int64_t ldw, const double* alphas, int n_alpha, int mode,
+                   double* err, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sq.SIGNATURES)
@@ -293,3 +293,31 @@ def test_group_validation(L):
     # no LoRA: A, B, T and the workspace are not needed
     d = _group(r=0, A=None, B=None, T=None, workspace=None, workspace_bytes=0)
     assert _run(L, d, flags=4) in (E.SQ_OK, E.SQ_ERR_UNSUPPORTED_ARCH)
+
+
+def test_alpha_sweep_validation(L):
+    f = L.sq_alpha_sweep
+    A = (ctypes.c_double * 3)(0.0, 0.5, 1.0)
+    BAD = (ctypes.c_double * 2)(0.5, 1.5)
+    need = L.sq_alpha_sweep_workspace_bytes(64, 32, 128)
+    assert need > 12 * 64 * 32 + 32 * 128 + 64 * 128
+    assert L.sq_alpha_sweep_workspace_bytes(0, 32, 128) == 0
+    W256 = ctypes.c_void_p(0x100000)
+
+    def call(X=P, xt=sq.SQ_BF16, M=64, K=128, ldx=128, W=P, wt=sq.SQ_BF16, N=32, ldw=128, al=A,
+             n=3, mode=0, err=P, ws=W256, wsb=None):
+        return f(X, xt, M, K, ldx, W, wt, N, ldw, al, n, mode, err, ws, need if wsb is None else wsb,
+                 S)
+    assert call(W=NULL) == sq.SQ_ERR_INVALID_ARG
+    assert call(N=24) == sq.SQ_ERR_MISALIGNED                      # N % 16
+    assert call(ldw=64) == sq.SQ_ERR_INVALID_ARG                   # ldw < K
+    assert call(al=None) == sq.SQ_ERR_INVALID_ARG
+    assert call(n=0) == sq.SQ_ERR_INVALID_ARG
+    assert call(al=BAD, n=2) == sq.SQ_ERR_INVALID_ARG              # alpha outside [0, 1]
+    assert call(mode=3) == sq.SQ_ERR_INVALID_ARG
+    assert call(err=P4) == sq.SQ_ERR_MISALIGNED
+    assert call(ws=NULL) == sq.SQ_ERR_WORKSPACE
+    assert call(wsb=need - 1) == sq.SQ_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x10010)) == sq.SQ_ERR_MISALIGNED  # not 256-byte aligned
+    assert call(wt=7) == sq.SQ_ERR_UNSUPPORTED_DTYPE
+    assert call(M=0, ws=NULL) == sq.SQ_OK

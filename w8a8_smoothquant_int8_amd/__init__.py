@@ -61,6 +61,9 @@ SIGNATURES = {
                                          _c_int, _vp, _vp, _vp, _c_int, _c_f, _vp, _c_int, _c_i64,
                                          _c_i64, _vp, _c_sz, _vp]),
     "sq_linear_group_run": (_c_int, [_vp, _c_int, _vp, _vp, _vp]),
+    "sq_alpha_sweep_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64]),
+    "sq_alpha_sweep": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _c_int, _c_i64, _c_i64,
+                                ctypes.POINTER(_c_d), _c_int, _c_int, _vp, _vp, _c_sz, _vp]),
 }
 
 SQ_GROUP_CALIBRATE, SQ_GROUP_FOLD, SQ_GROUP_FORWARD = 1, 2, 4
@@ -310,3 +313,19 @@ def sq_linear_group_run(desc: SqLinearGroup, flags: int, stream=None, gemm_begin
         return ctypes.c_void_p(e.cuda_event if hasattr(e, "cuda_event") else int(e))
     _check("sq_linear_group_run", lib().sq_linear_group_run(
         ctypes.byref(desc), int(flags), _stream(stream), ev(gemm_begin), ev(gemm_end)))
+
+
+def sq_alpha_sweep_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().sq_alpha_sweep_workspace_bytes(M, N, K))
+
+
+def sq_alpha_sweep(X: torch.Tensor, W: torch.Tensor, alphas, err: torch.Tensor, ws: torch.Tensor,
+                   mode: str = "dynamic", stream=None) -> None:
+    """err: [len(alphas), 2] float64 on the device, written with (sum of squared
+    errors, sum of squared reference outputs) per alpha."""
+    M, K = X.shape
+    N = W.shape[0]
+    a = (_c_d * len(alphas))(*[float(v) for v in alphas])
+    _check("sq_alpha_sweep", lib().sq_alpha_sweep(
+        _ptr(X), _dt(X), M, K, _ld(X), _ptr(W), _dt(W), N, _ld(W), a, len(alphas), MODES[mode],
+        _ptr(err), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))

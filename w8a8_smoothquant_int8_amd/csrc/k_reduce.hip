@@ -92,16 +92,16 @@ __global__ void k_fill_f32(float* __restrict__ p, int64_t n, float v) {
 }
 
 // s[k] = fp32(max(a^alpha / w^(1 - alpha), 1e-5)) with a = max(act_max[k], 1e-5),
-// w = max(w_max[k], 1e-5), all in fp64. On entry s holds w_max (in place).
+// w = max(w_max[k], 1e-5), all in fp64. w_max may be s itself (in place).
 // sqrt_form: alpha == 0.5, where both powers are square roots (correctly
 // rounded in fp64), so the result is the correctly rounded quotient.
-__global__ void k_smooth_scale(const float* __restrict__ act_max, float* __restrict__ s, int64_t K,
-                               double alpha, double one_minus_alpha, int sqrt_form) {
+__global__ void k_smooth_scale(const float* __restrict__ act_max, const float* w_max, float* s,
+                               int64_t K, double alpha, double one_minus_alpha, int sqrt_form) {
   int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (k >= K) return;
   const double lo = 1e-5;
   double a = (double)act_max[k];
-  double w = (double)s[k];
+  double w = (double)w_max[k];
   a = a > lo ? a : lo;
   w = w > lo ? w : lo;
   double v = sqrt_form ? __builtin_sqrt(a) / __builtin_sqrt(w) : pow(a, alpha) / pow(w, one_minus_alpha);
@@ -195,13 +195,19 @@ int launch_fill(float* p, int64_t n, float v, hipStream_t st) {
   return SQ_OK;
 }
 
-int launch_smooth_scale(const float* act_max, float* s_inout, int64_t K, double alpha,
-                        hipStream_t st) {
+// s from act_max and w_max (w_max may equal s).
+int launch_smooth_scale_from(const float* act_max, const float* w_max, float* s, int64_t K,
+                             double alpha, hipStream_t st) {
   const int sqrt_form = alpha == 0.5;
-  k_smooth_scale<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(act_max, s_inout, K, alpha,
+  k_smooth_scale<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(act_max, w_max, s, K, alpha,
                                                                1.0 - alpha, sqrt_form);
   SQ_LAUNCH_CHECK();
   return SQ_OK;
+}
+
+int launch_smooth_scale(const float* act_max, float* s_inout, int64_t K, double alpha,
+                        hipStream_t st) {
+  return launch_smooth_scale_from(act_max, s_inout, s_inout, K, alpha, st);
 }
 
 int launch_static_scale(const float* act_max, const float* s, int64_t K, float* a_scale,

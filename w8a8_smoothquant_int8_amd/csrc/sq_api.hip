@@ -21,6 +21,13 @@ int launch_colmax2(const void* X1, int xt1, int64_t M1, int64_t K1, int64_t ld1,
                    const void* X2, int xt2, int64_t M2, int64_t K2, int64_t ld2, float* out2,
                    hipStream_t st);
 int launch_smooth_scale(const float* act_max, float* s_inout, int64_t K, double alpha, hipStream_t st);
+int launch_smooth_scale_from(const float* act_max, const float* w_max, float* s, int64_t K,
+                             double alpha, hipStream_t st);
+int launch_ref_gemm(const void* X, int xt, int64_t ldx, const void* W, int wt, int64_t ldw,
+                    int64_t M, int64_t N, int64_t K, double* Y, hipStream_t st);
+int launch_sq_err(const float* q, const double* ref, int64_t n, double* part, double* out,
+                  hipStream_t st);
+size_t err_partials_bytes();
 int launch_static_scale(const float* act_max, const float* s, int64_t K, float* a_scale, hipStream_t st);
 int launch_fold_quant(const void* W, int wt, int64_t N, int64_t K, int64_t ldw, const float* s,
                       int8_t* Wq, float* w_scale, hipStream_t st);
@@ -52,6 +59,7 @@ namespace {
 
 constexpr int64_t kMaxK = 32768;     // row kernels hold a whole row in registers
 constexpr int64_t kMaxDim = (1LL << 31) - 1;
+constexpr int kMaxSweepAlphas = 1024;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
@@ -466,6 +474,90 @@ int sq_linear_group_run(const sq_linear_group* g, int flags, void* stream, void*
     if (rc != SQ_OK) return rc;
     if (gemm_end != nullptr && hipEventRecord((hipEvent_t)gemm_end, st) != hipSuccess)
       return SQ_ERR_HIP;
+  }
+  return SQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Per-layer alpha sweep.
+// ---------------------------------------------------------------------------
+namespace {
+// Workspace regions, each 256-byte aligned, in this order.
+struct SweepWs {
+  float *act_max, *w_max, *s, *w_scale, *a_scale, *y_q;
+  double* y_ref;
+  int8_t *Wq, *Xq;
+  double* part;
+  size_t bytes;
+};
+SweepWs sweep_layout(char* base, int64_t M, int64_t N, int64_t K) {
+  SweepWs w{};
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char* p = base ? base + off : nullptr;
+    off += (n + 255) & ~(size_t)255;
+    return p;
+  };
+  w.act_max = (float*)take(4 * K);
+  w.w_max = (float*)take(4 * K);
+  w.s = (float*)take(4 * K);
+  w.w_scale = (float*)take(4 * N);
+  w.a_scale = (float*)take(4 * (M > 0 ? M : 1));
+  w.y_ref = (double*)take(8 * (size_t)M * N);
+  w.y_q = (float*)take(4 * (size_t)M * N);
+  w.Wq = (int8_t*)take((size_t)N * K);
+  w.Xq = (int8_t*)take((size_t)M * K);
+  w.part = (double*)take(sq::err_partials_bytes());
+  w.bytes = off;
+  return w;
+}
+}  // namespace
+
+size_t sq_alpha_sweep_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return sweep_layout(nullptr, M, N, K).bytes;
+}
+
+int sq_alpha_sweep(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* W, int wt,
+                   int64_t N, int64_t ldw, const double* alphas, int n_alpha, int mode, double* err,
+                   void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_matrix(X, xt, M, K, ldx);
+  if (rc != SQ_OK) return rc;
+  if ((rc = check_matrix(W, wt, N, K, ldw)) != SQ_OK) return rc;
+  SQ_REQUIRE(N >= 1, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(N % 16 == 0, SQ_ERR_MISALIGNED);
+  SQ_REQUIRE(valid_mode(mode), SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(alphas != nullptr && err != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(n_alpha >= 1 && n_alpha <= kMaxSweepAlphas, SQ_ERR_INVALID_ARG);
+  for (int i = 0; i < n_alpha; ++i)
+    SQ_REQUIRE(alphas[i] >= 0.0 && alphas[i] <= 1.0, SQ_ERR_INVALID_ARG);   // NaN fails too
+  SQ_REQUIRE(((uintptr_t)err & 7u) == 0, SQ_ERR_MISALIGNED);
+  if (M == 0) return SQ_OK;
+  const size_t need = sq_alpha_sweep_workspace_bytes(M, N, K);
+  SQ_REQUIRE(ws != nullptr && ws_bytes >= need, SQ_ERR_WORKSPACE);
+  SQ_REQUIRE(((uintptr_t)ws & 255u) == 0, SQ_ERR_MISALIGNED);
+  if ((rc = gate()) != SQ_OK) return rc;
+  hipStream_t st = as_stream(stream);
+  const SweepWs w = sweep_layout((char*)ws, M, N, K);
+  const bool is_static = mode == SQ_ACT_PER_TENSOR_STATIC;
+  // alpha-independent: activation and weight column maxima, the unquantized output
+  if ((rc = sq::launch_fill2(w.act_max, K, w.w_max, K, 0.0f, st)) != SQ_OK) return rc;
+  if ((rc = sq::launch_colmax2(X, xt, M, K, ldx, w.act_max, W, wt, N, K, ldw, w.w_max, st)) != SQ_OK)
+    return rc;
+  if ((rc = sq::launch_ref_gemm(X, xt, ldx, W, wt, ldw, M, N, K, w.y_ref, st)) != SQ_OK) return rc;
+  for (int i = 0; i < n_alpha; ++i) {
+    if ((rc = sq::launch_smooth_scale_from(w.act_max, w.w_max, w.s, K, alphas[i], st)) != SQ_OK)
+      return rc;
+    if ((rc = sq::launch_fold_quant(W, wt, N, K, ldw, w.s, w.Wq, w.w_scale, st)) != SQ_OK) return rc;
+    if (is_static && (rc = sq::launch_static_scale(w.act_max, w.s, K, w.a_scale, st)) != SQ_OK)
+      return rc;
+    if ((rc = sq::launch_quant_act(X, xt, M, K, ldx, w.s, mode, w.Xq, w.a_scale, nullptr, st)) !=
+        SQ_OK)
+      return rc;
+    if ((rc = sq::launch_gemm(w.Xq, w.Wq, w.a_scale, mode, w.w_scale, M, N, K, w.y_q, SQ_F32, N,
+                              st)) != SQ_OK)
+      return rc;
+    if ((rc = sq::launch_sq_err(w.y_q, w.y_ref, M * N, w.part, err + 2 * i, st)) != SQ_OK) return rc;
   }
   return SQ_OK;
 }

@@ -34,7 +34,7 @@ from typing import Dict, List, Optional, Tuple
 import torch
 
 from . import (SQ_GROUP_CALIBRATE, SQ_GROUP_FOLD, SQ_GROUP_FORWARD, SQ_MAX_LORA_RANK,
-               sq_calibrate_absmax, sq_linear_group_desc, sq_linear_group_run, sq_lora_apply,
+               sq_alpha_sweep, sq_alpha_sweep_workspace_bytes, sq_calibrate_absmax, sq_linear_group_desc, sq_linear_group_run, sq_lora_apply,
                sq_lora_apply_segmented, sq_lora_shrink, sq_lora_workspace_bytes,
                sq_quant_per_token, sq_quant_static_clipped, sq_smooth_fold, sq_static_act_scale,
                sq_w8a8_gemm, sq_w8a8_gemm_lora)
@@ -47,6 +47,25 @@ ALL_PHASES = SQ_GROUP_CALIBRATE | SQ_GROUP_FOLD | SQ_GROUP_FORWARD
 MAX_CLIP_RATE = 5e-6
 
 _OUT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+def alpha_sweep(X: torch.Tensor, W: torch.Tensor, alphas, mode: str = "dynamic",
+                stream=None) -> dict:
+    """Output error of the quantized layer against the unquantized one for each
+    alpha, on the calibration batch X ("SmoothQuant" explainer, "Calibration in
+    practice"): one native call, then one read of the [len(alphas), 2] result.
+    Returns err (sum of squared errors), ref (sum of squared outputs), rel =
+    err / ref, and best (the alpha of the smallest rel, the first on ties)."""
+    M, K = X.shape
+    ws = torch.empty(max(sq_alpha_sweep_workspace_bytes(M, W.shape[0], K), 256),
+                     dtype=torch.uint8, device=X.device)
+    out = torch.empty(len(alphas), 2, dtype=torch.float64, device=X.device)
+    sq_alpha_sweep(X, W, alphas, out, ws, mode=mode, stream=stream)
+    host = out.cpu()
+    err, ref = host[:, 0].tolist(), float(host[0, 1])
+    rel = [e / ref if ref > 0 else 0.0 for e in err]
+    best = float(alphas[min(range(len(alphas)), key=lambda i: (rel[i], i))])
+    return {"err": err, "ref": ref, "rel": rel, "best": best}
 
 
 @dataclass
@@ -114,6 +133,14 @@ class LinearGroup:
         if reset:
             self.act_max.zero_()
         sq_calibrate_absmax(X_cal, self.act_max)
+
+    def choose_alpha(self, X_cal: torch.Tensor, alphas, mode: str = "dynamic") -> dict:
+        """Set this group's alpha to the sweep's best over `alphas` on X_cal
+        (over all the group's projections at once: they share one s)."""
+        r = alpha_sweep(X_cal, self.W, alphas, mode)
+        self.alpha = r["best"]
+        self._desc_key = None            # the native-call descriptor carries alpha
+        return r
 
     def fold(self) -> None:
         sq_smooth_fold(self.act_max, self.W, self.alpha, self.s, self.Wq, self.w_scale)
