@@ -48,9 +48,22 @@ Readings of points the pages leave open (each used below):
      supplies the activation maxima), relative to the squared norm of that
      output. The output is compared before any rounding to a 16-bit output
      type, so the error is the quantization error alone.
+  R9 the normalization before a projection ("How it works", Step 5: the
+     division by s can ride on the preceding normalization's weight; the
+     sketch divides the norm weight and bias by s) uses the textbook
+     definitions: RMSNorm x = h / sqrt(mean(h^2) + eps) * g, LayerNorm
+     x = (h - mean(h)) / sqrt(var(h) + eps) * g + b (biased variance). The
+     folded weight and bias g / s, b / s are single fp32 divisions. Row
+     statistics: sums taken exactly (correctly rounded fp64 sums), the mean
+     rounded to fp32, h - mean rounded to fp32, the inverse root
+     1 / sqrt(. + eps) evaluated in fp64 and rounded to fp32. Then
+     x_s = fp32(fp32(h * r) * g') (RMS) or
+     x_s = fp32(fp32(fp32((h - mean) * r) * g') + b') (LayerNorm), quantized
+     per token (or with a static scale) exactly as x_s from Step 5.
 """
 from __future__ import annotations
 
+import math
 from typing import Optional, Sequence, Tuple
 
 import numpy as np
@@ -336,3 +349,65 @@ def alpha_sweep(x_cal: np.ndarray, w: np.ndarray, alphas: Sequence[float],
     err = np.array(err, np.float64)
     rel = err / ref if ref > 0 else np.zeros_like(err)
     return {"err": err, "ref": ref, "rel": rel, "best": float(alphas[int(np.argmin(rel))])}
+
+
+# ----------------------------------------------------------------------------
+# [SQ] "How it works", Step 5 and the sketch's smooth_layer: 1/s folded into
+# the normalization that precedes the projection, then per-token quant.
+# ----------------------------------------------------------------------------
+def fold_norm_weight(gamma: np.ndarray, beta: Optional[np.ndarray],
+                     s: np.ndarray) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """R9: g' = fp32(g / s), b' = fp32(b / s) (IEEE fp32 divisions)."""
+    s = np.asarray(s, F32)
+    g = np.asarray(gamma, F32) / s
+    b = None if beta is None else np.asarray(beta, F32) / s
+    return g, b
+
+
+def norm_stats(h: np.ndarray, kind: str, eps: float) -> Tuple[np.ndarray, np.ndarray]:
+    """R9: per-row (mean, inverse root) in fp32. kind: 'rms' (mean 0) or 'layer'."""
+    h = np.asarray(h, F32)
+    M, K = h.shape
+    e = float(F32(eps))
+    mean = np.zeros(M, F32)
+    r = np.zeros(M, F32)
+    for m in range(M):
+        row = h[m].astype(np.float64)
+        if kind == "layer":
+            mean[m] = F32(math.fsum(row) / K)
+            d = (h[m] - mean[m]).astype(np.float64)          # fp32 subtraction, widened
+            ms = math.fsum(d * d) / K                        # products exact in fp64
+        else:
+            ms = math.fsum(row * row) / K
+        r[m] = F32(1.0 / math.sqrt(ms + e))
+    return mean, r
+
+
+def norm_smooth(h: np.ndarray, kind: str, g_fold: np.ndarray, b_fold: Optional[np.ndarray],
+                eps: float, stats: Optional[Tuple[np.ndarray, np.ndarray]] = None) -> np.ndarray:
+    """R9: the smoothed activations x_s straight from the residual stream h."""
+    h = np.asarray(h, F32)
+    mean, r = norm_stats(h, kind, eps) if stats is None else stats
+    g = np.asarray(g_fold, F32)[None, :]
+    if kind == "layer":
+        d = h - np.asarray(mean, F32)[:, None]
+        x = (d * np.asarray(r, F32)[:, None]) * g
+        return x + np.asarray(b_fold, F32)[None, :] if b_fold is not None else x
+    return (h * np.asarray(r, F32)[:, None]) * g
+
+
+def norm_quant(h: np.ndarray, kind: str, g_fold: np.ndarray, b_fold: Optional[np.ndarray],
+               eps: float, mode: str = "dynamic", a_static=None,
+               stats: Optional[Tuple[np.ndarray, np.ndarray]] = None):
+    """Normalization with the folded weight, then INT8 codes.
+
+    Returns (Xq, a_scale, (mean, r)); a_scale is [M] (dynamic) or the given
+    static scale. `stats` replaces the row statistics (to check codes given
+    another implementation's statistics)."""
+    st = norm_stats(h, kind, eps) if stats is None else stats
+    xs = norm_smooth(h, kind, g_fold, b_fold, eps, st)
+    if mode == "dynamic":
+        a = row_absmax_scale(xs)
+        return quantize_rows(xs, a), a, st
+    q, _ = quantize_per_tensor_static(xs, None, F32(a_static))
+    return q, F32(a_static), st

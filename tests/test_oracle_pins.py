@@ -559,3 +559,80 @@ def test_alpha_sweep_scale_invariance_at_the_ends():
     b = O.alpha_sweep(2 * x, w, [0.0, 1.0])
     assert np.array_equal(b["err"], 4 * a["err"]) and b["ref"] == 4 * a["ref"]
     assert np.array_equal(a["rel"], b["rel"])
+
+
+# ----------------------------------------------------------------------------
+# Normalization with the folded 1/s (R9)
+# ----------------------------------------------------------------------------
+def _norm_rows(seed, M=12, K=96):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((M, K)).astype(np.float32) * np.float32(3.0)
+    h[:, [5, 40]] *= 50.0
+    g = rng.uniform(0.5, 1.5, K).astype(np.float32)
+    b = (rng.standard_normal(K) * 0.1).astype(np.float32)
+    return h, g, b
+
+
+@pytest.mark.parametrize("kind", ["rms", "layer"])
+def test_norm_matches_torch_in_fp64(kind):
+    """Unfolded (s = 1): the textbook normalizations, as torch computes them in fp64."""
+    h, g, b = _norm_rows(1)
+    eps = 1e-5
+    ht, gt, bt = (torch.from_numpy(v).double() for v in (h, g, b))
+    e = float(np.float32(eps))
+    if kind == "rms":
+        ref = torch.nn.functional.rms_norm(ht, (h.shape[1],), gt, eps=e).numpy()
+        got = O.norm_smooth(h, "rms", g, None, eps)
+    else:
+        ref = torch.nn.functional.layer_norm(ht, (h.shape[1],), gt, bt, eps=e).numpy()
+        got = O.norm_smooth(h, "layer", g, b, eps)
+    assert got.dtype == np.float32
+    np.testing.assert_allclose(got, ref, rtol=4e-7 * 4, atol=1e-6)
+
+
+@pytest.mark.parametrize("kind", ["rms", "layer"])
+def test_norm_fold_with_power_of_two_s_is_exact(kind):
+    """With s a power of two, dividing g and b by s and dividing the norm output
+    by s are both exact, so x_s * s is the unfolded normalization bit for bit."""
+    h, g, b = _norm_rows(2)
+    s = np.exp2(np.random.default_rng(3).integers(-4, 5, h.shape[1])).astype(np.float32)
+    gf, bf = O.fold_norm_weight(g, b if kind == "layer" else None, s)
+    xs = O.norm_smooth(h, kind, gf, bf, 1e-5)
+    x = O.norm_smooth(h, kind, g, b if kind == "layer" else None, 1e-5)
+    assert np.array_equal(xs * s, x)
+    # and the smoothing direction: dividing x by s, not multiplying
+    assert not np.array_equal(xs, x * s)
+
+
+def test_norm_closed_forms():
+    K = 64
+    h = np.stack([np.full(K, 3.0, np.float32), np.full(K, -0.5, np.float32)])
+    g = np.linspace(0.5, 2.0, K).astype(np.float32)
+    b = np.linspace(-1.0, 1.0, K).astype(np.float32)
+    mean, r = O.norm_stats(h, "rms", 1e-5)
+    assert (mean == 0).all()
+    assert r[0] == np.float32(1.0 / math.sqrt(9.0 + float(np.float32(1e-5))))
+    # LayerNorm of a constant row: zero deviation, so the output is the bias
+    xs = O.norm_smooth(h, "layer", g, b, 1e-5)
+    assert np.array_equal(xs, np.stack([b, b]))
+    mean, r = O.norm_stats(h, "layer", 1e-5)
+    assert mean[0] == 3.0 and mean[1] == -0.5
+    assert r[0] == np.float32(1.0 / math.sqrt(float(np.float32(1e-5))))
+    # a row 0, 1, ..., K-1: mean (K-1)/2, biased variance (K^2 - 1)/12
+    ramp = np.arange(K, dtype=np.float32)[None, :]
+    mean, r = O.norm_stats(ramp, "layer", 0.0)
+    assert mean[0] == (K - 1) / 2
+    assert r[0] == np.float32(1.0 / math.sqrt((K * K - 1) / 12.0))
+
+
+def test_norm_quant_codes_and_scales():
+    h, g, b = _norm_rows(4)
+    q, a, (mean, r) = O.norm_quant(h, "layer", g, b, 1e-5)
+    xs = O.norm_smooth(h, "layer", g, b, 1e-5)
+    for m in range(h.shape[0]):
+        scale = brute.f32(max(abs(float(v)) for v in xs[m]) / 127.0)
+        assert a[m] == np.float32(scale)
+        assert list(q[m]) == brute.quant_row([float(v) for v in xs[m]], scale)
+    # static: the given scale, clipping allowed
+    qs, a_s, _ = O.norm_quant(h, "rms", g, None, 1e-5, mode="static", a_static=np.float32(0.01))
+    assert a_s == np.float32(0.01) and np.abs(qs).max() == 127
