@@ -381,7 +381,65 @@ def row_f4(args, torch):
     }
 
 
-ROWS = {"f3": row_f3, "f4": row_f4}
+def row_f2(args, torch):
+    """Normalization with the folded 1/s fused with the quantizer, on the
+    hidden-size inputs (the ones a norm precedes): Llama-3-8B (RMSNorm, bf16,
+    M=2048, K=4096), OPT-13B prefill (LayerNorm, fp16, M=4096, K=5120),
+    Llama-2-70B MLP (RMSNorm, bf16, M=8192, K=8192). Algorithmic bytes per
+    element: the 16-bit residual read and the INT8 code written (3), the same
+    as the quantizer alone; the unfused sequence (a norm kernel writing its
+    16-bit output, then the quantizer) moves 7."""
+    import w8a8_smoothquant_int8_amd as sq
+    from synth.workloads import cast_to
+    import numpy as np
+    cases = [("llama3_8b_hidden", "rms", "bf16", 2048, 4096),
+             ("opt13b_hidden", "layer", "f16", 4096, 5120),
+             ("llama2_70b_hidden", "rms", "bf16", 8192, 8192)]
+    reps = max(args.steps, 10)
+    out, best = {}, None
+    for name, kind, dt, M, K in cases:
+        rng = np.random.default_rng(M + K)
+        h = cast_to((rng.standard_normal((M, K)) * 2.0).astype(np.float32), dt).cuda()
+        g = torch.from_numpy(rng.uniform(0.5, 1.5, K).astype(np.float32)).to(h.dtype).cuda()
+        b = torch.zeros(K, dtype=h.dtype, device="cuda") if kind == "layer" else None
+        s = torch.from_numpy(np.exp(rng.uniform(-1.5, 2.0, K)).astype(np.float32)).cuda()
+        go = torch.empty(K, dtype=torch.float32, device="cuda")
+        bo = torch.empty(K, dtype=torch.float32, device="cuda") if b is not None else None
+        sq.sq_fold_norm_weight(g, b, s, go, bo)
+        Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+        a = torch.empty(M, dtype=torch.float32, device="cuda")
+        fused = time_launches(torch, lambda: sq.sq_norm_quant(h, kind, go, bo, 1e-5, Xq, a), reps)
+        quant = time_launches(torch, lambda: sq.sq_quant_per_token(h, s, Xq, a), reps)
+        if kind == "rms":
+            norm_fn = lambda: torch.nn.functional.rms_norm(h, (K,), g, eps=1e-5)
+        else:
+            norm_fn = lambda: torch.nn.functional.layer_norm(h, (K,), g, b, eps=1e-5)
+        xn = norm_fn()
+        unfused = time_launches(torch, lambda: (norm_fn(), sq.sq_quant_per_token(xn, s, Xq, a)), reps)
+        nbytes = 3.0 * M * K
+        out[name] = {"norm": kind, "dtype": dt, "M": M, "K": K,
+                     "fused_us": round(fused * 1e3, 2), "fused_gbs": round(nbytes / fused / 1e6, 1),
+                     "quant_alone_us": round(quant * 1e3, 2),
+                     "unfused_torch_norm_plus_quant_us": round(unfused * 1e3, 2)}
+        if best is None or nbytes > best[1]:
+            best = (fused, nbytes, name)
+        del h, Xq, xn
+        torch.cuda.empty_cache()
+    ms, nbytes, name = best
+    return {
+        "row": "f2", "metric": "fused norm + smoothing + per-token INT8 quant, GB/s",
+        "value": round(nbytes / ms / 1e6, 1), "unit": "GB/s", "higher_is_better": True,
+        "dtype": "bf16/f16->int8", "data": "synthetic",
+        "config": {"workload": "hidden-size norm inputs", "reps": reps},
+        "roofline": {"bound": "hbm", "kernel": f"k_norm_quant on {name}",
+                     "achieved": round(nbytes / ms / 1e6, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(ms, 5), "bytes_per_launch": nbytes},
+        "cases": out,
+    }
+
+
+ROWS = {"f2": row_f2, "f3": row_f3, "f4": row_f4}
 
 
 def main():

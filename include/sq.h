@@ -121,6 +121,40 @@ int sq_static_act_scale(const float* act_max, const float* s, int64_t K, float* 
 int sq_quant_per_token(const void* X, int xt, int64_t M, int64_t K, int64_t ldx,
                        const float* s, int mode, int8_t* Xq, float* a_scale, void* stream);
 
+/* Normalization kinds for sq_norm_quant. */
+typedef enum {
+  SQ_NORM_RMS = 0,    /* x = h / sqrt(mean_k h^2 + eps) * g */
+  SQ_NORM_LAYER = 1   /* x = (h - mean_k h) / sqrt(var_k h + eps) * g + b (biased variance) */
+} sq_norm_kind;
+
+/* [SQ] "How it works", Step 5 and the sketch's smooth_layer: the division by
+ * s rides on the normalization before the projection, whose weight and bias
+ * are divided by s once, offline.
+ * gamma_out[k] = fp32(gamma[k] / s[k]), beta_out[k] = fp32(beta[k] / s[k])
+ * (IEEE fp32 divisions; s == NULL: the values widened to fp32). gamma, beta:
+ * [K] of dtype gt (beta may be NULL, then beta_out must be NULL too);
+ * gamma_out, beta_out: [K] fp32, device, written. */
+int sq_fold_norm_weight(const void* gamma, const void* beta, int gt, int64_t K, const float* s,
+                        float* gamma_out, float* beta_out, void* stream);
+
+/* [SQ] Steps 5-6 fused with the normalization that precedes the projection:
+ * one pass over the residual stream H [M, K] (dtype ht, row stride ldh)
+ * writes the INT8 codes of x_s = norm(H) with the folded weight:
+ *   RMS:   x_s = fp32(fp32(h * r) * gamma)             r = fp32(1 / sqrt(ss / K + eps))
+ *   LAYER: x_s = fp32(fp32(fp32(fp32(h - mu) * r) * gamma) + beta)
+ *          mu = fp32(sum_k h / K), ss = sum_k fp32(h - mu)^2   (RMS: ss = sum_k h^2)
+ * Row sums in fp64 (squares exact), fixed order; sqrt and 1/x in fp64.
+ * gamma, beta: the folded [K] fp32 weight and bias (sq_fold_norm_weight),
+ * 16-byte aligned; beta NULL means 0 and must be NULL for RMS. eps >= 0.
+ * Then exactly sq_quant_per_token on x_s (no further division by s):
+ * dynamic writes a_scale [M]; static reads a_scale[0]. stats: NULL or
+ * [M, 2] fp32, written with (mu, r) per row (mu = 0 for RMS).
+ * K <= 16384 for 16-bit H and <= 4096 for fp32 H (SQ_ERR_INVALID_ARG
+ * beyond): a row lives in the registers of at most 4 waves. */
+int sq_norm_quant(const void* H, int ht, int64_t M, int64_t K, int64_t ldh, int norm,
+                  const float* gamma, const float* beta, float eps, int mode, int8_t* Xq,
+                  float* a_scale, float* stats, void* stream);
+
 /* [SQ] Step 6, static variant, with the clip count that "Calibration in
  * practice" and the page's closing advice ask to watch: a fixed per-tensor
  * scale lets values beyond the calibrated range clip, and the share of

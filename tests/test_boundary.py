@@ -36,7 +36,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sq.SIGNATURES)
@@ -321,3 +321,29 @@ def test_alpha_sweep_validation(L):
     assert call(ws=ctypes.c_void_p(0x10010)) == sq.SQ_ERR_MISALIGNED  # not 256-byte aligned
     assert call(wt=7) == sq.SQ_ERR_UNSUPPORTED_DTYPE
     assert call(M=0, ws=NULL) == sq.SQ_OK
+
+
+def test_norm_validation(L):
+    f = L.sq_norm_quant
+
+    def call(H=P, ht=sq.SQ_BF16, M=4, K=64, ldh=64, norm=0, g=P, b=NULL, eps=1e-5, mode=0, Xq=P,
+             a=P, st=NULL):
+        return f(H, ht, M, K, ldh, norm, g, b, ctypes.c_float(eps), mode, Xq, a, st, S)
+    assert call(norm=2) == sq.SQ_ERR_INVALID_ARG
+    assert call(b=P) == sq.SQ_ERR_INVALID_ARG                      # bias with RMS
+    assert call(g=NULL) == sq.SQ_ERR_INVALID_ARG
+    assert call(eps=-1.0) == sq.SQ_ERR_INVALID_ARG
+    assert call(eps=float("nan")) == sq.SQ_ERR_INVALID_ARG
+    assert call(mode=4) == sq.SQ_ERR_INVALID_ARG
+    assert call(K=16400, ldh=16400) == sq.SQ_ERR_INVALID_ARG       # beyond 16384 (16-bit)
+    assert call(ht=sq.SQ_F32, K=4112, ldh=4112) == sq.SQ_ERR_INVALID_ARG   # beyond 4096 (fp32)
+    assert call(g=P4) == sq.SQ_ERR_MISALIGNED
+    assert call(norm=1, b=P4) == sq.SQ_ERR_MISALIGNED
+    assert call(Xq=P4) == sq.SQ_ERR_MISALIGNED
+    assert call(M=0) == sq.SQ_OK
+    fold = L.sq_fold_norm_weight
+    assert fold(NULL, NULL, sq.SQ_BF16, 64, NULL, P, NULL, S) == sq.SQ_ERR_INVALID_ARG
+    assert fold(P, P, sq.SQ_BF16, 64, NULL, P, NULL, S) == sq.SQ_ERR_INVALID_ARG   # beta_out missing
+    assert fold(P, NULL, 9, 64, NULL, P, NULL, S) == sq.SQ_ERR_UNSUPPORTED_DTYPE
+    assert fold(P, NULL, sq.SQ_BF16, 0, NULL, P, NULL, S) == sq.SQ_ERR_INVALID_ARG
+    assert fold(P, NULL, sq.SQ_F32, 64, NULL, ctypes.c_void_p(0x10002), NULL, S) == sq.SQ_ERR_MISALIGNED

@@ -45,6 +45,9 @@ SIGNATURES = {
     "sq_smooth_fold": (_c_int, [_vp, _vp, _c_int, _c_i64, _c_i64, _c_i64, _c_d, _vp, _vp, _vp, _vp]),
     "sq_static_act_scale": (_c_int, [_vp, _vp, _c_i64, _vp, _vp]),
     "sq_quant_per_token": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _c_int, _vp, _vp, _vp]),
+    "sq_fold_norm_weight": (_c_int, [_vp, _vp, _c_int, _c_i64, _vp, _vp, _vp, _vp]),
+    "sq_norm_quant": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp, _c_f, _c_int,
+                               _vp, _vp, _vp, _vp]),
     "sq_quant_static_clipped": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp,
                                          _vp]),
     "sq_w8a8_gemm": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_int,
@@ -192,6 +195,28 @@ def sq_quant_per_token(X: torch.Tensor, s: Optional[torch.Tensor], Xq: torch.Ten
     _check("sq_quant_per_token", lib().sq_quant_per_token(
         _ptr(X), _dt(X), M, K, _ld(X), _ptr(s), MODES[mode], _ptr(Xq), _ptr(a_scale),
         _stream(stream)))
+
+
+SQ_NORM = {"rms": 0, "layer": 1}
+
+
+def sq_fold_norm_weight(gamma: torch.Tensor, beta: Optional[torch.Tensor], s: Optional[torch.Tensor],
+                        gamma_out: torch.Tensor, beta_out: Optional[torch.Tensor],
+                        stream=None) -> None:
+    """gamma_out = fp32(gamma / s), beta_out = fp32(beta / s); fp32 outputs."""
+    _check("sq_fold_norm_weight", lib().sq_fold_norm_weight(
+        _ptr(gamma), _ptr(beta), _dt(gamma), gamma.numel(), _ptr(s), _ptr(gamma_out),
+        _ptr(beta_out), _stream(stream)))
+
+
+def sq_norm_quant(H: torch.Tensor, kind: str, gamma: torch.Tensor, beta: Optional[torch.Tensor],
+                  eps: float, Xq: torch.Tensor, a_scale: torch.Tensor, mode: str = "dynamic",
+                  stats: Optional[torch.Tensor] = None, stream=None) -> None:
+    """RMSNorm / LayerNorm of H with the folded fp32 weight (and bias), then INT8 codes."""
+    M, K = H.shape
+    _check("sq_norm_quant", lib().sq_norm_quant(
+        _ptr(H), _dt(H), M, K, _ld(H), SQ_NORM[kind], _ptr(gamma), _ptr(beta), float(eps),
+        MODES[mode], _ptr(Xq), _ptr(a_scale), _ptr(stats), _stream(stream)))
 
 
 def sq_quant_static_clipped(X: torch.Tensor, s: Optional[torch.Tensor], a_scale: torch.Tensor,

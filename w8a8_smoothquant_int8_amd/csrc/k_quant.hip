@@ -49,27 +49,6 @@ __device__ __forceinline__ void load_row(RowChunks<DT, CPT>& r, const char* row,
   }
 }
 
-template <int DT>
-__device__ __forceinline__ void widen8(const uint4* w, float* out) {
-  if constexpr (DT == SQ_F32) {
-    out[0] = __uint_as_float(w[0].x); out[1] = __uint_as_float(w[0].y);
-    out[2] = __uint_as_float(w[0].z); out[3] = __uint_as_float(w[0].w);
-    out[4] = __uint_as_float(w[1].x); out[5] = __uint_as_float(w[1].y);
-    out[6] = __uint_as_float(w[1].z); out[7] = __uint_as_float(w[1].w);
-  } else {
-    uint32_t u[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (DT == SQ_BF16) {
-        out[2 * i] = __uint_as_float(u[i] << 16);
-        out[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
-      } else {
-        out[2 * i] = f16_bits_to_f32(u[i] & 0xFFFFu);
-        out[2 * i + 1] = f16_bits_to_f32(u[i] >> 16);
-      }
-    }
-  }
-}
 
 // rows: M (activations) or N (weights). in_ld_bytes: input row stride.
 // s: [K] or null (no smoothing). scale_io: [rows] written (FOLD, DYNAMIC) or
@@ -453,24 +432,6 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
   }
 }
 
-// Resident blocks of one kernel on the current device (occupancy x CUs),
-// cached per kernel instantiation and device.
-template <typename Tag>
-static int64_t resident_blocks(const void* f, int T) {
-  static int per_cu[16] = {0};
-  static int cus[16] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
-  if (per_cu[dev] == 0) {
-    int n = 0, b = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, f, T, 0) != hipSuccess || b <= 0) b = 1;
-    cus[dev] = n;
-    per_cu[dev] = b;
-  }
-  return (int64_t)per_cu[dev] * cus[dev];
-}
 
 template <int DT, int KIND, int CPL, int WPR>
 static void launch_wave(const char* p, int64_t rows, int64_t K, int64_t ldb, const float* s,

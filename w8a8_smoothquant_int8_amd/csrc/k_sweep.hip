@@ -129,12 +129,6 @@ k_ref_gemm(const char* __restrict__ X, int64_t ldx, const char* __restrict__ W, 
 constexpr int kErrBlocks = 1024;
 constexpr int kErrThreads = 256;
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
 // Sum of two values over a 256-thread block, the same order every run;
 // thread 0 gets the result.
 __device__ __forceinline__ void block_sum2(double& d, double& r) {

@@ -28,6 +28,11 @@ int launch_ref_gemm(const void* X, int xt, int64_t ldx, const void* W, int wt, i
 int launch_sq_err(const float* q, const double* ref, int64_t n, double* part, double* out,
                   hipStream_t st);
 size_t err_partials_bytes();
+int64_t norm_quant_max_k(int ht);
+int launch_norm_quant(const void* H, int ht, int64_t M, int64_t K, int64_t ldh, int norm,
+                      const float* g, const float* b, double eps, int mode, int8_t* Xq,
+                      float* a_scale, float* stats, hipStream_t st);
+int launch_fold_norm(const void* w, int wt, const float* s, int64_t K, float* out, hipStream_t st);
 int launch_static_scale(const float* act_max, const float* s, int64_t K, float* a_scale, hipStream_t st);
 int launch_fold_quant(const void* W, int wt, int64_t N, int64_t K, int64_t ldw, const float* s,
                       int8_t* Wq, float* w_scale, hipStream_t st);
@@ -225,6 +230,45 @@ int sq_quant_per_token(const void* X, int xt, int64_t M, int64_t K, int64_t ldx,
   if (M == 0) return SQ_OK;
   if ((rc = gate()) != SQ_OK) return rc;
   return sq::launch_quant_act(X, xt, M, K, ldx, s, mode, Xq, a_scale, nullptr, as_stream(stream));
+}
+
+int sq_fold_norm_weight(const void* gamma, const void* beta, int gt, int64_t K, const float* s,
+                        float* gamma_out, float* beta_out, void* stream) {
+  SQ_REQUIRE(gamma != nullptr && gamma_out != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE((beta == nullptr) == (beta_out == nullptr), SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(valid_dtype(gt), SQ_ERR_UNSUPPORTED_DTYPE);
+  SQ_REQUIRE(K >= 1 && K <= kMaxK, SQ_ERR_INVALID_ARG);
+  const int esz = gt == SQ_F32 ? 4 : 2;
+  SQ_REQUIRE(((uintptr_t)gamma % esz) == 0 && (beta == nullptr || ((uintptr_t)beta % esz) == 0) &&
+                 aligned4(gamma_out) && (beta_out == nullptr || aligned4(beta_out)) &&
+                 (s == nullptr || aligned4(s)),
+             SQ_ERR_MISALIGNED);
+  int rc = gate();
+  if (rc != SQ_OK) return rc;
+  hipStream_t st = as_stream(stream);
+  if ((rc = sq::launch_fold_norm(gamma, gt, s, K, gamma_out, st)) != SQ_OK) return rc;
+  if (beta != nullptr) rc = sq::launch_fold_norm(beta, gt, s, K, beta_out, st);
+  return rc;
+}
+
+int sq_norm_quant(const void* H, int ht, int64_t M, int64_t K, int64_t ldh, int norm,
+                  const float* gamma, const float* beta, float eps, int mode, int8_t* Xq,
+                  float* a_scale, float* stats, void* stream) {
+  int rc = check_matrix(H, ht, M, K, ldh);
+  if (rc != SQ_OK) return rc;
+  SQ_REQUIRE(norm == SQ_NORM_RMS || norm == SQ_NORM_LAYER, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(norm == SQ_NORM_LAYER || beta == nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(K <= sq::norm_quant_max_k(ht), SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(valid_mode(mode), SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(std::isfinite(eps) && eps >= 0.0f, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(gamma != nullptr && Xq != nullptr && a_scale != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(aligned16(gamma) && (beta == nullptr || aligned16(beta)) && aligned16(Xq) &&
+                 aligned4(a_scale) && (stats == nullptr || aligned4(stats)),
+             SQ_ERR_MISALIGNED);
+  if (M == 0) return SQ_OK;
+  if ((rc = gate()) != SQ_OK) return rc;
+  return sq::launch_norm_quant(H, ht, M, K, ldh, norm, gamma, beta, (double)eps, mode, Xq, a_scale,
+                               stats, as_stream(stream));
 }
 
 int sq_quant_static_clipped(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const float* s,

@@ -34,7 +34,8 @@ from typing import Dict, List, Optional, Tuple
 import torch
 
 from . import (SQ_GROUP_CALIBRATE, SQ_GROUP_FOLD, SQ_GROUP_FORWARD, SQ_MAX_LORA_RANK,
-               sq_alpha_sweep, sq_alpha_sweep_workspace_bytes, sq_calibrate_absmax, sq_linear_group_desc, sq_linear_group_run, sq_lora_apply,
+               sq_alpha_sweep, sq_alpha_sweep_workspace_bytes, sq_calibrate_absmax,
+               sq_fold_norm_weight, sq_norm_quant, sq_linear_group_desc, sq_linear_group_run, sq_lora_apply,
                sq_lora_apply_segmented, sq_lora_shrink, sq_lora_workspace_bytes,
                sq_quant_per_token, sq_quant_static_clipped, sq_smooth_fold, sq_static_act_scale,
                sq_w8a8_gemm, sq_w8a8_gemm_lora)
@@ -146,6 +147,37 @@ class LinearGroup:
         sq_smooth_fold(self.act_max, self.W, self.alpha, self.s, self.Wq, self.w_scale)
         if "static" in self.modes:
             sq_static_act_scale(self.act_max, self.s, self.static_scale)
+
+    # -- the normalization in front of the group ----------------------------
+    def set_norm(self, gamma: torch.Tensor, beta: Optional[torch.Tensor] = None,
+                 kind: str = "rms", eps: float = 1e-5) -> None:
+        """The RMSNorm / LayerNorm that produces this group's input. After
+        fold(), fold_norm() divides its weight and bias by s ("SmoothQuant"
+        explainer, "How it works", Step 5), and forward_norm() runs the group
+        straight from the residual stream."""
+        self.norm = (gamma, beta, kind, float(eps))
+        K = self.K
+        self.norm_g = torch.empty(K, dtype=torch.float32, device=gamma.device)
+        self.norm_b = torch.empty(K, dtype=torch.float32, device=gamma.device) \
+            if beta is not None else None
+
+    def fold_norm(self) -> None:
+        gamma, beta, _, _ = self.norm
+        sq_fold_norm_weight(gamma, beta, self.s, self.norm_g, self.norm_b)
+
+    def quantize_norm(self, H: torch.Tensor, mode: str = "dynamic") -> None:
+        _, _, kind, eps = self.norm
+        sq_norm_quant(H, kind, self.norm_g, self.norm_b, eps, self.Xq, self._a(mode), mode=mode)
+
+    def forward_norm(self, H: torch.Tensor, mode: str = "dynamic") -> Dict[str, torch.Tensor]:
+        """norm -> (folded) smoothing -> quant in one kernel, then the GEMM. The
+        LoRA path reads the unsmoothed norm output, which this kernel does not
+        write, so groups with adapters use forward() on the norm output."""
+        if self.lora or self.seg_lora:
+            raise ValueError("forward_norm covers groups without LoRA adapters")
+        self.quantize_norm(H, mode)
+        self.gemm_all(mode)
+        return self.Y
 
     # -- per batch ----------------------------------------------------------
     def _a(self, mode: str) -> torch.Tensor:
