@@ -155,6 +155,18 @@ int sq_norm_quant(const void* H, int ht, int64_t M, int64_t K, int64_t ldh, int 
                   const float* gamma, const float* beta, float eps, int mode, int8_t* Xq,
                   float* a_scale, float* stats, void* stream);
 
+/* [SQ] Steps 5-6 and the first half of [LoRA] Pitch from one read of X:
+ * Xq and a_scale exactly as sq_quant_per_token(X, s, mode), and
+ * T[m, i] = bf16(sum_k bf16(X[m, k]) * A[i, k]) (fp32 sums) as sq_lora_shrink
+ * computes it (the fp32 summation order differs, so T can differ from that
+ * call's in the last bf16 bit). X: bf16 with K <= 8192, or fp16 with
+ * K <= 4096 (SQ_ERR_UNSUPPORTED_DTYPE / SQ_ERR_INVALID_ARG otherwise); A: [r, K] bf16,
+ * 8 <= r <= SQ_MAX_LORA_RANK, r % 8 == 0; T: [M, r] bf16, row stride ldt
+ * (>= r, a multiple of 8). No workspace. */
+int sq_quant_shrink(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const float* s,
+                    int mode, int8_t* Xq, float* a_scale, const void* A, int r, void* T,
+                    int64_t ldt, void* stream);
+
 /* [SQ] Step 6, static variant, with the clip count that "Calibration in
  * practice" and the page's closing advice ask to watch: a fixed per-tensor
  * scale lets values beyond the calibrated range clip, and the share of

@@ -36,7 +36,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sq.SIGNATURES)
@@ -347,3 +347,23 @@ def test_norm_validation(L):
     assert fold(P, NULL, 9, 64, NULL, P, NULL, S) == sq.SQ_ERR_UNSUPPORTED_DTYPE
     assert fold(P, NULL, sq.SQ_BF16, 0, NULL, P, NULL, S) == sq.SQ_ERR_INVALID_ARG
     assert fold(P, NULL, sq.SQ_F32, 64, NULL, ctypes.c_void_p(0x10002), NULL, S) == sq.SQ_ERR_MISALIGNED
+
+
+def test_quant_shrink_validation(L):
+    f = L.sq_quant_shrink
+
+    def call(X=P, xt=sq.SQ_BF16, M=4, K=64, ldx=64, s=NULL, mode=0, Xq=P, a=P, A=P, r=16, T=P,
+             ldt=16):
+        return f(X, xt, M, K, ldx, s, mode, Xq, a, A, r, T, ldt, S)
+    assert call(xt=sq.SQ_F32) == sq.SQ_ERR_UNSUPPORTED_DTYPE
+    assert call(K=8208, ldx=8208) == sq.SQ_ERR_INVALID_ARG       # beyond 8192 (bf16)
+    assert call(xt=sq.SQ_F16, K=4112, ldx=4112) == sq.SQ_ERR_INVALID_ARG   # beyond 4096 (fp16)
+    assert call(r=0) == sq.SQ_ERR_INVALID_ARG
+    assert call(r=12) == sq.SQ_ERR_MISALIGNED
+    assert call(r=136, ldt=136) == sq.SQ_ERR_INVALID_ARG
+    assert call(A=NULL) == sq.SQ_ERR_INVALID_ARG
+    assert call(ldt=8) == sq.SQ_ERR_INVALID_ARG                  # ldt < r
+    assert call(ldt=20, r=16) == sq.SQ_ERR_MISALIGNED
+    assert call(A=P4) == sq.SQ_ERR_MISALIGNED
+    assert call(mode=2) == sq.SQ_ERR_INVALID_ARG
+    assert call(M=0) == sq.SQ_OK

@@ -48,6 +48,8 @@ SIGNATURES = {
     "sq_fold_norm_weight": (_c_int, [_vp, _vp, _c_int, _c_i64, _vp, _vp, _vp, _vp]),
     "sq_norm_quant": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp, _c_f, _c_int,
                                _vp, _vp, _vp, _vp]),
+    "sq_quant_shrink": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _c_int, _vp, _vp, _vp,
+                                 _c_int, _vp, _c_i64, _vp]),
     "sq_quant_static_clipped": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp,
                                          _vp]),
     "sq_w8a8_gemm": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_int,
@@ -195,6 +197,16 @@ def sq_quant_per_token(X: torch.Tensor, s: Optional[torch.Tensor], Xq: torch.Ten
     _check("sq_quant_per_token", lib().sq_quant_per_token(
         _ptr(X), _dt(X), M, K, _ld(X), _ptr(s), MODES[mode], _ptr(Xq), _ptr(a_scale),
         _stream(stream)))
+
+
+def sq_quant_shrink(X: torch.Tensor, s: Optional[torch.Tensor], Xq: torch.Tensor,
+                    a_scale: torch.Tensor, A: torch.Tensor, T: torch.Tensor, mode: str = "dynamic",
+                    stream=None) -> None:
+    """Per-token quant of X and T = bf16(X A^T) from one read of X (16-bit X, K <= 8192)."""
+    M, K = X.shape
+    _check("sq_quant_shrink", lib().sq_quant_shrink(
+        _ptr(X), _dt(X), M, K, _ld(X), _ptr(s), MODES[mode], _ptr(Xq), _ptr(a_scale), _ptr(A),
+        A.shape[0], _ptr(T), _ld(T), _stream(stream)))
 
 
 SQ_NORM = {"rms": 0, "layer": 1}

@@ -33,6 +33,10 @@ int launch_norm_quant(const void* H, int ht, int64_t M, int64_t K, int64_t ldh, 
                       const float* g, const float* b, double eps, int mode, int8_t* Xq,
                       float* a_scale, float* stats, hipStream_t st);
 int launch_fold_norm(const void* w, int wt, const float* s, int64_t K, float* out, hipStream_t st);
+int64_t quant_shrink_max_k(int xt);
+int launch_quant_shrink(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const float* s,
+                        int mode, int8_t* Xq, float* a_scale, const void* A, int r, void* T,
+                        int64_t ldt, hipStream_t st);
 int launch_static_scale(const float* act_max, const float* s, int64_t K, float* a_scale, hipStream_t st);
 int launch_fold_quant(const void* W, int wt, int64_t N, int64_t K, int64_t ldw, const float* s,
                       int8_t* Wq, float* w_scale, hipStream_t st);
@@ -271,6 +275,28 @@ int sq_norm_quant(const void* H, int ht, int64_t M, int64_t K, int64_t ldh, int 
                                stats, as_stream(stream));
 }
 
+static int check_rank(int r);
+
+int sq_quant_shrink(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const float* s,
+                    int mode, int8_t* Xq, float* a_scale, const void* A, int r, void* T,
+                    int64_t ldt, void* stream) {
+  int rc = check_matrix(X, xt, M, K, ldx);
+  if (rc != SQ_OK) return rc;
+  SQ_REQUIRE(xt == SQ_BF16 || xt == SQ_F16, SQ_ERR_UNSUPPORTED_DTYPE);
+  SQ_REQUIRE(K <= sq::quant_shrink_max_k(xt), SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(valid_mode(mode), SQ_ERR_INVALID_ARG);
+  if ((rc = check_rank(r)) != SQ_OK) return rc;
+  SQ_REQUIRE(Xq != nullptr && a_scale != nullptr && A != nullptr && T != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(ldt >= r, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(ldt % 8 == 0 && aligned16(Xq) && aligned16(A) && aligned16(T) && aligned4(a_scale) &&
+                 (s == nullptr || aligned4(s)),
+             SQ_ERR_MISALIGNED);
+  if (M == 0) return SQ_OK;
+  if ((rc = gate()) != SQ_OK) return rc;
+  return sq::launch_quant_shrink(X, xt, M, K, ldx, s, mode, Xq, a_scale, A, r, T, ldt,
+                                 as_stream(stream));
+}
+
 int sq_quant_static_clipped(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const float* s,
                             const float* a_scale, int8_t* Xq, unsigned long long* clipped,
                             void* stream) {
@@ -503,6 +529,10 @@ int sq_linear_group_run(const sq_linear_group* g, int flags, void* stream, void*
       return rc;
   }
   if ((flags & SQ_GROUP_FORWARD) && g->M > 0) {
+    // The quant and the shrink as two kernels: at the workload's shapes they
+    // are faster alone than the one-read sq_quant_shrink (and equal inside the
+    // overlapped step), which needs a 16-row block per CU and reads all of A
+    // per block.
     if ((rc = sq::launch_quant_act(g->X, g->xt, g->M, g->K, g->ldx, g->s, g->mode, g->Xq, g->a_scale,
                                    nullptr, st)) != SQ_OK)
       return rc;

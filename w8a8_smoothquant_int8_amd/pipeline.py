@@ -9,7 +9,8 @@ are stacked into one [sum N, K] matrix.
 Forward pass (fused, the default): one quantization of the input, one LoRA
 shrink with every projection's A stacked along the rank (X is read once for
 all adapters), and one GEMM over the stacked weights whose epilogue adds the
-LoRA delta. The stacked B is block-diagonal (projection p's rows carry its B
+LoRA delta. quantize_and_shrink() does the first two in one kernel that reads
+X once (sq_quant_shrink). The stacked B is block-diagonal (projection p's rows carry its B
 in its own rank columns and zeros elsewhere), so each output column gets only
 its own adapter's delta, exactly as separate per-projection calls would give.
 Per-projection outputs are column views of one [M, sum N] buffer.
@@ -35,7 +36,8 @@ import torch
 
 from . import (SQ_GROUP_CALIBRATE, SQ_GROUP_FOLD, SQ_GROUP_FORWARD, SQ_MAX_LORA_RANK,
                sq_alpha_sweep, sq_alpha_sweep_workspace_bytes, sq_calibrate_absmax,
-               sq_fold_norm_weight, sq_norm_quant, sq_linear_group_desc, sq_linear_group_run, sq_lora_apply,
+               sq_fold_norm_weight, sq_norm_quant, sq_quant_shrink, SQError, SQ_ERR_INVALID_ARG,
+               SQ_ERR_UNSUPPORTED_DTYPE, sq_linear_group_desc, sq_linear_group_run, sq_lora_apply,
                sq_lora_apply_segmented, sq_lora_shrink, sq_lora_workspace_bytes,
                sq_quant_per_token, sq_quant_static_clipped, sq_smooth_fold, sq_static_act_scale,
                sq_w8a8_gemm, sq_w8a8_gemm_lora)
@@ -214,6 +216,22 @@ class LinearGroup:
 
     def lora_shrink(self, X: torch.Tensor) -> None:
         sq_lora_shrink(X, self.A_stack, self.T, self.ws)
+
+    def quantize_and_shrink(self, X: torch.Tensor, mode: str = "dynamic") -> None:
+        """The quant and the stacked LoRA shrink: one kernel reading X once where
+        sq_quant_shrink takes the shape (16-bit X, K within its register budget),
+        else the two separate calls."""
+        if getattr(self, "_qs_ok", True):
+            try:
+                sq_quant_shrink(X, self.s, self.Xq, self._a(mode), self.A_stack, self.T, mode=mode)
+                self._qs_ok = True
+                return
+            except SQError as e:          # rejected on the host: nothing was enqueued
+                if e.status not in (SQ_ERR_INVALID_ARG, SQ_ERR_UNSUPPORTED_DTYPE):
+                    raise
+                self._qs_ok = False
+        self.quantize(X, mode)
+        self.lora_shrink(X)
 
     def gemm_all_lora(self, mode: str = "dynamic") -> None:
         """All projections' GEMMs as one call, each adding its LoRA delta in the epilogue."""
