@@ -6,13 +6,13 @@ CPU oracle's tests and the HIP path's tests and benchmark can take their
 inputs from it without sharing any computation.
 
 Structure of the inputs. The SmoothQuant explainer ("Why activations are
-harder than weights") describes activations with a few channels that are tens
-to hundreds of times larger than the rest, in the same channels for every
-token. Each activation input below is therefore N(0, 1) with a fixed set of
-outlier columns multiplied by per-column factors. Weights are N(0, 0.02);
-LoRA factors are N(0, 0.01) in bf16. A calibration batch for an input is an
-independent draw with the same outlier columns and factors ("Step 4:
-Estimate activation statistics with calibration"), min(M, 512) rows.
+harder than weights") describes activations where a few channels run one to
+two orders of magnitude above the others, and do so at the same channel
+positions for every token. Each activation input below is therefore N(0, 1)
+with a fixed set of outlier columns multiplied by per-column factors. Weights
+are N(0, 0.02); LoRA factors are N(0, 0.01) in bf16. A calibration batch for
+an input is an independent draw with the same outlier columns and factors
+("How it works", Step 4, the calibration statistics), min(M, 512) rows.
 
 Randomness. Every tensor has its own numpy PCG64 stream, derived from
 SeedSequence(entropy=seed, spawn_key=key) with a fixed integer key per tensor
