@@ -12,7 +12,8 @@ timed region starts.
 
 The input groups are independent, so a timed step issues every group as one
 native call (sq_linear_group_run: calibrate, fold, quantize, LoRA shrink,
-GEMM) on its own stream and the groups' kernels overlap.
+GEMM) on one of three streams, largest group first, and the groups' kernels
+overlap.
 
 Output: one JSON line. `value` is GEMM INT8 tera-operations per second of the
 whole step (2*M*N*K summed over the projections, divided by the step time).
@@ -149,31 +150,53 @@ def run_step(groups, tl=None):
     mark(None)
 
 
-class Streams:
-    """One stream per input group, default priority."""
+# HIP maps streams onto a few hardware queues (4 by default, one of them taken
+# by the null stream); two streams that share a queue run in order. Three
+# streams get a queue each.
+N_STREAMS = 3
 
-    def __init__(self, torch, n_groups):
+
+class Streams:
+    """The step's streams (default priority) and the group -> stream plan:
+    groups in descending order of GEMM work, each on the stream with the least
+    work so far (longest-processing-time first). The longest chain starts
+    first and never queues behind another group. Measured on the Llama-3-8B
+    step: 0.78 ms against 0.85 ms for one stream per group in workload order
+    (two of those four streams then shared a hardware queue)."""
+
+    def __init__(self, torch, groups, n_streams=N_STREAMS):
         self.torch = torch
-        self.main = [torch.cuda.Stream() for _ in range(n_groups)]
+        n = min(n_streams, len(groups))
+        self.main = [torch.cuda.Stream() for _ in range(n)]
+        work = [2.0 * g.M * g.Ntot * g.K for _inp, g, _x, _c in groups]
+        load = [0.0] * n
+        self.plan = []                                    # (group index, stream index), issue order
+        for gi in sorted(range(len(groups)), key=lambda i: -work[i]):
+            si = min(range(n), key=lambda j: load[j])
+            load[si] += work[gi]
+            self.plan.append((gi, si))
 
 
 def run_step_streams(groups, st, gemm_ev=None):
     """One pass of the whole path over one batch. The input groups are
     independent: each runs calibrate -> fold -> quantize -> LoRA shrink ->
-    GEMM as one native call (sq_linear_group_run) on its own stream, so the
-    groups' short, latency-bound kernels fill each other's gaps and a GEMM
-    whose tiles leave CUs idle in its last round shares the chip with the next
-    group's work. gemm_ev: {group: [(start, end), ...]} collects HIP events
-    that the library records on the group's stream right around its GEMM."""
+    GEMM as one native call (sq_linear_group_run) on the stream the plan gives
+    it, so the groups' short, latency-bound kernels fill each other's gaps and
+    a GEMM whose tiles leave CUs idle in its last round shares the chip with
+    another group's work. gemm_ev: {group: [(start, end), ...]} collects HIP
+    events that the library records on the group's stream right around its
+    GEMM."""
     torch = st.torch
     cur = torch.cuda.current_stream()
-    for (inp, g, X, Xc), sm in zip(groups, st.main):
+    for sm in st.main:
         sm.wait_stream(cur)
+    for gi, si in st.plan:
+        inp, g, X, Xc = groups[gi]
         e0 = e1 = None
         if gemm_ev is not None:
             e0, e1 = gemm_ev["pool"].pop()
             gemm_ev.setdefault(inp, []).append((e0, e1))
-        g.run(X, Xc, stream=sm, gemm_begin=e0, gemm_end=e1)
+        g.run(X, Xc, stream=st.main[si], gemm_begin=e0, gemm_end=e1)
     for sm in st.main:
         cur.wait_stream(sm)
 
@@ -521,7 +544,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    st = Streams(torch, len(groups))
+    st = Streams(torch, groups)
     for _ in range(args.warmup):
         run_step_streams(groups, st)
     torch.cuda.synchronize()
