@@ -166,15 +166,23 @@ class Streams:
 
     def __init__(self, torch, groups, n_streams=N_STREAMS):
         self.torch = torch
-        n = min(n_streams, len(groups))
-        self.main = [torch.cuda.Stream() for _ in range(n)]
         work = [2.0 * g.M * g.Ntot * g.K for _inp, g, _x, _c in groups]
-        load = [0.0] * n
-        self.plan = []                                    # (group index, stream index), issue order
-        for gi in sorted(range(len(groups)), key=lambda i: -work[i]):
-            si = min(range(n), key=lambda j: load[j])
-            load[si] += work[gi]
-            self.plan.append((gi, si))
+        self.plan = plan_streams(work, n_streams)       # (group index, stream index), issue order
+        self.main = [torch.cuda.Stream() for _ in range(min(n_streams, len(groups)))]
+
+
+def plan_streams(work, n_streams):
+    """Longest-processing-time plan: groups in descending work (ties in input
+    order), each to the stream with the least work so far (ties: the lowest
+    index). Returns [(group index, stream index)] in issue order."""
+    n = min(n_streams, len(work))
+    load = [0.0] * n
+    plan = []
+    for gi in sorted(range(len(work)), key=lambda i: (-work[i], i)):
+        si = min(range(n), key=lambda j: (load[j], j))
+        load[si] += work[gi]
+        plan.append((gi, si))
+    return plan
 
 
 def run_step_streams(groups, st, gemm_ev=None):

@@ -1,0 +1,42 @@
+"""Host-side logic of bench.py, without a GPU."""
+import os
+import subprocess
+import sys
+
+import bench
+from synth.workloads import get_workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_stream_plan_longest_first_least_loaded():
+    wl = get_workload("llama3_8b_proj_m2048")
+    work = [2.0 * wl.M * sum(p.N for p in wl.group(inp)) * K for inp, K in wl.inputs]
+    plan = bench.plan_streams(work, 3)
+    names = [wl.inputs[gi][0] for gi, _ in plan]
+    assert names == ["mlp_in", "down_in", "attn_in", "o_in"]
+    assert [si for _, si in plan] == [0, 1, 2, 2]          # QKV and O share the third stream
+    # every group once; never more streams than groups
+    assert sorted(gi for gi, _ in bench.plan_streams([5.0, 1.0], 3)) == [0, 1]
+    assert max(si for _, si in bench.plan_streams([5.0, 1.0], 3)) == 1
+    # equal work: input order, round robin
+    assert bench.plan_streams([1.0] * 4, 2) == [(0, 0), (1, 1), (2, 0), (3, 1)]
+
+
+def test_gemm_tile_rule_covers_the_workload():
+    wl = get_workload("llama3_8b_proj_m2048")
+    tiles = {inp: bench.gemm_tile(wl.M, sum(p.N for p in wl.group(inp)), K) for inp, K in wl.inputs}
+    assert set(tiles.values()) <= {"256x256", "128x128", "generic"}
+    assert tiles["mlp_in"] == "256x256"
+
+
+def test_cpu_baseline_on_the_tiny_workload():
+    cb = bench.cpu_baseline(get_workload("tiny_m16_k256_n256"), 8)
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
