@@ -456,3 +456,49 @@ def test_fused_group_matches_unfused():
         ok, rel = lora_close(out[0][p].float().cpu().numpy(), out[1][p].float().cpu().numpy())
         assert ok, (p, rel)
         assert (out[0][p] != out[1][p]).float().mean().item() < 0.01
+
+
+# ---------------------------------------------------------------------------
+# The largest K the calls accept (32768): one row per block at 8 chunks per
+# thread in the quantizer, the longest K loop in the GEMM.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_max_k_whole_path(dtype):
+    K, M, N = 32768, 19, 48
+    rng = np.random.default_rng(32768)
+    x, xn = acts(rng, M, K, dtype, factor=30.0)
+    w, wn = acts(rng, N, K, dtype, n_out=0, sigma=0.02)
+    am = torch.zeros(K, dtype=torch.float32, device="cuda")
+    sq.sq_calibrate_absmax(x, am)
+    act_max = O.calibrate_absmax(xn)
+    assert bits_equal(npf(am), act_max)
+    s = torch.empty(K, dtype=torch.float32, device="cuda")
+    Wq = torch.empty(N, K, dtype=torch.int8, device="cuda")
+    ws = torch.empty(N, dtype=torch.float32, device="cuda")
+    sq.sq_smooth_fold(am, w, 0.5, s, Wq, ws)
+    s_ref = O.smoothing_scale(act_max, O.weight_absmax(wn), 0.5)
+    assert bits_equal(npf(s), s_ref)
+    wq_ref, ws_ref = O.fold_and_quantize_weights(wn, s_ref)
+    assert bits_equal(Wq.cpu().numpy(), wq_ref) and bits_equal(npf(ws), ws_ref)
+    Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+    a = torch.empty(M, dtype=torch.float32, device="cuda")
+    sq.sq_quant_per_token(x, s, Xq, a)
+    xq_ref, a_ref = O.quantize_per_token(xn, s_ref)
+    assert bits_equal(Xq.cpu().numpy(), xq_ref) and bits_equal(npf(a), a_ref)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    sq.sq_w8a8_gemm(Xq, Wq, a, ws, Y)
+    y_ref = O.dequantize(O.int8_gemm(xq_ref, wq_ref), a_ref, ws_ref, "bf16")
+    assert bits_equal(npf(Y), y_ref)
+
+
+def test_max_k_extreme_accumulators():
+    K = 32768                                         # |acc| up to K * 127^2 = 528,482,304 < 2^31
+    xq = np.full((33, K), -127, np.int8)
+    xq[::2] = 127
+    wq = np.full((32, K), 127, np.int8)
+    wq[1::4] = -127
+    acc = torch.empty(33, 32, dtype=torch.int32, device="cuda")
+    sq.sq_w8a8_gemm_i32(dev(xq), dev(wq), acc)
+    ref = O.int8_gemm(xq, wq)
+    assert np.abs(ref).max() == K * 127 * 127
+    assert np.array_equal(acc.cpu().numpy(), ref)
