@@ -13,7 +13,8 @@ timed region starts.
 The input groups are independent, so a timed step issues every group as one
 native call (sq_linear_group_run: calibrate, fold, quantize, LoRA shrink,
 GEMM) on one of three streams, largest group first, and the groups' kernels
-overlap.
+overlap. The timed steps are issued back to back, each group staying on its
+own stream.
 
 Output: one JSON line. `value` is GEMM INT8 tera-operations per second of the
 whole step (2*M*N*K summed over the projections, divided by the step time).
@@ -185,7 +186,7 @@ def plan_streams(work, n_streams):
     return plan
 
 
-def run_step_streams(groups, st, gemm_ev=None):
+def run_step_streams(groups, st, gemm_ev=None, join=True):
     """One pass of the whole path over one batch. The input groups are
     independent: each runs calibrate -> fold -> quantize -> LoRA shrink ->
     GEMM as one native call (sq_linear_group_run) on the stream the plan gives
@@ -193,11 +194,17 @@ def run_step_streams(groups, st, gemm_ev=None):
     a GEMM whose tiles leave CUs idle in its last round shares the chip with
     another group's work. gemm_ev: {group: [(start, end), ...]} collects HIP
     events that the library records on the group's stream right around its
-    GEMM, for the groups in gemm_ev["groups"]."""
+    GEMM, for the groups in gemm_ev["groups"].
+
+    join=False leaves out the step's fork from and join into the current
+    stream: back-to-back steps then run as the streams allow. A group always
+    runs on the same stream, so its consecutive steps stay in order and its
+    buffers are never touched by two steps at once; groups share no buffers."""
     torch = st.torch
     cur = torch.cuda.current_stream()
-    for sm in st.main:
-        sm.wait_stream(cur)
+    if join:
+        for sm in st.main:
+            sm.wait_stream(cur)
     for gi, si in st.plan:
         inp, g, X, Xc = groups[gi]
         e0 = e1 = None
@@ -205,8 +212,9 @@ def run_step_streams(groups, st, gemm_ev=None):
             e0, e1 = gemm_ev["pool"].pop()
             gemm_ev.setdefault(inp, []).append((e0, e1))
         g.run(X, Xc, stream=st.main[si], gemm_begin=e0, gemm_end=e1)
-    for sm in st.main:
-        cur.wait_stream(sm)
+    if join:
+        for sm in st.main:
+            cur.wait_stream(sm)
 
 
 def event_pool(torch, n):
@@ -554,7 +562,7 @@ def main():
         del src, dst
     st = Streams(torch, groups)
     for _ in range(args.warmup):
-        run_step_streams(groups, st)
+        run_step_streams(groups, st, join=False)
     torch.cuda.synchronize()
 
     # The dominant kernel: the GEMM instantiation (tile configuration) with the
@@ -569,13 +577,14 @@ def main():
     dom_groups = {inp for inp, _K in wl.inputs
                   if gemm_tile(wl.M, sum(p.N for p in wl.group(inp)), wl.K_of(inp)) == dom}
 
-    # Timed region: exactly `steps` steps, synchronized on both sides. HIP
+    # Timed region: exactly `steps` steps, synchronized on both sides and
+    # issued back to back (no join between steps; see run_step_streams). HIP
     # events on the dominant GEMM's stream time its launches for the roofline.
     gemm_ev = {"pool": event_pool(torch, args.steps * len(dom_groups)), "groups": dom_groups}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        run_step_streams(groups, st, gemm_ev)
+        run_step_streams(groups, st, gemm_ev, join=False)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
