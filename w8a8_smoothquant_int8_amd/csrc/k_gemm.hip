@@ -666,12 +666,13 @@ static double tile_score(int64_t M, int64_t N, int64_t bm, int64_t bn, int64_t r
 
 static int pick_cfg(int64_t M, int64_t N, int64_t K) {
   if (K % kBK != 0 || M * K >= (1LL << 32) || N * K >= (1LL << 32)) return CFG_GENERIC;
-  // Tuning override: SQ_GEMM_TILE=0|1|2 forces a configuration.
-  const char* e = std::getenv("SQ_GEMM_TILE");
-  if (e && *e) {
-    const int o = std::atoi(e);
-    if (o >= 0 && o <= 2) return o;
-  }
+  // Tuning override: SQ_GEMM_TILE=0|1|2 forces a configuration (read once).
+  static const int forced = [] {
+    const char* e = std::getenv("SQ_GEMM_TILE");
+    const int o = (e && *e) ? std::atoi(e) : -1;
+    return (o >= 0 && o <= 2) ? o : -1;
+  }();
+  if (forced >= 0) return forced;
   // 256 CUs: one 256x256 block per CU, two 128x128 blocks per CU.
   const double s256 = tile_score(M, N, 256, 256, 256, 1.0);
   const double s128 = tile_score(M, N, 128, 128, 512, 0.8);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/sq.h"
 
 namespace sq {
@@ -169,22 +171,25 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 }
 
 // Resident blocks of one kernel on the current device (occupancy x CUs),
-// cached per kernel instantiation and device.
+// cached per kernel instantiation and device. The cache entries are atomics:
+// calls from several host threads may fill one at the same time, each with
+// the same value.
 template <typename Tag>
 inline int64_t resident_blocks(const void* f, int T) {
-  static int per_cu[16] = {0};
-  static int cus[16] = {0};
+  static std::atomic<int> per_cu[16];
+  static std::atomic<int> cus[16];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
-  if (per_cu[dev] == 0) {
-    int n = 0, b = 0;
+  int b = per_cu[dev].load(std::memory_order_relaxed);
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (b == 0 || n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, f, T, 0) != hipSuccess || b <= 0) b = 1;
-    cus[dev] = n;
-    per_cu[dev] = b;
+    cus[dev].store(n, std::memory_order_relaxed);
+    per_cu[dev].store(b, std::memory_order_relaxed);
   }
-  return (int64_t)per_cu[dev] * cus[dev];
+  return (int64_t)b * n;
 }
 
 }  // namespace sq
