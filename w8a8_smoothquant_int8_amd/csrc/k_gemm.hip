@@ -69,19 +69,57 @@ __device__ __forceinline__ bool xcd_tile(int tiles_m, int tiles, int& tm, int& t
 
 constexpr int kBK = 128;          // K-tile in bytes
 
-// Epilogue shared by both kernels: acc[i][j] is the 32x32 MFMA tile at rows
-// row0 + 32 i, columns col0 + 32 j. Output register q of a 32x32 tile holds
-// row 8*(q/4) + 4*(lane/32) + q%4 and column lane%32.
+// Epilogue shared by both kernels. The MFMAs take the B rows as their first
+// operand and the A rows as their second, so acc[i][j] holds the 32x32 tile
+// transposed: output register q holds row m = row0 + 32 i + lane % 32 and
+// column n = col0 + 32 j + 8 (q / 4) + 4 (lane / 32) + q % 4. Each lane thus
+// has 4 consecutive columns of one row per register group.
 //
 // With LORA, the rank-r product for the same tile comes from
-// V_MFMA_F32_32X32X16_BF16 (T rows as the first operand, B rows as the
-// second), whose output has that same layout, so it lines up register for
-// register with the INT32 accumulators. When scale is 1 the accumulators are
-// first turned in place into the output-rounded GEMM values, and the bf16
-// MFMAs accumulate T B^T straight onto them: no extra registers, and every
-// fragment of a 32-rank chunk is loaded at once. Other scales keep a separate
-// delta per tile. The MFMAs run in uniform control flow; rows and columns past
-// M and N read clamped (valid) addresses and are never stored.
+// V_MFMA_F32_32X32X16_BF16 with the B rows first and the T rows second, whose
+// output has that same layout, so it lines up register for register with the
+// INT32 accumulators. When scale is 1 the accumulators are first turned in
+// place into the output-rounded GEMM values, and the bf16 MFMAs accumulate
+// T B^T straight onto them. Other scales keep a separate delta per tile. The
+// MFMAs run in uniform control flow; rows and columns past M and N read
+// clamped (valid) addresses and are never stored.
+//
+// 16-bit outputs are rounded two at a time by V_CVT_PK_BF16_F32 /
+// V_CVT_PK_F16_F32 (round to nearest even). One V_PERMLANE32_SWAP per packed
+// register pair then gives every lane 8 consecutive columns, stored as one
+// 16-byte piece: lane l < 32 holds columns 0-7 of a 16-column group, lane
+// l + 32 columns 8-15.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <int OUT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (OUT == OUT_BF16) {
+    const bf16x2 p = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, p);
+  } else {
+    // The empty register barrier keeps the compiler from folding a preceding
+    // fp32 multiply into a mixed-precision FMA that rounds once, straight to
+    // fp16; the path's semantics are an fp32 rounding, then an fp16 one.
+    asm volatile("" : "+v"(a), "+v"(b));
+    const f16x2 p = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, p);
+  }
+}
+
+// Round a pair of fp32 values to the 16-bit output type and back (exact).
+template <int OUT>
+__device__ __forceinline__ void round2(float& a, float& b) {
+  const uint32_t p = pack2<OUT>(a, b);
+  if constexpr (OUT == OUT_BF16) {
+    a = __uint_as_float(p << 16);
+    b = __uint_as_float(p & 0xFFFF0000u);
+  } else {
+    a = f16_bits_to_f32(p & 0xFFFFu);
+    b = f16_bits_to_f32(p >> 16);
+  }
+}
+
 template <int OUT>
 __device__ __forceinline__ float round_out(float y) {
   if constexpr (OUT == OUT_BF16) return bf16_bits_to_f32(f32_to_bf16_bits(y));
@@ -89,13 +127,40 @@ __device__ __forceinline__ float round_out(float y) {
   else return y;
 }
 
+// Store one transposed 32x32 tile of final fp32 values (or INT32 bits for
+// OUT_I32): rows m = m_base + lane % 32, columns n_base + 0..31.
 template <int OUT>
-__device__ __forceinline__ void store_val(void* Y, int64_t ldy, int64_t m, int64_t n, float y) {
-  if constexpr (OUT == OUT_F32) ((float*)Y)[m * ldy + n] = y;
-  else if constexpr (OUT == OUT_BF16) ((unsigned short*)Y)[m * ldy + n] = (unsigned short)f32_to_bf16_bits(y);
-  else ((unsigned short*)Y)[m * ldy + n] = (unsigned short)f32_to_f16_bits(y);
+__device__ __forceinline__ void store_tile(const v16i& v, int64_t m, bool m_ok, int n_base, int N,
+                                           void* __restrict__ Y, int64_t ldy) {
+  const int lane = threadIdx.x & 63;
+  const int lhalf = lane >> 5;
+  if constexpr (OUT == OUT_BF16 || OUT == OUT_F16) {
+    const v16f y = __builtin_bit_cast(v16f, v);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      // groups g = 2p (columns 16p + 4 lhalf + 0..3) and 2p + 1 (16p + 8 + ...)
+      uint32_t lo0 = pack2<OUT>(y[8 * p + 0], y[8 * p + 1]);
+      uint32_t lo1 = pack2<OUT>(y[8 * p + 2], y[8 * p + 3]);
+      uint32_t hi0 = pack2<OUT>(y[8 * p + 4], y[8 * p + 5]);
+      uint32_t hi1 = pack2<OUT>(y[8 * p + 6], y[8 * p + 7]);
+      const auto s0 = __builtin_amdgcn_permlane32_swap(lo0, hi0, false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(lo1, hi1, false, false);
+      const int n = n_base + 16 * p + 8 * lhalf;
+      if (m_ok && n < N)
+        *(uint4*)((unsigned short*)Y + m * ldy + n) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int n = n_base + 8 * g + 4 * lhalf;
+      if (m_ok && n < N)
+        *(v4i*)((int32_t*)Y + m * ldy + n) = v4i{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+    }
+  }
 }
 
+// Non-staged epilogue (the generic kernel, INT32 output, and LoRA with a
+// scale other than 1): scales and LoRA fragments straight from global memory.
 // LORA: 0 none, 1 LoRA delta with scale 1 (accumulated onto y in place),
 // 2 LoRA delta with any scale (separate delta per tile).
 template <int OUT, bool STATIC_A, int LORA, int TM, int TN>
@@ -106,18 +171,30 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], int row0, int col0
   const int lane = threadIdx.x & 63;
   const int lrow = lane & 31, lhalf = lane >> 5;
   const float as_static = (STATIC_A && OUT != OUT_I32) ? a_scale[0] : 0.0f;
-  if constexpr (LORA == 2 || OUT == OUT_I32) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = col0 + j * 32 + lrow;
-      const bool n_ok = n < N;
-      const float ws = (OUT != OUT_I32 && n_ok) ? w_scale[n] : 0.0f;
+  for (int j = 0; j < TN; ++j) {
+    float ws[16];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        v16f d = {};
-        if constexpr (LORA == 2) {
-          const int64_t mr = row0 + i * 32 + lrow < M ? row0 + i * 32 + lrow : M - 1;
-          const int64_t nr = n_ok ? n : N - 1;
+    for (int q = 0; q < 16; ++q) {
+      const int n = col0 + j * 32 + 8 * (q >> 2) + 4 * lhalf + (q & 3);
+      ws[q] = (OUT != OUT_I32 && n < N) ? w_scale[n] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = row0 + i * 32 + lrow;
+      const bool m_ok = m < M;
+      if constexpr (OUT != OUT_I32) {
+        const float as = STATIC_A ? as_static : (m_ok ? a_scale[m] : 0.0f);
+        v16f y;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) y[q] = ((float)acc[i][j][q] * as) * ws[q];   // two roundings, left to right
+        if constexpr (LORA != 0) {
+          const int64_t mr = m_ok ? m : M - 1;
+          const int64_t nr = col0 + j * 32 + lrow < N ? col0 + j * 32 + lrow : N - 1;
+          // scale 1: accumulate onto the rounded GEMM values, as the staged epilogue does
+          v16f d;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) d[q] = LORA == 1 ? round_out<OUT>(y[q]) : 0.0f;
           for (int k0 = 0; k0 < le.r; k0 += 16) {
             const int k = k0 + 8 * lhalf;
             uint4 tu = make_uint4(0, 0, 0, 0), bu = make_uint4(0, 0, 0, 0);
@@ -125,86 +202,15 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], int row0, int col0
               tu = *(const uint4*)(le.T + mr * le.ldt + k);
               bu = *(const uint4*)(le.B + nr * le.r + k);
             }
-            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, tu),
-                                                        __builtin_bit_cast(v8bf, bu), d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, bu),
+                                                        __builtin_bit_cast(v8bf, tu), d, 0, 0, 0);
           }
+#pragma unroll
+          for (int q = 0; q < 16; ++q) y[q] = LORA == 1 ? d[q] : round_out<OUT>(y[q]) + le.scale * d[q];
         }
-        if (n_ok) {
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int m = row0 + i * 32 + 8 * (q >> 2) + 4 * lhalf + (q & 3);
-            if (m < M) {
-              if constexpr (OUT == OUT_I32) {
-                ((int32_t*)Y)[(int64_t)m * ldy + n] = acc[i][j][q];
-              } else {
-                const float as = STATIC_A ? as_static : a_scale[m];
-                float y = ((float)acc[i][j][q] * as) * ws;   // two fp32 roundings, left to right
-                if constexpr (LORA == 2) y = round_out<OUT>(y) + le.scale * d[q];
-                store_val<OUT>(Y, ldy, m, n, y);
-              }
-            }
-          }
-        }
-      }
-    }
-  } else if constexpr (OUT != OUT_I32) {
-    // No LoRA, or LoRA with scale 1: y takes over the accumulators' registers
-    // (the float bits are kept in the same vectors); with LoRA, y += T B^T on
-    // the matrix cores; then all stores.
-    // Row-block outer, so only one row block's 16 a_scale values are live.
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      float as[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = row0 + i * 32 + 8 * (q >> 2) + 4 * lhalf + (q & 3);
-        as[q] = STATIC_A ? as_static : (m < M ? a_scale[m] : 0.0f);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = col0 + j * 32 + lrow;
-        const float ws = n < N ? w_scale[n] : 0.0f;
-        v16f t;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) t[q] = round_out<OUT>(((float)acc[i][j][q] * as[q]) * ws);
-        acc[i][j] = __builtin_bit_cast(v16i, t);
-      }
-    }
-    for (int k0 = 0; LORA == 1 && k0 < le.r; k0 += 16) {
-      const int k = k0 + 8 * lhalf;
-      const bool kin = k < le.r;
-      uint4 tf[TM], bf[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int64_t mr = row0 + i * 32 + lrow < M ? row0 + i * 32 + lrow : M - 1;
-        tf[i] = kin ? *(const uint4*)(le.T + mr * le.ldt + k) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t nr = col0 + j * 32 + lrow < N ? col0 + j * 32 + lrow : N - 1;
-        bf[j] = kin ? *(const uint4*)(le.B + nr * le.r + k) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_bit_cast(
-              v16i, __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, tf[i]),
-                                                            __builtin_bit_cast(v8bf, bf[j]),
-                                                            __builtin_bit_cast(v16f, acc[i][j]),
-                                                            0, 0, 0));
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = col0 + j * 32 + lrow;
-      if (n >= N) continue;
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int m = row0 + i * 32 + 8 * (q >> 2) + 4 * lhalf + (q & 3);
-          if (m < M) store_val<OUT>(Y, ldy, m, n, __builtin_bit_cast(v16f, acc[i][j])[q]);
-        }
+        store_tile<OUT>(__builtin_bit_cast(v16i, y), m, m_ok, col0 + j * 32, N, Y, ldy);
+      } else {
+        store_tile<OUT>(acc[i][j], m, m_ok, col0 + j * 32, N, Y, ldy);
       }
     }
   }
@@ -212,18 +218,13 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], int row0, int col0
 
 // ---------------------------------------------------------------------------
 // LDS-staged epilogue of the main kernel (16-bit or fp32 output; no LoRA, or
-// LoRA with scale 1). The epilogue above is latency-bound when a block runs
-// it alone: one round trip for the scales, one per 16-rank LoRA chunk, and
-// 2-byte output stores scattered over 64-byte row pieces. Here the block's
-// LDS is free once the K loop is done (every wave has consumed its last
-// fragments), so:
-//   1. all waves issue direct global->LDS loads of the block's a_scale and
-//      w_scale slices and of the T and B rows of up to 64 ranks at once;
-//   2. one wait and barrier; the scales and LoRA fragments come from LDS;
-//   3. (more than 64 ranks: the next 64, same way);
-//   4. the rounded outputs go to LDS as a [BM, BN] tile, then every thread
-//      writes 16-byte pieces of whole rows (fp32 outputs are stored from the
-//      registers directly: the fp32 tile would not fit).
+// LoRA with scale 1). Its operands are already in LDS when the K loop ends:
+//   - the block's a_scale and w_scale slices, requested with direct
+//     global->LDS loads at the start of the kernel into a region of their own;
+//   - the T and B rows of the first 64 LoRA ranks, requested at the start of
+//     the last K-tile into the ring stage that tile does not use.
+// The K loop's last wait and barrier cover both. More than 64 ranks: the next
+// 64 go through the same stage, one wait and two barriers per pass.
 // Values and operation order are those of the epilogue above.
 // ---------------------------------------------------------------------------
 constexpr int kStageRanks = 64;
@@ -257,82 +258,78 @@ __device__ __forceinline__ void stage_rows(const char* src, char* dst, int rows,
   }
 }
 
+// LoRA ranks [k_base, k_base + 64) of the block's T rows and B rows into LDS
+// at dst: T [BM][rp] then B [BN][rp] bf16, rp = min(64, r - k_base).
+template <int NW, int BM, int BN>
+__device__ __forceinline__ void stage_lora(const LoraEpi& le, char* dst, int k_base, int m0, int n0,
+                                           int M, int N, int wave, int lane) {
+  const int rp = le.r - k_base < kStageRanks ? le.r - k_base : kStageRanks;
+  const int r16 = rp / 8;
+  stage_rows<NW>((const char*)le.T, dst, BM, r16, wave, lane, [&](int row) -> int64_t {
+    const int64_t m = m0 + row < M ? m0 + row : M - 1;
+    return (m * le.ldt + k_base) * 2;
+  });
+  stage_rows<NW>((const char*)le.B, dst + 2 * BM * rp, BN, r16, wave, lane, [&](int row) -> int64_t {
+    const int64_t n = n0 + row < N ? n0 + row : N - 1;
+    return (n * le.r + k_base) * 2;
+  });
+}
+
 template <int OUT, bool STATIC_A, int LORA, int BM, int BN, int WM, int WN>
-__device__ __forceinline__ void epilogue_staged(v16i (&acc)[BM / WM / 32][BN / WN / 32], char* smem,
-                                                int m0, int n0, int wm, int wn, int M, int N,
-                                                const float* __restrict__ a_scale,
-                                                const float* __restrict__ w_scale,
-                                                void* __restrict__ Y, int64_t ldy,
-                                                const LoraEpi& le) {
+__device__ __forceinline__ void epilogue_staged(v16i (&acc)[BM / WM / 32][BN / WN / 32],
+                                                const char* s_sc, char* s_lora, int m0, int n0,
+                                                int wm, int wn, int M, int N,
+                                                const float* __restrict__ a_scale, void* __restrict__ Y,
+                                                int64_t ldy, const LoraEpi& le) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int row0 = wm * (BM / WM), col0 = wn * (BN / WN);   // wave sub-tile within the block
-  // LDS layout: [a_scale BM][w_scale BN] fp32, then T [BM][<=64] and B [BN][<=64] bf16
-  char* s_as = smem;
-  char* s_ws = s_as + 4 * BM;
-  char* s_t = s_ws + 4 * BN;
-  const int rank_pass = le.r < kStageRanks ? le.r : kStageRanks;
-  char* s_b = s_t + 2 * BM * rank_pass;
-
-  auto stage_lora = [&](int k_base) {
-    const int rp = le.r - k_base < kStageRanks ? le.r - k_base : kStageRanks;
-    const int r16 = rp / 8;
-    stage_rows<NW>((const char*)le.T, s_t, BM, r16, wave, lane, [&](int row) -> int64_t {
-      const int64_t m = m0 + row < M ? m0 + row : M - 1;
-      return (m * le.ldt + k_base) * 2;
-    });
-    stage_rows<NW>((const char*)le.B, s_b, BN, r16, wave, lane, [&](int row) -> int64_t {
-      const int64_t n = n0 + row < N ? n0 + row : N - 1;
-      return (n * le.r + k_base) * 2;
-    });
-    return rp;
-  };
-
-  if constexpr (!STATIC_A)
-    stage_words<NW>(a_scale, s_as, BM, wave, lane, [&](int i) { return m0 + i < M ? m0 + i : M - 1; });
-  stage_words<NW>(w_scale, s_ws, BN, wave, lane, [&](int i) { return n0 + i < N ? n0 + i : N - 1; });
-  int rp = 0;
-  if constexpr (LORA == 1) rp = stage_lora(0);
-  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
+  const char* s_as = s_sc;            // [BM] fp32
+  const char* s_ws = s_sc + 4 * BM;   // [BN] fp32
 
   // y = out((fp32(acc) * a_scale[m]) * w_scale[n]), in place in the accumulators
+  // (rounded to the output type only when the LoRA delta is added after it)
   const float as_static = STATIC_A ? a_scale[0] : 0.0f;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    float as[16];
+  for (int j = 0; j < TN; ++j) {
+    float ws[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      // rows 8 g + 4 lhalf + 0..3 of the 32-row tile: 4 consecutive scales
-      const int r = row0 + i * 32 + 8 * g + 4 * lhalf;
-      if constexpr (STATIC_A) {
-        as[4 * g] = as[4 * g + 1] = as[4 * g + 2] = as[4 * g + 3] = as_static;
-      } else {
-        const float4 v = *(const float4*)(s_as + 4 * r);
-        as[4 * g] = v.x; as[4 * g + 1] = v.y; as[4 * g + 2] = v.z; as[4 * g + 3] = v.w;
-      }
+      const float4 v = *(const float4*)(s_ws + 4 * (col0 + j * 32 + 8 * g + 4 * lhalf));
+      ws[4 * g] = v.x; ws[4 * g + 1] = v.y; ws[4 * g + 2] = v.z; ws[4 * g + 3] = v.w;
     }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const float ws = *(const float*)(s_ws + 4 * (col0 + j * 32 + lrow));
-      v16f t;
+    for (int i = 0; i < TM; ++i) {
+      const float as = STATIC_A ? as_static : *(const float*)(s_as + 4 * (row0 + i * 32 + lrow));
+      float t[16];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) t[q] = round_out<OUT>(((float)acc[i][j][q] * as[q]) * ws);
-      acc[i][j] = __builtin_bit_cast(v16i, t);
+      for (int q = 0; q < 16; ++q) t[q] = ((float)acc[i][j][q] * as) * ws[q];
+      if constexpr (LORA == 1 && OUT != OUT_F32) {
+#pragma unroll
+        for (int q = 0; q < 16; q += 2) round2<OUT>(t[q], t[q + 1]);
+      }
+      v16f tv;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) tv[q] = t[q];
+      acc[i][j] = __builtin_bit_cast(v16i, tv);
     }
   }
 
   if constexpr (LORA == 1) {
     for (int k_base = 0; k_base < le.r; k_base += kStageRanks) {
       if (k_base > 0) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of the last pass are done
         __builtin_amdgcn_s_barrier();         // every wave is done with the previous ranks
-        rp = stage_lora(k_base);
+        stage_lora<NW, BM, BN>(le, s_lora, k_base, m0, n0, M, N, wave, lane);
         __builtin_amdgcn_s_waitcnt(0x0070);
         __builtin_amdgcn_s_barrier();
       }
+      const int rp = le.r - k_base < kStageRanks ? le.r - k_base : kStageRanks;
+      const char* s_t = s_lora;
+      const char* s_b = s_lora + 2 * BM * rp;
       for (int k0 = 0; k0 < rp; k0 += 16) {
         const int k = k0 + 8 * lhalf;          // rank within this pass
         const bool kin = k < rp;
@@ -348,53 +345,19 @@ __device__ __forceinline__ void epilogue_staged(v16i (&acc)[BM / WM / 32][BN / W
 #pragma unroll
           for (int j = 0; j < TN; ++j)
             acc[i][j] = __builtin_bit_cast(
-                v16i, __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, tf[i]),
-                                                              __builtin_bit_cast(v8bf, bf[j]),
+                v16i, __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, bf[j]),
+                                                              __builtin_bit_cast(v8bf, tf[i]),
                                                               __builtin_bit_cast(v16f, acc[i][j]),
                                                               0, 0, 0));
       }
     }
   }
 
-  if constexpr (OUT == OUT_F32) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + col0 + j * 32 + lrow;
-      if (n >= N) continue;
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + row0 + i * 32 + lrow;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int m = m0 + row0 + i * 32 + 8 * (q >> 2) + 4 * lhalf + (q & 3);
-          if (m < M) ((float*)Y)[(int64_t)m * ldy + n] = __builtin_bit_cast(v16f, acc[i][j])[q];
-        }
-    }
-  } else {
-    // [BM, BN] tile of output bits in LDS, then whole-row 16-byte stores
-    __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): this wave's LDS reads are done
-    __builtin_amdgcn_s_barrier();
-    unsigned short* s_y = (unsigned short*)smem;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int r = row0 + i * 32 + 8 * (q >> 2) + 4 * lhalf + (q & 3);
-          const float y = __builtin_bit_cast(v16f, acc[i][j])[q];
-          s_y[r * BN + col0 + j * 32 + lrow] =
-              (unsigned short)(OUT == OUT_BF16 ? f32_to_bf16_bits(y) : f32_to_f16_bits(y));
-        }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
-    constexpr int CPRow = BN / 8;            // 16-byte pieces per tile row
-#pragma unroll 4
-    for (int g = threadIdx.x; g < BM * CPRow; g += NW * 64) {
-      const int r = g / CPRow, c = g - r * CPRow;
-      const int m = m0 + r, n = n0 + 8 * c;
-      if (m < M && n < N)
-        *(uint4*)((unsigned short*)Y + (int64_t)m * ldy + n) = *(const uint4*)(s_y + r * BN + 8 * c);
-    }
+    for (int j = 0; j < TN; ++j) store_tile<OUT>(acc[i][j], m, m < M, n0 + col0 + j * 32, N, Y, ldy);
   }
 }
 
@@ -423,7 +386,11 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
   constexpr int IA = BM / 8 / NW, IB = BN / 8 / NW; // 1 KB direct loads per wave per stage
   constexpr int KS = kBK / 32;                      // MFMA k-steps per K-tile
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must split over waves");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  constexpr bool STAGED = OUT != OUT_I32 && LORA != 2;   // epilogue operands staged in LDS
+  static_assert((BM + BN) * 2 * kStageRanks <= STAGE, "64 LoRA ranks must fit one ring stage");
+  // ring of 2 stages, then the block's a_scale [BM] and w_scale [BN] slices
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + (STAGED ? 4 * (BM + BN) : 0)];
+  char* const s_sc = smem + 2 * STAGE;
 
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles = tiles_m * ((N + BN - 1) / BN);
@@ -494,6 +461,12 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
 
   const int nk = K / kBK;
   issue(0, 0);
+  if constexpr (STAGED) {
+    if constexpr (!STATIC_A)
+      stage_words<NW>(a_scale, s_sc, BM, wave, lane, [&](int i) { return m0 + i < M ? m0 + i : M - 1; });
+    stage_words<NW>(w_scale, s_sc + 4 * BM, BN, wave, lane,
+                    [&](int i) { return n0 + i < N ? n0 + i : N - 1; });
+  }
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
 
@@ -503,6 +476,8 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
     const int stage = kt & 1;
     const char* sa = smem + stage * STAGE;
     if (kt + 1 < nk) issue(kt + 1, stage ^ 1);
+    else if (LORA == 1 && STAGED)   // last K-tile: the first LoRA ranks into the free stage
+      stage_lora<NW, BM, BN>(le, smem + (stage ^ 1) * STAGE, 0, m0, n0, M, N, wave, lane);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int cur = ks & 1;
@@ -516,7 +491,7 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
       if constexpr (SCHED == 1) {
         constexpr int NR = TM + TN;
 #pragma unroll
@@ -534,9 +509,9 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
     }
   }
 
-  if constexpr (OUT != OUT_I32 && LORA != 2)
-    epilogue_staged<OUT, STATIC_A, LORA, BM, BN, WM, WN>(acc, smem, m0, n0, wm, wn, M, N, a_scale,
-                                                          w_scale, Y, ldy, le);
+  if constexpr (STAGED)
+    epilogue_staged<OUT, STATIC_A, LORA, BM, BN, WM, WN>(acc, s_sc, smem + (((nk - 1) & 1) ^ 1) * STAGE,
+                                                          m0, n0, wm, wn, M, N, a_scale, Y, ldy, le);
   else
     epilogue<OUT, STATIC_A, LORA, TM, TN>(acc, m0 + wm * (BM / WM), n0 + wn * (BN / WN), M, N,
                                           a_scale, w_scale, Y, ldy, le);
@@ -633,7 +608,7 @@ k_gemm_generic(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < nk) sstore(buf ^ 1);
     __syncthreads();
