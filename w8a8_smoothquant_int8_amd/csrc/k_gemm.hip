@@ -22,6 +22,7 @@
 // registers, zero-filling the K tail.
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "sq_internal.h"
 
@@ -365,18 +366,31 @@ __device__ __forceinline__ void epilogue_staged(v16i (&acc)[BM / WM / 32][BN / W
 // Main kernel, K % 128 == 0. WM x WN waves; each wave owns a (BM/WM) x (BN/WN)
 // sub-tile of 32x32 MFMA tiles. The MFMA operand fragments are double-buffered
 // in registers: the LDS reads for k-step s+1 are in flight while the MFMAs of
-// k-step s run.
-//   SCHED 1: scheduling hints interleave one LDS read after each MFMA, and the
-//            barrier closes each K-tile.
-//   SCHED 4: the barrier sits before the last k-step's MFMAs, which then cover
-//            the first fragment reads of the next K-tile.
-// The barrier carries no memory fence (a fence would also wait for the direct
-// loads just issued for the tile after next): each wave waits for its own
-// direct loads of the next tile (vmcnt) and its reads of this tile (lgkmcnt),
+// k-step s run (scheduling hints put one read after each MFMA). Two K-tiles
+// of direct loads are in flight, and each K-tile has one sync point, in its
+// last k-step: wait, barrier, then the loads of the K-tile after next and the
+// reads of the next K-tile's first fragments, interleaved with that k-step's
+// MFMAs. The barrier carries no memory fence (a fence would also wait for
+// direct loads still meant to be in flight): each wave waits for its own
+// direct loads of the next K-tile (vmcnt) and its reads of this one (lgkmcnt),
 // then all waves meet.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int OUT, bool STATIC_A, int SCHED, int LORA>
-__global__ void __launch_bounds__(WM * WN * 64)
+// Scheduling-group pattern for one k-step of NMF MFMAs: each MFMA is followed
+// by one LDS read while the NR reads last, and the NV direct loads are spread
+// over the MFMAs.
+template <int U, int NMF, int NR, int NV>
+__device__ __forceinline__ void sched_slots() {
+  if constexpr (U < NMF) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // one MFMA
+    if constexpr (U < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // one LDS read
+    constexpr int c = ((U + 1) * NV) / NMF - (U * NV) / NMF;
+    if constexpr (c > 0) __builtin_amdgcn_sched_group_barrier(0x060, c, 0);  // direct loads
+    sched_slots<U + 1, NMF, NR, NV>();
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int OUT, bool STATIC_A, int LORA>
+__global__ void __launch_bounds__(WM * WN * 64, 2)   // 2 waves per SIMD: 8-wave blocks, or 2 blocks of 4
 k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
             const float* __restrict__ a_scale, const float* __restrict__ w_scale, int M, int N,
             int K, void* __restrict__ Y, int64_t ldy, LoraEpi le) {
@@ -458,56 +472,75 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v16i{};
+  v4i fa[2][TM], fb[2][TN];   // operand fragments, double-buffered over k-steps
 
   const int nk = K / kBK;
-  issue(0, 0);
-  if constexpr (STAGED) {
-    if constexpr (!STATIC_A)
-      stage_words<NW>(a_scale, s_sc, BM, wave, lane, [&](int i) { return m0 + i < M ? m0 + i : M - 1; });
-    stage_words<NW>(w_scale, s_sc + 4 * BM, BN, wave, lane,
-                    [&](int i) { return n0 + i < N ? n0 + i : N - 1; });
-  }
-  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
+  constexpr int NL = IA + IB;                       // direct loads per wave per K-tile
+  static_assert(NL < 16, "vmcnt immediate below");
+  auto mfmas = [&](int cur) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+  };
+  auto stage_scales = [&]() {
+    if constexpr (STAGED) {
+      if constexpr (!STATIC_A)
+        stage_words<NW>(a_scale, s_sc, BM, wave, lane, [&](int i) { return m0 + i < M ? m0 + i : M - 1; });
+      stage_words<NW>(w_scale, s_sc + 4 * BM, BN, wave, lane,
+                      [&](int i) { return n0 + i < N ? n0 + i : N - 1; });
+    }
+  };
 
-  v4i fa[2][TM], fb[2][TN];
+  // Two K-tiles in flight. One sync point per K-tile, in its last k-step:
+  // wait for this wave's loads of the next K-tile and its reads of this
+  // one, barrier; then, interleaved with that k-step's MFMAs (whose
+  // fragments are already in registers), the reads of the next K-tile's
+  // first fragments and the loads of the K-tile after next into the stage
+  // just released. Scheduling barriers keep every MFMA on its side of the
+  // sync point.
+  stage_scales();
+  issue(0, 0);
+  if (nk > 1) {
+    issue(1, 1);
+    __builtin_amdgcn_s_waitcnt(0x0070 | NL);   // vmcnt(NL) lgkmcnt(0): K-tile 0 and the scales
+  } else {
+    if constexpr (LORA == 1 && STAGED) stage_lora<NW, BM, BN>(le, smem + STAGE, 0, m0, n0, M, N, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0x0070);
+  }
+  __builtin_amdgcn_s_barrier();
   load_frags(smem, 0, fa[0], fb[0]);
-  for (int kt = 0; kt < nk; ++kt) {
+
+  // MODE 0: K-tiles kt + 1 and kt + 2 exist; 1: only kt + 1 (the free stage
+  // takes the first LoRA ranks); 2: last K-tile.
+  auto ktile = [&](int kt, auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
     const int stage = kt & 1;
     const char* sa = smem + stage * STAGE;
-    if (kt + 1 < nk) issue(kt + 1, stage ^ 1);
-    else if (LORA == 1 && STAGED)   // last K-tile: the first LoRA ranks into the free stage
-      stage_lora<NW, BM, BN>(le, smem + (stage ^ 1) * STAGE, 0, m0, n0, M, N, wave, lane);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < KS) load_frags(sa, ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
-      if (SCHED == 4 && ks + 1 == KS) {
-        __builtin_amdgcn_s_waitcnt(0x0070);
-        __builtin_amdgcn_s_barrier();
-        if (kt + 1 < nk) load_frags(smem + (stage ^ 1) * STAGE, 0, fa[cur ^ 1], fb[cur ^ 1]);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
-      if constexpr (SCHED == 1) {
-        constexpr int NR = TM + TN;
-#pragma unroll
-        for (int u = 0; u < NR; ++u) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - NR, 0);
-      }
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      load_frags(sa, ks + 1, fa[(ks & 1) ^ 1], fb[(ks & 1) ^ 1]);
+      mfmas(ks & 1);
+      sched_slots<0, TM * TN, TM + TN, 0>();
     }
-    if constexpr (SCHED != 4) {
-      __builtin_amdgcn_s_waitcnt(0x0070);
-      __builtin_amdgcn_s_barrier();
-      if (kt + 1 < nk) load_frags(smem + (stage ^ 1) * STAGE, 0, fa[0], fb[0]);
-    }
-  }
+    constexpr int cur = (KS - 1) & 1;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0070);        // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MODE == 0) issue(kt + 2, stage);
+    if constexpr (MODE == 1 && LORA == 1 && STAGED)
+      stage_lora<NW, BM, BN>(le, smem + stage * STAGE, 0, m0, n0, M, N, wave, lane);
+    if constexpr (MODE != 2) load_frags(smem + (stage ^ 1) * STAGE, 0, fa[cur ^ 1], fb[cur ^ 1]);
+    mfmas(cur);
+    if constexpr (MODE == 0) sched_slots<0, TM * TN, TM + TN, NL>();
+    else if constexpr (MODE == 1) sched_slots<0, TM * TN, TM + TN, 0>();
+  };
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) ktile(kt, std::integral_constant<int, 0>{});
+  if (kt + 1 < nk) ktile(kt++, std::integral_constant<int, 1>{});
+  ktile(kt, std::integral_constant<int, 2>{});
 
   if constexpr (STAGED)
     epilogue_staged<OUT, STATIC_A, LORA, BM, BN, WM, WN>(acc, s_sc, smem + (((nk - 1) & 1) ^ 1) * STAGE,
@@ -622,11 +655,14 @@ k_gemm_generic(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
 // Host side: pick a kernel and tile for the shape.
 // ---------------------------------------------------------------------------
 // Tile configurations (measured on MI355X over the workload shapes):
-//   CFG_256: 256x256 tiles, 8 waves of 128x64, SCHED 1 - the faster one at
-//            full occupancy (256x256 tiles read the least L2 data per op);
-//   CFG_128: 128x128 tiles, 4 waves of 64x64, SCHED 4 - wins when 256x256
-//            tiles would leave CUs idle in the last round or pad small M.
-enum TileCfg { CFG_GENERIC = 0, CFG_256 = 1, CFG_128 = 2 };
+//   CFG_256:     256x256 tiles, 8 waves of 128x64 - the fastest at full
+//                occupancy (it reads the least L2 data per op);
+//   CFG_256x192: 256x192 tiles, 8 waves of 64x96 - fills the chip where
+//                256x256 tiles would leave CUs idle (M = 2048, N = 6144:
+//                256 tiles instead of 192);
+//   CFG_128:     128x128 tiles, 4 waves of 64x64, two blocks per CU - wins
+//                for narrow outputs (N = 4096) and small M.
+enum TileCfg { CFG_GENERIC = 0, CFG_256 = 1, CFG_128 = 2, CFG_256x192 = 3 };
 
 // Score of a tile configuration: the share of the launched tile work that is
 // useful (rows and columns padded up to whole tiles, and the last round of
@@ -641,26 +677,33 @@ static double tile_score(int64_t M, int64_t N, int64_t bm, int64_t bn, int64_t r
 
 static int pick_cfg(int64_t M, int64_t N, int64_t K) {
   if (K % kBK != 0 || M * K >= (1LL << 32) || N * K >= (1LL << 32)) return CFG_GENERIC;
-  // Tuning override: SQ_GEMM_TILE=0|1|2 forces a configuration (read once).
+  // Tuning override: SQ_GEMM_TILE=0|1|2|3 forces a configuration (read once per process).
   static const int forced = [] {
     const char* e = std::getenv("SQ_GEMM_TILE");
     const int o = (e && *e) ? std::atoi(e) : -1;
-    return (o >= 0 && o <= 2) ? o : -1;
+    return (o >= 0 && o <= 3) ? o : -1;
   }();
   if (forced >= 0) return forced;
-  // 256 CUs: one 256x256 block per CU, two 128x128 blocks per CU.
+  // 256 CUs: one 256x256 or 256x192 block per CU, two 128x128 blocks per CU.
+  // Rates relative to 256x256 at full occupancy, measured on MI355X: 256x192
+  // 0.94 (2048x24576x4096, whole rounds for both), taken as 0.93 so that
+  // near-ties go to 256x256, which fetches less from the memory fabric per op
+  // (the chip runs these GEMMs at its power limit; on the Llama-3-8B step,
+  // gate+up on 256x256 beat 256x192 by 3% with equal times alone); 128x128 0.8.
   const double s256 = tile_score(M, N, 256, 256, 256, 1.0);
+  const double s192 = tile_score(M, N, 256, 192, 256, 0.93);
   const double s128 = tile_score(M, N, 128, 128, 512, 0.8);
-  return s256 >= s128 ? CFG_256 : CFG_128;
+  if (s256 >= s192 && s256 >= s128) return CFG_256;
+  return s192 >= s128 ? CFG_256x192 : CFG_128;
 }
 
-template <int BM, int BN, int WM, int WN, int OUT, bool STATIC_A, int SCHED, int LORA>
+template <int BM, int BN, int WM, int WN, int OUT, bool STATIC_A, int LORA>
 static int launch_pipe(const int8_t* Xq, const int8_t* Wq, const float* a_scale, const float* w_scale,
                        int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy, const LoraEpi& le,
                        hipStream_t st) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int64_t blocks = (tiles + 7) / 8 * 8;
-  k_gemm_pipe<BM, BN, WM, WN, OUT, STATIC_A, SCHED, LORA><<<(unsigned)blocks, WM * WN * 64, 0, st>>>(
+  k_gemm_pipe<BM, BN, WM, WN, OUT, STATIC_A, LORA><<<(unsigned)blocks, WM * WN * 64, 0, st>>>(
       Xq, Wq, a_scale, w_scale, (int)M, (int)N, (int)K, Y, ldy, le);
   SQ_LAUNCH_CHECK();
   return SQ_OK;
@@ -672,10 +715,13 @@ static int launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* a_scal
                          int64_t ldy, const LoraEpi& le, hipStream_t st) {
   switch (pick_cfg(M, N, K)) {
     case CFG_256:
-      return launch_pipe<256, 256, 2, 4, OUT, STATIC_A, 1, LORA>(Xq, Wq, a_scale, w_scale, M, N, K, Y,
+      return launch_pipe<256, 256, 2, 4, OUT, STATIC_A, LORA>(Xq, Wq, a_scale, w_scale, M, N, K, Y,
                                                                  ldy, le, st);
+    case CFG_256x192:
+      return launch_pipe<256, 192, 4, 2, OUT, STATIC_A, LORA>(Xq, Wq, a_scale, w_scale, M, N, K, Y,
+                                                                  ldy, le, st);
     case CFG_128:
-      return launch_pipe<128, 128, 2, 2, OUT, STATIC_A, 4, LORA>(Xq, Wq, a_scale, w_scale, M, N, K, Y,
+      return launch_pipe<128, 128, 2, 2, OUT, STATIC_A, LORA>(Xq, Wq, a_scale, w_scale, M, N, K, Y,
                                                                  ldy, le, st);
     default:
       break;
