@@ -13,6 +13,7 @@ import sys
 import numpy as np
 import pytest
 
+from div_cases import near_midpoint_pairs  # noqa: E402
 import w8a8_smoothquant_int8_amd as sq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -218,10 +219,36 @@ def test_fp64_reciprocal_division_identity():
     d2 = np.exp(rng.uniform(-12, 2, n)).astype(F)
     x2 = (k * d2.astype(np.float64)).astype(F)
     x2 = np.nextafter(x2, np.where(rng.random(n) < 0.5, -np.inf, np.inf).astype(F))
-    for a, b in ((x, d), (x2, d2)):
+    # the hardest quotients: within about 2^-48 of an fp32 rounding midpoint
+    x3, d3, _r = near_midpoint_pairs(20000, 1)
+    q = x3.astype(np.float64) / d3.astype(np.float64)
+    mid = np.abs(q) * 2.0 ** 25
+    mid = mid / 2.0 ** np.floor(np.log2(mid) - 24)          # odd multiples of 2^-25 -> odd integers
+    assert np.all(np.abs(mid - np.round(mid)) < 2.0 ** -20)  # the construction lands next to a midpoint
+    for a, b in ((x, d), (x2, d2), (x3, d3)):
         ref = a / b
         got = (a.astype(np.float64) * (1.0 / b.astype(np.float64))).astype(F)
         assert np.array_equal(got, ref)
+    # the near-midpoint cases tell a plain fp32 reciprocal multiply from a division
+    approx = x3 * (F(1.0) / d3)
+    assert np.mean(approx != x3 / d3) > 0.2
+
+
+def test_code_word_rounding():
+    """The quantizers' one-add code: clamp to [-127, 127], add 1.5 * 2^23 in
+    fp32 (round half to even), take the low byte as int8. Emulated with numpy
+    fp32 arithmetic against clamp(rint(q)) on every half-integer and its fp32
+    neighbours in [-140, 140], and on random quotients."""
+    F = np.float32
+    h = np.arange(-280, 281, dtype=np.float64) / 2.0
+    q = np.concatenate([h, np.nextafter(h.astype(F), F(-np.inf)).astype(np.float64),
+                        np.nextafter(h.astype(F), F(np.inf)).astype(np.float64),
+                        np.random.default_rng(3).uniform(-200, 200, 200000)]).astype(F)
+    t = np.minimum(np.maximum(q, F(-127.0)), F(127.0))
+    word = (t + F(12582912.0)).view(np.uint32)
+    got = (word & 0xFF).astype(np.uint8).view(np.int8)
+    ref = np.clip(np.rint(q), -127, 127).astype(np.int8)
+    assert np.array_equal(got, ref)
 
 
 def _group(**over):

@@ -187,6 +187,34 @@ def test_quant_division_vectors_and_ties():
                                                  [127, -32, 127, 64], [-127, 32, -16, 95]]
 
 
+@pytest.mark.parametrize("K,per_row", [(256, 1), (4096, 3), (14336, 2), (20480, 1)])
+def test_quant_smoothing_division_near_midpoints(K, per_row):
+    """x / s on quotients within about 2^-48 of an fp32 rounding midpoint (the
+    cases an approximate division rounds the wrong way first). Each row holds
+    per_row such quotients, the largest one alone setting the row max, so the
+    row's a_scale = fp32(fp32(x / s) / 127) exposes any error in fp32(x / s);
+    a_scale and the codes must be bit-exact. K spans the wave-per-row and the
+    block-per-row quantizers."""
+    from div_cases import near_midpoint_pairs
+    M = min(1024, K // per_row)              # every pair gets a channel of its own
+    xs, ds, _r = near_midpoint_pairs(M * per_row, K + per_row, exp_range=0)   # x / s in [0.5, 1)
+    s = np.exp(np.random.default_rng(K).uniform(-1, 1, K)).astype(F32)
+    x = np.zeros((M, K), F32)
+    cols = np.random.default_rng(K + 7).permutation(K)[:M * per_row].reshape(M, per_row)
+    for i in range(M):
+        for t in range(per_row):
+            c = cols[i, t]
+            s[c] = ds[i * per_row + t]
+            # 4^-t keeps the first pair the row max (quotients below 0.25 for t >= 1)
+            x[i, c] = np.ldexp(xs[i * per_row + t], -2 * t)
+    Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+    a = torch.empty(M, dtype=torch.float32, device="cuda")
+    sq.sq_quant_per_token(dev(x), dev(s), Xq, a)
+    rq, ra = O.quantize_per_token(x, s)
+    assert bits_equal(npf(a), ra)
+    assert bits_equal(Xq.cpu().numpy(), rq)
+
+
 # ---------------------------------------------------------------------------
 # INT8 GEMM
 # ---------------------------------------------------------------------------

@@ -114,7 +114,7 @@ k_norm_quant(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
   double r_static = 0.0;
   if constexpr (STATIC) {
     a_static = scale_io[0];
-    r_static = a_static != 0.0f ? 1.0 / (double)a_static : 0.0;
+    r_static = a_static != 0.0f ? rcp_rn64(a_static) : 0.0;
   }
 
   for (int64_t it = 0; it < iters; ++it, m += row_step) {
@@ -204,7 +204,7 @@ k_norm_quant(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
         for (int w = 1; w < WPR; ++w) amax = __builtin_fmaxf(amax, red_max[par][WPR * slot + w]);
       }
       scale = amax / 127.0f;                                     // IEEE fp32 division
-      rscale = scale != 0.0f ? 1.0 / (double)scale : 0.0;
+      rscale = scale != 0.0f ? rcp_rn64(scale) : 0.0;
       if (active && half == 0 && lane == 0) scale_io[m] = scale;
     }
     if (!active) continue;
@@ -217,12 +217,12 @@ k_norm_quant(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = c0 + 64 * j;
-      int q[8];
+      uint32_t q[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = quant_code(div_rn(v[j][e], rscale));
+      for (int e = 0; e < 8; ++e) q[e] = code_word(div_rn(v[j][e], rscale));
       uint2 pk;
-      pk.x = pack4_i8(q[0], q[1], q[2], q[3]) & keep;
-      pk.y = pack4_i8(q[4], q[5], q[6], q[7]) & keep;
+      pk.x = pack4_codes(q[0], q[1], q[2], q[3]) & keep;
+      pk.y = pack4_codes(q[4], q[5], q[6], q[7]) & keep;
       if (c < nch) *(uint2*)(orow + c * 8) = pk;
     }
   }

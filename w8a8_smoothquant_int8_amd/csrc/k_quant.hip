@@ -13,9 +13,10 @@
 // block's next rows are loaded into them while this row group is reduced
 // (wave max, then LDS across waves: one barrier per group) and quantized from
 // v (at 8 chunks per thread v is recomputed instead, for registers, and the
-// next rows load after the group). The per-channel factors (fp32 s for FOLD, the fp64 reciprocals 1/s that
-// make the divisions exact for the others, see div_rn) are computed once per
-// block, after its first loads are issued, and reused for all its rows.
+// next rows load after the group). The per-channel factors (fp32 s for FOLD,
+// the fp64 reciprocals 1/s that make the divisions exact for the others, see
+// div_rn and rcp_rn64) are computed once per block, after its first loads are
+// issued, and reused for all its rows.
 #include "sq_internal.h"
 
 namespace sq {
@@ -88,7 +89,7 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
     for (int e = 0; e < 8; ++e) {
       const float sv = (s != nullptr && c * 8 < K) ? s[c * 8 + e] : 1.0f;
       if constexpr (KIND == Q_FOLD) sm[j][e] = sv;
-      else rs[j][e] = 1.0 / (double)sv;      // RN64(1/s), IEEE fp64 division
+      else rs[j][e] = rcp_rn64(sv);           // RN64(1/s)
     }
   }
 
@@ -98,7 +99,7 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
   double r_static = 0.0;
   if constexpr (kStaticKind<KIND>) {
     a_static = scale_io[0];
-    r_static = a_static != 0.0f ? 1.0 / (double)a_static : 0.0;
+    r_static = a_static != 0.0f ? rcp_rn64(a_static) : 0.0;
   }
 
   __shared__ float red[2][RPB][kQuantMaxThreads / 64];
@@ -152,7 +153,7 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
         float a = red[parity][r][0];
         for (int w = 1; w < nwaves; ++w) a = __builtin_fmaxf(a, red[parity][r][w]);
         scale[r] = a / 127.0f;                                   // IEEE fp32 division
-        rscale[r] = scale[r] != 0.0f ? 1.0 / (double)scale[r] : 0.0;
+        rscale[r] = scale[r] != 0.0f ? rcp_rn64(scale[r]) : 0.0;
         if (tid == 0 && m0 + r < rows) scale_io[m0 + r] = scale[r];
       }
       parity ^= 1;
@@ -182,12 +183,14 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[e] = smooth(y[e], j, e);
           }
-          int q[8];
+          // scale == 0 (all-zero row, or a zero static scale): every code is 0
+          const uint32_t keep = scale[r] != 0.0f ? 0xFFFFFFFFu : 0u;
+          uint32_t q[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) q[e] = scale[r] != 0.0f ? quant_code(div_rn(y[e], rscale[r])) : 0;
+          for (int e = 0; e < 8; ++e) q[e] = code_word(div_rn(y[e], rscale[r]));
           uint2 pk;
-          pk.x = pack4_i8(q[0], q[1], q[2], q[3]);
-          pk.y = pack4_i8(q[4], q[5], q[6], q[7]);
+          pk.x = pack4_codes(q[0], q[1], q[2], q[3]) & keep;
+          pk.y = pack4_codes(q[4], q[5], q[6], q[7]) & keep;
           *(uint2*)(orow + c * 8) = pk;
         }
       }
@@ -297,8 +300,8 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const double r0 = 1.0 / (double)sv[2 * q];       // RN64(1/s), IEEE fp64 division
-        const double r1 = 1.0 / (double)sv[2 * q + 1];
+        const double r0 = rcp_rn64(sv[2 * q]);            // RN64(1/s)
+        const double r1 = rcp_rn64(sv[2 * q + 1]);
         const unsigned long long b0 = __double_as_longlong(r0), b1 = __double_as_longlong(r1);
         tab[q * kSpan * WPR + c] = make_uint4((uint32_t)b0, (uint32_t)(b0 >> 32), (uint32_t)b1,
                                               (uint32_t)(b1 >> 32));
@@ -339,7 +342,7 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
   double r_static = 0.0;
   if constexpr (kStaticKind<KIND>) {
     a_static = scale_io[0];
-    r_static = a_static != 0.0f ? 1.0 / (double)a_static : 0.0;
+    r_static = a_static != 0.0f ? rcp_rn64(a_static) : 0.0;
   }
 
   for (int64_t it = 0; it < iters; ++it, m += row_step) {
@@ -356,12 +359,15 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
         float x[8];
         widen8<DT>(raw[j], x);
         smooth8(j, x, dep);
+        // the chunk's max, masked once per chunk (chunks past the row end hold a re-read)
         const bool in_row = c0 + 64 * j < nch;
+        float cm = __builtin_fabsf(x[0]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           v[j][e] = x[e];
-          amax = __builtin_fmaxf(amax, in_row ? __builtin_fabsf(x[e]) : 0.0f);
+          cm = __builtin_fmaxf(cm, __builtin_fabsf(x[e]));
         }
+        amax = __builtin_fmaxf(amax, in_row ? cm : 0.0f);
       }
       // The next row's loads reuse the raw registers: they must not be
       // issued before pass 1 is done with them (an opaque zero that depends
@@ -390,7 +396,7 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
         for (int w = 1; w < WPR; ++w) amax = __builtin_fmaxf(amax, r[WPR * slot + w]);
       }
       scale = amax / 127.0f;                                     // IEEE fp32 division
-      rscale = scale != 0.0f ? 1.0 / (double)scale : 0.0;
+      rscale = scale != 0.0f ? rcp_rn64(scale) : 0.0;
       if (active && half == 0 && lane == 0) scale_io[m] = scale;
     }
     if (!active) continue;
@@ -405,12 +411,12 @@ k_quant_wave(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = c0 + 64 * j;
-      int q[8];
+      uint32_t q[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = quant_code(div_rn(v[j][e], rscale));
+      for (int e = 0; e < 8; ++e) q[e] = code_word(div_rn(v[j][e], rscale));
       uint2 pk;
-      pk.x = pack4_i8(q[0], q[1], q[2], q[3]) & keep;
-      pk.y = pack4_i8(q[4], q[5], q[6], q[7]) & keep;
+      pk.x = pack4_codes(q[0], q[1], q[2], q[3]) & keep;
+      pk.y = pack4_codes(q[4], q[5], q[6], q[7]) & keep;
       if (c < nch) *(uint2*)(orow + c * 8) = pk;
     }
     // the rare count, in a loop of its own; chunks past the row end hold a

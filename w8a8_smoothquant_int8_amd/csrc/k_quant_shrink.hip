@@ -67,7 +67,7 @@ k_quant_shrink(const char* __restrict__ X, int64_t ldx_bytes, int M, int K,
   for (int j = 0; j < CPL; ++j)
     xr[j] = kof(j) < K ? *(const uint4*)(xrow + (int64_t)kof(j) * 2) : make_uint4(0, 0, 0, 0);
 
-  for (int k = tid; k < K; k += W * 64) rtab[k] = s != nullptr ? 1.0 / (double)s[k] : 1.0;
+  for (int k = tid; k < K; k += W * 64) rtab[k] = s != nullptr ? rcp_rn64(s[k]) : 1.0;
 
   // The shrink. Register e of rank tile t: rank 16 t + 4 kg + e, row lrow.
   v4f acc[NT];
@@ -141,7 +141,7 @@ k_quant_shrink(const char* __restrict__ X, int64_t ldx_bytes, int M, int K,
     if (wave == 0 && kg == 0 && row_ok) scale_io[m0 + lrow] = scale;
   }
   if (!row_ok) return;
-  const double rscale = scale != 0.0f ? 1.0 / (double)scale : 0.0;
+  const double rscale = scale != 0.0f ? rcp_rn64(scale) : 0.0;
   const uint32_t keep = scale != 0.0f ? 0xFFFFFFFFu : 0u;
   int8_t* orow = Xq + (int64_t)(m0 + lrow) * K;
   // pass 2: the codes
@@ -158,12 +158,12 @@ k_quant_shrink(const char* __restrict__ X, int64_t ldx_bytes, int M, int K,
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = div_rn(y[e], rtab[k + e]);
       }
-      int q[8];
+      uint32_t q[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = quant_code(div_rn(y[e], rscale));
+      for (int e = 0; e < 8; ++e) q[e] = code_word(div_rn(y[e], rscale));
       uint2 pk;
-      pk.x = pack4_i8(q[0], q[1], q[2], q[3]) & keep;
-      pk.y = pack4_i8(q[4], q[5], q[6], q[7]) & keep;
+      pk.x = pack4_codes(q[0], q[1], q[2], q[3]) & keep;
+      pk.y = pack4_codes(q[4], q[5], q[6], q[7]) & keep;
       *(uint2*)(orow + k) = pk;
     }
   }
