@@ -182,6 +182,155 @@ k_lora_shrink(const char* __restrict__ X, int64_t ldx_bytes, int M, int K,
   }
 }
 
+// 8 values of a 16-bit X as bf16 bits (RNE from fp16; identity for bf16).
+template <int XT>
+__device__ __forceinline__ uint4 raw16_as_bf16(uint4 raw) {
+  if constexpr (XT == SQ_BF16) {
+    return raw;
+  } else {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = f32_to_bf16_bits(f16_bits_to_f32(w[q] & 0xFFFFu)) |
+             (f32_to_bf16_bits(f16_bits_to_f32(w[q] >> 16)) << 16);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// Pipelined single-adapter shrink for 16-bit X: the same partial sums P[s] as
+// k_lora_shrink, with one chunk of loads always in flight. Per chunk:
+//   wait for this wave's loads of the chunk (vmcnt(0): they are the only
+//   ones outstanding), barrier (the chunk's staged A is complete for every
+//   wave, and every wave is done with the chunk before);
+//   stage the next chunk's A into the other slot of a two-slot LDS ring and
+//   load this wave's X for it into the other register set;
+//   multiply the current chunk.
+// A slot holds NT * 16 staged rows (rows past R re-read row R - 1; their
+// products land in ranks that are never stored), swizzled as in
+// k_lora_shrink. Every load is unconditional, with addresses past K clamped
+// to valid ones and the X values zeroed on use, so each wave issues the same
+// loads per chunk. grid: (ceil(M / (64 * RT)), S); block: 4 waves of RT row
+// tiles of 16 rows.
+template <int XT, int KS, int RT, int NT>
+__global__ void __launch_bounds__(kLoraThreads)
+k_lora_shrink_pipe(const char* __restrict__ X, int64_t ldx_bytes, int M, int K,
+                   const unsigned short* __restrict__ A, int R, int S, float* __restrict__ P) {
+  extern __shared__ __attribute__((aligned(1024))) char lds_a[];   // 2 x (NT*16) x KC bf16
+  constexpr int KC = 32 * KS;        // k elements per chunk
+  constexpr int CPR = KC / 8;        // 16-byte slots per staged row
+  constexpr int RPI = 64 / CPR;      // staged rows per direct load
+  constexpr int ROWS = NT * 16;      // staged rows per slot
+  constexpr int NA = ROWS / RPI / 4; // direct loads per wave per chunk
+  constexpr int SLOT = ROWS * KC * 2;
+  static_assert(ROWS % (RPI * 4) == 0, "staged rows must split over the 4 waves");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lrow = lane & 15, kg = lane >> 4;
+  const int nchunks = (K + KC - 1) / KC;
+  const int m0 = blockIdx.x * (64 * RT) + wave * (16 * RT);
+
+  // Rows past M read row M - 1; their sums are never stored.
+  const char* xrow[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    int m = m0 + rt * 16 + lrow;
+    m = m < M ? m : M - 1;
+    xrow[rt] = X + (int64_t)m * ldx_bytes;
+  }
+
+  auto stage = [&](int c, int slot) {
+    const int kc0 = c * KC;
+    char* dst = lds_a + slot * SLOT;
+#pragma unroll
+    for (int q = 0; q < NA; ++q) {
+      const int j = wave + 4 * q;
+      const int i = j * RPI + lane / CPR;
+      const int isrc = i < R ? i : R - 1;
+      const int kk = kc0 + ((lane % CPR) ^ (i & 15)) * 8;
+      const int ksrc = kk < K ? kk : K - 8;
+      __builtin_amdgcn_global_load_lds((const void*)(A + (int64_t)isrc * K + ksrc),
+                                       (lds_ptr_t)(dst + 1024 * j), 16, 0, 0);
+    }
+  };
+  auto load_x = [&](int c, uint4 (&xu)[RT][KS]) {
+#pragma unroll
+    for (int u = 0; u < KS; ++u) {
+      const int kk = c * KC + u * 32 + kg * 8;
+      const int ksrc = kk < K ? kk : K - 8;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) xu[rt][u] = *(const uint4*)(xrow[rt] + (int64_t)ksrc * 2);
+    }
+  };
+
+  v4f acc[RT][NT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[rt][t] = v4f{0, 0, 0, 0};
+
+  auto multiply = [&](int c, int slot, const uint4 (&xu)[RT][KS]) {
+    const int kc0 = c * KC;
+    const char* sa = lds_a + slot * SLOT;
+#pragma unroll
+    for (int u = 0; u < KS; ++u) {
+      const int sl = u * 4 + kg;
+      const bool kin = kc0 + sl * 8 < K;
+      uint4 xv[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) xv[rt] = kin ? raw16_as_bf16<XT>(xu[rt][u]) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int i = t * 16 + lrow;
+        const uint4 au = *(const uint4*)(sa + i * (KC * 2) + ((sl ^ (i & 15)) << 4));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_v8bf(au), bits_to_v8bf(xv[rt]),
+                                                              acc[rt][t], 0, 0, 0);
+      }
+    }
+  };
+
+  // one chunk: the current loads in `cur`, slot `slot`; the next chunk's into `nxt`
+  auto step = [&](int c, int slot, const uint4 (&cur)[RT][KS], uint4 (&nxt)[RT][KS]) {
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    __syncthreads();
+    if (c + S < nchunks) {
+      stage(c + S, slot ^ 1);
+      load_x(c + S, nxt);
+    }
+    multiply(c, slot, cur);
+  };
+
+  uint4 xa[RT][KS], xb[RT][KS];
+  int c = blockIdx.y;
+  if (c < nchunks) {
+    stage(c, 0);
+    load_x(c, xa);
+  }
+#pragma unroll 1
+  for (; c < nchunks; c += 2 * S) {
+    step(c, 0, xa, xb);
+    if (c + S >= nchunks) break;
+    step(c + S, 1, xb, xa);
+  }
+
+  // Register j of rank tile t: rank 16 t + 4 (lane / 16) + j, row lane % 16.
+  float* Ps = P + (int64_t)blockIdx.y * M * R;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int m = m0 + rt * 16 + lrow;
+    if (m >= M) continue;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int i = t * 16 + kg * 4;
+      if (i < R)
+        *(float4*)(Ps + (int64_t)m * R + i) =
+            make_float4(acc[rt][t][0], acc[rt][t][1], acc[rt][t][2], acc[rt][t][3]);
+    }
+  }
+}
+
 // Segmented shrink. grid: (ceil(M / 64), S); 4 waves, each a 16-row tile of
 // its K slice. A fragments come straight from global memory (L2): the
 // adapter can change from one row tile to the next.
@@ -439,6 +588,27 @@ static ShrinkPlan plan_shrink(int64_t M, int64_t K, int R) {
   return p;
 }
 
+// Plan of the pipelined shrink (16-bit X): one row tile per wave (64 rows per
+// block), about 512 blocks (two per CU, the LDS ring allowing), and as few
+// K slices as that takes, so that blocks keep several chunks for the
+// pipeline and the partial sums stay small.
+static ShrinkPlan plan_shrink_pipe(int64_t M, int64_t K, int R) {
+  ShrinkPlan p;
+  p.ks = R <= 64 ? 8 : 4;
+  p.nt = R <= 16 ? 1 : R <= 32 ? 2 : R <= 64 ? 4 : 8;
+  const int64_t kc = 32 * p.ks;
+  const int64_t nch = (K + kc - 1) / kc;
+  p.rt = 1;
+  p.blocks_m = (M + 63) / 64;
+  int64_t s = (512 + p.blocks_m - 1) / p.blocks_m;
+  if (s > 32) s = 32;
+  if (s > nch) s = nch;
+  if (s < 1) s = 1;
+  const int64_t j = (nch + s - 1) / s;
+  p.S = (int)((nch + j - 1) / j);
+  return p;
+}
+
 // Split of K for the segmented shrink: about 2048 (16-row tile, slice) waves,
 // slices of at least 256 and a multiple of 32 elements, at most 16 slices.
 static void seg_split(int64_t M, int64_t K, int* S, int* kchunk) {
@@ -464,6 +634,8 @@ size_t lora_ws_bytes(int64_t M, int64_t K, int R) {
   for (int q = 0; q < 2; ++q) {
     const ShrinkPlan p = plan_shrink(M, K, probe[q]);
     if (p.S > smax) smax = p.S;
+    const ShrinkPlan pp = plan_shrink_pipe(M, K, probe[q]);
+    if (pp.S > smax) smax = pp.S;
   }
   return (size_t)smax * (size_t)M * (size_t)R * sizeof(float);
 }
@@ -472,6 +644,20 @@ size_t lora_ws_bytes(int64_t M, int64_t K, int R) {
 template <int XT>
 static int launch_shrink_p(const void* X, int64_t M, int64_t K, int64_t ldx, const unsigned short* A,
                            int R, float* P, hipStream_t st) {
+  if constexpr (XT != SQ_F32) {
+    const ShrinkPlan p = plan_shrink_pipe(M, K, R);
+    const dim3 grid((unsigned)p.blocks_m, (unsigned)p.S);
+    const size_t lds = 2 * (size_t)p.nt * 16 * 32 * p.ks * 2;
+    const char* x = (const char*)X;
+    const int64_t ldb = ldx * DtSize<XT>::v;
+    switch (p.nt) {
+      case 1: k_lora_shrink_pipe<XT, 8, 1, 1><<<grid, kLoraThreads, lds, st>>>(x, ldb, (int)M, (int)K, A, R, p.S, P); break;
+      case 2: k_lora_shrink_pipe<XT, 8, 1, 2><<<grid, kLoraThreads, lds, st>>>(x, ldb, (int)M, (int)K, A, R, p.S, P); break;
+      case 4: k_lora_shrink_pipe<XT, 8, 1, 4><<<grid, kLoraThreads, lds, st>>>(x, ldb, (int)M, (int)K, A, R, p.S, P); break;
+      default: k_lora_shrink_pipe<XT, 4, 1, 8><<<grid, kLoraThreads, lds, st>>>(x, ldb, (int)M, (int)K, A, R, p.S, P); break;
+    }
+    return p.S;
+  }
   const ShrinkPlan p = plan_shrink(M, K, R);
   const dim3 grid((unsigned)p.blocks_m, (unsigned)p.S);
   const size_t lds = (size_t)R * 32 * p.ks * 2;
