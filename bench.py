@@ -533,7 +533,139 @@ def row_f1(args, torch):
     }
 
 
-ROWS = {"f1": row_f1, "f2": row_f2, "f3": row_f3, "f4": row_f4}
+KERNEL_WORKLOADS = ("tiny_m16_k256_n256", "llama3_8b_proj_m2048", "opt13b_layer_decode_m64",
+                    "opt13b_layer_prefill_m4096", "multitenant_lora_m8192", "llama2_70b_mlp_m8192")
+
+
+def time_rotated(torch, fns, reps):
+    """Average ms per call over reps calls cycling through fns (one per input
+    copy), after one warm call each: with enough copies the inputs do not stay
+    in the 256 MB MALL between their calls."""
+    for f in fns:
+        f()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(reps):
+        fns[i % len(fns)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def row_kernels(args, torch):
+    """Every kernel of the path (a1-a9), timed alone at every configuration's
+    shapes: each input group's calibration absmax (a1), smoothing scale and
+    fold (a2, a3: two passes over W), per-token quant (a4), INT8 GEMM with
+    the dequant epilogue (a5, a6), stacked LoRA shrink with its reduce (a7),
+    the same GEMM with the LoRA expand in its epilogue (a8), and the
+    segmented LoRA (a9, shrink + expand). Inputs are seeded device-random
+    tensors of the shapes; each kernel cycles through enough copies of its
+    streamed input that the set exceeds 512 MB (at most 64 copies), so the
+    MALL does not serve repeats. Memory-bound kernels report algorithmic GB/s
+    and the fraction of 8 TB/s, the GEMMs TOP/s and the fraction of 5 POP/s."""
+    from synth.workloads import get_workload
+    import w8a8_smoothquant_int8_amd as sq
+    torch.manual_seed(0)
+    reps = max(args.steps, 20)
+    dt_of = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+    out, fracs = {}, []
+
+    def copies(nbytes):
+        return int(min(64, max(2, -(-(512 << 20) // max(nbytes, 1)))))
+
+    def rec(ms, nbytes=None, ops=None, big=False):
+        r = {"us": round(ms * 1e3, 2)}
+        if nbytes is not None:
+            gbs = nbytes / ms / 1e6
+            r.update(gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 3))
+            if big:
+                fracs.append(gbs / HBM_PEAK_GBS)
+        if ops is not None:
+            tops = ops / ms / 1e9
+            r.update(tops=round(tops, 1), frac_int8=round(tops / INT8_PEAK_TOPS, 3))
+        return r
+
+    for name in KERNEL_WORKLOADS:
+        wl = get_workload(name)
+        dt, esz = dt_of[wl.dtype], (4 if wl.dtype == "f32" else 2)
+        odt = dt_of[wl.out_dtype]
+        M, C = wl.M, wl.calib_rows()
+        big = M >= 4096
+        res = {}
+        for inp, K in wl.inputs:
+            N = sum(p.N for p in wl.group(inp))
+            g = {"M": M, "N": N, "K": K}
+            Xs = [torch.randn(M, K, device="cuda").to(dt) for _ in range(copies(M * K * esz))]
+            Xc = [x[:C] for x in Xs]
+            amax = torch.zeros(K, device="cuda")
+            ms = time_rotated(torch, [lambda x=x: sq.sq_calibrate_absmax(x, amax) for x in Xc], reps)
+            g["a1_calibrate"] = rec(ms, esz * C * K, big=big)
+            Ws = [(torch.randn(N, K, device="cuda") * 0.02).to(dt) for _ in range(copies(N * K * esz))]
+            s = torch.empty(K, device="cuda")
+            Wq = torch.empty(N, K, dtype=torch.int8, device="cuda")
+            ws_ = torch.empty(N, device="cuda")
+            amax.copy_(torch.rand(K, device="cuda") * 10 + 0.1)
+            ms = time_rotated(torch, [lambda w=w: sq.sq_smooth_fold(amax, w, wl.alpha, s, Wq, ws_)
+                                      for w in Ws], max(reps // 2, 10))
+            g["a2_a3_smooth_fold"] = rec(ms, 2 * esz * N * K + N * K + 4 * N, big=big)
+            del Ws
+            Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+            a = torch.empty(M, device="cuda")
+            ms = time_rotated(torch, [lambda x=x: sq.sq_quant_per_token(x, s, Xq, a) for x in Xs], reps)
+            g["a4_quant"] = rec(ms, (esz + 1) * M * K + 4 * M, big=big)
+            Wq.copy_(torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda"))
+            Xq.copy_(torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda"))
+            a.copy_(torch.rand(M, device="cuda") * 1e-2)
+            ws_.copy_(torch.rand(N, device="cuda") * 1e-3)
+            Y = torch.empty(M, N, dtype=odt, device="cuda")
+            ms = time_launches(torch, lambda: sq.sq_w8a8_gemm(Xq, Wq, a, ws_, Y), reps)
+            g["a5_a6_gemm"] = rec(ms, ops=2.0 * M * N * K)
+            r = wl.lora_rank * len(wl.group(inp))
+            if r:
+                A = (torch.randn(r, K, device="cuda") * 0.01).bfloat16()
+                Bb = (torch.randn(N, r, device="cuda") * 0.01).bfloat16()
+                T = torch.empty(M, r, dtype=torch.bfloat16, device="cuda")
+                wsp = torch.empty(sq.sq_lora_workspace_bytes(M, K, r), dtype=torch.uint8, device="cuda")
+                ms = time_rotated(torch, [lambda x=x: sq.sq_lora_shrink(x, A, T, wsp) for x in Xs], reps)
+                g["a7_shrink"] = rec(ms, esz * M * K + 2 * r * K + 2 * M * r, big=big)
+                g["a7_shrink"]["rank"] = r
+                ms = time_launches(torch, lambda: sq.sq_w8a8_gemm_lora(Xq, Wq, a, ws_, T, Bb, Y), reps)
+                g["a8_gemm_lora"] = rec(ms, ops=2.0 * M * N * K)
+            if wl.segmented:
+                seg = wl.segments(0)
+                ranks = seg["ranks"]
+                for proj in [p.name for p in wl.group(inp)][:1]:
+                    Np = [p.N for p in wl.group(inp) if p.name == proj][0]
+                    As = [(torch.randn(int(rk), K, device="cuda") * 0.01).bfloat16() for rk in ranks]
+                    Bs = [(torch.randn(Np, int(rk), device="cuda") * 0.01).bfloat16() for rk in ranks]
+                    Yp = torch.zeros(M, Np, dtype=odt, device="cuda")
+                    mr = int(ranks.max())
+                    wsp = torch.empty(sq.sq_lora_workspace_bytes(M, K, mr), dtype=torch.uint8, device="cuda")
+                    st_ = torch.from_numpy(seg["seg_start"]).cuda()
+                    sa_ = torch.from_numpy(seg["seg_adapter"]).cuda()
+                    rk_ = torch.from_numpy(ranks).cuda()
+                    ap, bp = sq.pointer_table(As, "cuda"), sq.pointer_table(Bs, "cuda")
+                    ms = time_rotated(torch, [lambda x=x: sq.sq_lora_apply_segmented(
+                        x, st_, sa_, ap, bp, rk_, mr, Yp, wsp) for x in Xs], reps)
+                    nbytes = esz * M * K + 2 * 2 * M * Np + sum(2 * int(rk) * (K + Np) for rk in ranks)
+                    g["a9_segmented_" + proj] = rec(ms, nbytes, big=big)
+            res[inp] = g
+            del Xs, Xc, Xq, Y
+            torch.cuda.empty_cache()
+        out[name] = res
+    fracs.sort()
+    med = fracs[len(fracs) // 2] if fracs else None
+    return {
+        "row": "kernels", "metric": "per-kernel rates of the path at every configuration (median "
+                                    "HBM fraction of the memory-bound kernels at M >= 4096)",
+        "value": round(med, 3) if med is not None else None, "unit": "fraction of 8 TB/s",
+        "higher_is_better": True, "data": "synthetic (device-random tensors of each configuration's shapes)",
+        "config": {"workloads": list(KERNEL_WORKLOADS), "reps": reps}, "kernels": out,
+    }
+
+
+ROWS = {"f1": row_f1, "f2": row_f2, "f3": row_f3, "f4": row_f4, "kernels": row_kernels}
 
 
 def main():

@@ -89,7 +89,7 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
     for (int e = 0; e < 8; ++e) {
       const float sv = (s != nullptr && c * 8 < K) ? s[c * 8 + e] : 1.0f;
       if constexpr (KIND == Q_FOLD) sm[j][e] = sv;
-      else rs[j][e] = rcp_rn64(sv);           // RN64(1/s)
+      else rs[j][e] = 1.0 / (double)sv;       // RN64(1/s), IEEE fp64 division (once per block)
     }
   }
 
@@ -184,13 +184,13 @@ k_quant_rows(const char* __restrict__ in, int64_t rows, int64_t K, int64_t in_ld
             for (int e = 0; e < 8; ++e) y[e] = smooth(y[e], j, e);
           }
           // scale == 0 (all-zero row, or a zero static scale): every code is 0
-          const uint32_t keep = scale[r] != 0.0f ? 0xFFFFFFFFu : 0u;
+          // (selected per element: a row mask here costs this kernel a spill)
           uint32_t q[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) q[e] = code_word(div_rn(y[e], rscale[r]));
+          for (int e = 0; e < 8; ++e) q[e] = scale[r] != 0.0f ? code_word(div_rn(y[e], rscale[r])) : 0u;
           uint2 pk;
-          pk.x = pack4_codes(q[0], q[1], q[2], q[3]) & keep;
-          pk.y = pack4_codes(q[4], q[5], q[6], q[7]) & keep;
+          pk.x = pack4_codes(q[0], q[1], q[2], q[3]);
+          pk.y = pack4_codes(q[4], q[5], q[6], q[7]);
           *(uint2*)(orow + c * 8) = pk;
         }
       }

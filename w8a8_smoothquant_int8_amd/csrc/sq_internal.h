@@ -127,6 +127,18 @@ __device__ __forceinline__ uint32_t code_word(float q) {
   return __float_as_uint(t + 12582912.0f);
 }
 
+// The same code as an int: round half to even, clamp to [-127, 127].
+__device__ __forceinline__ int quant_code(float q) {
+  float r = __builtin_rintf(q);
+  r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
+         ((uint32_t)(d & 0xFF) << 24);
+}
+
 // Four code words (low bytes) into one packed word, first in the low byte.
 __device__ __forceinline__ uint32_t pack4_codes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return (a & 0xFFu) | ((b & 0xFFu) << 8) | ((c & 0xFFu) << 16) | (d << 24);
