@@ -241,12 +241,16 @@ def _tile_score(M, N, bm, bn, resident, rate):
 def gemm_tile(M: int, N: int, K: int) -> str:
     """The tile configuration libsq picks for an INT8 GEMM of this shape (the
     library's rule: the generic kernel when K is not a multiple of 128 or an
-    operand reaches 4 GiB, else the best of 256x256 tiles and 256x192 tiles,
+    operand reaches 4 GiB, the skinny kernel for M <= 64 with fewer than 96
+    column tiles of 128, else the best of
+    256x256 tiles and 256x192 tiles,
     one block per CU, at rates 1 and 0.93, and 128x128 tiles, two blocks per
     CU, at 0.8, each scored by the padding and the fraction of the last round
     of blocks that does useful work; ties go to 256x256, then 256x192)."""
     if K % 128 or M * K >= 1 << 32 or N * K >= 1 << 32:
         return "generic"
+    if M <= 64 and (N + 127) // 128 < 96:
+        return "skinny"
     s256 = _tile_score(M, N, 256, 256, 256, 1.0)
     s192 = _tile_score(M, N, 256, 192, 256, 0.93)
     s128 = _tile_score(M, N, 128, 128, 512, 0.8)

@@ -20,7 +20,8 @@ from synth.workloads import cast_to  # noqa: E402
 
 F32 = np.float32
 DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-SHAPES = [(300, 400, 128), (300, 400, 256), (257, 448, 384), (513, 1040, 1024), (64, 208, 512)]
+SHAPES = [(300, 400, 128), (300, 400, 256), (257, 448, 384), (513, 1040, 1024), (64, 208, 512),
+          (1, 48, 128), (17, 400, 1024), (33, 1040, 384), (64, 5120, 2560)]
 
 
 def dev(x):

@@ -33,7 +33,7 @@ def test_stream_plan_longest_first_least_loaded():
 def test_gemm_tile_rule_covers_the_workload():
     wl = get_workload("llama3_8b_proj_m2048")
     tiles = {inp: bench.gemm_tile(wl.M, sum(p.N for p in wl.group(inp)), K) for inp, K in wl.inputs}
-    assert set(tiles.values()) <= {"256x256", "256x192", "128x128", "generic"}
+    assert set(tiles.values()) <= {"256x256", "256x192", "128x128", "skinny", "generic"}
     # M = 2048: 256x192 tiles fill the chip for QKV (N = 6144: 256 tiles, 192 at
     # 256x256); gate+up keeps 256x256 (a near-tie, and less data per op); the
     # N = 4096 groups take 128x128
@@ -45,6 +45,9 @@ def test_gemm_tile_rule_prefers_whole_rounds():
     assert bench.gemm_tile(4096, 6144, 4096) == "256x192"     # 512 tiles instead of 384
     assert bench.gemm_tile(2048, 4096, 14336) == "128x128"
     assert bench.gemm_tile(2048, 4096, 4100) == "generic"
+    assert bench.gemm_tile(64, 5120, 20480) == "skinny"          # decode
+    assert bench.gemm_tile(65, 5120, 20480) == "128x128"
+    assert bench.gemm_tile(64, 15360, 5120) == "128x128"         # wide: 120 column tiles
 
 
 def test_cpu_baseline_on_the_tiny_workload():

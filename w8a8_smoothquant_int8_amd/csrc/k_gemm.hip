@@ -551,6 +551,92 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
 }
 
 // ---------------------------------------------------------------------------
+// Skinny kernel (M <= 64, K % 128 == 0): decode-sized GEMMs stream the
+// weights once and are HBM-bound, and 128x128 tiles would leave most CUs
+// idle (N = 5120 gives 40 of them). Here a block owns 32 output columns
+// over all M rows (one row tile of 32 for M <= 32, two for M <= 64), and its
+// 8 waves split K: wave w takes the 128-byte K-tiles w, w + 8, ... Operand
+// fragments come straight from global memory into registers, double-buffered
+// over the wave's K-tiles (the few A rows are shared by every block through
+// L2). The waves' INT32 partial sums meet in LDS (exact in any order) and
+// wave 0 runs the epilogue. Accumulators are transposed as in the other
+// kernels (B rows as the first MFMA operand).
+// ---------------------------------------------------------------------------
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyBN = 32;
+
+template <int OUT, bool STATIC_A, int LORA, int TM>
+__global__ void __launch_bounds__(kSkinnyWaves * 64)
+k_gemm_skinny(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+              const float* __restrict__ a_scale, const float* __restrict__ w_scale, int M, int N,
+              int K, void* __restrict__ Y, int64_t ldy, LoraEpi le) {
+  __shared__ int32_t red[kSkinnyWaves - 1][TM][16][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * kSkinnyBN;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  // lane l supplies 16 bytes (k-half l / 32 of a 32-byte step) of row l % 32;
+  // rows past N or M read the last valid row and are never stored
+  const int nrow = n0 + lrow < N ? n0 + lrow : N - 1;
+  const int8_t* bp = B + (int64_t)nrow * K + 16 * lhalf;
+  const int8_t* ap[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int mrow = 32 * i + lrow < M ? 32 * i + lrow : M - 1;
+    ap[i] = A + (int64_t)mrow * K + 16 * lhalf;
+  }
+  const int nk = K / kBK;
+
+  auto load = [&](int kt, v4i (&fb)[4], v4i (&fa)[4][TM]) {
+    const int64_t off = (int64_t)kt * kBK;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      fb[st] = *(const v4i*)(bp + off + 32 * st);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[st][i] = *(const v4i*)(ap[i] + off + 32 * st);
+    }
+  };
+  v16i acc[TM][1];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) acc[i][0] = v16i{};
+  auto mma = [&](const v4i (&fb)[4], const v4i (&fa)[4][TM]) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        acc[i][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[st], fa[st][i], acc[i][0], 0, 0, 0);
+  };
+
+  v4i fb0[4], fa0[4][TM], fb1[4], fa1[4][TM];
+  constexpr int W = kSkinnyWaves;
+  if (wave < nk) load(wave, fb0, fa0);
+  for (int kt = wave; kt < nk; kt += 2 * W) {
+    const bool more = kt + W < nk;
+    if (more) load(kt + W, fb1, fa1);
+    mma(fb0, fa0);
+    if (!more) break;
+    if (kt + 2 * W < nk) load(kt + 2 * W, fb0, fa0);
+    mma(fb1, fa1);
+  }
+
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) red[wave - 1][i][q][lane] = acc[i][0][q];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll 1   // one wave's partials at a time (all at once would not fit the registers)
+  for (int w = 0; w < W - 1; ++w)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][0][q] += red[w][i][q][lane];
+  epilogue<OUT, STATIC_A, LORA, TM, 1>(acc, 0, n0, M, N, a_scale, w_scale, Y, ldy, le);
+}
+
+// ---------------------------------------------------------------------------
 // Generic kernel: any K % 16 == 0; 128 x 128 tiles staged through registers.
 // ---------------------------------------------------------------------------
 constexpr int kGBM = 128, kGBN = 128;
@@ -661,8 +747,10 @@ k_gemm_generic(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
 //                256x256 tiles would leave CUs idle (M = 2048, N = 6144:
 //                256 tiles instead of 192);
 //   CFG_128:     128x128 tiles, 4 waves of 64x64, two blocks per CU - wins
-//                for narrow outputs (N = 4096) and small M.
-enum TileCfg { CFG_GENERIC = 0, CFG_256 = 1, CFG_128 = 2, CFG_256x192 = 3 };
+//                for narrow outputs (N = 4096) and small M;
+//   CFG_SKINNY:  M <= 64 and N < 12288 (decode): 32-column blocks over all
+//                rows, K split over the block's waves.
+enum TileCfg { CFG_GENERIC = 0, CFG_256 = 1, CFG_128 = 2, CFG_256x192 = 3, CFG_SKINNY = 4 };
 
 // Score of a tile configuration: the share of the launched tile work that is
 // useful (rows and columns padded up to whole tiles, and the last round of
@@ -677,13 +765,18 @@ static double tile_score(int64_t M, int64_t N, int64_t bm, int64_t bn, int64_t r
 
 static int pick_cfg(int64_t M, int64_t N, int64_t K) {
   if (K % kBK != 0 || M * K >= (1LL << 32) || N * K >= (1LL << 32)) return CFG_GENERIC;
-  // Tuning override: SQ_GEMM_TILE=0|1|2|3 forces a configuration (read once per process).
+  // Tuning override: SQ_GEMM_TILE=0|1|2|3|4 forces a configuration (read once
+  // per process; 4, the skinny kernel, only where M <= 64).
   static const int forced = [] {
     const char* e = std::getenv("SQ_GEMM_TILE");
     const int o = (e && *e) ? std::atoi(e) : -1;
-    return (o >= 0 && o <= 3) ? o : -1;
+    return (o >= 0 && o <= 4) ? o : -1;
   }();
-  if (forced >= 0) return forced;
+  if (forced >= 0 && (forced != CFG_SKINNY || M <= 64)) return forced;
+  // M <= 64 with fewer than 96 column tiles of 128: the skinny kernel (measured
+  // 1.7-3.6x faster at N = 5120); with more, 128x128 tiles already spread the
+  // weight stream over the chip and win (by 8-34% at N = 15360 ... 28672).
+  if (M <= 64 && (N + 127) / 128 < 96) return CFG_SKINNY;
   // 256 CUs: one 256x256 or 256x192 block per CU, two 128x128 blocks per CU.
   // Rates relative to 256x256 at full occupancy, measured on MI355X: 256x192
   // 0.94 (2048x24576x4096, whole rounds for both), taken as 0.93 so that
@@ -723,6 +816,17 @@ static int launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* a_scal
     case CFG_128:
       return launch_pipe<128, 128, 2, 2, OUT, STATIC_A, LORA>(Xq, Wq, a_scale, w_scale, M, N, K, Y,
                                                                  ldy, le, st);
+    case CFG_SKINNY: {
+      const unsigned blocks = (unsigned)((N + kSkinnyBN - 1) / kSkinnyBN);
+      if (M <= 32)
+        k_gemm_skinny<OUT, STATIC_A, LORA, 1><<<blocks, kSkinnyWaves * 64, 0, st>>>(
+            Xq, Wq, a_scale, w_scale, (int)M, (int)N, (int)K, Y, ldy, le);
+      else
+        k_gemm_skinny<OUT, STATIC_A, LORA, 2><<<blocks, kSkinnyWaves * 64, 0, st>>>(
+            Xq, Wq, a_scale, w_scale, (int)M, (int)N, (int)K, Y, ldy, le);
+      SQ_LAUNCH_CHECK();
+      return SQ_OK;
+    }
     default:
       break;
   }
