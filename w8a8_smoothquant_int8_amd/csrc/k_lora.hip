@@ -360,25 +360,42 @@ k_lora_shrink_seg(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, L
     while (g1 + 1 < la.nseg && la.seg_start[g1 + 1] < mend) ++g1;
   }
 
-  for (int k = ks; k < ke; k += 32) {
-    const int kk = k + kg * 8;
-    const bool kin = kk < ke;
-    uint4 xu = make_uint4(0, 0, 0, 0);
-    if (kin && my_m < M) xu = load8_as_bf16<XT>(X + (int64_t)my_m * ldx_bytes + (int64_t)kk * DtSize<XT>::v);
+  // U k-steps per batch: the batch's X fragments, then per request and rank
+  // tile its U adapter fragments, are all issued before their MFMAs, so
+  // loads overlap instead of one load -> MFMA round trip per k-step. For each
+  // row only its own request contributes (other rows' fragments are zero),
+  // in increasing k, as with one k-step at a time.
+  constexpr int U = 8;
+  for (int k = ks; k < ke; k += 32 * U) {
+    uint4 xu[U];
+    bool kin[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = k + 32 * u + kg * 8;
+      kin[u] = kk < ke;
+      xu[u] = (kin[u] && my_m < M)
+                  ? load8_as_bf16<XT>(X + (int64_t)my_m * ldx_bytes + (int64_t)kk * DtSize<XT>::v)
+                  : make_uint4(0, 0, 0, 0);
+    }
     for (int g = g0; g <= g1; ++g) {
       const int ad = la.seg_adapter[g];
       if (ad < 0) continue;
       const int ra = la.ranks[ad];
       const unsigned short* Ag = (const unsigned short*)la.A_ptrs[ad];
       const bool mine = my_m >= la.seg_start[g] && my_m < la.seg_start[g + 1];
-      const v8bf xf = bits_to_v8bf(mine ? xu : make_uint4(0, 0, 0, 0));
 #pragma unroll
       for (int t = 0; t < kMaxRankTiles; ++t) {
         if (t < NT) {
           const int i = t * 16 + lrow;
-          uint4 au = make_uint4(0, 0, 0, 0);
-          if (kin && i < ra) au = *(const uint4*)(Ag + (int64_t)i * K + kk);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, bits_to_v8bf(au), acc[t], 0, 0, 0);
+          uint4 au[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            au[u] = (kin[u] && i < ra) ? *(const uint4*)(Ag + (int64_t)i * K + k + 32 * u + kg * 8)
+                                       : make_uint4(0, 0, 0, 0);
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                bits_to_v8bf(mine ? xu[u] : make_uint4(0, 0, 0, 0)), bits_to_v8bf(au[u]), acc[t], 0, 0, 0);
         }
       }
     }
