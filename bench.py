@@ -66,8 +66,14 @@ def parse():
 
 
 def kernel_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source's code: comments and whitespace are stripped, so
+    editing a comment does not invalidate the counters taken on the code."""
+    with open(path, encoding="utf-8") as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def stored_traffic(tile: str):

@@ -18,6 +18,9 @@
 // walks patches of 8 tile rows column by column, so the blocks an XCD runs at
 // once share operand panels in its L2.
 //
+// Skinny kernel (M <= 64, narrow N): 32-column blocks over all rows, K split
+// across the block's waves, fragments straight from global memory.
+//
 // Generic kernel (any K multiple of 16): 128 x 128 tiles staged through
 // registers, zero-filling the K tail.
 #include <cstdlib>
@@ -222,8 +225,9 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], int row0, int col0
 // LoRA with scale 1). Its operands are already in LDS when the K loop ends:
 //   - the block's a_scale and w_scale slices, requested with direct
 //     global->LDS loads at the start of the kernel into a region of their own;
-//   - the T and B rows of the first 64 LoRA ranks, requested at the start of
-//     the last K-tile into the ring stage that tile does not use.
+//   - the T and B rows of the first 64 LoRA ranks, requested at the sync point
+//     of the K-tile before the last, into the ring stage it releases (at the
+//     start of the kernel when there is a single K-tile).
 // The K loop's last wait and barrier cover both. More than 64 ranks: the next
 // 64 go through the same stage, one wait and two barriers per pass.
 // Values and operation order are those of the epilogue above.
