@@ -2,16 +2,17 @@
 // Pitch), for one adapter or one adapter per request segment ([GRP]).
 //
 //   shrink:  P[s, m, i] = sum_{k in split s} bf16(X[m, k]) * A[i, k]   (fp32)
-//   expand:  T[m, i]    = bf16(sum_s P[s, m, i])        (fixed order of s)
-//            Y[m, n]    = out(fp32(Y[m, n]) + scale * sum_i T[m, i] * B[n, i])
+//   reduce:  T[m, i]    = bf16(sum_s P[s, m, i])        (fixed order of s)
+//   expand:  Y[m, n]    = out(fp32(Y[m, n]) + scale * sum_i T[m, i] * B[n, i])
 //
 // Both are dense contractions and run on the gfx950 bf16 matrix instruction
 // V_MFMA_F32_16X16X32_BF16. The shrink reads X once and is HBM-bound; with
 // few row blocks at small M it splits K into S slices so enough blocks stream
 // X, and writes fp32 partial sums to the caller's workspace. There is no
-// atomic: the expand (or, for the fused GEMM epilogue, a small reduce kernel)
-// sums the S partials in a fixed order, so results are reproducible bit for
-// bit. The expand's traffic is the read-modify-write of Y; it computes
+// atomic: a small reduce kernel sums the S partials in a fixed order into T
+// (in the workspace, after the partials, for the separate expand; in the
+// caller's T for the fused GEMM epilogue), so results are reproducible bit
+// for bit. The expand's traffic is the read-modify-write of Y; it computes
 // the transposed product (B rows as the first operand) so every lane owns 4
 // consecutive columns of one row of Y (8-byte accesses for bf16).
 //
@@ -418,17 +419,35 @@ k_lora_shrink_seg(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, L
   }
 }
 
+// 4 consecutive Y values as raw bits (16 bytes for fp32, 8 for 16-bit types),
+// loaded ahead of the add that rmw4_from completes.
 template <int YT>
-__device__ __forceinline__ void rmw4(void* Y, int64_t off, float scale, const v4f& d) {
+struct Y4 { uint4 v; };
+template <int YT>
+__device__ __forceinline__ Y4<YT> load_y4(const void* Y, int64_t off) {
+  Y4<YT> r;
   if constexpr (YT == SQ_F32) {
-    float4* p = (float4*)((float*)Y + off);
-    float4 y = *p;
+    r.v = *(const uint4*)((const float*)Y + off);
+  } else {
+    const uint2 u = *(const uint2*)((const unsigned short*)Y + off);
+    r.v = make_uint4(u.x, u.y, 0, 0);
+  }
+  return r;
+}
+
+// Y[off .. off + 3] = out(fp32(y) + scale * d[j]) from the values loaded before.
+template <int YT>
+__device__ __forceinline__ void rmw4_from(void* Y, int64_t off, const Y4<YT>& yv, float scale,
+                                          const v4f& d) {
+  if constexpr (YT == SQ_F32) {
+    float4 y = make_float4(__uint_as_float(yv.v.x), __uint_as_float(yv.v.y),
+                           __uint_as_float(yv.v.z), __uint_as_float(yv.v.w));
     y.x = y.x + scale * d[0]; y.y = y.y + scale * d[1];
     y.z = y.z + scale * d[2]; y.w = y.w + scale * d[3];
-    *p = y;
+    *(float4*)((float*)Y + off) = y;
   } else {
     uint2* p = (uint2*)((unsigned short*)Y + off);
-    uint2 u = *p;
+    uint2 u = make_uint2(yv.v.x, yv.v.y);
     uint32_t h[4] = {u.x & 0xFFFFu, u.x >> 16, u.y & 0xFFFFu, u.y >> 16};
     uint32_t o[4];
 #pragma unroll
@@ -447,7 +466,7 @@ __device__ __forceinline__ void rmw4(void* Y, int64_t off, float scale, const v4
 // owns the block's 16 rows and `chunks_per_wave` column chunks of 64.
 template <int YT, bool SEG>
 __global__ void __launch_bounds__(kLoraThreads)
-k_lora_expand(const float* __restrict__ P, int S, int R, int M, int N, LoraArgs la, float scale,
+k_lora_expand(const unsigned short* __restrict__ T, int R, int M, int N, LoraArgs la, float scale,
               void* __restrict__ Y, int64_t ldy, int chunks_per_wave) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -456,25 +475,14 @@ k_lora_expand(const float* __restrict__ P, int S, int R, int M, int N, LoraArgs 
   const int my_m = m0 + lrow;
   const int KS = (R + 31) / 32;        // rank steps of 32
 
-  // T operand: T[my_m, ks*32 + kg*8 .. +8] = bf16(sum_s P[s, m, .]), fixed order.
+  // T operand: T[my_m, ks*32 + kg*8 .. +8] (T [M, R] bf16, reduced once from
+  // the shrink's partial sums by k_lora_reduce).
   uint4 tu[kMaxRankSteps];
 #pragma unroll
   for (int ks = 0; ks < kMaxRankSteps; ++ks) {
-    tu[ks] = make_uint4(0, 0, 0, 0);
     const int k = ks * 32 + kg * 8;
-    if (ks < KS && k < R && my_m < M) {
-      float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int s = 0; s < S; ++s) {
-        const float4* p = (const float4*)(P + ((int64_t)s * M + my_m) * R + k);
-        const float4 a = p[0], b = p[1];
-        t[0] += a.x; t[1] += a.y; t[2] += a.z; t[3] += a.w;
-        t[4] += b.x; t[5] += b.y; t[6] += b.z; t[7] += b.w;
-      }
-      tu[ks].x = f32_to_bf16_bits(t[0]) | (f32_to_bf16_bits(t[1]) << 16);
-      tu[ks].y = f32_to_bf16_bits(t[2]) | (f32_to_bf16_bits(t[3]) << 16);
-      tu[ks].z = f32_to_bf16_bits(t[4]) | (f32_to_bf16_bits(t[5]) << 16);
-      tu[ks].w = f32_to_bf16_bits(t[6]) | (f32_to_bf16_bits(t[7]) << 16);
-    }
+    tu[ks] = (ks < KS && k < R && my_m < M) ? *(const uint4*)(T + (int64_t)my_m * R + k)
+                                            : make_uint4(0, 0, 0, 0);
   }
 
   int g0 = 0, g1 = 0;
@@ -491,9 +499,21 @@ k_lora_expand(const float* __restrict__ P, int S, int R, int M, int N, LoraArgs 
 
   const int n_chunks = (N + 63) / 64;
   const int cbase = (blockIdx.y * 4 + wave) * chunks_per_wave;
+  // The Y values of the next chunk load while this chunk multiplies, so the
+  // read of the read-modify-write is off the critical path.
+  Y4<YT> ycur[4], ynext[4];
+  auto load_chunk_y = [&](int chunk, Y4<YT> (&yv)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int n = chunk * 64 + t * 16 + kg * 4;
+      if (my_m < M && n < N) yv[t] = load_y4<YT>(Y, (int64_t)my_m * ldy + n);
+    }
+  };
+  if (cbase < n_chunks) load_chunk_y(cbase, ycur);
   for (int cc = 0; cc < chunks_per_wave; ++cc) {
     const int chunk = cbase + cc;
     if (chunk >= n_chunks) break;
+    if (cc + 1 < chunks_per_wave && chunk + 1 < n_chunks) load_chunk_y(chunk + 1, ynext);
     const int nb = chunk * 64;
     v4f acc[4];
 #pragma unroll
@@ -535,9 +555,11 @@ k_lora_expand(const float* __restrict__ P, int S, int R, int M, int N, LoraArgs 
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int n = nb + t * 16 + kg * 4;
-        if (n < N) rmw4<YT>(Y, (int64_t)my_m * ldy + n, scale, acc[t]);
+        if (n < N) rmw4_from<YT>(Y, (int64_t)my_m * ldy + n, ycur[t], scale, acc[t]);
       }
     }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ycur[t] = ynext[t];
   }
 }
 
@@ -654,7 +676,8 @@ size_t lora_ws_bytes(int64_t M, int64_t K, int R) {
     const ShrinkPlan pp = plan_shrink_pipe(M, K, probe[q]);
     if (pp.S > smax) smax = pp.S;
   }
-  return (size_t)smax * (size_t)M * (size_t)R * sizeof(float);
+  // fp32 partial sums of up to smax slices, then the reduced T [M, R] bf16
+  return (size_t)smax * (size_t)M * (size_t)R * sizeof(float) + (size_t)M * (size_t)R * 2;
 }
 
 // Single-adapter shrink into P; returns the number of slices written.
@@ -713,12 +736,18 @@ static int launch_lora_t(const void* X, int64_t M, int64_t K, int64_t ldx, const
   const int S = SEG ? launch_shrink_seg_p<XT>(X, M, K, ldx, la, R, P, st)
                     : launch_shrink_p<XT>(X, M, K, ldx, la.A, R, P, st);
   SQ_LAUNCH_CHECK();
+  // T = bf16(sum of the S partials) once, after the partials in the workspace;
+  // the expand's waves then read it instead of each summing the partials again
+  unsigned short* Tw = (unsigned short*)((char*)ws + (size_t)S * (size_t)M * (size_t)R * sizeof(float));
+  const int64_t rthreads = M * (R / 4);
+  k_lora_reduce<<<(unsigned)((rthreads + 63) / 64), 64, 0, st>>>(P, S, R, (int)M, Tw, R);
+  SQ_LAUNCH_CHECK();
   const int64_t m_tiles = (M + 15) / 16;
   const int64_t n_chunks = (N + 63) / 64;
   int64_t cpw = (m_tiles * n_chunks + 8191) / 8192;   // aim for ~8192 waves
   if (cpw < 1) cpw = 1;
   dim3 g2((unsigned)m_tiles, (unsigned)((n_chunks + 4 * cpw - 1) / (4 * cpw)));
-  k_lora_expand<YT, SEG><<<g2, kLoraThreads, 0, st>>>(P, S, R, (int)M, (int)N, la, scale, Y, ldy,
+  k_lora_expand<YT, SEG><<<g2, kLoraThreads, 0, st>>>(Tw, R, (int)M, (int)N, la, scale, Y, ldy,
                                                       (int)cpw);
   SQ_LAUNCH_CHECK();
   return SQ_OK;
