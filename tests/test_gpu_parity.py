@@ -345,6 +345,43 @@ def test_lora_segmented(M, K, N, ydt):
         assert torch.equal(Y[r0:r1].cpu(), y[r0:r1])
 
 
+@pytest.mark.parametrize("xdt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("ranks", [[8, 24, 64, 16], [128, 8, 40]])
+def test_lora_segmented_short_and_empty_requests(xdt, ranks):
+    """Many requests per 64-row block (lengths 0-5 among longer ones), empty
+    requests, requests without adapter, ranks that are not a multiple of 16,
+    and K not a multiple of the 256-element chunk."""
+    rng = np.random.default_rng(len(ranks) * 7 + len(xdt))
+    M, K, N = 333, 528, 208
+    lens = []
+    while sum(lens) < M:
+        lens.append(int(rng.integers(0, 6)) if rng.random() < 0.7 else int(rng.integers(20, 90)))
+    lens[-1] -= sum(lens) - M
+    seg_start = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    nseg = len(lens)
+    seg_adapter = rng.integers(0, len(ranks), nseg).astype(np.int32)
+    seg_adapter[rng.random(nseg) < 0.15] = -1
+    x, xn = acts(rng, M, K, xdt, factor=20.0)
+    As = [cast_to(rng.normal(0, 0.01, (r, K)).astype(F32), "bf16") for r in ranks]
+    Bs = [cast_to(rng.normal(0, 0.01, (N, r)).astype(F32), "bf16") for r in ranks]
+    y = cast_to(rng.normal(0, 0.5, (M, N)).astype(F32), "bf16")
+    Ad = [t.cuda() for t in As]
+    Bd = [t.cuda() for t in Bs]
+    Y = y.cuda()
+    mr = max(ranks)
+    ws = torch.empty(sq.sq_lora_workspace_bytes(M, K, mr), dtype=torch.uint8, device="cuda")
+    sq.sq_lora_apply_segmented(x, dev(seg_start), dev(seg_adapter), sq.pointer_table(Ad, "cuda"),
+                               sq.pointer_table(Bd, "cuda"), dev(np.array(ranks, np.int32)), mr, Y, ws)
+    ref = O.lora_apply_segmented(y.float().numpy(), xn, xdt, seg_start, seg_adapter,
+                                 [t.float().numpy() for t in As], [t.float().numpy() for t in Bs],
+                                 1.0, "bf16")
+    ok, rel = lora_close(Y.cpu().float().numpy(), ref)
+    assert ok, rel
+    for g in np.nonzero(seg_adapter < 0)[0]:
+        r0, r1 = seg_start[g], seg_start[g + 1]
+        assert torch.equal(Y[r0:r1].cpu(), y[r0:r1])
+
+
 def test_lora_segmented_single_adapter_equals_single():
     rng = np.random.default_rng(9)
     M, K, N, r = 300, 1024, 256, 16

@@ -12,11 +12,11 @@
 // atomic: a small reduce kernel sums the S partials in a fixed order into T
 // (in the workspace, after the partials, for the separate expand; in the
 // caller's T for the fused GEMM epilogue), so results are reproducible bit
-// for bit. The expand's traffic is the read-modify-write of Y; it computes
-// the transposed product (B rows as the first operand) so every lane owns 4
-// consecutive columns of one row of Y (8-byte accesses for bf16).
+// for bit. The expand's traffic is the read-modify-write of Y; its product
+// goes through LDS so that Y is read and written in whole rows per
+// instruction.
 //
-// Segments: each 16-row tile finds the requests that overlap it by binary
+// Segments: each block finds the requests that overlap its rows by binary
 // search in seg_start, and runs the MFMAs once per overlapping request with
 // the rows of other requests zeroed, so each row picks up only its own
 // adapter's product. Rows of requests without an adapter (-1) are not written.
@@ -419,147 +419,317 @@ k_lora_shrink_seg(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, L
   }
 }
 
-// 4 consecutive Y values as raw bits (16 bytes for fp32, 8 for 16-bit types),
-// loaded ahead of the add that rmw4_from completes.
-template <int YT>
-struct Y4 { uint4 v; };
-template <int YT>
-__device__ __forceinline__ Y4<YT> load_y4(const void* Y, int64_t off) {
-  Y4<YT> r;
-  if constexpr (YT == SQ_F32) {
-    r.v = *(const uint4*)((const float*)Y + off);
-  } else {
-    const uint2 u = *(const uint2*)((const unsigned short*)Y + off);
-    r.v = make_uint4(u.x, u.y, 0, 0);
-  }
-  return r;
-}
-
-// Y[off .. off + 3] = out(fp32(y) + scale * d[j]) from the values loaded before.
-template <int YT>
-__device__ __forceinline__ void rmw4_from(void* Y, int64_t off, const Y4<YT>& yv, float scale,
-                                          const v4f& d) {
-  if constexpr (YT == SQ_F32) {
-    float4 y = make_float4(__uint_as_float(yv.v.x), __uint_as_float(yv.v.y),
-                           __uint_as_float(yv.v.z), __uint_as_float(yv.v.w));
-    y.x = y.x + scale * d[0]; y.y = y.y + scale * d[1];
-    y.z = y.z + scale * d[2]; y.w = y.w + scale * d[3];
-    *(float4*)((float*)Y + off) = y;
-  } else {
-    uint2* p = (uint2*)((unsigned short*)Y + off);
-    uint2 u = make_uint2(yv.v.x, yv.v.y);
-    uint32_t h[4] = {u.x & 0xFFFFu, u.x >> 16, u.y & 0xFFFFu, u.y >> 16};
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float y = YT == SQ_BF16 ? bf16_bits_to_f32(h[j]) : f16_bits_to_f32(h[j]);
-      y = y + scale * d[j];
-      o[j] = YT == SQ_BF16 ? f32_to_bf16_bits(y) : f32_to_f16_bits(y);
-    }
-    u.x = o[0] | (o[1] << 16);
-    u.y = o[2] | (o[3] << 16);
-    *p = u;
-  }
-}
-
-// grid: (ceil(M / 16), ceil(N / (4 * 64 * chunks_per_wave))); 4 waves, each
-// owns the block's 16 rows and `chunks_per_wave` column chunks of 64.
-template <int YT, bool SEG>
+// Pipelined segmented shrink for 16-bit X: k_lora_shrink_pipe with one
+// adapter per request. A block of 4 waves covers 64 rows; its work is a list
+// of items, chunk by chunk, and within a chunk one item per request that
+// overlaps the block's rows and has an adapter. An item stages that
+// adapter's A[0:r, chunk] (r rounded up to 16; rows past r re-read row r - 1)
+// in one slot of the two-slot LDS ring. Each wave multiplies it only if the
+// request overlaps the wave's 16 rows, with the X of other requests' rows
+// zeroed, and only over the adapter's rank tiles, so every row gets exactly
+// its own adapter's product; ranks no item of its request reaches stay 0.
+// Per item: wait for this wave's loads and a barrier, then issue the next
+// item's staging (and, at a chunk's last item, the next chunk's X into the
+// other register set), then multiply. The item list depends only on the
+// block and the request tables, so every wave runs the same barriers.
+// grid: (ceil(M / 64), S); the block takes chunks blockIdx.y, + S, ...
+template <int XT, int KS, int NT>
 __global__ void __launch_bounds__(kLoraThreads)
-k_lora_expand(const unsigned short* __restrict__ T, int R, int M, int N, LoraArgs la, float scale,
-              void* __restrict__ Y, int64_t ldy, int chunks_per_wave) {
+k_lora_shrink_seg_pipe(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, LoraArgs la,
+                       int R, int S, float* __restrict__ P) {
+  extern __shared__ __attribute__((aligned(1024))) char lds_a[];   // 2 x (NT*16) x KC bf16
+  constexpr int KC = 32 * KS;
+  constexpr int CPR = KC / 8;
+  constexpr int RPI = 64 / CPR;
+  constexpr int ROWS = NT * 16;
+  constexpr int NA = ROWS / RPI / 4;
+  constexpr int SLOT = ROWS * KC * 2;
+  static_assert(ROWS % (RPI * 4) == 0, "staged rows must split over the 4 waves");
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int m0 = blockIdx.x * 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lrow = lane & 15, kg = lane >> 4;
-  const int my_m = m0 + lrow;
-  const int KS = (R + 31) / 32;        // rank steps of 32
+  const int nchunks = (K + KC - 1) / KC;
+  const int b0 = blockIdx.x * 64;
+  const int w0 = b0 + wave * 16;
+  const int my_m = w0 + lrow;
+  const char* xrow = X + (int64_t)(my_m < M ? my_m : M - 1) * ldx_bytes;
 
-  // T operand: T[my_m, ks*32 + kg*8 .. +8] (T [M, R] bf16, reduced once from
-  // the shrink's partial sums by k_lora_reduce).
-  uint4 tu[kMaxRankSteps];
-#pragma unroll
-  for (int ks = 0; ks < kMaxRankSteps; ++ks) {
-    const int k = ks * 32 + kg * 8;
-    tu[ks] = (ks < KS && k < R && my_m < M) ? *(const uint4*)(T + (int64_t)my_m * R + k)
-                                            : make_uint4(0, 0, 0, 0);
+  // Requests g0..g1 overlap rows [b0, min(b0 + 64, M)).
+  const int g0 = find_segment(la.seg_start, la.nseg, b0);
+  int g1 = g0;
+  {
+    const int bend = b0 + 64 < M ? b0 + 64 : M;
+    while (g1 + 1 < la.nseg && la.seg_start[g1 + 1] < bend) ++g1;
   }
+  auto next_active = [&](int g) {
+    while (g <= g1 && (la.seg_adapter[g] < 0 || la.seg_start[g] >= la.seg_start[g + 1])) ++g;
+    return g;
+  };
+  const int gfirst = next_active(g0);
 
-  int g0 = 0, g1 = 0;
-  bool row_has_adapter = !SEG;
-  if constexpr (SEG) {
-    g0 = find_segment(la.seg_start, la.nseg, m0 < M ? m0 : M - 1);
-    g1 = g0;
-    const int mend = m0 + 16 < M ? m0 + 16 : M;
-    while (g1 + 1 < la.nseg && la.seg_start[g1 + 1] < mend) ++g1;
-    for (int g = g0; g <= g1; ++g)
-      if (la.seg_adapter[g] >= 0 && my_m >= la.seg_start[g] && my_m < la.seg_start[g + 1])
-        row_has_adapter = true;
-  }
-
-  const int n_chunks = (N + 63) / 64;
-  const int cbase = (blockIdx.y * 4 + wave) * chunks_per_wave;
-  // The Y values of the next chunk load while this chunk multiplies, so the
-  // read of the read-modify-write is off the critical path.
-  Y4<YT> ycur[4], ynext[4];
-  auto load_chunk_y = [&](int chunk, Y4<YT> (&yv)[4]) {
+  auto stage = [&](int g, int c, int slot) {
+    const int ad = la.seg_adapter[g];
+    const int ra = la.ranks[ad];
+    const int rows_g = (ra + 15) & ~15;
+    const unsigned short* Ag = (const unsigned short*)la.A_ptrs[ad];
+    const int kc0 = c * KC;
+    char* dst = lds_a + slot * SLOT;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int n = chunk * 64 + t * 16 + kg * 4;
-      if (my_m < M && n < N) yv[t] = load_y4<YT>(Y, (int64_t)my_m * ldy + n);
+    for (int q = 0; q < NA; ++q) {
+      const int j = wave + 4 * q;
+      if (j * RPI < rows_g) {
+        const int i = j * RPI + lane / CPR;
+        const int isrc = i < ra ? i : ra - 1;
+        const int kk = kc0 + ((lane % CPR) ^ (i & 15)) * 8;
+        const int ksrc = kk < K ? kk : K - 8;
+        __builtin_amdgcn_global_load_lds((const void*)(Ag + (int64_t)isrc * K + ksrc),
+                                         (lds_ptr_t)(dst + 1024 * j), 16, 0, 0);
+      }
     }
   };
-  if (cbase < n_chunks) load_chunk_y(cbase, ycur);
-  for (int cc = 0; cc < chunks_per_wave; ++cc) {
-    const int chunk = cbase + cc;
-    if (chunk >= n_chunks) break;
-    if (cc + 1 < chunks_per_wave && chunk + 1 < n_chunks) load_chunk_y(chunk + 1, ynext);
-    const int nb = chunk * 64;
-    v4f acc[4];
+  auto load_x = [&](int c, uint4 (&xu)[KS]) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = v4f{0, 0, 0, 0};
+    for (int u = 0; u < KS; ++u) {
+      const int kk = c * KC + u * 32 + kg * 8;
+      const int ksrc = kk < K ? kk : K - 8;
+      xu[u] = *(const uint4*)(xrow + (int64_t)ksrc * 2);
+    }
+  };
 
-    auto accumulate = [&](const unsigned short* Bm, int r, const uint4* tsel) {
+  v4f acc[NT];
 #pragma unroll
-      for (int ks = 0; ks < kMaxRankSteps; ++ks) {
-        if (ks < KS) {
-          const int k = ks * 32 + kg * 8;
-          const v8bf tf = bits_to_v8bf(tsel[ks]);
+  for (int t = 0; t < NT; ++t) acc[t] = v4f{0, 0, 0, 0};
+
+  auto multiply = [&](int c, int slot, const uint4 (&xu)[KS], int g) {
+    const int s0 = la.seg_start[g], s1 = la.seg_start[g + 1];
+    if (s0 >= w0 + 16 || s1 <= w0) return;   // no row of this wave is in request g
+    const int ntg = (la.ranks[la.seg_adapter[g]] + 15) >> 4;
+    const bool mine = my_m >= s0 && my_m < s1;
+    const int kc0 = c * KC;
+    const char* sa = lds_a + slot * SLOT;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int n = nb + t * 16 + lrow;
-            uint4 bu = make_uint4(0, 0, 0, 0);
-            if (n < N && k < r) bu = *(const uint4*)(Bm + (int64_t)n * r + k);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_v8bf(bu), tf, acc[t], 0, 0, 0);
-          }
+    for (int u = 0; u < KS; ++u) {
+      const int sl = u * 4 + kg;
+      const uint4 xv = (mine && kc0 + sl * 8 < K) ? raw16_as_bf16<XT>(xu[u]) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t < ntg) {
+          const int i = t * 16 + lrow;
+          const uint4 au = *(const uint4*)(sa + i * (KC * 2) + ((sl ^ (i & 15)) << 4));
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_v8bf(au), bits_to_v8bf(xv), acc[t],
+                                                           0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // The items of chunk c: its X is in `cur`; at its last item the next
+  // chunk's X goes into `nxt`. `slot` alternates per item.
+  int slot = 0;
+  auto run_chunk = [&](int c, const uint4 (&cur)[KS], uint4 (&nxt)[KS]) {
+    for (int g = gfirst; g <= g1;) {
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+      __syncthreads();
+      const int gn = next_active(g + 1);
+      if (gn <= g1) {
+        stage(gn, c, slot ^ 1);
+      } else if (c + S < nchunks) {
+        stage(gfirst, c + S, slot ^ 1);
+        load_x(c + S, nxt);
+      }
+      multiply(c, slot, cur, g);
+      slot ^= 1;
+      g = gn;
+    }
+  };
+
+  if (gfirst <= g1) {
+    uint4 xa[KS], xb[KS];
+    int c = blockIdx.y;
+    if (c < nchunks) {
+      stage(gfirst, c, 0);
+      load_x(c, xa);
+    }
+#pragma unroll 1
+    for (; c < nchunks; c += 2 * S) {
+      run_chunk(c, xa, xb);
+      if (c + S >= nchunks) break;
+      run_chunk(c + S, xb, xa);
+    }
+  }
+
+  // Register j of rank tile t: rank 16 t + 4 (lane / 16) + j, row lane % 16.
+  float* Ps = P + (int64_t)blockIdx.y * M * R;
+  if (my_m < M) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int i = t * 16 + kg * 4;
+      if (i < R)
+        *(float4*)(Ps + (int64_t)my_m * R + i) =
+            make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+    }
+  }
+}
+
+// Expand over 64 x 256 output tiles, with the product passed through LDS so
+// that the read-modify-write of Y is coalesced. grid: (ceil(M / 64),
+// ceil(N / 256)); 4 waves.
+//   1. Every thread issues its loads of the Y tile first: 16 bytes per lane,
+//      consecutive lanes along a row (a row of the tile is 512 bytes of
+//      16-bit Y or 1024 of fp32).
+//   2. Wave w computes D = T[rows] . B[cols 64 w .. 64 w + 63]^T for all 64
+//      rows (4 x 4 tiles of 16 x 16), so every B fragment it loads serves 64
+//      rows. With segments it does so once per request that overlaps the
+//      block and has an adapter, with the T rows of other requests zeroed and
+//      only the row tiles that hold rows of the request.
+//   3. D goes to LDS as fp32 (float4 slot c of row i stored at c ^ (i & 15):
+//      the 16 rows of an MFMA tile land on all 64 banks); after a barrier each
+//      thread reads the D values of its Y elements and writes
+//      out(fp32(y) + scale * d). Rows without an adapter are not written.
+// KSM: rank steps of 32 the template holds (R <= 32 * KSM).
+template <int YT, bool SEG, int KSM>
+__global__ void __launch_bounds__(kLoraThreads, 2)
+k_lora_expand(const unsigned short* __restrict__ T, int R, int M, int N, LoraArgs la, float scale,
+                   void* __restrict__ Y, int64_t ldy) {
+  constexpr int BM = 64, BN = 256;
+  __shared__ __attribute__((aligned(16))) float dl[BM * BN];   // 64 KB
+  constexpr int VPT = YT == SQ_F32 ? 4 : 8;   // Y values per 16-byte access
+  constexpr int TPR = BN / VPT;               // threads per tile row
+  constexpr int RPP = 256 / TPR;              // tile rows per pass
+  constexpr int NP = BM / RPP;                // passes
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane & 15, kg = lane >> 4;
+  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  const int pr = tid / TPR, pc = (tid % TPR) * VPT;
+  const bool col_ok = n0 + pc < N;
+
+  // 1. The Y tile, coalesced.
+  uint4 yv[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int m = m0 + p * RPP + pr;
+    yv[p] = make_uint4(0, 0, 0, 0);
+    if (m < M && col_ok) {
+      const int64_t off = (int64_t)m * ldy + n0 + pc;
+      yv[p] = YT == SQ_F32 ? *(const uint4*)((const float*)Y + off)
+                           : *(const uint4*)((const unsigned short*)Y + off);
+    }
+  }
+
+  // Requests g0..g1 overlap the block's rows.
+  int g0 = 0, g1 = 0;
+  if constexpr (SEG) {
+    g0 = find_segment(la.seg_start, la.nseg, m0);
+    g1 = g0;
+    const int mend = m0 + BM < M ? m0 + BM : M;
+    while (g1 + 1 < la.nseg && la.seg_start[g1 + 1] < mend) ++g1;
+  }
+
+  // 2. D for rows m0 .. m0 + 63, columns nw .. nw + 63.
+  const int nw = n0 + 64 * wave;
+  const int KS = (R + 31) >> 5;
+  v4f acc[4][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[rt][t] = v4f{0, 0, 0, 0};
+  if (nw < N) {
+    // The product of one adapter (B [N, r]) for the rows in [s0, s1), one
+    // rank step of 32 at a time: its 4 B and 4 T fragments, then 16 MFMAs.
+    auto accumulate = [&](const unsigned short* Bm, int r, int s0, int s1) {
+#pragma unroll
+      for (int ks = 0; ks < KSM; ++ks) {
+        if (ks >= KS) break;
+        const int k = ks * 32 + kg * 8;
+        uint4 bu[4], tu[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int n = nw + t * 16 + lrow;
+          bu[t] = (k < r && n < N) ? *(const uint4*)(Bm + (int64_t)n * r + k) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const int m = m0 + rt * 16 + lrow;
+          const bool mine = m < M && (!SEG || (m >= s0 && m < s1));
+          tu[rt] = (mine && k < R) ? *(const uint4*)(T + (int64_t)m * R + k) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const int r0 = m0 + rt * 16;
+          if (SEG && (s0 >= r0 + 16 || s1 <= r0)) continue;   // no row of this tile in the request
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_v8bf(bu[t]), bits_to_v8bf(tu[rt]),
+                                                                 acc[rt][t], 0, 0, 0);
         }
       }
     };
     if constexpr (!SEG) {
-      accumulate(la.B, la.r, tu);
+      accumulate(la.B, la.r, 0, M);
     } else {
       for (int g = g0; g <= g1; ++g) {
         const int ad = la.seg_adapter[g];
-        if (ad < 0) continue;
-        const bool mine = my_m >= la.seg_start[g] && my_m < la.seg_start[g + 1];
-        uint4 ts[kMaxRankSteps];
-#pragma unroll
-        for (int ks = 0; ks < kMaxRankSteps; ++ks) ts[ks] = mine ? tu[ks] : make_uint4(0, 0, 0, 0);
-        accumulate((const unsigned short*)la.B_ptrs[ad], la.ranks[ad], ts);
+        const int s0 = la.seg_start[g], s1 = la.seg_start[g + 1];
+        if (ad < 0 || s0 >= s1) continue;
+        accumulate((const unsigned short*)la.B_ptrs[ad], la.ranks[ad], s0, s1);
       }
     }
+  }
 
-    // Transposed product: register j of tile t holds column nb + 16t + 4*kg + j,
-    // row my_m.
-    if (my_m < M && row_has_adapter) {
+  // 3. Register j of tile (rt, t): row 16 rt + lane % 16, column 64 w + 16 t + 4 kg + j.
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int n = nb + t * 16 + kg * 4;
-        if (n < N) rmw4_from<YT>(Y, (int64_t)my_m * ldy + n, ycur[t], scale, acc[t]);
-      }
+  for (int rt = 0; rt < 4; ++rt) {
+    const int i = rt * 16 + lrow;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c4 = 16 * wave + 4 * t + kg;
+      *(float4*)(dl + i * BN + ((c4 ^ (i & 15)) << 2)) =
+          make_float4(acc[rt][t][0], acc[rt][t][1], acc[rt][t][2], acc[rt][t][3]);
     }
+  }
+  __syncthreads();
+
 #pragma unroll
-    for (int t = 0; t < 4; ++t) ycur[t] = ynext[t];
+  for (int p = 0; p < NP; ++p) {
+    const int i = p * RPP + pr;
+    const int m = m0 + i;
+    if (m >= M || !col_ok) continue;
+    if constexpr (SEG) {
+      bool has = false;
+      for (int g = g0; g <= g1; ++g)
+        has |= la.seg_adapter[g] >= 0 && m >= la.seg_start[g] && m < la.seg_start[g + 1];
+      if (!has) continue;
+    }
+    const int64_t off = (int64_t)m * ldy + n0 + pc;
+    const int c4 = pc >> 2;
+    const float4 d0 = *(const float4*)(dl + i * BN + ((c4 ^ (i & 15)) << 2));
+    if constexpr (YT == SQ_F32) {
+      float4 y = make_float4(__uint_as_float(yv[p].x), __uint_as_float(yv[p].y),
+                             __uint_as_float(yv[p].z), __uint_as_float(yv[p].w));
+      y.x = y.x + scale * d0.x; y.y = y.y + scale * d0.y;
+      y.z = y.z + scale * d0.z; y.w = y.w + scale * d0.w;
+      *(float4*)((float*)Y + off) = y;
+    } else {
+      const float4 d1 = *(const float4*)(dl + i * BN + (((c4 + 1) ^ (i & 15)) << 2));
+      const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      const uint32_t w[4] = {yv[p].x, yv[p].y, yv[p].z, yv[p].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t h[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t b = e ? w[q] >> 16 : w[q] & 0xFFFFu;
+          float y = YT == SQ_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+          y = y + scale * d[2 * q + e];
+          h[e] = YT == SQ_BF16 ? f32_to_bf16_bits(y) : f32_to_f16_bits(y);
+        }
+        o[q] = h[0] | (h[1] << 16);
+      }
+      *(uint4*)((unsigned short*)Y + off) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
   }
 }
 
@@ -721,6 +891,20 @@ static int launch_shrink_p(const void* X, int64_t M, int64_t K, int64_t ldx, con
 template <int XT>
 static int launch_shrink_seg_p(const void* X, int64_t M, int64_t K, int64_t ldx, const LoraArgs& la,
                                int R, float* P, hipStream_t st) {
+  if constexpr (XT != SQ_F32) {
+    const ShrinkPlan p = plan_shrink_pipe(M, K, R);
+    const dim3 grid((unsigned)p.blocks_m, (unsigned)p.S);
+    const size_t lds = 2 * (size_t)p.nt * 16 * 32 * p.ks * 2;
+    const char* x = (const char*)X;
+    const int64_t ldb = ldx * DtSize<XT>::v;
+    switch (p.nt) {
+      case 1: k_lora_shrink_seg_pipe<XT, 8, 1><<<grid, kLoraThreads, lds, st>>>(x, ldb, (int)M, (int)K, la, R, p.S, P); break;
+      case 2: k_lora_shrink_seg_pipe<XT, 8, 2><<<grid, kLoraThreads, lds, st>>>(x, ldb, (int)M, (int)K, la, R, p.S, P); break;
+      case 4: k_lora_shrink_seg_pipe<XT, 8, 4><<<grid, kLoraThreads, lds, st>>>(x, ldb, (int)M, (int)K, la, R, p.S, P); break;
+      default: k_lora_shrink_seg_pipe<XT, 4, 8><<<grid, kLoraThreads, lds, st>>>(x, ldb, (int)M, (int)K, la, R, p.S, P); break;
+    }
+    return p.S;
+  }
   int S, kc;
   seg_split(M, K, &S, &kc);
   dim3 g1((unsigned)((M + 63) / 64), (unsigned)S);
@@ -742,13 +926,13 @@ static int launch_lora_t(const void* X, int64_t M, int64_t K, int64_t ldx, const
   const int64_t rthreads = M * (R / 4);
   k_lora_reduce<<<(unsigned)((rthreads + 63) / 64), 64, 0, st>>>(P, S, R, (int)M, Tw, R);
   SQ_LAUNCH_CHECK();
-  const int64_t m_tiles = (M + 15) / 16;
-  const int64_t n_chunks = (N + 63) / 64;
-  int64_t cpw = (m_tiles * n_chunks + 8191) / 8192;   // aim for ~8192 waves
-  if (cpw < 1) cpw = 1;
-  dim3 g2((unsigned)m_tiles, (unsigned)((n_chunks + 4 * cpw - 1) / (4 * cpw)));
-  k_lora_expand<YT, SEG><<<g2, kLoraThreads, 0, st>>>(Tw, R, (int)M, (int)N, la, scale, Y, ldy,
-                                                      (int)cpw);
+  const dim3 g2((unsigned)((M + 63) / 64), (unsigned)((N + 255) / 256));
+  if (R <= 32)
+    k_lora_expand<YT, SEG, 1><<<g2, kLoraThreads, 0, st>>>(Tw, R, (int)M, (int)N, la, scale, Y, ldy);
+  else if (R <= 64)
+    k_lora_expand<YT, SEG, 2><<<g2, kLoraThreads, 0, st>>>(Tw, R, (int)M, (int)N, la, scale, Y, ldy);
+  else
+    k_lora_expand<YT, SEG, 4><<<g2, kLoraThreads, 0, st>>>(Tw, R, (int)M, (int)N, la, scale, Y, ldy);
   SQ_LAUNCH_CHECK();
   return SQ_OK;
 }
