@@ -419,20 +419,61 @@ k_lora_shrink_seg(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, L
   }
 }
 
+// Block b of a segmented launch takes the b-th (request, 64-row tile) pair,
+// counting, in request order, ceil(len / 64) tiles for every non-empty
+// request with an adapter. The block's 256 threads scan the request table
+// 256 requests at a time (wave prefix sums with lane shifts, then the four
+// wave totals). Returns false (for the whole block) when b is past the last
+// tile. Contains barriers: call it from block-uniform control flow only.
+__device__ bool seg_tile_of_block(const LoraArgs& la, int b, int* g_out, int* tile_out) {
+  __shared__ int s_wsum[4];
+  __shared__ int s_hit[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_hit[0] = -1;
+  int base = 0;
+  for (int c0 = 0; c0 < la.nseg; c0 += 256) {
+    const int g = c0 + tid;
+    int tiles = 0;
+    if (g < la.nseg && la.seg_adapter[g] >= 0) {
+      const int len = la.seg_start[g + 1] - la.seg_start[g];
+      tiles = len > 0 ? (len + 63) >> 6 : 0;
+    }
+    int incl = tiles;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int before = base;
+    for (int w = 0; w < wave; ++w) before += s_wsum[w];
+    const int total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+    const int excl = before + incl - tiles;
+    if (tiles > 0 && b >= excl && b < excl + tiles) {
+      s_hit[0] = g;
+      s_hit[1] = b - excl;
+    }
+    base += total;
+    __syncthreads();   // s_wsum is rewritten by the next round; s_hit is complete
+    if (base > b) break;
+  }
+  const int g = s_hit[0];
+  *g_out = g;
+  *tile_out = s_hit[1];
+  return g >= 0;
+}
+
 // Pipelined segmented shrink for 16-bit X: k_lora_shrink_pipe with one
-// adapter per request. A block of 4 waves covers 64 rows; its work is a list
-// of items, chunk by chunk, and within a chunk one item per request that
-// overlaps the block's rows and has an adapter. An item stages that
-// adapter's A[0:r, chunk] (r rounded up to 16; rows past r re-read row r - 1)
-// in one slot of the two-slot LDS ring. Each wave multiplies it only if the
-// request overlaps the wave's 16 rows, with the X of other requests' rows
-// zeroed, and only over the adapter's rank tiles, so every row gets exactly
-// its own adapter's product; ranks no item of its request reaches stay 0.
-// Per item: wait for this wave's loads and a barrier, then issue the next
-// item's staging (and, at a chunk's last item, the next chunk's X into the
-// other register set), then multiply. The item list depends only on the
-// block and the request tables, so every wave runs the same barriers.
-// grid: (ceil(M / 64), S); the block takes chunks blockIdx.y, + S, ...
+// adapter per block. Block (b, s) takes the b-th (request, 64-row tile) pair
+// (seg_tile_of_block), so every row of the block uses one adapter: its
+// A[0:r, chunk] is staged in the two-slot LDS ring (r rounded up to 16; rows
+// past r re-read row r - 1) and multiplied over the adapter's rank tiles
+// only (ranks beyond them stay 0). Rows past the request's end read its last
+// row and are not stored. The K slices, the chunk order and the arithmetic
+// per row are those of k_lora_shrink_pipe for the same S, so a single
+// adapter over all rows gives the same partial sums bit for bit.
+// grid: (ceil(M / 64) + requests, S); blocks past the last tile exit.
 template <int XT, int KS, int NT>
 __global__ void __launch_bounds__(kLoraThreads)
 k_lora_shrink_seg_pipe(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, LoraArgs la,
@@ -445,39 +486,29 @@ k_lora_shrink_seg_pipe(const char* __restrict__ X, int64_t ldx_bytes, int M, int
   constexpr int NA = ROWS / RPI / 4;
   constexpr int SLOT = ROWS * KC * 2;
   static_assert(ROWS % (RPI * 4) == 0, "staged rows must split over the 4 waves");
+  int g, tile;
+  if (!seg_tile_of_block(la, blockIdx.x, &g, &tile)) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lrow = lane & 15, kg = lane >> 4;
   const int nchunks = (K + KC - 1) / KC;
-  const int b0 = blockIdx.x * 64;
-  const int w0 = b0 + wave * 16;
+  const int s_end = la.seg_start[g + 1];
+  const int w0 = la.seg_start[g] + tile * 64 + wave * 16;
   const int my_m = w0 + lrow;
-  const char* xrow = X + (int64_t)(my_m < M ? my_m : M - 1) * ldx_bytes;
+  const bool wave_rows = w0 < s_end;   // the wave holds rows of the request
+  const char* xrow = X + (int64_t)(my_m < s_end ? my_m : s_end - 1) * ldx_bytes;
+  const int ad = la.seg_adapter[g];
+  const int ra = la.ranks[ad];
+  const int ntg = (ra + 15) >> 4;
+  const unsigned short* Ag = (const unsigned short*)la.A_ptrs[ad];
 
-  // Requests g0..g1 overlap rows [b0, min(b0 + 64, M)).
-  const int g0 = find_segment(la.seg_start, la.nseg, b0);
-  int g1 = g0;
-  {
-    const int bend = b0 + 64 < M ? b0 + 64 : M;
-    while (g1 + 1 < la.nseg && la.seg_start[g1 + 1] < bend) ++g1;
-  }
-  auto next_active = [&](int g) {
-    while (g <= g1 && (la.seg_adapter[g] < 0 || la.seg_start[g] >= la.seg_start[g + 1])) ++g;
-    return g;
-  };
-  const int gfirst = next_active(g0);
-
-  auto stage = [&](int g, int c, int slot) {
-    const int ad = la.seg_adapter[g];
-    const int ra = la.ranks[ad];
-    const int rows_g = (ra + 15) & ~15;
-    const unsigned short* Ag = (const unsigned short*)la.A_ptrs[ad];
+  auto stage = [&](int c, int slot) {
     const int kc0 = c * KC;
     char* dst = lds_a + slot * SLOT;
 #pragma unroll
     for (int q = 0; q < NA; ++q) {
       const int j = wave + 4 * q;
-      if (j * RPI < rows_g) {
+      if (j * RPI < ntg * 16) {
         const int i = j * RPI + lane / CPR;
         const int isrc = i < ra ? i : ra - 1;
         const int kk = kc0 + ((lane % CPR) ^ (i & 15)) * 8;
@@ -500,17 +531,14 @@ k_lora_shrink_seg_pipe(const char* __restrict__ X, int64_t ldx_bytes, int M, int
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = v4f{0, 0, 0, 0};
 
-  auto multiply = [&](int c, int slot, const uint4 (&xu)[KS], int g) {
-    const int s0 = la.seg_start[g], s1 = la.seg_start[g + 1];
-    if (s0 >= w0 + 16 || s1 <= w0) return;   // no row of this wave is in request g
-    const int ntg = (la.ranks[la.seg_adapter[g]] + 15) >> 4;
-    const bool mine = my_m >= s0 && my_m < s1;
+  auto multiply = [&](int c, int slot, const uint4 (&xu)[KS]) {
+    if (!wave_rows) return;
     const int kc0 = c * KC;
     const char* sa = lds_a + slot * SLOT;
 #pragma unroll
     for (int u = 0; u < KS; ++u) {
       const int sl = u * 4 + kg;
-      const uint4 xv = (mine && kc0 + sl * 8 < K) ? raw16_as_bf16<XT>(xu[u]) : make_uint4(0, 0, 0, 0);
+      const uint4 xv = kc0 + sl * 8 < K ? raw16_as_bf16<XT>(xu[u]) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if (t < ntg) {
@@ -523,44 +551,32 @@ k_lora_shrink_seg_pipe(const char* __restrict__ X, int64_t ldx_bytes, int M, int
     }
   };
 
-  // The items of chunk c: its X is in `cur`; at its last item the next
-  // chunk's X goes into `nxt`. `slot` alternates per item.
-  int slot = 0;
-  auto run_chunk = [&](int c, const uint4 (&cur)[KS], uint4 (&nxt)[KS]) {
-    for (int g = gfirst; g <= g1;) {
-      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-      __syncthreads();
-      const int gn = next_active(g + 1);
-      if (gn <= g1) {
-        stage(gn, c, slot ^ 1);
-      } else if (c + S < nchunks) {
-        stage(gfirst, c + S, slot ^ 1);
-        load_x(c + S, nxt);
-      }
-      multiply(c, slot, cur, g);
-      slot ^= 1;
-      g = gn;
+  auto step = [&](int c, int slot, const uint4 (&cur)[KS], uint4 (&nxt)[KS]) {
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    __syncthreads();
+    if (c + S < nchunks) {
+      stage(c + S, slot ^ 1);
+      load_x(c + S, nxt);
     }
+    multiply(c, slot, cur);
   };
 
-  if (gfirst <= g1) {
-    uint4 xa[KS], xb[KS];
-    int c = blockIdx.y;
-    if (c < nchunks) {
-      stage(gfirst, c, 0);
-      load_x(c, xa);
-    }
+  uint4 xa[KS], xb[KS];
+  int c = blockIdx.y;
+  if (c < nchunks) {
+    stage(c, 0);
+    load_x(c, xa);
+  }
 #pragma unroll 1
-    for (; c < nchunks; c += 2 * S) {
-      run_chunk(c, xa, xb);
-      if (c + S >= nchunks) break;
-      run_chunk(c + S, xb, xa);
-    }
+  for (; c < nchunks; c += 2 * S) {
+    step(c, 0, xa, xb);
+    if (c + S >= nchunks) break;
+    step(c + S, 1, xb, xa);
   }
 
   // Register j of rank tile t: rank 16 t + 4 (lane / 16) + j, row lane % 16.
   float* Ps = P + (int64_t)blockIdx.y * M * R;
-  if (my_m < M) {
+  if (my_m < s_end) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int i = t * 16 + kg * 4;
@@ -892,8 +908,10 @@ template <int XT>
 static int launch_shrink_seg_p(const void* X, int64_t M, int64_t K, int64_t ldx, const LoraArgs& la,
                                int R, float* P, hipStream_t st) {
   if constexpr (XT != SQ_F32) {
+    // the single-adapter plan's slices; one block per (request, 64-row tile)
     const ShrinkPlan p = plan_shrink_pipe(M, K, R);
-    const dim3 grid((unsigned)p.blocks_m, (unsigned)p.S);
+    const int64_t tiles_max = (M + 63) / 64 + (la.nseg < M ? la.nseg : M);
+    const dim3 grid((unsigned)tiles_max, (unsigned)p.S);
     const size_t lds = 2 * (size_t)p.nt * 16 * 32 * p.ks * 2;
     const char* x = (const char*)X;
     const int64_t ldb = ldx * DtSize<XT>::v;
