@@ -469,7 +469,7 @@ __device__ bool seg_tile_of_block(const LoraArgs& la, int b, int* g_out, int* ti
 // (seg_tile_of_block), so every row of the block uses one adapter: its
 // A[0:r, chunk] is staged in the two-slot LDS ring (r rounded up to 16; rows
 // past r re-read row r - 1) and multiplied over the adapter's rank tiles
-// only (ranks beyond them stay 0). Rows past the request's end read its last
+// only; ranks r .. R - 1 of the partial sums are stored as 0. Rows past the request's end read its last
 // row and are not stored. The K slices, the chunk order and the arithmetic
 // per row are those of k_lora_shrink_pipe for the same S, so a single
 // adapter over all rows gives the same partial sums bit for bit.
@@ -575,6 +575,8 @@ k_lora_shrink_seg_pipe(const char* __restrict__ X, int64_t ldx_bytes, int M, int
   }
 
   // Register j of rank tile t: rank 16 t + 4 (lane / 16) + j, row lane % 16.
+  // Ranks from the adapter's r up to R are stored as 0 (r is a multiple of 8,
+  // so a group of 4 is wholly in or out).
   float* Ps = P + (int64_t)blockIdx.y * M * R;
   if (my_m < s_end) {
 #pragma unroll
@@ -582,31 +584,32 @@ k_lora_shrink_seg_pipe(const char* __restrict__ X, int64_t ldx_bytes, int M, int
       const int i = t * 16 + kg * 4;
       if (i < R)
         *(float4*)(Ps + (int64_t)my_m * R + i) =
-            make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+            i < ra ? make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
 }
 
 // Expand over 64 x 256 output tiles, with the product passed through LDS so
-// that the read-modify-write of Y is coalesced. grid: (ceil(M / 64),
-// ceil(N / 256)); 4 waves.
+// that the read-modify-write of Y is coalesced. 4 waves.
 //   1. Every thread issues its loads of the Y tile first: 16 bytes per lane,
 //      consecutive lanes along a row (a row of the tile is 512 bytes of
 //      16-bit Y or 1024 of fp32).
 //   2. Wave w computes D = T[rows] . B[cols 64 w .. 64 w + 63]^T for all 64
 //      rows (4 x 4 tiles of 16 x 16), so every B fragment it loads serves 64
-//      rows. With segments it does so once per request that overlaps the
-//      block and has an adapter, with the T rows of other requests zeroed and
-//      only the row tiles that hold rows of the request.
+//      rows. With segments, block x takes the x-th (request, 64-row tile)
+//      pair (seg_tile_of_block): all its rows use one adapter, and rows past
+//      the request's end are neither read nor written.
 //   3. D goes to LDS as fp32 (float4 slot c of row i stored at c ^ (i & 15):
 //      the 16 rows of an MFMA tile land on all 64 banks); after a barrier each
 //      thread reads the D values of its Y elements and writes
 //      out(fp32(y) + scale * d). Rows without an adapter are not written.
-// KSM: rank steps of 32 the template holds (R <= 32 * KSM).
+// KSM: rank steps of 32, ceil(R / 32): T's rows hold 32 * KSM ranks, zero from R on.
+// grid: (ceil(M / 64), ceil(N / 256)); with segments ceil(M / 64) + min(requests, M)
+// row blocks, those past the last (request, tile) pair exiting at once.
 template <int YT, bool SEG, int KSM>
 __global__ void __launch_bounds__(kLoraThreads, 2)
-k_lora_expand(const unsigned short* __restrict__ T, int R, int M, int N, LoraArgs la, float scale,
-                   void* __restrict__ Y, int64_t ldy) {
+k_lora_expand(const unsigned short* __restrict__ T, int M, int N, LoraArgs la, float scale,
+              void* __restrict__ Y, int64_t ldy) {
   constexpr int BM = 64, BN = 256;
   __shared__ __attribute__((aligned(16))) float dl[BM * BN];   // 64 KB
   constexpr int VPT = YT == SQ_F32 ? 4 : 8;   // Y values per 16-byte access
@@ -617,82 +620,91 @@ k_lora_expand(const unsigned short* __restrict__ T, int R, int M, int N, LoraArg
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 15, kg = lane >> 4;
-  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+
+  // The block's rows [m0, mend) and their adapter.
+  int m0, mend, r;
+  const unsigned short* Bm;
+  if constexpr (SEG) {
+    int g, tile;
+    if (!seg_tile_of_block(la, blockIdx.x, &g, &tile)) return;
+    m0 = la.seg_start[g] + tile * BM;
+    const int s1 = la.seg_start[g + 1];
+    mend = m0 + BM < s1 ? m0 + BM : s1;
+    const int ad = la.seg_adapter[g];
+    Bm = (const unsigned short*)la.B_ptrs[ad];
+    r = la.ranks[ad];
+  } else {
+    m0 = blockIdx.x * BM;
+    mend = m0 + BM < M ? m0 + BM : M;
+    Bm = la.B;
+    r = la.r;
+  }
+  const int n0 = blockIdx.y * BN;
   const int pr = tid / TPR, pc = (tid % TPR) * VPT;
   const bool col_ok = n0 + pc < N;
+
+  // Every load below is unconditional, with out-of-range addresses clamped to
+  // valid ones, and no value needs masking: T rows are zero from the
+  // adapter's rank up to Rp (its B columns past r, clamped, meet zeros),
+  // clamped T rows stay inside the block's request (finite values whose D
+  // rows are not stored), and D columns past N are not stored either.
+  // (A select between a loaded value and 0, or a load skipped by a branch,
+  // would end in a wait for all loads in flight, the Y tile's included.)
+  const int nw = n0 + 64 * wave;   // this wave's 64 columns of the tile
+  constexpr int Rp = 32 * KSM;     // T's row stride (R rounded up to 32)
+  // The B and T fragments of rank step ks: B rows nw + 16 t + lane % 16,
+  // T rows m0 + 16 rt + lane % 16, ranks 32 ks + 8 (lane / 16) .. + 7.
+  auto load_bt = [&](int ks, uint4 (&bu)[4], uint4 (&tu)[4]) {
+    const int k = ks * 32 + kg * 8;
+    const int kb = k < r ? k : r - 8;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int n = nw + t * 16 + lrow;
+      bu[t] = *(const uint4*)(Bm + (int64_t)(n < N ? n : N - 1) * r + kb);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int m = m0 + rt * 16 + lrow;
+      tu[rt] = *(const uint4*)(T + (int64_t)(m < mend ? m : mend - 1) * Rp + k);
+    }
+  };
+  // The fragments of the first PRE rank steps load before the Y tile (the
+  // scheduling barrier keeps that order), so the MFMAs wait only for them
+  // and the Y loads stay in flight through the product.
+  constexpr int PRE = YT == SQ_F32 && KSM > 2 ? 2 : KSM;
+  uint4 bf[KSM][4], tf[KSM][4];
+#pragma unroll
+  for (int ks = 0; ks < PRE; ++ks) load_bt(ks, bf[ks], tf[ks]);
+  __builtin_amdgcn_sched_barrier(0);
 
   // 1. The Y tile, coalesced.
   uint4 yv[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int m = m0 + p * RPP + pr;
-    yv[p] = make_uint4(0, 0, 0, 0);
-    if (m < M && col_ok) {
-      const int64_t off = (int64_t)m * ldy + n0 + pc;
-      yv[p] = YT == SQ_F32 ? *(const uint4*)((const float*)Y + off)
-                           : *(const uint4*)((const unsigned short*)Y + off);
-    }
+    const int64_t off = (int64_t)(m < mend ? m : m0) * ldy + (col_ok ? n0 + pc : n0);
+    yv[p] = YT == SQ_F32 ? *(const uint4*)((const float*)Y + off)
+                         : *(const uint4*)((const unsigned short*)Y + off);
   }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = PRE; ks < KSM; ++ks) load_bt(ks, bf[ks], tf[ks]);
 
-  // Requests g0..g1 overlap the block's rows.
-  int g0 = 0, g1 = 0;
-  if constexpr (SEG) {
-    g0 = find_segment(la.seg_start, la.nseg, m0);
-    g1 = g0;
-    const int mend = m0 + BM < M ? m0 + BM : M;
-    while (g1 + 1 < la.nseg && la.seg_start[g1 + 1] < mend) ++g1;
-  }
-
-  // 2. D for rows m0 .. m0 + 63, columns nw .. nw + 63.
-  const int nw = n0 + 64 * wave;
-  const int KS = (R + 31) >> 5;
+  // 2. D for rows m0 .. m0 + 63, columns nw .. nw + 63: per rank step 16
+  //    MFMAs (4 row tiles x 4 column tiles of 16 x 16).
   v4f acc[4][4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[rt][t] = v4f{0, 0, 0, 0};
-  if (nw < N) {
-    // The product of one adapter (B [N, r]) for the rows in [s0, s1), one
-    // rank step of 32 at a time: its 4 B and 4 T fragments, then 16 MFMAs.
-    auto accumulate = [&](const unsigned short* Bm, int r, int s0, int s1) {
 #pragma unroll
-      for (int ks = 0; ks < KSM; ++ks) {
-        if (ks >= KS) break;
-        const int k = ks * 32 + kg * 8;
-        uint4 bu[4], tu[4];
+  for (int ks = 0; ks < KSM; ++ks)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int n = nw + t * 16 + lrow;
-          bu[t] = (k < r && n < N) ? *(const uint4*)(Bm + (int64_t)n * r + k) : make_uint4(0, 0, 0, 0);
-        }
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const int m = m0 + rt * 16 + lrow;
-          const bool mine = m < M && (!SEG || (m >= s0 && m < s1));
-          tu[rt] = (mine && k < R) ? *(const uint4*)(T + (int64_t)m * R + k) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const int r0 = m0 + rt * 16;
-          if (SEG && (s0 >= r0 + 16 || s1 <= r0)) continue;   // no row of this tile in the request
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_v8bf(bu[t]), bits_to_v8bf(tu[rt]),
-                                                                 acc[rt][t], 0, 0, 0);
-        }
-      }
-    };
-    if constexpr (!SEG) {
-      accumulate(la.B, la.r, 0, M);
-    } else {
-      for (int g = g0; g <= g1; ++g) {
-        const int ad = la.seg_adapter[g];
-        const int s0 = la.seg_start[g], s1 = la.seg_start[g + 1];
-        if (ad < 0 || s0 >= s1) continue;
-        accumulate((const unsigned short*)la.B_ptrs[ad], la.ranks[ad], s0, s1);
-      }
-    }
-  }
+      for (int t = 0; t < 4; ++t)
+        acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_v8bf(bf[ks][t]), bits_to_v8bf(tf[ks][rt]),
+                                                             acc[rt][t], 0, 0, 0);
 
   // 3. Register j of tile (rt, t): row 16 rt + lane % 16, column 64 w + 16 t + 4 kg + j.
 #pragma unroll
@@ -711,13 +723,7 @@ k_lora_expand(const unsigned short* __restrict__ T, int R, int M, int N, LoraArg
   for (int p = 0; p < NP; ++p) {
     const int i = p * RPP + pr;
     const int m = m0 + i;
-    if (m >= M || !col_ok) continue;
-    if constexpr (SEG) {
-      bool has = false;
-      for (int g = g0; g <= g1; ++g)
-        has |= la.seg_adapter[g] >= 0 && m >= la.seg_start[g] && m < la.seg_start[g + 1];
-      if (!has) continue;
-    }
+    if (m >= mend || !col_ok) continue;
     const int64_t off = (int64_t)m * ldy + n0 + pc;
     const int c4 = pc >> 2;
     const float4 d0 = *(const float4*)(dl + i * BN + ((c4 ^ (i & 15)) << 2));
@@ -749,33 +755,36 @@ k_lora_expand(const unsigned short* __restrict__ T, int R, int M, int N, LoraArg
   }
 }
 
-// T[m, i] = bf16(sum_s P[s, m, i]) (fixed order of s) for the fused GEMM
-// epilogue. One thread per 4 consecutive ranks of one row, 64-thread blocks
+// T[m, i] = bf16(sum_s P[s, m, i]) (fixed order of s) for i < R, and 0 for
+// R <= i < RT (zero padding of T's rows up to a whole rank step of the
+// expand). One thread per 4 consecutive ranks of one row, 64-thread blocks
 // (enough blocks at small M). The loads of 8 slices are issued together; the
 // sums stay in slice order.
 __global__ void __launch_bounds__(64)
-k_lora_reduce(const float* __restrict__ P, int S, int R, int M, unsigned short* __restrict__ T,
+k_lora_reduce(const float* __restrict__ P, int S, int R, int RT, int M, unsigned short* __restrict__ T,
               int64_t ldt) {
   const int64_t id = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  const int per_row = R / 4;
+  const int per_row = RT / 4;
   if (id >= (int64_t)M * per_row) return;
   const int m = (int)(id / per_row), i = (int)(id % per_row) * 4;
-  const int64_t slice = (int64_t)M * R;
-  const float* p = P + (int64_t)m * R + i;
   float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-  int s = 0;
-  for (; s + 8 <= S; s += 8) {
-    float4 a[8];
+  if (i < R) {
+    const int64_t slice = (int64_t)M * R;
+    const float* p = P + (int64_t)m * R + i;
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
+      float4 a[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) a[u] = *(const float4*)(p + (s + u) * slice);
+      for (int u = 0; u < 8; ++u) a[u] = *(const float4*)(p + (s + u) * slice);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      t.x += a[u].x; t.y += a[u].y; t.z += a[u].z; t.w += a[u].w;
+      for (int u = 0; u < 8; ++u) {
+        t.x += a[u].x; t.y += a[u].y; t.z += a[u].z; t.w += a[u].w;
+      }
     }
-  }
-  for (; s < S; ++s) {
-    const float4 a = *(const float4*)(p + s * slice);
-    t.x += a.x; t.y += a.y; t.z += a.z; t.w += a.w;
+    for (; s < S; ++s) {
+      const float4 a = *(const float4*)(p + s * slice);
+      t.x += a.x; t.y += a.y; t.z += a.z; t.w += a.w;
+    }
   }
   uint2 u;
   u.x = f32_to_bf16_bits(t.x) | (f32_to_bf16_bits(t.y) << 16);
@@ -862,8 +871,10 @@ size_t lora_ws_bytes(int64_t M, int64_t K, int R) {
     const ShrinkPlan pp = plan_shrink_pipe(M, K, probe[q]);
     if (pp.S > smax) smax = pp.S;
   }
-  // fp32 partial sums of up to smax slices, then the reduced T [M, R] bf16
-  return (size_t)smax * (size_t)M * (size_t)R * sizeof(float) + (size_t)M * (size_t)R * 2;
+  // fp32 partial sums of up to smax slices, then the reduced T [M, Rp] bf16
+  // (rows zero-padded to Rp = 32 * ceil(R / 32) ranks)
+  const int64_t Rp = (R + 31) / 32 * 32;
+  return (size_t)smax * (size_t)M * (size_t)R * sizeof(float) + (size_t)M * (size_t)Rp * 2;
 }
 
 // Single-adapter shrink into P; returns the number of slices written.
@@ -940,17 +951,20 @@ static int launch_lora_t(const void* X, int64_t M, int64_t K, int64_t ldx, const
   SQ_LAUNCH_CHECK();
   // T = bf16(sum of the S partials) once, after the partials in the workspace;
   // the expand's waves then read it instead of each summing the partials again
+  // (rows padded with zeros to Rp = 32 * ceil(R / 32) ranks)
   unsigned short* Tw = (unsigned short*)((char*)ws + (size_t)S * (size_t)M * (size_t)R * sizeof(float));
-  const int64_t rthreads = M * (R / 4);
-  k_lora_reduce<<<(unsigned)((rthreads + 63) / 64), 64, 0, st>>>(P, S, R, (int)M, Tw, R);
+  const int Rp = (R + 31) / 32 * 32;
+  const int64_t rthreads = M * (Rp / 4);
+  k_lora_reduce<<<(unsigned)((rthreads + 63) / 64), 64, 0, st>>>(P, S, R, Rp, (int)M, Tw, Rp);
   SQ_LAUNCH_CHECK();
-  const dim3 g2((unsigned)((M + 63) / 64), (unsigned)((N + 255) / 256));
-  if (R <= 32)
-    k_lora_expand<YT, SEG, 1><<<g2, kLoraThreads, 0, st>>>(Tw, R, (int)M, (int)N, la, scale, Y, ldy);
-  else if (R <= 64)
-    k_lora_expand<YT, SEG, 2><<<g2, kLoraThreads, 0, st>>>(Tw, R, (int)M, (int)N, la, scale, Y, ldy);
-  else
-    k_lora_expand<YT, SEG, 4><<<g2, kLoraThreads, 0, st>>>(Tw, R, (int)M, (int)N, la, scale, Y, ldy);
+  const int64_t row_blocks = (M + 63) / 64 + (SEG ? (la.nseg < M ? la.nseg : M) : 0);
+  const dim3 g2((unsigned)row_blocks, (unsigned)((N + 255) / 256));
+  switch (Rp / 32) {
+    case 1: k_lora_expand<YT, SEG, 1><<<g2, kLoraThreads, 0, st>>>(Tw, (int)M, (int)N, la, scale, Y, ldy); break;
+    case 2: k_lora_expand<YT, SEG, 2><<<g2, kLoraThreads, 0, st>>>(Tw, (int)M, (int)N, la, scale, Y, ldy); break;
+    case 3: k_lora_expand<YT, SEG, 3><<<g2, kLoraThreads, 0, st>>>(Tw, (int)M, (int)N, la, scale, Y, ldy); break;
+    default: k_lora_expand<YT, SEG, 4><<<g2, kLoraThreads, 0, st>>>(Tw, (int)M, (int)N, la, scale, Y, ldy); break;
+  }
   SQ_LAUNCH_CHECK();
   return SQ_OK;
 }
@@ -980,7 +994,7 @@ static int launch_shrink_t(const void* X, int64_t M, int64_t K, int64_t ldx, con
   const int S = launch_shrink_p<XT>(X, M, K, ldx, la.A, R, P, st);
   SQ_LAUNCH_CHECK();
   const int64_t threads = M * (R / 4);
-  k_lora_reduce<<<(unsigned)((threads + 63) / 64), 64, 0, st>>>(P, S, R, (int)M, T, ldt);
+  k_lora_reduce<<<(unsigned)((threads + 63) / 64), 64, 0, st>>>(P, S, R, R, (int)M, T, ldt);
   SQ_LAUNCH_CHECK();
   return SQ_OK;
 }
