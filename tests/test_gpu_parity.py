@@ -284,7 +284,9 @@ def lora_inputs(rng, M, K, N, r, xdt, ydt):
     return x, xn, a, b, y
 
 
-@pytest.mark.parametrize("r", [8, 16, 64])
+# ranks 40, 72 and 128: the expand's rank steps of 32 (2, 3, 4; T zero-padded
+# past r), the 128-rank shrink chunking, and fp32 Y with four rank steps
+@pytest.mark.parametrize("r", [8, 16, 40, 64, 72, 128])
 @pytest.mark.parametrize("xdt,ydt", [("bf16", "bf16"), ("f32", "bf16"), ("f16", "f16"), ("bf16", "f32")])
 @pytest.mark.parametrize("M,K,N", [(1, 16, 16), (33, 272, 144), (300, 4096, 1024), (70, 14336, 64)])
 def test_lora_apply(r, xdt, ydt, M, K, N):
