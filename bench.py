@@ -629,7 +629,10 @@ def row_kernels(args, torch):
             a.copy_(torch.rand(M, device="cuda") * 1e-2)
             ws_.copy_(torch.rand(N, device="cuda") * 1e-3)
             Y = torch.empty(M, N, dtype=odt, device="cuda")
-            ms = time_launches(torch, lambda: sq.sq_w8a8_gemm(Xq, Wq, a, ws_, Y), reps)
+            # decode-sized shapes split K across blocks with a workspace (0 bytes elsewhere)
+            gws = sq.sq_w8a8_gemm_workspace_bytes(M, N, K)
+            wsg = torch.empty(gws, dtype=torch.uint8, device="cuda") if gws else None
+            ms = time_launches(torch, lambda: sq.sq_w8a8_gemm_ws(Xq, Wq, a, ws_, Y, wsg), reps)
             g["a5_a6_gemm"] = rec(ms, ops=2.0 * M * N * K)
             r = wl.lora_rank * len(wl.group(inp))
             if r:

@@ -191,6 +191,22 @@ int sq_w8a8_gemm(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int m
                  const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
                  int64_t ldy, void* stream);
 
+/* Bytes of device workspace sq_w8a8_gemm_ws uses for this shape: 0 where it
+ * runs as sq_w8a8_gemm. Nonzero for decode-sized GEMMs (M <= 64, few
+ * 32-column tiles), whose K is then split across blocks: INT32 partial sums
+ * per K slice, KS x ceil(N / 32) x (1 or 2) x 4 KB. 0 for invalid shapes. */
+size_t sq_w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* sq_w8a8_gemm with a caller's device workspace (ws, ws_bytes >=
+ * sq_w8a8_gemm_workspace_bytes(M, N, K), 16-byte aligned; ignored, and may
+ * be NULL, when that is 0). Same arguments, errors and results bit for bit:
+ * the split partial sums are INT32, added in a fixed order before the same
+ * epilogue. The workspace is overwritten; calls that share one must not
+ * overlap. SQ_ERR_WORKSPACE if it is missing or too small. */
+int sq_w8a8_gemm_ws(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
+                    const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
+                    int64_t ldy, void* ws, size_t ws_bytes, void* stream);
+
 /* The same GEMM with the raw INT32 accumulators as output ([M, N] contiguous),
  * for checking the integer products on their own. */
 int sq_w8a8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, int64_t K,

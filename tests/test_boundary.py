@@ -37,7 +37,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 24
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sq.SIGNATURES)
@@ -138,6 +138,30 @@ def test_static_clipped_validation(L):
     assert f(P, sq.SQ_BF16, 4, 40, 48, NULL, P, P, P, S) == sq.SQ_ERR_MISALIGNED        # K % 16
     assert f(P, 9, 4, 64, 64, NULL, P, P, P, S) == sq.SQ_ERR_UNSUPPORTED_DTYPE
     assert f(P, sq.SQ_BF16, 0, 64, 64, NULL, P, P, P8, S) == sq.SQ_OK                   # M == 0
+
+
+def test_gemm_workspace_rules(L):
+    wsb = L.sq_w8a8_gemm_workspace_bytes
+    # decode shapes with few 32-column tiles split K: slices x ceil(N/32) x row tiles x 4 KB
+    need = wsb(64, 5120, 20480)
+    assert need > 0 and need % (160 * 2 * 4096) == 0
+    assert wsb(32, 5120, 20480) % (160 * 4096) == 0 and wsb(32, 5120, 20480) > 0
+    assert wsb(128, 5120, 20480) == 0          # not decode-sized
+    assert wsb(64, 20480, 5120) == 0           # 128x128 tiles already fill the chip
+    assert wsb(64, 5120, 1024) == 0            # too few K-tiles to split
+    assert wsb(64, 5120, 5120) == 0            # fewer than 4 slices of 16 K-tiles
+    assert wsb(64, 5120, 8192) > 0
+    assert wsb(64, 5120, 1000) == 0            # K not a multiple of 128
+    assert wsb(0, 5120, 20480) == 0 and wsb(-1, 64, 64) == 0
+    f = L.sq_w8a8_gemm_ws
+    args = lambda **kw: [kw.get(k, v) for k, v in dict(
+        xq=P, wq=P, a=P, mode=0, w=P, M=64, N=5120, K=20480, Y=P, yt=sq.SQ_BF16, ldy=5120,
+        ws=P, wsb=need, st=S).items()]
+    assert f(*args(ws=NULL)) == sq.SQ_ERR_WORKSPACE
+    assert f(*args(wsb=need - 1)) == sq.SQ_ERR_WORKSPACE
+    assert f(*args(ws=P4)) == sq.SQ_ERR_MISALIGNED
+    assert f(*args(xq=NULL)) == sq.SQ_ERR_INVALID_ARG
+    assert f(*args(M=0)) == sq.SQ_OK
 
 
 def test_gemm_validation(L):

@@ -245,6 +245,38 @@ def test_gemm_i32_extreme_magnitude():
     assert np.array_equal(acc.cpu().numpy(), ref)
 
 
+# Decode shapes whose K is split across blocks with a workspace (two row tiles
+# and one; 4, 4 and 9 slices; a ragged last column tile; the last slice
+# shorter than the others at K = 20352), plus shapes that take no workspace
+# (too many column tiles; K too short to split): bit-exact against the oracle
+# and the unsplit call.
+@pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("mode", ["dynamic", "static"])
+@pytest.mark.parametrize("M,N,K,split", [(64, 5120, 20480, True), (17, 1040, 8192, True),
+                                         (40, 208, 20352, True), (64, 20480, 5120, False),
+                                         (64, 5120, 5120, False)])
+def test_gemm_ws_split_k(out, mode, M, N, K, split):
+    rng = np.random.default_rng(M + N + K)
+    xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    wq = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    a = rng.uniform(1e-3, 5e-2, M if mode == "dynamic" else 1).astype(F32)
+    w = rng.uniform(1e-5, 1e-3, N).astype(F32)
+    need = sq.sq_w8a8_gemm_workspace_bytes(M, N, K)
+    assert (need > 0) == split
+    ws = torch.full((max(need, 16),), 0x5A, dtype=torch.uint8, device="cuda") if need else None
+    X, W, A, Wsc = dev(xq), dev(wq), dev(a), dev(w)
+    Y1 = torch.zeros(M, N, dtype=DT[out], device="cuda")
+    Y2 = torch.zeros(M, N, dtype=DT[out], device="cuda")
+    for _ in range(2):   # the second call finds the first call's partial sums in the workspace
+        sq.sq_w8a8_gemm_ws(X, W, A, Wsc, Y1, ws, mode=mode)
+    sq.sq_w8a8_gemm(X, W, A, Wsc, Y2, mode=mode)
+    assert torch.equal(Y1.view(torch.uint8), Y2.view(torch.uint8))
+    ref = O.dequantize(O.int8_gemm(xq, wq), a if mode == "dynamic" else a[0], w, out)
+    got = Y1.cpu()
+    got = got.float().numpy() if out != "f16" else got.numpy()
+    assert bits_equal(got, ref)
+
+
 @pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("mode", ["dynamic", "static"])
 @pytest.mark.parametrize("M,N,K", [(33, 48, 272), (300, 1024, 4096), (64, 20480, 5120)])

@@ -55,6 +55,9 @@ SIGNATURES = {
     "sq_w8a8_gemm": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_int,
                               _c_i64, _vp]),
     "sq_w8a8_gemm_i32": (_c_int, [_vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp]),
+    "sq_w8a8_gemm_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64]),
+    "sq_w8a8_gemm_ws": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_int,
+                                 _c_i64, _vp, _c_sz, _vp]),
     "sq_w8a8_gemm_lora": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_i64,
                                    _vp, _c_int, _c_f, _vp, _c_int, _c_i64, _vp]),
     "sq_lora_shrink": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _c_int, _vp, _c_i64, _vp,
@@ -248,6 +251,21 @@ def sq_w8a8_gemm(Xq: torch.Tensor, Wq: torch.Tensor, a_scale: torch.Tensor, w_sc
     _check("sq_w8a8_gemm", lib().sq_w8a8_gemm(
         _ptr(Xq), _ptr(Wq), _ptr(a_scale), MODES[mode], _ptr(w_scale), M, N, K, _ptr(Y), _dt(Y),
         _ld(Y), _stream(stream)))
+
+
+def sq_w8a8_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().sq_w8a8_gemm_workspace_bytes(int(M), int(N), int(K)))
+
+
+def sq_w8a8_gemm_ws(Xq: torch.Tensor, Wq: torch.Tensor, a_scale: torch.Tensor, w_scale: torch.Tensor,
+                    Y: torch.Tensor, ws, mode: str = "dynamic", stream=None) -> None:
+    """ws: a uint8 device tensor of sq_w8a8_gemm_workspace_bytes(M, N, K) bytes, or None when that is 0."""
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    _check("sq_w8a8_gemm_ws", lib().sq_w8a8_gemm_ws(
+        _ptr(Xq), _ptr(Wq), _ptr(a_scale), MODES[mode], _ptr(w_scale), M, N, K, _ptr(Y), _dt(Y),
+        _ld(Y), _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0,
+        _stream(stream)))
 
 
 def sq_w8a8_gemm_i32(Xq: torch.Tensor, Wq: torch.Tensor, acc: torch.Tensor, stream=None) -> None:

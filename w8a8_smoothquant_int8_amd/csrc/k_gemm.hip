@@ -569,11 +569,17 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyBN = 32;
 
-template <int OUT, bool STATIC_A, int LORA, int TM>
+// SPLITK: block (x, y) takes the K-tiles [y * kps, (y + 1) * kps) only and
+// writes its INT32 sums to part (slice y, column tile x; 1024 words per row
+// tile, in register order: word q * 64 + lane); k_gemm_skinny_finish adds the
+// slices and runs the epilogue. INT32 addition is exact (and wraps the same
+// in any order), so the result is that of the unsplit kernel bit for bit.
+template <int OUT, bool STATIC_A, int LORA, int TM, bool SPLITK = false>
 __global__ void __launch_bounds__(kSkinnyWaves * 64)
 k_gemm_skinny(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
               const float* __restrict__ a_scale, const float* __restrict__ w_scale, int M, int N,
-              int K, void* __restrict__ Y, int64_t ldy, LoraEpi le) {
+              int K, void* __restrict__ Y, int64_t ldy, LoraEpi le, int kps = 0,
+              int32_t* __restrict__ part = nullptr) {
   __shared__ int32_t red[kSkinnyWaves - 1][TM][16][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -590,6 +596,8 @@ k_gemm_skinny(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
     ap[i] = A + (int64_t)mrow * K + 16 * lhalf;
   }
   const int nk = K / kBK;
+  const int t0 = SPLITK ? (int)blockIdx.y * kps : 0;             // this block's K-tiles [t0, t1)
+  const int t1 = SPLITK ? (t0 + kps < nk ? t0 + kps : nk) : nk;
 
   auto load = [&](int kt, v4i (&fb)[4], v4i (&fa)[4][TM]) {
     const int64_t off = (int64_t)kt * kBK;
@@ -613,13 +621,13 @@ k_gemm_skinny(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
 
   v4i fb0[4], fa0[4][TM], fb1[4], fa1[4][TM];
   constexpr int W = kSkinnyWaves;
-  if (wave < nk) load(wave, fb0, fa0);
-  for (int kt = wave; kt < nk; kt += 2 * W) {
-    const bool more = kt + W < nk;
+  if (t0 + wave < t1) load(t0 + wave, fb0, fa0);
+  for (int kt = t0 + wave; kt < t1; kt += 2 * W) {
+    const bool more = kt + W < t1;
     if (more) load(kt + W, fb1, fa1);
     mma(fb0, fa0);
     if (!more) break;
-    if (kt + 2 * W < nk) load(kt + 2 * W, fb0, fa0);
+    if (kt + 2 * W < t1) load(kt + 2 * W, fb0, fa0);
     mma(fb1, fa1);
   }
 
@@ -637,7 +645,38 @@ k_gemm_skinny(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][0][q] += red[w][i][q][lane];
-  epilogue<OUT, STATIC_A, LORA, TM, 1>(acc, 0, n0, M, N, a_scale, w_scale, Y, ldy, le);
+  if constexpr (SPLITK) {
+    int32_t* dst = part + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * (TM * 1024);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) dst[i * 1024 + q * 64 + lane] = acc[i][0][q];
+  } else {
+    epilogue<OUT, STATIC_A, LORA, TM, 1>(acc, 0, n0, M, N, a_scale, w_scale, Y, ldy, le);
+  }
+}
+
+// The KS slices of a split skinny GEMM, added in slice order, then the
+// epilogue. One wave per 32-column tile.
+template <int OUT, bool STATIC_A, int TM>
+__global__ void __launch_bounds__(64)
+k_gemm_skinny_finish(const int32_t* __restrict__ part, int KS, const float* __restrict__ a_scale,
+                     const float* __restrict__ w_scale, int M, int N, void* __restrict__ Y,
+                     int64_t ldy) {
+  const int lane = threadIdx.x;
+  v16i acc[TM][1];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) acc[i][0] = v16i{};
+  for (int sl = 0; sl < KS; ++sl) {
+    const int32_t* src = part + ((int64_t)sl * gridDim.x + blockIdx.x) * (TM * 1024);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][0][q] += src[i * 1024 + q * 64 + lane];
+  }
+  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f};
+  epilogue<OUT, STATIC_A, 0, TM, 1>(acc, 0, blockIdx.x * kSkinnyBN, M, N, a_scale, w_scale, Y, ldy,
+                                    none);
 }
 
 // ---------------------------------------------------------------------------
@@ -806,10 +845,61 @@ static int launch_pipe(const int8_t* Xq, const int8_t* Wq, const float* a_scale,
   return SQ_OK;
 }
 
+// K split of the skinny kernel across blocks, given a workspace: slices of
+// whole K-tiles so that about 512 blocks run (the column tiles alone give
+// N / 32), each slice at least 16 K-tiles (two per wave), and only where at
+// least 4 such slices fit (K >= 8192). Measured at M = 64, N = 5120 with the
+// weights rotated past the MALL: K = 20480 69 -> 61 us in 4 slices; K = 5120
+// in 2 slices was slower (22 -> 26 us: the partial sums and the second
+// launch cost more than the wider grid gains). 1: no split.
+static int skinny_splits(int64_t M, int64_t N, int64_t K) {
+  if (M > 64 || pick_cfg(M, N, K) != CFG_SKINNY) return 1;
+  const int64_t ct = (N + kSkinnyBN - 1) / kSkinnyBN;
+  const int64_t kmax = (K / kBK) / 16;
+  if (kmax < 4) return 1;
+  int64_t ks = (512 + ct - 1) / ct;
+  if (ks > kmax) ks = kmax;
+  return ks > 1 ? (int)ks : 1;
+}
+
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  const int ks = skinny_splits(M, N, K);
+  if (ks <= 1) return 0;
+  const int64_t ct = (N + kSkinnyBN - 1) / kSkinnyBN;
+  const int64_t tm = M <= 32 ? 1 : 2;
+  return (size_t)ks * (size_t)ct * (size_t)tm * 1024 * sizeof(int32_t);
+}
+
+template <int OUT, bool STATIC_A, int TM>
+static int launch_skinny_split(const int8_t* Xq, const int8_t* Wq, const float* a_scale,
+                               const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y,
+                               int64_t ldy, int ks, int32_t* part, hipStream_t st) {
+  const unsigned ct = (unsigned)((N + kSkinnyBN - 1) / kSkinnyBN);
+  const int nk = (int)(K / kBK);
+  const int kps = (nk + ks - 1) / ks;
+  const int slices = (nk + kps - 1) / kps;   // every slice non-empty
+  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f};
+  k_gemm_skinny<OUT, STATIC_A, 0, TM, true><<<dim3(ct, (unsigned)slices), kSkinnyWaves * 64, 0, st>>>(
+      Xq, Wq, a_scale, w_scale, (int)M, (int)N, (int)K, Y, ldy, none, kps, part);
+  SQ_LAUNCH_CHECK();
+  k_gemm_skinny_finish<OUT, STATIC_A, TM><<<ct, 64, 0, st>>>(part, slices, a_scale, w_scale, (int)M,
+                                                            (int)N, Y, ldy);
+  SQ_LAUNCH_CHECK();
+  return SQ_OK;
+}
+
 template <int OUT, bool STATIC_A, int LORA>
 static int launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* a_scale,
                          const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y,
-                         int64_t ldy, const LoraEpi& le, hipStream_t st) {
+                         int64_t ldy, const LoraEpi& le, hipStream_t st, int32_t* part = nullptr) {
+  if constexpr (LORA == 0 && OUT != OUT_I32) {
+    const int ks = part != nullptr ? skinny_splits(M, N, K) : 1;
+    if (ks > 1)
+      return M <= 32 ? launch_skinny_split<OUT, STATIC_A, 1>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy,
+                                                               ks, part, st)
+                     : launch_skinny_split<OUT, STATIC_A, 2>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy,
+                                                               ks, part, st);
+  }
   switch (pick_cfg(M, N, K)) {
     case CFG_256:
       return launch_pipe<256, 256, 2, 4, OUT, STATIC_A, LORA>(Xq, Wq, a_scale, w_scale, M, N, K, Y,
@@ -845,12 +935,13 @@ static int launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* a_scal
 template <int LORA>
 static int launch_gemm_any(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
                            const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
-                           int64_t ldy, const LoraEpi& le, hipStream_t st) {
+                           int64_t ldy, const LoraEpi& le, hipStream_t st,
+                           int32_t* part = nullptr) {
   if (M == 0) return SQ_OK;
   const bool stat = mode == SQ_ACT_PER_TENSOR_STATIC;
 #define SQ_GEMM_OUT(O)                                                                               \
-  return stat ? launch_gemm_t<O, true, LORA>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, le, st)      \
-              : launch_gemm_t<O, false, LORA>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, le, st);
+  return stat ? launch_gemm_t<O, true, LORA>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, le, st, part)      \
+              : launch_gemm_t<O, false, LORA>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, le, st, part);
   switch (yt) {
     case SQ_BF16: SQ_GEMM_OUT(OUT_BF16)
     case SQ_F16:  SQ_GEMM_OUT(OUT_F16)
@@ -864,6 +955,14 @@ int launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mo
                 int64_t ldy, hipStream_t st) {
   const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f};
   return launch_gemm_any<0>(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, none, st);
+}
+
+int launch_gemm_ws(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
+                   const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
+                   int64_t ldy, void* ws, hipStream_t st) {
+  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f};
+  return launch_gemm_any<0>(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, none, st,
+                            (int32_t*)ws);
 }
 
 int launch_gemm_lora(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,

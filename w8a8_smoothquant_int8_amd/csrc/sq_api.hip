@@ -45,6 +45,10 @@ int launch_quant_act(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, c
 int launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
                 const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
                 int64_t ldy, hipStream_t st);
+int launch_gemm_ws(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
+                   const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
+                   int64_t ldy, void* ws, hipStream_t st);
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
 int launch_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, int64_t K,
                     int32_t* acc, hipStream_t st);
 int launch_gemm_lora(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
@@ -334,6 +338,32 @@ int sq_w8a8_gemm(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int m
   if (M == 0) return SQ_OK;
   if ((rc = gate()) != SQ_OK) return rc;
   return sq::launch_gemm(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, as_stream(stream));
+}
+
+size_t sq_w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxK) return 0;
+  return sq::gemm_ws_bytes(M, N, K);
+}
+
+int sq_w8a8_gemm_ws(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
+                    const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
+                    int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_gemm(Xq, Wq, M, N, K);
+  if (rc != SQ_OK) return rc;
+  SQ_REQUIRE(valid_mode(mode), SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(a_scale != nullptr && w_scale != nullptr && Y != nullptr, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(valid_dtype(yt), SQ_ERR_UNSUPPORTED_DTYPE);
+  SQ_REQUIRE(ldy >= N, SQ_ERR_INVALID_ARG);
+  SQ_REQUIRE(ldy % 16 == 0 && aligned16(Y) && aligned4(a_scale) && aligned4(w_scale), SQ_ERR_MISALIGNED);
+  if (M == 0) return SQ_OK;
+  const size_t need = sq::gemm_ws_bytes(M, N, K);
+  if (need > 0) {
+    SQ_REQUIRE(ws != nullptr && ws_bytes >= need, SQ_ERR_WORKSPACE);
+    SQ_REQUIRE(aligned16(ws), SQ_ERR_MISALIGNED);
+  }
+  if ((rc = gate()) != SQ_OK) return rc;
+  return sq::launch_gemm_ws(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy,
+                            need > 0 ? ws : nullptr, as_stream(stream));
 }
 
 static int check_rank(int r) {
