@@ -197,7 +197,7 @@ int sq_w8a8_gemm(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int m
  * per K slice, KS x ceil(N / 32) x (1 or 2) x 4 KB. 0 for invalid shapes. */
 size_t sq_w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
-/* sq_w8a8_gemm with a caller's device workspace (ws, ws_bytes >=
+/* [SQ] Step 7, as sq_w8a8_gemm, with a caller's device workspace (ws, ws_bytes >=
  * sq_w8a8_gemm_workspace_bytes(M, N, K), 16-byte aligned; ignored, and may
  * be NULL, when that is 0). Same arguments, errors and results bit for bit:
  * the split partial sums are INT32, added in a fixed order before the same
