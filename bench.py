@@ -6,23 +6,27 @@ A step is one pass of the whole path over one batch of the workload, for
 every input group: calibrate the per-channel maxima, compute the smoothing
 vector and fold it into INT8 weights, quantize the activations per token,
 run the INT8 GEMM with its dequant epilogue for every projection, and add the
-bf16 LoRA delta. The default workload is the Llama-3-8B projection set at
-M=2048 tokens. Inputs are seeded synthetic tensors, resident in HBM before the
+bf16 LoRA delta (the stacked shrink, then the expand inside the GEMM
+epilogue; per-request adapters as a segmented call). The default workload is
+the Llama-2-70B MLP block at M=8192 tokens, the largest configuration that
+fits one GPU. Inputs are seeded synthetic tensors, resident in HBM before the
 timed region starts.
 
-The input groups are independent, so a timed step issues every group as one
-native call (sq_linear_group_run: calibrate, fold, quantize, LoRA shrink,
-GEMM) on one of three streams, largest group first, and the groups' kernels
-overlap. The timed steps are issued back to back, each group staying on its
-own stream.
+Each input group runs as one native call (sq_linear_group_run), which records
+HIP events between its launches on its stream. By default every group runs on
+one stream, in order of decreasing GEMM work, so each kernel has the chip to
+itself and the events time it alone; --streams N spreads the groups over N
+streams instead (their kernels then overlap).
 
-Output: one JSON line. `value` is GEMM INT8 tera-operations per second of the
-whole step (2*M*N*K summed over the projections, divided by the step time).
-HIP events that the library records on each GEMM's stream right around its
-launch give the GEMM's own rate, reported as its roofline fraction against the
-MI355X dense INT8 MFMA peak. Per-stage times come from a few extra untimed steps issued in order
-on one stream. The CPU oracle is timed on a bounded sample of the same step
-(cpu_baseline).
+Output: one JSON line. `value` is the GEMM+LoRA effective INT8 rate:
+2*M*N*K summed over the projections, divided by the summed time of the GEMMs
+(dequant and LoRA expand in their epilogue), the LoRA shrinks and any
+segmented LoRA calls, all measured with HIP events inside the timed steps.
+`full_step_tops` divides the same operations by the wall-clock step time,
+which also holds the calibration, the fold and the activation quant.
+`roofline` is the dominant GEMM kernel against the MI355X dense INT8 MFMA
+peak. The CPU oracle is timed stage by stage on a bounded sample of the same
+step (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -39,23 +43,24 @@ sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, 5.0 POP/s
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
-DEFAULT_WORKLOAD = "llama3_8b_proj_m2048"
+DEFAULT_WORKLOAD = "llama2_70b_mlp_m8192"
 GEMM_KERNEL_SRC = os.path.join(ROOT, "w8a8_smoothquant_int8_amd", "csrc", "k_gemm.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_{tile}_hbm_traffic_llama3_8b_proj_m2048.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_{tile}_hbm_traffic_{workload}.txt")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--streams", type=int, default=1,
+                    help="streams the input groups are spread over (1: in order on one stream)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=128,
                     help="activation rows per input in the CPU-oracle sample")
-    ap.add_argument("--no-stages", action="store_true",
-                    help="skip the untimed per-stage pass (so a kernel trace of the run covers "
-                         "only the warmup and timed steps)")
+    ap.add_argument("--cpu-wrows", type=int, default=1024,
+                    help="weight rows (output columns) per input in the CPU-oracle sample")
     ap.add_argument("--row", choices=sorted(ROWS), default=None,
                     help="measure one of the widened rows instead of the whole step "
                          "(one JSON line of its own)")
@@ -76,10 +81,11 @@ def kernel_hash(path: str) -> str:
     return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
-def stored_traffic(tile: str):
+def stored_traffic(tile: str, workload: str):
     """HBM bytes per launch of the dominant GEMM kernel from the rocprofv3
-    FETCH_SIZE/WRITE_SIZE runs, if they were taken on the current GEMM source."""
-    path = TRAFFIC_FILE.format(tile=tile)
+    FETCH_SIZE/WRITE_SIZE runs on this workload, if they were taken on the
+    current GEMM source."""
+    path = TRAFFIC_FILE.format(tile=tile, workload=workload)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -95,29 +101,23 @@ def stored_traffic(tile: str):
         return None
 
 
-class Timeline:
-    """HIP events recorded on the launch stream between kernel calls."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.marks = []
-
-    def mark(self, tag, group=None):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.marks.append((tag, group, e))
-
-    def durations(self):
-        """{tag: [ms, ...]} and {group: [ms, ...]} for the GEMM launches."""
-        out, gemm = {}, {}
-        for (tag, grp, e0), (_, _, e1) in zip(self.marks, self.marks[1:]):
-            if tag is None:
-                continue
-            ms = e0.elapsed_time(e1)
-            out.setdefault(tag, []).append(ms)
-            if tag == "gemm":
-                gemm.setdefault(grp, []).append(ms)
-        return out, gemm
+def segmented_lora(wl, proj, torch, seed=0):
+    """The per-request adapters of a multi-tenant workload for one projection."""
+    import w8a8_smoothquant_int8_amd as sq
+    from w8a8_smoothquant_int8_amd.pipeline import SegmentedLora
+    seg = wl.segments(seed)
+    ranks = seg["ranks"]
+    As, Bs = [], []
+    for ad, r in enumerate(ranks):
+        a, b = wl.lora(proj, rank=int(r), adapter=ad, seed=seed)
+        As.append(a.cuda())
+        Bs.append(b.cuda())
+    return SegmentedLora(
+        seg_start=torch.from_numpy(seg["seg_start"]).cuda(),
+        seg_adapter=torch.from_numpy(seg["seg_adapter"]).cuda(),
+        A=As, B=Bs, ranks=torch.from_numpy(ranks).cuda(),
+        A_ptrs=sq.pointer_table(As, "cuda"), B_ptrs=sq.pointer_table(Bs, "cuda"),
+        max_rank=int(ranks.max()))
 
 
 def setup(wl, torch):
@@ -126,52 +126,20 @@ def setup(wl, torch):
     for inp, _K in wl.inputs:
         rows = wl.group_rows(inp)
         loras = {p: tuple(t.cuda() for t in wl.lora(p)) for p in rows} if wl.lora_rank else {}
-        g = LinearGroup(wl.w_group(inp).cuda(), rows, wl.alpha, wl.out_dtype, wl.M, lora=loras)
+        segs = {p: segmented_lora(wl, p, torch) for p in rows} if wl.segmented else {}
+        g = LinearGroup(wl.w_group(inp).cuda(), rows, wl.alpha, wl.out_dtype, wl.M, lora=loras,
+                        seg_lora=segs)
         groups.append((inp, g, wl.x(inp).cuda(), wl.x_cal(inp).cuda()))
     torch.cuda.synchronize()
     return groups
 
 
-def run_step(groups, tl=None):
-    """One pass of the whole path over one batch, every input group, in issue
-    order on the current stream (the instrumented pass: HIP events between
-    the launches give the per-stage times)."""
-    mark = tl.mark if tl is not None else (lambda tag, **kw: None)
-    for inp, g, X, Xc in groups:
-        mark("calibrate")
-        g.calibrate(Xc)
-    for inp, g, X, Xc in groups:
-        mark("smooth_fold")
-        g.fold()
-    for inp, g, X, Xc in groups:
-        mark("quant")
-        g.quantize(X)
-        if g.fused:
-            mark("lora_shrink")
-            g.lora_shrink(X)
-            mark("gemm", group=inp)
-            g.gemm_all_lora()
-        else:
-            mark("gemm", group=inp)
-            g.gemm_all()
-    mark(None)
-
-
-# HIP maps streams onto a few hardware queues (4 by default, one of them taken
-# by the null stream); two streams that share a queue run in order. Three
-# streams get a queue each.
-N_STREAMS = 3
-
-
 class Streams:
     """The step's streams (default priority) and the group -> stream plan:
     groups in descending order of GEMM work, each on the stream with the least
-    work so far (longest-processing-time first). The longest chain starts
-    first and never queues behind another group. Measured on the Llama-3-8B
-    step: 0.78 ms against 0.85 ms for one stream per group in workload order
-    (two of those four streams then shared a hardware queue)."""
+    work so far (longest-processing-time first)."""
 
-    def __init__(self, torch, groups, n_streams=N_STREAMS):
+    def __init__(self, torch, groups, n_streams):
         self.torch = torch
         work = [2.0 * g.M * g.Ntot * g.K for _inp, g, _x, _c in groups]
         self.plan = plan_streams(work, n_streams)       # (group index, stream index), issue order
@@ -192,15 +160,15 @@ def plan_streams(work, n_streams):
     return plan
 
 
-def run_step_streams(groups, st, gemm_ev=None, join=True):
-    """One pass of the whole path over one batch. The input groups are
-    independent: each runs calibrate -> fold -> quantize -> LoRA shrink ->
-    GEMM as one native call (sq_linear_group_run) on the stream the plan gives
-    it, so the groups' short, latency-bound kernels fill each other's gaps and
-    a GEMM whose tiles leave CUs idle in its last round shares the chip with
-    another group's work. gemm_ev: {group: [(start, end), ...]} collects HIP
-    events that the library records on the group's stream right around its
-    GEMM, for the groups in gemm_ev["groups"].
+STAGE_EVENTS = ("begin", "quant_begin", "shrink_begin", "gemm_begin", "gemm_end")
+
+
+def run_step_streams(groups, st, rec=None, join=True):
+    """One pass of the whole path over one batch: each input group runs
+    calibrate -> fold -> quantize -> LoRA shrink -> GEMM (LoRA expand in its
+    epilogue) as one native call, plus its segmented LoRA calls, on the stream
+    the plan gives it. rec: None, or a recorder whose take(group) gives the
+    HIP events the library records between that group's launches.
 
     join=False leaves out the step's fork from and join into the current
     stream: back-to-back steps then run as the streams allow. A group always
@@ -213,27 +181,56 @@ def run_step_streams(groups, st, gemm_ev=None, join=True):
             sm.wait_stream(cur)
     for gi, si in st.plan:
         inp, g, X, Xc = groups[gi]
-        e0 = e1 = None
-        if gemm_ev is not None and inp in gemm_ev["groups"]:
-            e0, e1 = gemm_ev["pool"].pop()
-            gemm_ev.setdefault(inp, []).append((e0, e1))
-        g.run(X, Xc, stream=st.main[si], gemm_begin=e0, gemm_end=e1)
+        ev, seg_ev = rec.take(inp) if rec is not None else (None, None)
+        g.run(X, Xc, stream=st.main[si], events=ev, seg_events=seg_ev)
     if join:
         for sm in st.main:
             cur.wait_stream(sm)
 
 
-def event_pool(torch, n):
-    """n (start, end) pairs of timing events, created up front (a first record
-    creates the underlying HIP event) so the library can record them."""
-    pool = []
-    for _ in range(n):
-        pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-        for e in pair:
-            e.record()
-        pool.append(pair)
-    torch.cuda.synchronize()
-    return pool
+class StageRecorder:
+    """Pre-created HIP event sets, one per (step, group): the group call's
+    stage events and a pair around its segmented LoRA calls."""
+
+    def __init__(self, torch, groups, steps):
+        import w8a8_smoothquant_int8_amd as sq
+        self.sq = sq
+        self.sets = {inp: [] for inp, _g, _x, _c in groups}
+        self.seg = {inp: bool(g.seg_lora) for inp, g, _x, _c in groups}
+        for inp in self.sets:
+            for _ in range(steps):
+                evs = {k: torch.cuda.Event(enable_timing=True) for k in STAGE_EVENTS}
+                pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for e in list(evs.values()) + list(pair):
+                    e.record()          # the first record creates the HIP event
+                self.sets[inp].append((evs, pair))
+        torch.cuda.synchronize()
+        self.used = {inp: [] for inp in self.sets}
+
+    def take(self, inp):
+        evs, pair = self.sets[inp][len(self.used[inp])]
+        self.used[inp].append((evs, pair))
+        return self.sq.sq_group_events(**evs), (pair if self.seg[inp] else None)
+
+    def stage_ms(self, inp, has_lora):
+        """Per-step average ms of each stage of a group's call."""
+        out = {"calibrate_fold": 0.0, "quant": 0.0, "shrink": 0.0, "gemm": 0.0, "seg_lora": 0.0,
+               "gemm_launches": []}
+        for evs, pair in self.used[inp]:
+            out["calibrate_fold"] += evs["begin"].elapsed_time(evs["quant_begin"])
+            nxt = evs["shrink_begin"] if has_lora else evs["gemm_begin"]
+            out["quant"] += evs["quant_begin"].elapsed_time(nxt)
+            if has_lora:
+                out["shrink"] += evs["shrink_begin"].elapsed_time(evs["gemm_begin"])
+            g = evs["gemm_begin"].elapsed_time(evs["gemm_end"])
+            out["gemm"] += g
+            out["gemm_launches"].append(g)
+            if self.seg[inp]:
+                out["seg_lora"] += pair[0].elapsed_time(pair[1])
+        n = max(len(self.used[inp]), 1)
+        for k in ("calibrate_fold", "quant", "shrink", "gemm", "seg_lora"):
+            out[k] /= n
+        return out
 
 
 def _tile_score(M, N, bm, bn, resident, rate):
@@ -265,47 +262,121 @@ def gemm_tile(M: int, N: int, K: int) -> str:
     return "256x192" if s192 >= s128 else "128x128"
 
 
-def cpu_baseline(wl, rows_per_input: int):
-    """The oracle as it stands, on a bounded sample of one step: weights are
-    folded in full; the activation path (quantize, INT8 GEMM, dequant, LoRA)
-    runs on `rows_per_input` rows of each input and is scaled to all M rows."""
+def tile_dims(tile: str):
+    """(rows, columns) of one output tile of a configuration."""
+    return {"256x256": (256, 256), "256x192": (256, 192), "128x128": (128, 128),
+            "generic": (128, 128), "skinny": (64, 32)}[tile]
+
+
+def host_info():
+    """nproc and the CPU model of this host."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return nproc, model
+
+
+def blas_threads():
+    from threadpoolctl import threadpool_info
+    return max([d.get("num_threads", 1) for d in threadpool_info()
+                if d.get("user_api") == "blas"] or [1])
+
+
+def cpu_baseline(wl, rows_per_input: int, wrows_per_input: int):
+    """The oracle as it stands, timed stage by stage on a bounded sample of one
+    step, each stage scaled to the whole workload by its own size:
+    calibration absmax over the full calibration batch; weight absmax and the
+    fold + weight quant on `wrows_per_input` weight rows (scaled by N / rows);
+    the smoothing vector in full; per-token quant on `rows_per_input`
+    activation rows (scaled by M / rows); the INT8 GEMM + dequant on those
+    rows against the sampled weight rows (scaled by M N / (rows wrows)); the
+    LoRA shrink on the sampled rows (scaled by M / rows) and the expand on
+    the sampled rows and columns (scaled like the GEMM); segmented adapters
+    likewise on the sampled rows' requests."""
     import numpy as np
     import oracle.sq_oracle as O
-    from threadpoolctl import threadpool_info
 
-    t_fixed = 0.0
-    t_rows = 0.0
+    st = {k: 0.0 for k in ("calibrate", "weight_absmax", "smoothing_scale", "fold_quant",
+                           "quant", "gemm_dequant", "lora_shrink", "lora_expand")}
     m = min(rows_per_input, wl.M)
-    for inp, _K in wl.inputs:
+    for inp, K in wl.inputs:
         X = wl.x(inp).float().numpy()[:m]
         Xc = wl.x_cal(inp).float().numpy()
         W = wl.w_group(inp).float().numpy()
-        rows = wl.group_rows(inp)
-        t0 = time.perf_counter()
-        act_max = O.calibrate_absmax(Xc)
-        s = O.smoothing_scale(act_max, O.weight_absmax(W), wl.alpha)
-        wq, wsc = O.fold_and_quantize_weights(W, s)
-        t1 = time.perf_counter()
-        xq, a = O.quantize_per_token(X, s)
-        for p, (r0, r1) in rows.items():
-            y = O.dequantize(O.int8_gemm(xq, wq[r0:r1]), a, wsc[r0:r1], wl.out_dtype)
-            if wl.lora_rank:
-                A, B = wl.lora(p)
-                O.lora_apply(y, X, wl.dtype, A.float().numpy(), B.float().numpy(), 1.0, wl.out_dtype)
-        t2 = time.perf_counter()
-        t_fixed += t1 - t0
-        t_rows += t2 - t1
-    step_s = t_fixed + t_rows * (wl.M / m)
-    threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+        N = W.shape[0]
+        n = min(wrows_per_input, N)
+        cols = np.linspace(0, N - 1, n).astype(np.int64)
+        Ws = np.ascontiguousarray(W[cols])
+        del W
+        t = time.perf_counter
+        t0 = t(); act_max = O.calibrate_absmax(Xc); st["calibrate"] += t() - t0
+        t0 = t(); w_max = O.weight_absmax(Ws); st["weight_absmax"] += (t() - t0) * N / n
+        t0 = t(); s = O.smoothing_scale(act_max, w_max, wl.alpha); st["smoothing_scale"] += t() - t0
+        t0 = t(); wq, wsc = O.fold_and_quantize_weights(Ws, s); st["fold_quant"] += (t() - t0) * N / n
+        t0 = t(); xq, a = O.quantize_per_token(X, s); st["quant"] += (t() - t0) * wl.M / m
+        t0 = t()
+        y = O.dequantize(O.int8_gemm(xq, wq), a, wsc, wl.out_dtype)
+        st["gemm_dequant"] += (t() - t0) * (wl.M / m) * (N / n)
+        if wl.lora_rank:
+            # the group's adapters stacked along r, as the GPU path runs them
+            rows = wl.group_rows(inp)
+            A = np.concatenate([wl.lora(p)[0].float().numpy() for p in rows], axis=0)
+            B = np.zeros((n, A.shape[0]), dtype=np.float32)
+            c = 0
+            for p, (r0, r1) in rows.items():
+                Bp = wl.lora(p)[1].float().numpy()
+                sel = (cols >= r0) & (cols < r1)
+                B[sel, c:c + wl.lora_rank] = Bp[cols[sel] - r0]
+                c += wl.lora_rank
+            t0 = t(); T = O.lora_shrink(X, wl.dtype, A); st["lora_shrink"] += (t() - t0) * wl.M / m
+            t0 = t(); O.lora_expand_add(y, T, B, 1.0, wl.out_dtype)
+            st["lora_expand"] += (t() - t0) * (wl.M / m) * (N / n)
+        elif wl.segmented:
+            seg = wl.segments(0)
+            ranks = seg["ranks"]
+            for p, (r0, r1) in wl.group_rows(inp).items():
+                As, Bs = [], []
+                for ad, rk in enumerate(ranks):
+                    a_, b_ = wl.lora(p, rank=int(rk), adapter=ad)
+                    As.append(a_.float().numpy())
+                    Bs.append(b_.float().numpy())
+                sel = (cols >= r0) & (cols < r1)
+                if not sel.any():
+                    continue
+                Bsel = [b[cols[sel] - r0] for b in Bs]
+                t0 = t()
+                O.lora_apply_segmented(y[:, sel], X, wl.dtype, np.minimum(seg["seg_start"], m),
+                                       seg["seg_adapter"], As, Bsel, 1.0, wl.out_dtype)
+                # shrink and expand together; scaled like the expand (rows x columns)
+                st["lora_expand"] += (t() - t0) * (wl.M / m) * ((r1 - r0) / sel.sum())
+    ops = wl.gemm_ops()
+    gemm_lora_s = st["gemm_dequant"] + st["lora_shrink"] + st["lora_expand"]
+    full_s = sum(st.values())
+    nproc, model = host_info()
+    thr = blas_threads()
     return {
-        "value": wl.gemm_ops() / step_s / 1e12,
+        "value": ops / gemm_lora_s / 1e12,
         "unit": "TOPS",
-        "cores": int(threads),
+        "cores": int(thr),
         "kind": "oracle",
-        "sample": (f"one step of {wl.name}: weights calibrated/smoothed/folded in full "
-                   f"({t_fixed:.1f} s); quantize+GEMM+dequant+LoRA on {m} of {wl.M} rows per input "
-                   f"({t_rows:.1f} s) scaled x{wl.M / m:g}; numpy oracle, BLAS threads={threads}"),
-        "step_s": step_s,
+        "sample": (f"one step of {wl.name}, stage by stage: calibration batch in full; "
+                   f"{n} weight rows and {m} activation rows per input, each stage's time "
+                   f"scaled to the full sizes; value = GEMM+LoRA ops over the GEMM + dequant + "
+                   f"LoRA time, as for the GPU; numpy oracle, BLAS threads={thr}"),
+        "nproc": nproc,
+        "cpu_model": model,
+        "stages_s": {k: round(v, 4) for k, v in st.items()},
+        "full_step_s": round(full_s, 3),
+        "full_step_tops": ops / full_s / 1e12,
     }
 
 
@@ -624,16 +695,25 @@ def row_kernels(args, torch):
             a = torch.empty(M, device="cuda")
             ms = time_rotated(torch, [lambda x=x: sq.sq_quant_per_token(x, s, Xq, a) for x in Xs], reps)
             g["a4_quant"] = rec(ms, (esz + 1) * M * K + 4 * M, big=big)
-            Wq.copy_(torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda"))
+            del Wq
+            # the GEMMs cycle through enough weight copies that the MALL does not serve repeats
+            Wqs = [torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda")
+                   for _ in range(copies(N * K))]
             Xq.copy_(torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda"))
             a.copy_(torch.rand(M, device="cuda") * 1e-2)
             ws_.copy_(torch.rand(N, device="cuda") * 1e-3)
             Y = torch.empty(M, N, dtype=odt, device="cuda")
-            # decode-sized shapes split K across blocks with a workspace (0 bytes elsewhere)
-            gws = sq.sq_w8a8_gemm_workspace_bytes(M, N, K)
-            wsg = torch.empty(gws, dtype=torch.uint8, device="cuda") if gws else None
-            ms = time_launches(torch, lambda: sq.sq_w8a8_gemm_ws(Xq, Wq, a, ws_, Y, wsg), reps)
+            ms = time_rotated(torch, [lambda w=w: sq.sq_w8a8_gemm(Xq, w, a, ws_, Y) for w in Wqs], reps)
             g["a5_a6_gemm"] = rec(ms, ops=2.0 * M * N * K)
+            g["a5_a6_gemm"]["weight_gbs"] = round(N * K / ms / 1e6, 1)
+            # decode-sized shapes can split K across blocks with a workspace (0 bytes elsewhere)
+            gws = sq.sq_w8a8_gemm_workspace_bytes(M, N, K)
+            if gws:
+                wsg = torch.empty(gws, dtype=torch.uint8, device="cuda")
+                ms = time_rotated(torch, [lambda w=w: sq.sq_w8a8_gemm_ws(Xq, w, a, ws_, Y, wsg)
+                                          for w in Wqs], reps)
+                g["a5_a6_gemm_split_k"] = rec(ms, ops=2.0 * M * N * K)
+                g["a5_a6_gemm_split_k"]["weight_gbs"] = round(N * K / ms / 1e6, 1)
             r = wl.lora_rank * len(wl.group(inp))
             if r:
                 A = (torch.randn(r, K, device="cuda") * 0.01).bfloat16()
@@ -643,7 +723,8 @@ def row_kernels(args, torch):
                 ms = time_rotated(torch, [lambda x=x: sq.sq_lora_shrink(x, A, T, wsp) for x in Xs], reps)
                 g["a7_shrink"] = rec(ms, esz * M * K + 2 * r * K + 2 * M * r, big=big)
                 g["a7_shrink"]["rank"] = r
-                ms = time_launches(torch, lambda: sq.sq_w8a8_gemm_lora(Xq, Wq, a, ws_, T, Bb, Y), reps)
+                ms = time_rotated(torch, [lambda w=w: sq.sq_w8a8_gemm_lora(Xq, w, a, ws_, T, Bb, Y)
+                                          for w in Wqs], reps)
                 g["a8_gemm_lora"] = rec(ms, ops=2.0 * M * N * K)
             if wl.segmented:
                 seg = wl.segments(0)
@@ -664,7 +745,7 @@ def row_kernels(args, torch):
                     nbytes = esz * M * K + 2 * 2 * M * Np + sum(2 * int(rk) * (K + Np) for rk in ranks)
                     g["a9_segmented_" + proj] = rec(ms, nbytes, big=big)
             res[inp] = g
-            del Xs, Xc, Xq, Y
+            del Xs, Xc, Xq, Y, Wqs
             torch.cuda.empty_cache()
         out[name] = res
     fracs.sort()
@@ -709,78 +790,71 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    st = Streams(torch, groups)
+    st = Streams(torch, groups, max(1, args.streams))
     for _ in range(args.warmup):
         run_step_streams(groups, st, join=False)
     torch.cuda.synchronize()
 
-    # The dominant kernel: the GEMM instantiation (tile configuration) with the
-    # most GEMM work per step. Only its launches carry timing events (each
-    # event pair costs some step time).
-    cfg_ops = {}
-    for inp, _K in wl.inputs:
-        Ntot = sum(p.N for p in wl.group(inp))
-        cfg = gemm_tile(wl.M, Ntot, wl.K_of(inp))
-        cfg_ops[cfg] = cfg_ops.get(cfg, 0.0) + 2.0 * wl.M * Ntot * wl.K_of(inp)
-    dom = max(cfg_ops, key=cfg_ops.get)
-    dom_groups = {inp for inp, _K in wl.inputs
-                  if gemm_tile(wl.M, sum(p.N for p in wl.group(inp)), wl.K_of(inp)) == dom}
-
     # Timed region: exactly `steps` steps, synchronized on both sides and
-    # issued back to back (no join between steps; see run_step_streams). HIP
-    # events on the dominant GEMM's stream time its launches for the roofline.
-    gemm_ev = {"pool": event_pool(torch, args.steps * len(dom_groups)), "groups": dom_groups}
+    # issued back to back. Every group call records its stage events.
+    rec = StageRecorder(torch, groups, args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        run_step_streams(groups, st, gemm_ev, join=False)
+        run_step_streams(groups, st, rec, join=False)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-
     ms_per_step = elapsed * 1e3 / args.steps
     ops = wl.gemm_ops()
-    value = ops * args.steps / elapsed / 1e12
-    gemm_ev.pop("pool")
-    gemm_ev.pop("groups")
-    gemm_by_group = {g: [a.elapsed_time(b) for a, b in evs] for g, evs in gemm_ev.items()}
 
-    # Per-stage times: a few more steps, untimed, with every launch issued in
-    # order on one stream and HIP events between the launches; the GEMMs there
-    # run alone on the chip.
-    stage_ms, gemm_alone = {}, {}
-    if not args.no_stages:
-        run_step(groups)                  # first use of the single-purpose calls, untimed
-        torch.cuda.synchronize()
-        tl = Timeline(torch)
-        n_inst = min(args.steps, 5)
-        for _ in range(n_inst):
-            run_step(groups, tl)
-        torch.cuda.synchronize()
-        d, gemm_alone = tl.durations()
-        stage_ms = {k: sum(v) / n_inst for k, v in d.items()}
-    # The dominant kernel's timed launches
-    kd = {"ms": [], "ops": 0.0, "launches": 0}
-    for inp in sorted(dom_groups):
-        Ntot = sum(p.N for p in wl.group(inp))
-        kd["ms"] += gemm_by_group[inp]
-        kd["ops"] += 2.0 * wl.M * Ntot * wl.K_of(inp) * len(gemm_by_group[inp])
-        kd["launches"] += len(gemm_by_group[inp])
-    gemm_avg_ms = sum(kd["ms"]) / kd["launches"]
-    gemm_tops = (kd["ops"] / kd["launches"]) / (gemm_avg_ms * 1e-3) / 1e12
-    traffic = stored_traffic(dom)
-    # The same kernel's launches in the serialized pass, where nothing else runs
-    alone_tops = None
-    if gemm_alone:
-        ms, ops = 0.0, 0.0
-        for inp, _K in wl.inputs:
-            Ntot = sum(p.N for p in wl.group(inp))
-            if gemm_tile(wl.M, Ntot, wl.K_of(inp)) == dom:
-                ms += sum(gemm_alone[inp])
-                ops += 2.0 * wl.M * Ntot * wl.K_of(inp) * len(gemm_alone[inp])
-        alone_tops = ops / (ms * 1e-3) / 1e12
+    # Per group (one GEMM launch over the stacked projections) and per projection.
+    per_group, per_proj, tile_of = {}, {}, {}
+    tot = {"calibrate_fold": 0.0, "quant": 0.0, "shrink": 0.0, "gemm": 0.0, "seg_lora": 0.0}
+    for inp, g, _x, _c in groups:
+        K = wl.K_of(inp)
+        d = rec.stage_ms(inp, g.fused)
+        g_ops = 2.0 * wl.M * g.Ntot * K
+        lora_ms = d["shrink"] + d["seg_lora"]
+        tile_of[inp] = gemm_tile(wl.M, g.Ntot, K)
+        per_group[inp] = {
+            "projections": list(g.rows), "M": wl.M, "N": g.Ntot, "K": K, "tile": tile_of[inp],
+            "lora_rank": (g.A_stack.shape[0] if g.fused else
+                          (max(s.max_rank for s in g.seg_lora.values()) if g.seg_lora else 0)),
+            "ms": {k: round(v, 5) for k, v in d.items() if k != "gemm_launches"},
+            "gemm_tops": round(g_ops / d["gemm"] / 1e9, 1),
+            "gemm_lora_tops": round(g_ops / (d["gemm"] + lora_ms) / 1e9, 1)}
+        for p, (r0, r1) in g.rows.items():
+            per_proj[p] = {"input": inp, "M": wl.M, "N": r1 - r0, "K": K,
+                           "gemm_tops": per_group[inp]["gemm_tops"],
+                           "gemm_lora_tops": per_group[inp]["gemm_lora_tops"]}
+        for k in tot:
+            tot[k] += d[k]
+    gemm_lora_ms = tot["gemm"] + tot["shrink"] + tot["seg_lora"]
+    value = ops / (gemm_lora_ms * 1e-3) / 1e12
 
-    quant_bytes = sum((2 if wl.dtype != "f32" else 4) * wl.M * K + wl.M * K + 4 * wl.M
-                      for _i, K in wl.inputs)
+    # The dominant kernel: the GEMM instantiation (tile configuration) with the
+    # most GEMM work per step; its launches in the timed region.
+    cfg_ops = {}
+    for inp, g, _x, _c in groups:
+        cfg_ops[tile_of[inp]] = cfg_ops.get(tile_of[inp], 0.0) + 2.0 * wl.M * g.Ntot * g.K
+    dom = max(cfg_ops, key=cfg_ops.get)
+    launches, dom_ms, dom_ops = 0, 0.0, 0.0
+    dom_inputs = []
+    for inp, g, _x, _c in groups:
+        if tile_of[inp] != dom:
+            continue
+        dom_inputs.append(inp)
+        ls = rec.stage_ms(inp, g.fused)["gemm_launches"]
+        launches += len(ls)
+        dom_ms += sum(ls)
+        dom_ops += 2.0 * wl.M * g.Ntot * g.K * len(ls)
+    avg_launch_ms = dom_ms / launches
+    achieved = dom_ops / launches / (avg_launch_ms * 1e-3) / 1e12
+    traffic = stored_traffic(dom, wl.name)
+    lora_epi = any(groups[i][1].fused for i in range(len(groups)) if groups[i][0] in dom_inputs)
+
+    esz = 4 if wl.dtype == "f32" else 2
+    quant_bytes = sum((esz + 1) * wl.M * K + 4 * wl.M for _i, K in wl.inputs)
     line = {
         "metric": "W8A8 GEMM+LoRA INT8 TOPS and % of MI355X INT8 MFMA peak (1 GPU)",
         "value": round(value, 2),
@@ -797,27 +871,28 @@ def main():
         "config": {"workload": wl.name, "M": wl.M, "act_dtype": wl.dtype, "out_dtype": wl.out_dtype,
                    "alpha": wl.alpha, "lora_rank": wl.lora_rank,
                    "projections": {p.name: [p.N, wl.K_of(p.input)] for p in wl.projections},
-                   "parallelism": "none (1 GPU)"},
+                   "streams": len(st.main), "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma",
-                     "kernel": f"k_gemm_pipe {dom} tiles, LoRA epilogue" if any(
-                         g.fused for _i, g, _x, _c in groups) else f"k_gemm_pipe {dom} tiles",
-                     "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
-                     "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": traffic,
-                     "launches_per_step": kd["launches"] // args.steps,
-                     "avg_launch_ms": round(gemm_avg_ms, 5),
-                     "note": "timed-region launches, which share the chip with the other "
-                             "groups' kernels; achieved_alone: the same kernel with nothing "
-                             "else running (serialized pass)",
-                     "achieved_alone": round(alone_tops, 1) if alone_tops else None},
+                     "kernel": f"k_gemm_pipe {dom} tiles" + (", LoRA epilogue" if lora_epi else "")
+                               + f" ({', '.join(dom_inputs)})",
+                     "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
+                     "launches_per_step": launches // args.steps,
+                     "ops_per_launch": dom_ops / launches,
+                     "avg_launch_ms": round(avg_launch_ms, 5)},
+        "value_formula": "sum 2MNK / sum (t_gemm incl. dequant and LoRA expand epilogue + "
+                         "t_lora_shrink + t_segmented_lora), HIP events in the timed steps",
         "value_pct_of_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2),
+        "full_step_tops": round(ops / (ms_per_step * 1e-3) / 1e12, 2),
+        "stages_ms_per_step": {k: round(v, 4) for k, v in tot.items()},
+        "quant_gbs": round(quant_bytes / (tot["quant"] * 1e-3) / 1e9, 1),
+        "groups": per_group,
+        "projections": per_proj,
     }
-    if stage_ms:
-        line["stages_ms_per_step_serialized"] = {k: round(v, 4) for k, v in stage_ms.items()}
-        line["quant_gbs"] = round(quant_bytes / (stage_ms["quant"] * 1e-3) / 1e9, 1)
     if not args.no_cpu_baseline:
-        cb = cpu_baseline(wl, args.cpu_rows)
-        cb.pop("step_s")
+        cb = cpu_baseline(wl, args.cpu_rows, args.cpu_wrows)
         cb["value"] = round(cb["value"], 6)
+        cb["full_step_tops"] = round(cb["full_step_tops"], 6)
         line["cpu_baseline"] = cb
     print(json.dumps(line))
 

@@ -62,6 +62,8 @@ typedef enum {
 
 /* Largest LoRA rank the LoRA calls accept. */
 #define SQ_MAX_LORA_RANK 128
+/* Most projections one group call stacks adapters for (Q/K/V is three). */
+#define SQ_MAX_LORA_PARTS 4
 
 /* Capability query ([GRP]: gate on what the library was compiled for).
  * Sets *supported to 1 if `device` is a gfx950 device this library has code
@@ -303,23 +305,54 @@ typedef struct {
   float lora_scale;
   void* T;                /* [M, r] bf16, row stride ldt */
   int64_t ldt;
-  void* workspace;        /* >= sq_lora_workspace_bytes(M, K, r) bytes when r > 0 */
+  void* workspace;        /* r > 0: >= sq_lora_workspace_bytes(M, K, r) bytes. r == 0:
+                             optional; with at least sq_w8a8_gemm_workspace_bytes(M, N, K)
+                             bytes (16-byte aligned) the GEMM runs as sq_w8a8_gemm_ws */
   size_t workspace_bytes;
   void* Y;                /* [M, N] dtype yt, row stride ldy */
   int yt;
   int64_t ldy;
+  /* Stacked adapters ([LoRA] Pitch, one adapter per projection of the group):
+   * lora_parts = P in 2..SQ_MAX_LORA_PARTS splits the N output columns into
+   * P projections, projection p owning columns [n_end[p-1], n_end[p]) and
+   * ranks [r_end[p-1], r_end[p]) (n_end[-1] = r_end[-1] = 0), with
+   * lora_n_end[P-1] == N and lora_r_end[P-1] == r, both strictly increasing;
+   * column bounds multiples of 16, rank bounds multiples of 8. B must then be
+   * zero outside each projection's ranks (block-diagonal), which is what
+   * stacking separate adapters gives; the GEMM epilogue skips the all-zero
+   * rank steps, and Y is bit for bit what the full rank range gives.
+   * lora_parts 0 or 1: every column uses all r ranks (no further rule). */
+  int lora_parts;
+  int64_t lora_n_end[SQ_MAX_LORA_PARTS];
+  int lora_r_end[SQ_MAX_LORA_PARTS];
 } sq_linear_group;
+
+/* Optional HIP events (hipEvent_t as void*, or NULL) that sq_linear_group_run
+ * records on its stream between its launches, so a caller can time each stage
+ * of the group without issuing the stages one by one:
+ *   begin        - before the first launch of the call;
+ *   quant_begin  - before the activation quant (FORWARD);
+ *   shrink_begin - before the LoRA shrink (FORWARD with r > 0);
+ *   gemm_begin   - before the GEMM (FORWARD);
+ *   gemm_end     - after the GEMM (FORWARD).
+ * FORWARD events are recorded only when M > 0. A failed record returns
+ * SQ_ERR_HIP. */
+typedef struct {
+  void* begin;
+  void* quant_begin;
+  void* shrink_begin;
+  void* gemm_begin;
+  void* gemm_end;
+} sq_group_events;
 
 /* Runs the phases selected by `flags` (a nonzero OR of SQ_GROUP_*) for group
  * `g`, in the order calibrate, fold, forward, all on `stream`. Every phase's
  * arguments are validated before anything is enqueued; on an argument error
- * nothing runs. gemm_begin / gemm_end: hipEvent_t handles (as void*) or NULL;
- * when given, FORWARD records them on `stream` immediately before and after
- * the GEMM launch (if M > 0), so the caller can time the GEMM alone; a failed
- * record returns SQ_ERR_HIP. The call
- * allocates nothing and may be captured into a HIP graph. */
-int sq_linear_group_run(const sq_linear_group* g, int flags, void* stream, void* gemm_begin,
-                        void* gemm_end);
+ * nothing runs. events: NULL, or the events to record between the launches
+ * (sq_group_events). The call allocates nothing and may be captured into a
+ * HIP graph. */
+int sq_linear_group_run(const sq_linear_group* g, int flags, void* stream,
+                        const sq_group_events* events);
 
 /* Bytes of device workspace sq_alpha_sweep needs for an [M, K] calibration
  * batch and [N, K] weights (0 if any size is <= 0). About
@@ -338,17 +371,20 @@ size_t sq_alpha_sweep_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * products, fp64 sums: within about K * 2^-53 of the exact value):
  *   err[2 i]     = sum_{m,n} (y[m, n] - y_ref[m, n])^2
  *   err[2 i + 1] = sum_{m,n} y_ref[m, n]^2
- * both summed in fp64 in a fixed order (deterministic). err[2i] / err[2i+1]
- * is the relative squared error at alphas[i]; the best alpha is the smallest.
+ * both summed in fp64 in a fixed order (deterministic). Then the choice:
+ *   rel[i] = err[2 i] / err[2 i + 1]   (fp64; 0 when err[2 i + 1] == 0)
+ *   best[0] = the i of the smallest rel[i], the first one on ties.
  * X: [M, K] dtype xt, row stride ldx; W: [N, K] dtype wt, row stride ldw
  * (N a multiple of 16). alphas: host array of n_alpha values in [0, 1]
- * (1 <= n_alpha <= 1024). err: device, [n_alpha, 2] fp64, written.
+ * (1 <= n_alpha <= 1024). err: device, [n_alpha, 2] fp64, written. rel:
+ * device [n_alpha] fp64, or NULL; best: device [1] int32, or NULL.
  * ws: device workspace, 256-byte aligned, at least
  * sq_alpha_sweep_workspace_bytes(M, N, K) bytes (SQ_ERR_WORKSPACE if not).
  * M == 0 writes nothing. */
 int sq_alpha_sweep(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* W,
                    int wt, int64_t N, int64_t ldw, const double* alphas, int n_alpha, int mode,
-                   double* err, void* ws, size_t ws_bytes, void* stream);
+                   double* err, double* rel, int32_t* best, void* ws, size_t ws_bytes,
+                   void* stream);
 
 #ifdef __cplusplus
 }

@@ -51,5 +51,19 @@ def test_gemm_tile_rule_prefers_whole_rounds():
 
 
 def test_cpu_baseline_on_the_tiny_workload():
-    cb = bench.cpu_baseline(get_workload("tiny_m16_k256_n256"), 8)
+    cb = bench.cpu_baseline(get_workload("tiny_m16_k256_n256"), 8, 64)
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
+    assert cb["nproc"] >= 1 and set(cb["stages_s"]) >= {"fold_quant", "quant", "gemm_dequant",
+                                                         "lora_shrink", "lora_expand"}
+    assert cb["full_step_tops"] < cb["value"]
+
+
+def test_cpu_baseline_on_segmented_adapters():
+    """The multi-tenant workload's oracle leg, on a tiny sample (rows and weight rows)."""
+    cb = bench.cpu_baseline(get_workload("multitenant_lora_m8192"), 4, 32)
+    assert cb["value"] > 0 and cb["stages_s"]["lora_expand"] > 0
+
+
+def test_tile_dims_known_for_every_rule():
+    for t in ("256x256", "256x192", "128x128", "generic", "skinny"):
+        assert len(bench.tile_dims(t)) == 2

@@ -297,33 +297,36 @@ def _group(**over):
     return d
 
 
-def _run(L, d, flags=7):
-    return L.sq_linear_group_run(ctypes.byref(d), flags, S, None, None)
+def _run(L, d, flags=7, events=None):
+    return L.sq_linear_group_run(ctypes.byref(d), flags, S,
+                                 ctypes.byref(events) if events is not None else None)
 
 
-def test_group_struct_layout_matches_header(tmp_path):
-    """The ctypes mirror of sq_linear_group has the C struct's size and field offsets."""
-    fields = [f for f, _ in sq.SqLinearGroup._fields_]
+@pytest.mark.parametrize("cname,py", [("sq_linear_group", sq.SqLinearGroup),
+                                      ("sq_group_events", sq.SqGroupEvents)])
+def test_group_struct_layout_matches_header(tmp_path, cname, py):
+    """The ctypes mirrors of the C structs have their size and field offsets."""
+    fields = [f for f, _ in py._fields_]
     src = tmp_path / "layout.c"
-    body = "".join(f'  printf(" %zu", offsetof(sq_linear_group, {f}));\n' for f in fields)
+    body = "".join(f'  printf(" %zu", offsetof({cname}, {f}));\n' for f in fields)
     src.write_text("#include <stdio.h>\n#include <stddef.h>\n"
                    f'#include "{HEADER}"\n'
                    "int main(void) {\n"
-                   '  printf("%zu", sizeof(sq_linear_group));\n'
+                   f'  printf("%zu", sizeof({cname}));\n'
                    + body +
                    '  printf("\\n");\n  return 0;\n}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-o", str(exe), str(src)], check=True)
     out = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
                                           check=True).stdout.split()]
-    assert out[0] == ctypes.sizeof(sq.SqLinearGroup)
-    assert out[1:] == [getattr(sq.SqLinearGroup, f).offset for f in fields]
+    assert out[0] == ctypes.sizeof(py)
+    assert out[1:] == [getattr(py, f).offset for f in fields]
 
 
 def test_group_validation(L):
     """Every phase's arguments are checked before anything is enqueued."""
     E = sq
-    assert L.sq_linear_group_run(None, 7, S, None, None) == E.SQ_ERR_INVALID_ARG
+    assert L.sq_linear_group_run(None, 7, S, None) == E.SQ_ERR_INVALID_ARG
     assert _run(L, _group(), flags=0) == E.SQ_ERR_INVALID_ARG
     assert _run(L, _group(), flags=8) == E.SQ_ERR_INVALID_ARG
     assert _run(L, _group(mode=5)) == E.SQ_ERR_INVALID_ARG
@@ -351,6 +354,41 @@ def test_group_validation(L):
     assert _run(L, d, flags=4) in (E.SQ_OK, E.SQ_ERR_UNSUPPORTED_ARCH)
 
 
+def _parts(d, parts):
+    d.lora_parts = len(parts)
+    for i, (n, r) in enumerate(parts):
+        d.lora_n_end[i], d.lora_r_end[i] = n, r
+    return d
+
+
+def test_group_lora_parts_validation(L):
+    """The projection table of stacked adapters: increasing column and rank
+    bounds ending at N and r, columns on 16, ranks on 8, at most 4 parts."""
+    E = sq
+    ok = (E.SQ_OK, E.SQ_ERR_UNSUPPORTED_ARCH)
+    assert _run(L, _parts(_group(), [(64, 8), (128, 16)]), flags=4) in ok
+    assert _run(L, _parts(_group(), [(128, 16)]), flags=4) in ok          # one part: no table
+    assert _run(L, _group(lora_parts=-1), flags=4) == E.SQ_ERR_INVALID_ARG
+    assert _run(L, _parts(_group(), [(64, 8), (112, 16)]), flags=4) == E.SQ_ERR_INVALID_ARG  # != N
+    assert _run(L, _parts(_group(), [(64, 8), (128, 24)]), flags=4) == E.SQ_ERR_INVALID_ARG  # != r
+    assert _run(L, _parts(_group(), [(56, 8), (128, 16)]), flags=4) == E.SQ_ERR_MISALIGNED
+    assert _run(L, _parts(_group(), [(64, 4), (128, 16)]), flags=4) == E.SQ_ERR_MISALIGNED
+    assert _run(L, _parts(_group(), [(64, 8), (64, 16)]), flags=4) == E.SQ_ERR_INVALID_ARG
+    assert _run(L, _parts(_group(), [(64, 8), (128, 8)]), flags=4) == E.SQ_ERR_INVALID_ARG
+    d = _parts(_group(), [(32, 8), (64, 16), (96, 16), (128, 16)])
+    d.lora_parts = 5
+    assert _run(L, d, flags=4) == E.SQ_ERR_INVALID_ARG
+    # the table is read only with LoRA
+    d = _group(r=0, A=None, B=None, T=None, workspace=None, workspace_bytes=0, lora_parts=9)
+    assert _run(L, d, flags=4) in ok
+
+
+def test_group_events_accepted(L):
+    """A group call with an events struct of NULL entries is valid (nothing recorded)."""
+    ev = sq.SqGroupEvents()
+    assert _run(L, _group(), flags=4, events=ev) in (sq.SQ_OK, sq.SQ_ERR_UNSUPPORTED_ARCH)
+
+
 def test_alpha_sweep_validation(L):
     f = L.sq_alpha_sweep
     A = (ctypes.c_double * 3)(0.0, 0.5, 1.0)
@@ -361,9 +399,9 @@ def test_alpha_sweep_validation(L):
     W256 = ctypes.c_void_p(0x100000)
 
     def call(X=P, xt=sq.SQ_BF16, M=64, K=128, ldx=128, W=P, wt=sq.SQ_BF16, N=32, ldw=128, al=A,
-             n=3, mode=0, err=P, ws=W256, wsb=None):
-        return f(X, xt, M, K, ldx, W, wt, N, ldw, al, n, mode, err, ws, need if wsb is None else wsb,
-                 S)
+             n=3, mode=0, err=P, rel=NULL, best=NULL, ws=W256, wsb=None):
+        return f(X, xt, M, K, ldx, W, wt, N, ldw, al, n, mode, err, rel, best, ws,
+                 need if wsb is None else wsb, S)
     assert call(W=NULL) == sq.SQ_ERR_INVALID_ARG
     assert call(N=24) == sq.SQ_ERR_MISALIGNED                      # N % 16
     assert call(ldw=64) == sq.SQ_ERR_INVALID_ARG                   # ldw < K
@@ -372,6 +410,8 @@ def test_alpha_sweep_validation(L):
     assert call(al=BAD, n=2) == sq.SQ_ERR_INVALID_ARG              # alpha outside [0, 1]
     assert call(mode=3) == sq.SQ_ERR_INVALID_ARG
     assert call(err=P4) == sq.SQ_ERR_MISALIGNED
+    assert call(rel=P4) == sq.SQ_ERR_MISALIGNED                    # fp64 output
+    assert call(best=ctypes.c_void_p(0x10002)) == sq.SQ_ERR_MISALIGNED
     assert call(ws=NULL) == sq.SQ_ERR_WORKSPACE
     assert call(wsb=need - 1) == sq.SQ_ERR_WORKSPACE
     assert call(ws=ctypes.c_void_p(0x10010)) == sq.SQ_ERR_MISALIGNED  # not 256-byte aligned

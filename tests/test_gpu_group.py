@@ -9,6 +9,7 @@ test_gpu_workloads.py.
 import pytest
 import torch
 
+import bench
 import w8a8_smoothquant_int8_amd as sq
 from synth.workloads import get_workload
 from w8a8_smoothquant_int8_amd.pipeline import ALL_PHASES, LinearGroup
@@ -20,7 +21,9 @@ def make_group(wl, inp, lora=True, modes=("dynamic",)):
     W = wl.w_group(inp).cuda()
     rows = wl.group_rows(inp)
     loras = {p: tuple(t.cuda() for t in wl.lora(p)) for p in rows} if (lora and wl.lora_rank) else {}
-    return LinearGroup(W, rows, wl.alpha, wl.out_dtype, wl.M, lora=loras, modes=modes)
+    segs = {p: bench.segmented_lora(wl, p, torch) for p in rows} if (lora and wl.segmented) else {}
+    return LinearGroup(W, rows, wl.alpha, wl.out_dtype, wl.M, lora=loras, seg_lora=segs,
+                       modes=modes)
 
 
 def outputs(g, mode="dynamic"):
@@ -41,11 +44,24 @@ def assert_same(a, b):
         assert torch.equal(x, y), i
 
 
-@pytest.mark.parametrize("inp", ["attn_in", "o_in", "mlp_in", "down_in"])
-def test_group_run_equals_separate_calls(inp):
-    wl = get_workload("llama3_8b_proj_m2048")
+@pytest.mark.parametrize("name,inp", [("llama3_8b_proj_m2048", "attn_in"),
+                                      ("llama3_8b_proj_m2048", "o_in"),
+                                      ("llama3_8b_proj_m2048", "mlp_in"),
+                                      ("llama3_8b_proj_m2048", "down_in"),
+                                      ("llama2_70b_mlp_m8192", "mlp_in"),
+                                      ("llama2_70b_mlp_m8192", "down_in"),
+                                      ("multitenant_lora_m8192", "attn_in"),
+                                      ("multitenant_lora_m8192", "o_in"),
+                                      ("opt13b_layer_decode_m64", "fc2_in")])
+def test_group_run_equals_separate_calls(name, inp):
+    """Bit for bit: the group call (stacked adapters with their rank windows,
+    or segmented adapters after it, or the split-K decode GEMM) against the
+    single-purpose calls (full-rank stacked GEMM epilogue, separate GEMM)."""
+    wl = get_workload(name)
     g = make_group(wl, inp)
-    assert g.fused
+    assert g.fused == bool(wl.lora_rank)
+    if wl.lora_rank and len(g.rows) > 1:
+        assert g.lora_parts is not None
     X, Xc = wl.x(inp).cuda(), wl.x_cal(inp).cuda()
     ref = separate(g, X, Xc)
     for t in (g.act_max, g.s, g.Wq, g.w_scale, g.Xq, g.a_scale, g.Yg):
@@ -76,14 +92,18 @@ def test_group_run_phases_one_by_one_and_events():
     torch.cuda.synchronize()
     ref = outputs(g)
     g.Yg.zero_()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    e1.record()
+    evs = {k: torch.cuda.Event(enable_timing=True) for k in sq.EVENT_FIELDS}
+    for e in evs.values():
+        e.record()
     for flags in (sq.SQ_GROUP_CALIBRATE, sq.SQ_GROUP_FOLD, sq.SQ_GROUP_FORWARD):
-        g.run(X, Xc, flags=flags, gemm_begin=e0, gemm_end=e1)
+        g.run(X, Xc, flags=flags, events=sq.sq_group_events(**evs))
     torch.cuda.synchronize()
     assert_same(outputs(g), ref)
-    assert e0.elapsed_time(e1) > 0.0
+    # the forward call recorded its events in launch order: quant, shrink, GEMM
+    assert evs["begin"].elapsed_time(evs["quant_begin"]) >= 0.0
+    assert evs["quant_begin"].elapsed_time(evs["shrink_begin"]) > 0.0
+    assert evs["shrink_begin"].elapsed_time(evs["gemm_begin"]) > 0.0
+    assert evs["gemm_begin"].elapsed_time(evs["gemm_end"]) > 0.0
 
 
 def test_group_run_graph_replays_match_eager():

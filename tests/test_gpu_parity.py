@@ -248,13 +248,13 @@ def test_gemm_i32_extreme_magnitude():
 # Decode shapes whose K is split across blocks with a workspace (two row tiles
 # and one; 4, 4 and 9 slices; a ragged last column tile; the last slice
 # shorter than the others at K = 20352), plus shapes that take no workspace
-# (too many column tiles; K too short to split): bit-exact against the oracle
-# and the unsplit call.
+# (too many column tiles; K too short to split; fewer than 4 slices wanted, as
+# at N = 8192, K = 8192): bit-exact against the oracle and the unsplit call.
 @pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("mode", ["dynamic", "static"])
 @pytest.mark.parametrize("M,N,K,split", [(64, 5120, 20480, True), (17, 1040, 8192, True),
                                          (40, 208, 20352, True), (64, 20480, 5120, False),
-                                         (64, 5120, 5120, False)])
+                                         (64, 5120, 5120, False), (64, 8192, 8192, False)])
 def test_gemm_ws_split_k(out, mode, M, N, K, split):
     rng = np.random.default_rng(M + N + K)
     xq = rng.integers(-127, 128, (M, K)).astype(np.int8)

@@ -1,21 +1,35 @@
-"""Every workload at full size through the pipeline the benchmark times (GPU).
+"""Every workload at full size through the call the benchmark times (GPU).
 
-The whole path runs on the GPU at the workload's real shapes. The oracle then
-recomputes what it can afford one output at a time: the calibration maxima and
-the smoothing vector in full, and for sampled rows of X and sampled rows of W
-the INT8 codes and scales, the dequantized outputs at the sampled (row,
-column) pairs and the LoRA-added outputs there. Properties that hold at any
-size (|code| <= 127, every nonzero row reaching 127) are checked on the full
-GPU outputs. The tiny workload is compared in full.
+Each input group runs as one sq_linear_group_run call (calibrate, smooth and
+fold, quantize, LoRA shrink, GEMM with the dequant and LoRA epilogue; then the
+segmented LoRA calls for per-request adapters), at the workload's real
+shapes, in the launch configuration bench.py uses. The oracle then recomputes
+what it can afford one output at a time:
+  - the calibration maxima and the smoothing vector, in full;
+  - the weight codes and scales of sampled weight rows, the activation codes
+    and scales of sampled activation rows;
+  - the outputs at every (row, column) pair of the samples. The samples take
+    one row in every tile row and one column in every tile column of the
+    tile configuration the library picks for the group's GEMM (at an offset
+    inside the tile that changes from tile to tile, so different waves and
+    lanes are checked), plus the first and last row and column, each
+    projection's edges and the rows holding the largest outliers: every
+    output tile has compared elements;
+  - for the group's first projection, one whole tile-wide column band over
+    all M rows, in chunks of rows.
+Properties that hold at any size (|code| <= 127, every nonzero row reaching
+127) are checked on the full GPU outputs. The tiny workload is compared in
+full.
 """
 import numpy as np
 import pytest
 import torch
 
+import bench
 import oracle.sq_oracle as O
 import w8a8_smoothquant_int8_amd as sq
-from synth.workloads import WORKLOADS, get_workload, sample_rows
-from w8a8_smoothquant_int8_amd.pipeline import LinearGroup, SegmentedLora
+from synth.workloads import WORKLOADS, get_workload
+from w8a8_smoothquant_int8_amd.pipeline import ALL_PHASES, LinearGroup, SegmentedLora
 
 pytestmark = pytest.mark.gpu
 F32 = np.float32
@@ -60,6 +74,50 @@ def build_segmented(wl, proj, seed=0):
     return sl, seg, As, Bs
 
 
+def per_tile(n, t, salt):
+    """One index in every tile [i t, min((i + 1) t, n)), at an offset inside the
+    tile that moves from tile to tile."""
+    out = []
+    for i in range(-(-n // t)):
+        lo, hi = i * t, min(n, (i + 1) * t)
+        out.append(lo + (i * salt + 5) % (hi - lo))
+    return out
+
+
+def tile_samples(M, Ntot, K, rows, extra_rows=()):
+    """Sampled rows and columns of a group output: every tile row and tile
+    column of the library's tile configuration, plus the edges."""
+    tile = bench.gemm_tile(M, Ntot, K)
+    BM, BN = bench.tile_dims(tile)
+    if tile == "skinny":
+        BM = 8            # M <= 64: rows of both 32-row MFMA tiles, 8 apart
+    r = set(per_tile(M, BM, 37)) | {0, M - 1} | {int(v) for v in extra_rows if 0 <= v < M}
+    c = set(per_tile(Ntot, BN, 53)) | {0, Ntot - 1}
+    for r0, r1 in rows.values():
+        c |= {r0, r1 - 1}
+    return np.array(sorted(r), np.int64), np.array(sorted(c), np.int64), tile, BN
+
+
+def ref_outputs(wl, p, rows_m, cols_g, r0, Xn, xq_ref, a_use, Wn, s_ref, host, loras, segs):
+    """The oracle's outputs of projection p at rows_m x cols_g (group columns)."""
+    wq_p, ws_p = O.fold_and_quantize_weights(Wn[cols_g], s_ref)
+    y_ref = O.dequantize(O.int8_gemm(xq_ref, wq_p), a_use, ws_p, wl.out_dtype)
+    if p in loras:
+        a, b = host[p]
+        return O.lora_apply(y_ref, Xn[rows_m], wl.dtype, a, b[cols_g - r0], 1.0, wl.out_dtype), True
+    if p in segs:
+        seg, As, Bs = host[p]
+        y_ref = np.array(y_ref, copy=True)
+        gidx = np.searchsorted(seg["seg_start"], rows_m, side="right") - 1
+        for i, m in enumerate(rows_m):
+            ad = seg["seg_adapter"][gidx[i]]
+            if ad >= 0:
+                y_ref[i:i + 1] = O.lora_apply(y_ref[i:i + 1], Xn[m:m + 1], wl.dtype, As[ad],
+                                              Bs[ad][cols_g - r0], 1.0, wl.out_dtype)
+        return y_ref, True
+    return y_ref, False
+
+
 def check_group(wl, inp, seed=0):
     X = wl.x(inp, seed)
     Xc = wl.x_cal(inp, seed)
@@ -75,44 +133,45 @@ def check_group(wl, inp, seed=0):
             sl, seg, As, Bs = build_segmented(wl, p, seed)
             segs[p] = sl
             host[p] = (seg, [t.float().numpy() for t in As], [t.float().numpy() for t in Bs])
-    Xd = X.cuda()
+    Xd, Xcd = X.cuda(), Xc.cuda()
     g = LinearGroup(W.cuda(), rows, wl.alpha, wl.out_dtype, wl.M, lora=loras, seg_lora=segs,
                     modes=wl.act_modes)
-    g.calibrate(Xc.cuda())
-    g.fold()
-    torch.cuda.synchronize()
-
-    # calibration maxima and smoothing vector, in full
+    if wl.lora_rank and len(rows) > 1:
+        assert g.lora_parts is not None          # the run takes the projections' rank windows
     Xn, Xcn, Wn = X.float().numpy(), Xc.float().numpy(), W.float().numpy()
     act_max = O.calibrate_absmax(Xcn)
-    assert bits_equal(npf(g.act_max), act_max)
     s_ref = O.smoothing_scale(act_max, O.weight_absmax(Wn), wl.alpha)
-    s_gpu = npf(g.s)
-    if not bits_equal(s_gpu, s_ref):
-        # fp64 pow may land one fp32 ulp apart at a rounding boundary (alpha != 0.5);
-        # then the GPU's later stages run again on the oracle's s, so the comparison
-        # below checks each stage on the oracle's own inputs.
-        assert wl.alpha != 0.5
-        ulps = np.abs(s_gpu.view(np.int32).astype(np.int64) - s_ref.view(np.int32).astype(np.int64))
-        assert ulps.max() <= 1 and np.count_nonzero(ulps) <= 2
-        g.s.copy_(torch.from_numpy(s_ref))
-        sq.sq_fold_quant_weights(g.W, g.s, g.Wq, g.w_scale)
-        sq.sq_static_act_scale(g.act_max, g.s, g.static_scale)
-
-    Ntot = W.shape[0]
-    n_rows = sample_rows(Ntot, max(1, Ntot // 96))
-    wq_ref, wsc_ref = O.fold_and_quantize_weights(Wn[n_rows], s_ref)
-    assert bits_equal(g.Wq[n_rows].cpu().numpy(), wq_ref)
-    assert bits_equal(npf(g.w_scale)[n_rows], wsc_ref)
-    # properties of the full weight codes
-    assert int(g.Wq.abs().amax()) <= 127
-    assert bool((g.Wq[g.W.abs().amax(dim=1) > 0].abs().amax(dim=1) == 127).all())
-
+    Ntot, K = W.shape
     outlier_rows = np.argsort(-np.abs(Xn).max(axis=1))[:4]
-    m_rows = sample_rows(wl.M, max(1, wl.M // 96), extra=outlier_rows)
+    m_rows, cols, tile, BN = tile_samples(wl.M, Ntot, K, rows, outlier_rows)
+    print(f"[{wl.name}/{inp}] tile {tile}: {len(m_rows)} rows x {len(cols)} columns", flush=True)
+
     for mode in wl.act_modes:
-        Y = {p: t.clone() for p, t in g.forward(Xd, mode).items()}
+        g.run(Xd, Xcd, ALL_PHASES, mode=mode)
         torch.cuda.synchronize()
+        assert bits_equal(npf(g.act_max), act_max)
+        s_gpu = npf(g.s)
+        if not bits_equal(s_gpu, s_ref):
+            # fp64 pow may land one fp32 ulp apart at a rounding boundary (alpha != 0.5);
+            # then the later stages run again on the oracle's s, so the comparison
+            # below checks each stage on the oracle's own inputs.
+            assert wl.alpha != 0.5
+            ulps = np.abs(s_gpu.view(np.int32).astype(np.int64) - s_ref.view(np.int32).astype(np.int64))
+            assert ulps.max() <= 1 and np.count_nonzero(ulps) <= 2
+            g.s.copy_(torch.from_numpy(s_ref))
+            sq.sq_fold_quant_weights(g.W, g.s, g.Wq, g.w_scale)
+            sq.sq_static_act_scale(g.act_max, g.s, g.static_scale)
+            g.run(Xd, Xcd, sq.SQ_GROUP_FORWARD, mode=mode)
+            torch.cuda.synchronize()
+        Yg = g.Yg.clone()
+
+        # weight codes and scales of the sampled output columns; properties in full
+        wq_ref, wsc_ref = O.fold_and_quantize_weights(Wn[cols], s_ref)
+        assert bits_equal(g.Wq[cols].cpu().numpy(), wq_ref)
+        assert bits_equal(npf(g.w_scale)[cols], wsc_ref)
+        assert int(g.Wq.abs().amax()) <= 127
+        assert bool((g.Wq[g.W.abs().amax(dim=1) > 0].abs().amax(dim=1) == 127).all())
+
         if mode == "dynamic":
             xq_ref, a_ref = O.quantize_per_token(Xn[m_rows], s_ref)
             assert bits_equal(npf(g.a_scale)[m_rows], a_ref)
@@ -123,29 +182,34 @@ def check_group(wl, inp, seed=0):
         else:
             a_use = O.static_activation_scale(act_max, s_ref)
             assert npf(g.static_scale)[0] == a_use
-            xq_ref, clipped = O.quantize_per_tensor_static(Xn[m_rows], s_ref, a_use)
+            xq_ref, _clipped = O.quantize_per_tensor_static(Xn[m_rows], s_ref, a_use)
         assert bits_equal(g.Xq[m_rows].cpu().numpy(), xq_ref)
+
+        got_all = out_np(Yg, wl.out_dtype)
         for p, (r0, r1) in rows.items():
-            cols = sample_rows(r1 - r0, max(1, (r1 - r0) // 64))
-            wq_p, ws_p = O.fold_and_quantize_weights(Wn[r0 + cols], s_ref)
-            y_ref = O.dequantize(O.int8_gemm(xq_ref, wq_p), a_use, ws_p, wl.out_dtype)
-            got = out_np(Y[p], wl.out_dtype)[np.ix_(m_rows, cols)]
-            if p in loras:
-                a, b = host[p]
-                y_ref = O.lora_apply(y_ref, Xn[m_rows], wl.dtype, a, b[cols], 1.0, wl.out_dtype)
-                assert lora_ok(got, y_ref), p
-            elif p in segs:
-                seg, As, Bs = host[p]
-                y_ref = np.array(y_ref, copy=True)
-                gidx = np.searchsorted(seg["seg_start"], m_rows, side="right") - 1
-                for i, m in enumerate(m_rows):
-                    ad = seg["seg_adapter"][gidx[i]]
-                    if ad >= 0:
-                        y_ref[i:i + 1] = O.lora_apply(y_ref[i:i + 1], Xn[m:m + 1], wl.dtype, As[ad],
-                                                      Bs[ad][cols], 1.0, wl.out_dtype)
-                assert lora_ok(got, y_ref), p
+            cg = cols[(cols >= r0) & (cols < r1)]
+            y_ref, lora = ref_outputs(wl, p, m_rows, cg, r0, Xn, xq_ref, a_use, Wn, s_ref, host,
+                                      loras, segs)
+            got = got_all[np.ix_(m_rows, cg)]
+            assert (lora_ok(got, y_ref) if lora else bits_equal(got, y_ref)), (mode, p)
+
+        # one whole tile-wide column band of the first projection, all rows
+        p0, (r0, r1) = next(iter(rows.items()))
+        b0 = r0 + ((r1 - r0) // 2 // BN) * BN
+        band = np.arange(b0, min(b0 + BN, r1), dtype=np.int64)
+        for c0 in range(0, wl.M, 2048):
+            mr = np.arange(c0, min(c0 + 2048, wl.M), dtype=np.int64)
+            if mode == "dynamic":
+                xq_b, a_b = O.quantize_per_token(Xn[mr], s_ref)
+                assert bits_equal(npf(g.a_scale)[mr], a_b)
             else:
-                assert bits_equal(got, y_ref), p
+                a_b = a_use
+                xq_b, _ = O.quantize_per_tensor_static(Xn[mr], s_ref, a_use)
+            assert bits_equal(g.Xq[mr].cpu().numpy(), xq_b)
+            y_ref, lora = ref_outputs(wl, p0, mr, band, r0, Xn, xq_b, a_b, Wn, s_ref, host,
+                                      loras, segs)
+            got = got_all[np.ix_(mr, band)]
+            assert (lora_ok(got, y_ref) if lora else bits_equal(got, y_ref)), (mode, p0, c0)
 
 
 @pytest.mark.parametrize("name", sorted(WORKLOADS))

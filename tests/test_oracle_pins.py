@@ -394,6 +394,7 @@ def test_segmented_reduces_to_single_adapter():
     assert np.array_equal(one, O.lora_apply(y, x, "bf16", a, b, 1.0, "bf16"))
     # mixed: each segment equals single-adapter LoRA on its rows; adapter -1 leaves rows alone
     mix = O.lora_apply_segmented(y, x, "bf16", seg, [1, -1, 0, 1], [a, a2], [b, b2], 1.0, "bf16")
+    assert np.array_equal(mix[:30], O.lora_apply(y[:30], x[:30], "bf16", a2, b2, 1.0, "bf16"))
     assert np.array_equal(mix[30:31], y[30:31])
     assert np.array_equal(mix[31:77], O.lora_apply(y[31:77], x[31:77], "bf16", a, b, 1.0, "bf16"))
     assert np.array_equal(mix[77:], O.lora_apply(y[77:], x[77:], "bf16", a2, b2, 1.0, "bf16"))
@@ -458,6 +459,17 @@ def test_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(O, "lora_shrink", lambda x, dt, a: orig_shrink(x, "bf16", a) * 0)
     assert _fails(lambda: test_brute_force_lora(1))
     monkeypatch.setattr(O, "lora_shrink", orig_shrink)
+
+    # segment bounds off by one: every request starts one row late (or early)
+    orig_seg = O.lora_apply_segmented
+    for shift in (1, -1):
+        def seg_shifted(y, x, dt, seg_start, seg_adapter, A, B, scale, out, shift=shift):
+            st = [min(max(int(v) + shift, 0), len(y)) if 0 < i < len(seg_start) - 1 else int(v)
+                  for i, v in enumerate(seg_start)]
+            return orig_seg(y, x, dt, st, seg_adapter, A, B, scale, out)
+        monkeypatch.setattr(O, "lora_apply_segmented", seg_shifted)
+        assert _fails(test_segmented_reduces_to_single_adapter)
+    monkeypatch.setattr(O, "lora_apply_segmented", orig_seg)
 
 
 def test_static_clip_count_brute_force_ties():

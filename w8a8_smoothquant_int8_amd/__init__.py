@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Sequence
+from typing import Optional, Sequence, Tuple
 
 import torch
 
@@ -29,6 +29,7 @@ SQ_ERR_HIP = -6
 SQ_F32, SQ_F16, SQ_BF16 = 0, 1, 2
 SQ_ACT_PER_TOKEN_DYNAMIC, SQ_ACT_PER_TENSOR_STATIC = 0, 1
 SQ_MAX_LORA_RANK = 128
+SQ_MAX_LORA_PARTS = 4
 
 MODES = {"dynamic": SQ_ACT_PER_TOKEN_DYNAMIC, "static": SQ_ACT_PER_TENSOR_STATIC}
 _DT = {torch.float32: SQ_F32, torch.float16: SQ_F16, torch.bfloat16: SQ_BF16}
@@ -68,10 +69,11 @@ SIGNATURES = {
     "sq_lora_apply_segmented": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp,
                                          _c_int, _vp, _vp, _vp, _c_int, _c_f, _vp, _c_int, _c_i64,
                                          _c_i64, _vp, _c_sz, _vp]),
-    "sq_linear_group_run": (_c_int, [_vp, _c_int, _vp, _vp, _vp]),
+    "sq_linear_group_run": (_c_int, [_vp, _c_int, _vp, _vp]),
     "sq_alpha_sweep_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64]),
     "sq_alpha_sweep": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _c_int, _c_i64, _c_i64,
-                                ctypes.POINTER(_c_d), _c_int, _c_int, _vp, _vp, _c_sz, _vp]),
+                                ctypes.POINTER(_c_d), _c_int, _c_int, _vp, _vp, _vp, _vp, _c_sz,
+                                _vp]),
 }
 
 SQ_GROUP_CALIBRATE, SQ_GROUP_FOLD, SQ_GROUP_FORWARD = 1, 2, 4
@@ -88,7 +90,15 @@ class SqLinearGroup(ctypes.Structure):
         ("A", _vp), ("B", _vp), ("r", _c_int), ("lora_scale", _c_f), ("T", _vp), ("ldt", _c_i64),
         ("workspace", _vp), ("workspace_bytes", _c_sz),
         ("Y", _vp), ("yt", _c_int), ("ldy", _c_i64),
+        ("lora_parts", _c_int), ("lora_n_end", _c_i64 * SQ_MAX_LORA_PARTS),
+        ("lora_r_end", _c_int * SQ_MAX_LORA_PARTS),
     ]
+
+
+class SqGroupEvents(ctypes.Structure):
+    """Mirror of the C struct sq_group_events (include/sq.h)."""
+    _fields_ = [("begin", _vp), ("quant_begin", _vp), ("shrink_begin", _vp),
+                ("gemm_begin", _vp), ("gemm_end", _vp)]
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -336,9 +346,12 @@ def sq_linear_group_desc(X: torch.Tensor, X_cal: Optional[torch.Tensor], W: torc
                          a_scale: torch.Tensor, Y: torch.Tensor, A: Optional[torch.Tensor] = None,
                          B: Optional[torch.Tensor] = None, T: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None,
-                         lora_scale: float = 1.0) -> SqLinearGroup:
+                         lora_scale: float = 1.0,
+                         lora_parts: Optional[Sequence[Tuple[int, int]]] = None) -> SqLinearGroup:
     """Fill an sq_linear_group from tensors. The struct holds raw pointers:
-    the tensors must stay alive (and in place) while it is used."""
+    the tensors must stay alive (and in place) while it is used.
+    lora_parts: [(n_end, r_end)] per projection of a block-diagonal B (the
+    projection's last output column + 1 and last stacked rank + 1)."""
     M, K = X.shape
     N = W.shape[0]
     d = SqLinearGroup()
@@ -350,24 +363,43 @@ def sq_linear_group_desc(X: torch.Tensor, X_cal: Optional[torch.Tensor], W: torc
     d.act_max, d.s, d.Wq, d.w_scale = (act_max.data_ptr(), s.data_ptr(), Wq.data_ptr(),
                                        w_scale.data_ptr())
     d.Xq, d.a_scale = Xq.data_ptr(), a_scale.data_ptr()
+    if workspace is not None:
+        d.workspace, d.workspace_bytes = workspace.data_ptr(), workspace.numel()
     if A is not None:
         d.A, d.B, d.r, d.lora_scale = A.data_ptr(), B.data_ptr(), A.shape[0], float(lora_scale)
         d.T, d.ldt = T.data_ptr(), _ld(T)
-        d.workspace, d.workspace_bytes = workspace.data_ptr(), workspace.numel()
+        if lora_parts and len(lora_parts) > 1:
+            if len(lora_parts) > SQ_MAX_LORA_PARTS:
+                raise ValueError(f"at most {SQ_MAX_LORA_PARTS} LoRA parts")
+            d.lora_parts = len(lora_parts)
+            for i, (n_end, r_end) in enumerate(lora_parts):
+                d.lora_n_end[i], d.lora_r_end[i] = int(n_end), int(r_end)
     d.Y, d.yt, d.ldy = Y.data_ptr(), _dt(Y), _ld(Y)
     return d
 
 
-def sq_linear_group_run(desc: SqLinearGroup, flags: int, stream=None, gemm_begin=None,
-                        gemm_end=None) -> None:
-    """gemm_begin / gemm_end: torch.cuda.Event objects (already created, e.g.
-    recorded once) or raw hipEvent_t handles, or None."""
-    def ev(e):
-        if e is None:
-            return None
-        return ctypes.c_void_p(e.cuda_event if hasattr(e, "cuda_event") else int(e))
+EVENT_FIELDS = ("begin", "quant_begin", "shrink_begin", "gemm_begin", "gemm_end")
+
+
+def sq_group_events(**events) -> SqGroupEvents:
+    """An sq_group_events from torch.cuda.Event objects (already created, e.g.
+    recorded once) or raw hipEvent_t handles; missing or None entries are not
+    recorded."""
+    ev = SqGroupEvents()
+    for k, e in events.items():
+        if k not in EVENT_FIELDS:
+            raise KeyError(k)
+        if e is not None:
+            setattr(ev, k, e.cuda_event if hasattr(e, "cuda_event") else int(e))
+    return ev
+
+
+def sq_linear_group_run(desc: SqLinearGroup, flags: int, stream=None,
+                        events: Optional[SqGroupEvents] = None) -> None:
+    """events: None or an SqGroupEvents (sq_group_events(...))."""
     _check("sq_linear_group_run", lib().sq_linear_group_run(
-        ctypes.byref(desc), int(flags), _stream(stream), ev(gemm_begin), ev(gemm_end)))
+        ctypes.byref(desc), int(flags), _stream(stream),
+        ctypes.byref(events) if events is not None else None))
 
 
 def sq_alpha_sweep_workspace_bytes(M: int, N: int, K: int) -> int:
@@ -375,12 +407,16 @@ def sq_alpha_sweep_workspace_bytes(M: int, N: int, K: int) -> int:
 
 
 def sq_alpha_sweep(X: torch.Tensor, W: torch.Tensor, alphas, err: torch.Tensor, ws: torch.Tensor,
-                   mode: str = "dynamic", stream=None) -> None:
+                   mode: str = "dynamic", rel: Optional[torch.Tensor] = None,
+                   best: Optional[torch.Tensor] = None, stream=None) -> None:
     """err: [len(alphas), 2] float64 on the device, written with (sum of squared
-    errors, sum of squared reference outputs) per alpha."""
+    errors, sum of squared reference outputs) per alpha. rel: None or a
+    [len(alphas)] float64 device tensor (err[:, 0] / err[:, 1]); best: None or
+    a [1] int32 device tensor (index of the smallest rel, the first on ties)."""
     M, K = X.shape
     N = W.shape[0]
     a = (_c_d * len(alphas))(*[float(v) for v in alphas])
     _check("sq_alpha_sweep", lib().sq_alpha_sweep(
         _ptr(X), _dt(X), M, K, _ld(X), _ptr(W), _dt(W), N, _ld(W), a, len(alphas), MODES[mode],
-        _ptr(err), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(err), _ptr(rel), _ptr(best), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))

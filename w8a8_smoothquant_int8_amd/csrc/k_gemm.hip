@@ -43,13 +43,42 @@ __device__ __forceinline__ int swz(int r, int c) { return (c ^ ((r >> 1) & 7)) <
 
 // Optional LoRA delta added in the epilogue ([LoRA] Pitch): T [M, r] bf16
 // (row stride ldt) and B [N, r] bf16, Y = out(out(y) + scale * T B^T).
+//
+// Parts: adapters of projections that share one input are stacked along r,
+// and B is block-diagonal (part p = columns [n_end[p-1], n_end[p]) uses only
+// ranks [r_end[p-1], r_end[p]); B is zero elsewhere). A tile then multiplies
+// only the ranks of the parts its columns touch, rounded out to whole 16-rank
+// MFMA steps: the steps it leaves out hold only zero products, and the steps
+// it keeps are the same 16-aligned steps in the same order, so the result is
+// that of the full rank range bit for bit. parts <= 1: every column uses all
+// r ranks.
+constexpr int kMaxLoraParts = 4;
 struct LoraEpi {
   const unsigned short* T;
   int64_t ldt;
   const unsigned short* B;
   int r;
   float scale;
+  int parts;
+  int n_end[kMaxLoraParts];
+  int r_end[kMaxLoraParts];
 };
+
+// Rank window [klo, khi) for output columns [c0, c1) (c1 exclusive, c0 < c1).
+__device__ __forceinline__ void lora_window(const LoraEpi& le, int c0, int c1, int& klo, int& khi) {
+  if (le.parts <= 1) {
+    klo = 0;
+    khi = le.r;
+    return;
+  }
+  int plo = 0;
+  while (plo + 1 < le.parts && le.n_end[plo] <= c0) ++plo;
+  int phi = plo;
+  while (phi + 1 < le.parts && le.n_end[phi] < c1) ++phi;
+  klo = (plo == 0 ? 0 : le.r_end[plo - 1]) & ~15;
+  khi = (le.r_end[phi] + 15) & ~15;
+  khi = khi < le.r ? khi : le.r;
+}
 
 // Map a block to its (tile_m, tile_n), grouping tiles by XCD. Returns false
 // for padding blocks beyond the last tile.
@@ -175,6 +204,8 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], int row0, int col0
   const int lane = threadIdx.x & 63;
   const int lrow = lane & 31, lhalf = lane >> 5;
   const float as_static = (STATIC_A && OUT != OUT_I32) ? a_scale[0] : 0.0f;
+  int klo = 0, khi = 0;
+  if constexpr (LORA != 0) lora_window(le, col0, col0 + 32 * TN < N ? col0 + 32 * TN : N, klo, khi);
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     float ws[16];
@@ -199,10 +230,10 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], int row0, int col0
           v16f d;
 #pragma unroll
           for (int q = 0; q < 16; ++q) d[q] = LORA == 1 ? round_out<OUT>(y[q]) : 0.0f;
-          for (int k0 = 0; k0 < le.r; k0 += 16) {
+          for (int k0 = klo; k0 < khi; k0 += 16) {
             const int k = k0 + 8 * lhalf;
             uint4 tu = make_uint4(0, 0, 0, 0), bu = make_uint4(0, 0, 0, 0);
-            if (k < le.r) {
+            if (k < khi) {
               tu = *(const uint4*)(le.T + mr * le.ldt + k);
               bu = *(const uint4*)(le.B + nr * le.r + k);
             }
@@ -264,11 +295,11 @@ __device__ __forceinline__ void stage_rows(const char* src, char* dst, int rows,
 }
 
 // LoRA ranks [k_base, k_base + 64) of the block's T rows and B rows into LDS
-// at dst: T [BM][rp] then B [BN][rp] bf16, rp = min(64, r - k_base).
+// at dst: T [BM][rp] then B [BN][rp] bf16, rp = min(64, khi - k_base).
 template <int NW, int BM, int BN>
-__device__ __forceinline__ void stage_lora(const LoraEpi& le, char* dst, int k_base, int m0, int n0,
-                                           int M, int N, int wave, int lane) {
-  const int rp = le.r - k_base < kStageRanks ? le.r - k_base : kStageRanks;
+__device__ __forceinline__ void stage_lora(const LoraEpi& le, char* dst, int k_base, int khi, int m0,
+                                           int n0, int M, int N, int wave, int lane) {
+  const int rp = khi - k_base < kStageRanks ? khi - k_base : kStageRanks;
   const int r16 = rp / 8;
   stage_rows<NW>((const char*)le.T, dst, BM, r16, wave, lane, [&](int row) -> int64_t {
     const int64_t m = m0 + row < M ? m0 + row : M - 1;
@@ -285,7 +316,7 @@ __device__ __forceinline__ void epilogue_staged(v16i (&acc)[BM / WM / 32][BN / W
                                                 const char* s_sc, char* s_lora, int m0, int n0,
                                                 int wm, int wn, int M, int N,
                                                 const float* __restrict__ a_scale, void* __restrict__ Y,
-                                                int64_t ldy, const LoraEpi& le) {
+                                                int64_t ldy, const LoraEpi& le, int klo, int khi) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
   const int lane = threadIdx.x & 63;
@@ -324,15 +355,15 @@ __device__ __forceinline__ void epilogue_staged(v16i (&acc)[BM / WM / 32][BN / W
   }
 
   if constexpr (LORA == 1) {
-    for (int k_base = 0; k_base < le.r; k_base += kStageRanks) {
-      if (k_base > 0) {
+    for (int k_base = klo; k_base < khi; k_base += kStageRanks) {
+      if (k_base > klo) {
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of the last pass are done
         __builtin_amdgcn_s_barrier();         // every wave is done with the previous ranks
-        stage_lora<NW, BM, BN>(le, s_lora, k_base, m0, n0, M, N, wave, lane);
+        stage_lora<NW, BM, BN>(le, s_lora, k_base, khi, m0, n0, M, N, wave, lane);
         __builtin_amdgcn_s_waitcnt(0x0070);
         __builtin_amdgcn_s_barrier();
       }
-      const int rp = le.r - k_base < kStageRanks ? le.r - k_base : kStageRanks;
+      const int rp = khi - k_base < kStageRanks ? khi - k_base : kStageRanks;
       const char* s_t = s_lora;
       const char* s_b = s_lora + 2 * BM * rp;
       for (int k0 = 0; k0 < rp; k0 += 16) {
@@ -415,6 +446,8 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
   int tm, tn;
   if (!xcd_tile(tiles_m, tiles, tm, tn)) return;
   const int m0 = tm * BM, n0 = tn * BN;
+  int klo = 0, khi = 0;   // the block's LoRA rank window
+  if constexpr (LORA == 1 && STAGED) lora_window(le, n0, n0 + BN < N ? n0 + BN : N, klo, khi);
 
   const int lane = threadIdx.x & 63;
   // wave index as a scalar: the LDS destination of a direct load must be uniform
@@ -510,7 +543,8 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
     issue(1, 1);
     __builtin_amdgcn_s_waitcnt(0x0070 | NL);   // vmcnt(NL) lgkmcnt(0): K-tile 0 and the scales
   } else {
-    if constexpr (LORA == 1 && STAGED) stage_lora<NW, BM, BN>(le, smem + STAGE, 0, m0, n0, M, N, wave, lane);
+    if constexpr (LORA == 1 && STAGED)
+      stage_lora<NW, BM, BN>(le, smem + STAGE, klo, khi, m0, n0, M, N, wave, lane);
     __builtin_amdgcn_s_waitcnt(0x0070);
   }
   __builtin_amdgcn_s_barrier();
@@ -535,7 +569,7 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (MODE == 0) issue(kt + 2, stage);
     if constexpr (MODE == 1 && LORA == 1 && STAGED)
-      stage_lora<NW, BM, BN>(le, smem + stage * STAGE, 0, m0, n0, M, N, wave, lane);
+      stage_lora<NW, BM, BN>(le, smem + stage * STAGE, klo, khi, m0, n0, M, N, wave, lane);
     if constexpr (MODE != 2) load_frags(smem + (stage ^ 1) * STAGE, 0, fa[cur ^ 1], fb[cur ^ 1]);
     mfmas(cur);
     if constexpr (MODE == 0) sched_slots<0, TM * TN, TM + TN, NL>();
@@ -548,7 +582,8 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
 
   if constexpr (STAGED)
     epilogue_staged<OUT, STATIC_A, LORA, BM, BN, WM, WN>(acc, s_sc, smem + (((nk - 1) & 1) ^ 1) * STAGE,
-                                                          m0, n0, wm, wn, M, N, a_scale, Y, ldy, le);
+                                                          m0, n0, wm, wn, M, N, a_scale, Y, ldy, le,
+                                                          klo, khi);
   else
     epilogue<OUT, STATIC_A, LORA, TM, TN>(acc, m0 + wm * (BM / WM), n0 + wn * (BN / WN), M, N,
                                           a_scale, w_scale, Y, ldy, le);
@@ -674,7 +709,7 @@ k_gemm_skinny_finish(const int32_t* __restrict__ part, int KS, const float* __re
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][0][q] += src[i * 1024 + q * 64 + lane];
   }
-  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f};
+  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f, 0, {}, {}};
   epilogue<OUT, STATIC_A, 0, TM, 1>(acc, 0, blockIdx.x * kSkinnyBN, M, N, a_scale, w_scale, Y, ldy,
                                     none);
 }
@@ -848,7 +883,7 @@ static int launch_pipe(const int8_t* Xq, const int8_t* Wq, const float* a_scale,
 // K split of the skinny kernel across blocks, given a workspace: slices of
 // whole K-tiles so that about 512 blocks run (the column tiles alone give
 // N / 32), each slice at least 16 K-tiles (two per wave), and only where at
-// least 4 such slices fit (K >= 8192). Measured at M = 64, N = 5120 with the
+// least 4 slices are wanted and fit (K >= 8192). Measured at M = 64, N = 5120 with the
 // weights rotated past the MALL: K = 20480 69 -> 61 us in 4 slices; K = 5120
 // in 2 slices was slower (22 -> 26 us: the partial sums and the second
 // launch cost more than the wider grid gains). 1: no split.
@@ -859,7 +894,7 @@ static int skinny_splits(int64_t M, int64_t N, int64_t K) {
   if (kmax < 4) return 1;
   int64_t ks = (512 + ct - 1) / ct;
   if (ks > kmax) ks = kmax;
-  return ks > 1 ? (int)ks : 1;
+  return ks >= 4 ? (int)ks : 1;   // 2 or 3 slices: not measured faster than one
 }
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
@@ -878,7 +913,7 @@ static int launch_skinny_split(const int8_t* Xq, const int8_t* Wq, const float* 
   const int nk = (int)(K / kBK);
   const int kps = (nk + ks - 1) / ks;
   const int slices = (nk + kps - 1) / kps;   // every slice non-empty
-  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f};
+  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f, 0, {}, {}};
   k_gemm_skinny<OUT, STATIC_A, 0, TM, true><<<dim3(ct, (unsigned)slices), kSkinnyWaves * 64, 0, st>>>(
       Xq, Wq, a_scale, w_scale, (int)M, (int)N, (int)K, Y, ldy, none, kps, part);
   SQ_LAUNCH_CHECK();
@@ -953,14 +988,14 @@ static int launch_gemm_any(const int8_t* Xq, const int8_t* Wq, const float* a_sc
 int launch_gemm(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
                 const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
                 int64_t ldy, hipStream_t st) {
-  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f};
+  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f, 0, {}, {}};
   return launch_gemm_any<0>(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, none, st);
 }
 
 int launch_gemm_ws(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
                    const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int yt,
                    int64_t ldy, void* ws, hipStream_t st) {
-  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f};
+  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f, 0, {}, {}};
   return launch_gemm_any<0>(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, none, st,
                             (int32_t*)ws);
 }
@@ -968,8 +1003,15 @@ int launch_gemm_ws(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int
 int launch_gemm_lora(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
                      const float* w_scale, int64_t M, int64_t N, int64_t K, const void* T,
                      int64_t ldt, const void* B, int r, float scale, void* Y, int yt, int64_t ldy,
-                     hipStream_t st) {
-  const LoraEpi le{(const unsigned short*)T, ldt, (const unsigned short*)B, r, scale};
+                     hipStream_t st, int parts, const int64_t* n_end, const int* r_end) {
+  LoraEpi le{(const unsigned short*)T, ldt, (const unsigned short*)B, r, scale, 0, {}, {}};
+  if (parts > 1) {
+    le.parts = parts;
+    for (int p = 0; p < parts; ++p) {
+      le.n_end[p] = (int)n_end[p];
+      le.r_end[p] = r_end[p];
+    }
+  }
   if (scale == 1.0f)
     return launch_gemm_any<1>(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, le, st);
   return launch_gemm_any<2>(Xq, Wq, a_scale, mode, w_scale, M, N, K, Y, yt, ldy, le, st);
@@ -978,7 +1020,7 @@ int launch_gemm_lora(const int8_t* Xq, const int8_t* Wq, const float* a_scale, i
 int launch_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, int64_t K,
                     int32_t* acc, hipStream_t st) {
   if (M == 0) return SQ_OK;
-  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f};
+  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f, 0, {}, {}};
   return launch_gemm_t<OUT_I32, false, 0>(Xq, Wq, nullptr, nullptr, M, N, K, acc, N, none, st);
 }
 

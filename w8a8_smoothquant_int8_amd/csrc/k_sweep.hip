@@ -174,10 +174,37 @@ k_err_final(const double* __restrict__ part, double* __restrict__ out) {
   if (threadIdx.x == 0) { out[0] = d; out[1] = r; }
 }
 
+// The choice among the alphas: rel[i] = err[2i] / err[2i + 1] (fp64; 0 when
+// the reference norm is 0), best = the index of the smallest rel, the first
+// on ties. One thread walks the (at most 1024) alphas in order.
+__global__ void __launch_bounds__(64)
+k_sweep_pick(const double* __restrict__ err, int n, double* __restrict__ rel,
+             int32_t* __restrict__ best) {
+  if (threadIdx.x != 0) return;
+  int b = 0;
+  double rb = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const double ref = err[2 * i + 1];
+    const double r = ref > 0.0 ? err[2 * i] / ref : 0.0;
+    if (rel != nullptr) rel[i] = r;
+    if (i == 0 || r < rb) {
+      rb = r;
+      b = i;
+    }
+  }
+  if (best != nullptr) best[0] = b;
+}
+
 // ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
 size_t err_partials_bytes() { return 2 * kErrBlocks * sizeof(double); }
+
+int launch_sweep_pick(const double* err, int n, double* rel, int32_t* best, hipStream_t st) {
+  k_sweep_pick<<<1, 64, 0, st>>>(err, n, rel, best);
+  SQ_LAUNCH_CHECK();
+  return SQ_OK;
+}
 
 template <int XT>
 static void launch_ref_w(const void* X, int64_t ldx, const void* W, int wt, int64_t ldw, int M,

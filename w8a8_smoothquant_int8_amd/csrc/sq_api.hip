@@ -28,6 +28,7 @@ int launch_ref_gemm(const void* X, int xt, int64_t ldx, const void* W, int wt, i
 int launch_sq_err(const float* q, const double* ref, int64_t n, double* part, double* out,
                   hipStream_t st);
 size_t err_partials_bytes();
+int launch_sweep_pick(const double* err, int n, double* rel, int32_t* best, hipStream_t st);
 int64_t norm_quant_max_k(int ht);
 int launch_norm_quant(const void* H, int ht, int64_t M, int64_t K, int64_t ldh, int norm,
                       const float* g, const float* b, double eps, int mode, int8_t* Xq,
@@ -54,7 +55,7 @@ int launch_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, in
 int launch_gemm_lora(const int8_t* Xq, const int8_t* Wq, const float* a_scale, int mode,
                      const float* w_scale, int64_t M, int64_t N, int64_t K, const void* T,
                      int64_t ldt, const void* B, int r, float scale, void* Y, int yt, int64_t ldy,
-                     hipStream_t st);
+                     hipStream_t st, int parts, const int64_t* n_end, const int* r_end);
 int launch_lora_shrink(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* A,
                        int r, void* T, int64_t ldt, void* ws, hipStream_t st);
 size_t lora_ws_bytes(int64_t M, int64_t K, int R);
@@ -391,7 +392,7 @@ int sq_w8a8_gemm_lora(const int8_t* Xq, const int8_t* Wq, const float* a_scale, 
   if (M == 0) return SQ_OK;
   if ((rc = gate()) != SQ_OK) return rc;
   return sq::launch_gemm_lora(Xq, Wq, a_scale, mode, w_scale, M, N, K, T, ldt, B, r, scale, Y, yt,
-                              ldy, as_stream(stream));
+                              ldy, as_stream(stream), 0, nullptr, nullptr);
 }
 
 int sq_w8a8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, int64_t K,
@@ -479,8 +480,32 @@ int sq_lora_apply_segmented(const void* X, int xt, int64_t M, int64_t K, int64_t
                                    as_stream(stream));
 }
 
-int sq_linear_group_run(const sq_linear_group* g, int flags, void* stream, void* gemm_begin,
-                        void* gemm_end) {
+// Projection table of a group's stacked adapters (sq_linear_group.lora_parts).
+static int check_lora_parts(const sq_linear_group* g) {
+  if (g->lora_parts <= 1) {
+    SQ_REQUIRE(g->lora_parts >= 0, SQ_ERR_INVALID_ARG);
+    return SQ_OK;
+  }
+  SQ_REQUIRE(g->lora_parts <= SQ_MAX_LORA_PARTS, SQ_ERR_INVALID_ARG);
+  int64_t n_prev = 0;
+  int r_prev = 0;
+  for (int p = 0; p < g->lora_parts; ++p) {
+    SQ_REQUIRE(g->lora_n_end[p] > n_prev && g->lora_r_end[p] > r_prev, SQ_ERR_INVALID_ARG);
+    SQ_REQUIRE(g->lora_n_end[p] % 16 == 0 && g->lora_r_end[p] % 8 == 0, SQ_ERR_MISALIGNED);
+    n_prev = g->lora_n_end[p];
+    r_prev = g->lora_r_end[p];
+  }
+  SQ_REQUIRE(n_prev == g->N && r_prev == g->r, SQ_ERR_INVALID_ARG);
+  return SQ_OK;
+}
+
+static int record(void* ev, hipStream_t st) {
+  if (ev != nullptr && hipEventRecord((hipEvent_t)ev, st) != hipSuccess) return SQ_ERR_HIP;
+  return SQ_OK;
+}
+
+int sq_linear_group_run(const sq_linear_group* g, int flags, void* stream,
+                        const sq_group_events* events) {
   SQ_REQUIRE(g != nullptr, SQ_ERR_INVALID_ARG);
   constexpr int kAll = SQ_GROUP_CALIBRATE | SQ_GROUP_FOLD | SQ_GROUP_FORWARD;
   SQ_REQUIRE(flags != 0 && (flags & ~kAll) == 0, SQ_ERR_INVALID_ARG);
@@ -523,6 +548,7 @@ int sq_linear_group_run(const sq_linear_group* g, int flags, void* stream, void*
       SQ_REQUIRE(g->ldt >= g->r, SQ_ERR_INVALID_ARG);
       SQ_REQUIRE(g->ldt % 8 == 0 && aligned16(g->A) && aligned16(g->B) && aligned16(g->T),
                  SQ_ERR_MISALIGNED);
+      if ((rc = check_lora_parts(g)) != SQ_OK) return rc;
       if (g->M > 0) {
         SQ_REQUIRE(g->workspace != nullptr &&
                        g->workspace_bytes >= sq_lora_workspace_bytes(g->M, g->K, g->r),
@@ -533,7 +559,9 @@ int sq_linear_group_run(const sq_linear_group* g, int flags, void* stream, void*
   }
   if ((rc = gate()) != SQ_OK) return rc;
   hipStream_t st = as_stream(stream);
+  const sq_group_events ev = events != nullptr ? *events : sq_group_events{};
   // 2. launch
+  if ((rc = record(ev.begin, st)) != SQ_OK) return rc;
   const bool cal = flags & SQ_GROUP_CALIBRATE, fold = flags & SQ_GROUP_FOLD;
   if (cal && fold) {
     // both column maxima (act_max over X_cal, w_max over W, accumulated in s)
@@ -563,21 +591,34 @@ int sq_linear_group_run(const sq_linear_group* g, int flags, void* stream, void*
     // are faster alone than the one-read sq_quant_shrink (and equal inside the
     // overlapped step), which needs a 16-row block per CU and reads all of A
     // per block.
+    if ((rc = record(ev.quant_begin, st)) != SQ_OK) return rc;
     if ((rc = sq::launch_quant_act(g->X, g->xt, g->M, g->K, g->ldx, g->s, g->mode, g->Xq, g->a_scale,
                                    nullptr, st)) != SQ_OK)
       return rc;
-    if (lora && (rc = sq::launch_lora_shrink(g->X, g->xt, g->M, g->K, g->ldx, g->A, g->r, g->T,
-                                             g->ldt, g->workspace, st)) != SQ_OK)
-      return rc;
-    if (gemm_begin != nullptr && hipEventRecord((hipEvent_t)gemm_begin, st) != hipSuccess)
-      return SQ_ERR_HIP;
-    rc = lora ? sq::launch_gemm_lora(g->Xq, g->Wq, g->a_scale, g->mode, g->w_scale, g->M, g->N, g->K,
-                                     g->T, g->ldt, g->B, g->r, g->lora_scale, g->Y, g->yt, g->ldy, st)
-              : sq::launch_gemm(g->Xq, g->Wq, g->a_scale, g->mode, g->w_scale, g->M, g->N, g->K, g->Y,
-                                g->yt, g->ldy, st);
+    if (lora) {
+      if ((rc = record(ev.shrink_begin, st)) != SQ_OK) return rc;
+      if ((rc = sq::launch_lora_shrink(g->X, g->xt, g->M, g->K, g->ldx, g->A, g->r, g->T, g->ldt,
+                                       g->workspace, st)) != SQ_OK)
+        return rc;
+    }
+    if ((rc = record(ev.gemm_begin, st)) != SQ_OK) return rc;
+    // Without LoRA, a workspace large enough for the split-K GEMM of decode
+    // shapes lets the GEMM use it (sq_w8a8_gemm_ws); the result is the same.
+    const size_t gws = lora ? 0 : sq::gemm_ws_bytes(g->M, g->N, g->K);
+    const bool split = gws > 0 && g->workspace != nullptr && g->workspace_bytes >= gws &&
+                       aligned16(g->workspace);
+    if (lora)
+      rc = sq::launch_gemm_lora(g->Xq, g->Wq, g->a_scale, g->mode, g->w_scale, g->M, g->N, g->K, g->T,
+                                g->ldt, g->B, g->r, g->lora_scale, g->Y, g->yt, g->ldy, st,
+                                g->lora_parts, g->lora_n_end, g->lora_r_end);
+    else if (split)
+      rc = sq::launch_gemm_ws(g->Xq, g->Wq, g->a_scale, g->mode, g->w_scale, g->M, g->N, g->K, g->Y,
+                              g->yt, g->ldy, g->workspace, st);
+    else
+      rc = sq::launch_gemm(g->Xq, g->Wq, g->a_scale, g->mode, g->w_scale, g->M, g->N, g->K, g->Y,
+                           g->yt, g->ldy, st);
     if (rc != SQ_OK) return rc;
-    if (gemm_end != nullptr && hipEventRecord((hipEvent_t)gemm_end, st) != hipSuccess)
-      return SQ_ERR_HIP;
+    if ((rc = record(ev.gemm_end, st)) != SQ_OK) return rc;
   }
   return SQ_OK;
 }
@@ -624,7 +665,7 @@ size_t sq_alpha_sweep_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 int sq_alpha_sweep(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, const void* W, int wt,
                    int64_t N, int64_t ldw, const double* alphas, int n_alpha, int mode, double* err,
-                   void* ws, size_t ws_bytes, void* stream) {
+                   double* rel, int32_t* best, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_matrix(X, xt, M, K, ldx);
   if (rc != SQ_OK) return rc;
   if ((rc = check_matrix(W, wt, N, K, ldw)) != SQ_OK) return rc;
@@ -635,7 +676,8 @@ int sq_alpha_sweep(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, con
   SQ_REQUIRE(n_alpha >= 1 && n_alpha <= kMaxSweepAlphas, SQ_ERR_INVALID_ARG);
   for (int i = 0; i < n_alpha; ++i)
     SQ_REQUIRE(alphas[i] >= 0.0 && alphas[i] <= 1.0, SQ_ERR_INVALID_ARG);   // NaN fails too
-  SQ_REQUIRE(((uintptr_t)err & 7u) == 0, SQ_ERR_MISALIGNED);
+  SQ_REQUIRE(((uintptr_t)err & 7u) == 0 && ((uintptr_t)rel & 7u) == 0 && ((uintptr_t)best & 3u) == 0,
+             SQ_ERR_MISALIGNED);
   if (M == 0) return SQ_OK;
   const size_t need = sq_alpha_sweep_workspace_bytes(M, N, K);
   SQ_REQUIRE(ws != nullptr && ws_bytes >= need, SQ_ERR_WORKSPACE);
@@ -663,6 +705,7 @@ int sq_alpha_sweep(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, con
       return rc;
     if ((rc = sq::launch_sq_err(w.y_q, w.y_ref, M * N, w.part, err + 2 * i, st)) != SQ_OK) return rc;
   }
+  if (rel != nullptr || best != nullptr) return sq::launch_sweep_pick(err, n_alpha, rel, best, st);
   return SQ_OK;
 }
 

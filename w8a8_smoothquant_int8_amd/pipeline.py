@@ -34,13 +34,14 @@ from typing import Dict, List, Optional, Tuple
 
 import torch
 
-from . import (SQ_GROUP_CALIBRATE, SQ_GROUP_FOLD, SQ_GROUP_FORWARD, SQ_MAX_LORA_RANK,
+from . import (SQ_GROUP_CALIBRATE, SQ_GROUP_FOLD, SQ_GROUP_FORWARD, SQ_MAX_LORA_PARTS,
+               SQ_MAX_LORA_RANK,
                sq_alpha_sweep, sq_alpha_sweep_workspace_bytes, sq_calibrate_absmax,
                sq_fold_norm_weight, sq_norm_quant, sq_quant_shrink, SQError, SQ_ERR_INVALID_ARG,
                SQ_ERR_UNSUPPORTED_DTYPE, sq_linear_group_desc, sq_linear_group_run, sq_lora_apply,
                sq_lora_apply_segmented, sq_lora_shrink, sq_lora_workspace_bytes,
                sq_quant_per_token, sq_quant_static_clipped, sq_smooth_fold, sq_static_act_scale,
-               sq_w8a8_gemm, sq_w8a8_gemm_lora)
+               sq_w8a8_gemm, sq_w8a8_gemm_lora, sq_w8a8_gemm_workspace_bytes, sq_w8a8_gemm_ws)
 
 ALL_PHASES = SQ_GROUP_CALIBRATE | SQ_GROUP_FOLD | SQ_GROUP_FORWARD
 
@@ -56,19 +57,20 @@ def alpha_sweep(X: torch.Tensor, W: torch.Tensor, alphas, mode: str = "dynamic",
                 stream=None) -> dict:
     """Output error of the quantized layer against the unquantized one for each
     alpha, on the calibration batch X ("SmoothQuant" explainer, "Calibration in
-    practice"): one native call, then one read of the [len(alphas), 2] result.
-    Returns err (sum of squared errors), ref (sum of squared outputs), rel =
-    err / ref, and best (the alpha of the smallest rel, the first on ties)."""
+    practice"): one native call, which also forms the relative errors and
+    picks the best alpha, then one read of its results. Returns err (sum of
+    squared errors), ref (sum of squared outputs), rel = err / ref, and best
+    (the alpha of the smallest rel, the first on ties)."""
     M, K = X.shape
     ws = torch.empty(max(sq_alpha_sweep_workspace_bytes(M, W.shape[0], K), 256),
                      dtype=torch.uint8, device=X.device)
     out = torch.empty(len(alphas), 2, dtype=torch.float64, device=X.device)
-    sq_alpha_sweep(X, W, alphas, out, ws, mode=mode, stream=stream)
-    host = out.cpu()
-    err, ref = host[:, 0].tolist(), float(host[0, 1])
-    rel = [e / ref if ref > 0 else 0.0 for e in err]
-    best = float(alphas[min(range(len(alphas)), key=lambda i: (rel[i], i))])
-    return {"err": err, "ref": ref, "rel": rel, "best": best}
+    rel = torch.empty(len(alphas), dtype=torch.float64, device=X.device)
+    best = torch.empty(1, dtype=torch.int32, device=X.device)
+    sq_alpha_sweep(X, W, alphas, out, ws, mode=mode, rel=rel, best=best, stream=stream)
+    host, rel_h, ib = out.cpu(), rel.cpu().tolist(), int(best.cpu()[0])
+    return {"err": host[:, 0].tolist(), "ref": float(host[0, 1]), "rel": rel_h,
+            "best": float(alphas[ib])}
 
 
 @dataclass
@@ -115,21 +117,31 @@ class LinearGroup:
         r_tot = sum(a.shape[0] for a, _ in self.lora.values())
         self.fused = bool(fuse and self.lora and set(self.lora) == set(rows)
                           and r_tot <= SQ_MAX_LORA_RANK)
+        self.lora_parts = None
         if self.fused:
-            order = list(rows)
+            order = sorted(rows, key=lambda p: rows[p][0])     # adapters stacked in column order
             self.A_stack = torch.cat([self.lora[p][0] for p in order], dim=0).contiguous()
             self.B_blk = torch.zeros(Ntot, r_tot, dtype=torch.bfloat16, device=dev)
-            c = 0
+            c, parts, n_prev = 0, [], 0
             for p in order:
                 A, B = self.lora[p]
                 r0, r1 = rows[p]
                 self.B_blk[r0:r1, c:c + A.shape[0]] = B
                 c += A.shape[0]
+                parts.append((r1, c) if r0 == n_prev else None)
+                n_prev = r1
+            # The projection table lets the GEMM epilogue skip the zero blocks of
+            # B_blk; it needs the projections to tile the columns in order.
+            if (len(parts) > 1 and None not in parts and n_prev == Ntot
+                    and len(parts) <= SQ_MAX_LORA_PARTS):
+                self.lora_parts = parts
             self.T = torch.empty(self.M, r_tot, dtype=torch.bfloat16, device=dev)
         ranks = ([r_tot] if self.fused else [a.shape[0] for a, _ in self.lora.values()]) + \
                 [s.max_rank for s in self.seg_lora.values()]
         wsb = sq_lora_workspace_bytes(self.M, K, max(ranks)) if ranks and self.M else 0
-        self.ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        # decode-sized GEMMs without LoRA split K across blocks in the same workspace
+        self.gemm_ws_bytes = sq_w8a8_gemm_workspace_bytes(self.M, Ntot, K) if self.M else 0
+        self.ws = torch.empty(max(wsb, self.gemm_ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     # -- offline ------------------------------------------------------------
     def calibrate(self, X_cal: torch.Tensor, reset: bool = True) -> None:
@@ -211,8 +223,10 @@ class LinearGroup:
         return self.Y[proj]
 
     def gemm_all(self, mode: str = "dynamic") -> None:
-        """All projections' GEMMs as one call over the stacked weights, without LoRA."""
-        sq_w8a8_gemm(self.Xq, self.Wq, self._a(mode), self.w_scale, self.Yg, mode=mode)
+        """All projections' GEMMs as one call over the stacked weights, without LoRA
+        (with the split-K workspace where the shape uses one)."""
+        sq_w8a8_gemm_ws(self.Xq, self.Wq, self._a(mode), self.w_scale, self.Yg,
+                        self.ws if self.gemm_ws_bytes else None, mode=mode)
 
     def lora_shrink(self, X: torch.Tensor) -> None:
         sq_lora_shrink(X, self.A_stack, self.T, self.ws)
@@ -238,34 +252,47 @@ class LinearGroup:
         sq_w8a8_gemm_lora(self.Xq, self.Wq, self._a(mode), self.w_scale, self.T, self.B_blk,
                           self.Yg, scale=self.lora_scale, mode=mode)
 
-    def apply_lora(self, proj: str, X: torch.Tensor) -> None:
+    def apply_lora(self, proj: str, X: torch.Tensor, stream=None) -> None:
         """One projection's LoRA delta as a separate shrink + expand call."""
         if proj in self.lora:
             A, B = self.lora[proj]
-            sq_lora_apply(X, A, B, self.Y[proj], self.ws, scale=self.lora_scale)
+            sq_lora_apply(X, A, B, self.Y[proj], self.ws, scale=self.lora_scale, stream=stream)
         elif proj in self.seg_lora:
             g = self.seg_lora[proj]
             sq_lora_apply_segmented(X, g.seg_start, g.seg_adapter, g.A_ptrs, g.B_ptrs, g.ranks,
-                                    g.max_rank, self.Y[proj], self.ws, scale=self.lora_scale)
+                                    g.max_rank, self.Y[proj], self.ws, scale=self.lora_scale,
+                                    stream=stream)
 
     # -- one native call per step ---------------------------------------------
     def run(self, X: torch.Tensor, X_cal: Optional[torch.Tensor], flags: int = ALL_PHASES,
-            mode: str = "dynamic", stream=None, gemm_begin=None, gemm_end=None) -> None:
+            mode: str = "dynamic", stream=None, events=None, seg_events=None) -> None:
         """The selected phases (calibrate, fold, forward) as one sq_linear_group_run
         call: the same kernels as calibrate() + fold() + forward() on the fused
-        path, launched from native code. Needs the fused LoRA path or no LoRA."""
-        if self.seg_lora or (self.lora and not self.fused):
-            raise ValueError("run() covers the stacked-LoRA (fused) and no-LoRA groups")
+        path, launched from native code. Groups with per-request (segmented)
+        adapters then issue each projection's segmented LoRA call on the same
+        stream, as forward() does. Not for unstacked single adapters.
+        events: None or sq_group_events(...) for the group call; seg_events:
+        None or a (begin, end) pair of torch events around the segmented calls."""
+        if self.lora and not self.fused:
+            raise ValueError("run() covers the stacked-LoRA (fused), segmented and no-LoRA groups")
         key = (X.data_ptr(), None if X_cal is None else X_cal.data_ptr(), mode)
         if getattr(self, "_desc_key", None) != key:
-            lora = dict(A=self.A_stack, B=self.B_blk, T=self.T, workspace=self.ws,
-                        lora_scale=self.lora_scale) if self.fused else {}
+            lora = dict(A=self.A_stack, B=self.B_blk, T=self.T, lora_scale=self.lora_scale,
+                        lora_parts=self.lora_parts) if self.fused else {}
             self._desc = sq_linear_group_desc(X, X_cal, self.W, self.alpha, mode, self.act_max,
                                               self.s, self.Wq, self.w_scale, self.Xq, self._a(mode),
-                                              self.Yg, **lora)
+                                              self.Yg, workspace=self.ws, **lora)
             self._desc_inputs = (X, X_cal)      # keep the tensors the pointers refer to alive
             self._desc_key = key
-        sq_linear_group_run(self._desc, flags, stream, gemm_begin, gemm_end)
+        sq_linear_group_run(self._desc, flags, stream, events)
+        if self.seg_lora and (flags & SQ_GROUP_FORWARD) and self.M > 0:
+            st = stream if stream is not None else torch.cuda.current_stream()
+            if seg_events is not None:
+                seg_events[0].record(st)
+            for p in self.seg_lora:
+                self.apply_lora(p, X, stream=st)
+            if seg_events is not None:
+                seg_events[1].record(st)
 
     def forward_static_checked(self, X: torch.Tensor, max_rate: float = MAX_CLIP_RATE
                                ) -> Tuple[Dict[str, torch.Tensor], float, bool]:
