@@ -271,6 +271,24 @@ int sq_lora_apply_segmented(const void* X, int xt, int64_t M, int64_t K, int64_t
                             const int32_t* ranks, int max_rank, float scale, void* Y, int yt,
                             int64_t N, int64_t ldy, void* ws, size_t ws_bytes, void* stream);
 
+/* sq_lora_apply_segmented for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without ws / ws_bytes, the same kernels and
+ * the same results bit for bit. Its scratch memory is a 32 MiB device array
+ * inside the library, one per device, kept until the process ends; the call
+ * allocates and frees nothing. Shapes whose workspace
+ * sq_lora_workspace_bytes(M, K, max_rank) exceeds 32 MiB return
+ * SQ_ERR_WORKSPACE (then use sq_lora_apply_segmented). Every call on one
+ * device shares that device's array and nothing in it needs clearing (each
+ * call writes what it reads); calls that overlap on one device (other
+ * streams, other host threads) race and must not be issued. */
+int sq_lora_apply_segmented_noalloc(const void* X, int xt, int64_t M, int64_t K, int64_t ldx,
+                                    int num_segments, const int32_t* seg_start,
+                                    const int32_t* seg_adapter, int num_adapters,
+                                    const void* const* A_ptrs, const void* const* B_ptrs,
+                                    const int32_t* ranks, int max_rank, float scale, void* Y,
+                                    int yt, int64_t N, int64_t ldy, void* stream);
+
 /* The whole path for one input group ([SQ] "How it works", Steps 4-7, in
  * order; [LoRA] Pitch): the projections that read the same activations, with
  * their weights stacked along N and their adapters stacked along r, run as

@@ -37,7 +37,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 24
+    assert len(names) == 25
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sq.SIGNATURES)
@@ -214,6 +214,18 @@ def test_lora_validation(L):
     assert g(*bad) == sq.SQ_ERR_WORKSPACE
     bad = list(seg); bad[5] = 0
     assert g(*bad) == sq.SQ_OK                      # no segments: no-op
+    # the allocation-free variant: same checks, no workspace, its scratch bounds the shape
+    h = L.sq_lora_apply_segmented_noalloc
+    na = seg[:19] + [S]
+    bad = list(na); bad[6] = NULL
+    assert h(*bad) == sq.SQ_ERR_INVALID_ARG
+    bad = list(na); bad[12] = 136
+    assert h(*bad) == sq.SQ_ERR_INVALID_ARG
+    bad = list(na); bad[5] = 0
+    assert h(*bad) == sq.SQ_OK
+    bad = list(na); bad[2], bad[3], bad[4], bad[12] = 65536, 256, 256, 128
+    assert L.sq_lora_workspace_bytes(65536, 256, 128) > 32 << 20
+    assert h(*bad) == sq.SQ_ERR_WORKSPACE           # refused before anything runs
 
 
 def test_lora_workspace_grows_with_rank(L):

@@ -69,6 +69,9 @@ SIGNATURES = {
     "sq_lora_apply_segmented": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp,
                                          _c_int, _vp, _vp, _vp, _c_int, _c_f, _vp, _c_int, _c_i64,
                                          _c_i64, _vp, _c_sz, _vp]),
+    "sq_lora_apply_segmented_noalloc": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp,
+                                                 _vp, _c_int, _vp, _vp, _vp, _c_int, _c_f, _vp,
+                                                 _c_int, _c_i64, _c_i64, _vp]),
     "sq_linear_group_run": (_c_int, [_vp, _c_int, _vp, _vp]),
     "sq_alpha_sweep_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64]),
     "sq_alpha_sweep": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _c_int, _c_i64, _c_i64,
@@ -333,6 +336,19 @@ def sq_lora_apply_segmented(X: torch.Tensor, seg_start: torch.Tensor, seg_adapte
         _ptr(X), _dt(X), M, K, _ld(X), seg_adapter.numel(), _ptr(seg_start), _ptr(seg_adapter),
         ranks.numel(), _ptr(A_ptrs), _ptr(B_ptrs), _ptr(ranks), int(max_rank), float(scale),
         _ptr(Y), _dt(Y), N, _ld(Y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def sq_lora_apply_segmented_noalloc(X: torch.Tensor, seg_start: torch.Tensor,
+                                    seg_adapter: torch.Tensor, A_ptrs: torch.Tensor,
+                                    B_ptrs: torch.Tensor, ranks: torch.Tensor, max_rank: int,
+                                    Y: torch.Tensor, scale: float = 1.0, stream=None) -> None:
+    """sq_lora_apply_segmented with the library's own scratch memory (no workspace)."""
+    M, K = X.shape
+    N = Y.shape[1]
+    _check("sq_lora_apply_segmented_noalloc", lib().sq_lora_apply_segmented_noalloc(
+        _ptr(X), _dt(X), M, K, _ld(X), seg_adapter.numel(), _ptr(seg_start), _ptr(seg_adapter),
+        ranks.numel(), _ptr(A_ptrs), _ptr(B_ptrs), _ptr(ranks), int(max_rank), float(scale),
+        _ptr(Y), _dt(Y), N, _ld(Y), _stream(stream)))
 
 
 def pointer_table(tensors: Sequence[torch.Tensor], device) -> torch.Tensor:

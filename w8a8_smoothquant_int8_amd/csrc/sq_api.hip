@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "sq_internal.h"
 
@@ -456,11 +457,12 @@ int sq_lora_apply(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, cons
   return sq::launch_lora(X, xt, M, K, ldx, A, B, r, scale, Y, yt, N, ldy, ws, as_stream(stream));
 }
 
-int sq_lora_apply_segmented(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, int num_segments,
-                            const int32_t* seg_start, const int32_t* seg_adapter, int num_adapters,
-                            const void* const* A_ptrs, const void* const* B_ptrs,
-                            const int32_t* ranks, int max_rank, float scale, void* Y, int yt,
-                            int64_t N, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+// Arguments of the segmented LoRA call other than the workspace.
+static int check_segmented(const void* X, int xt, int64_t M, int64_t K, int64_t ldx,
+                           int num_segments, const int32_t* seg_start, const int32_t* seg_adapter,
+                           int num_adapters, const void* const* A_ptrs, const void* const* B_ptrs,
+                           const int32_t* ranks, int max_rank, float scale, void* Y, int yt,
+                           int64_t N, int64_t ldy) {
   int rc = check_lora_common(X, xt, M, K, ldx, Y, yt, N, ldy, max_rank, scale);
   if (rc != SQ_OK) return rc;
   SQ_REQUIRE(num_segments >= 0 && num_adapters >= 1, SQ_ERR_INVALID_ARG);
@@ -470,6 +472,17 @@ int sq_lora_apply_segmented(const void* X, int xt, int64_t M, int64_t K, int64_t
   SQ_REQUIRE(aligned4(seg_start) && aligned4(seg_adapter) && aligned4(ranks) &&
                  ((uintptr_t)A_ptrs & 7u) == 0 && ((uintptr_t)B_ptrs & 7u) == 0,
              SQ_ERR_MISALIGNED);
+  return SQ_OK;
+}
+
+int sq_lora_apply_segmented(const void* X, int xt, int64_t M, int64_t K, int64_t ldx, int num_segments,
+                            const int32_t* seg_start, const int32_t* seg_adapter, int num_adapters,
+                            const void* const* A_ptrs, const void* const* B_ptrs,
+                            const int32_t* ranks, int max_rank, float scale, void* Y, int yt,
+                            int64_t N, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_segmented(X, xt, M, K, ldx, num_segments, seg_start, seg_adapter, num_adapters,
+                           A_ptrs, B_ptrs, ranks, max_rank, scale, Y, yt, N, ldy);
+  if (rc != SQ_OK) return rc;
   if (M == 0 || num_segments == 0) return SQ_OK;
   const size_t need = sq_lora_workspace_bytes(M, K, max_rank);
   SQ_REQUIRE(ws != nullptr && ws_bytes >= need, SQ_ERR_WORKSPACE);
@@ -502,6 +515,58 @@ static int check_lora_parts(const sq_linear_group* g) {
 static int record(void* ev, hipStream_t st) {
   if (ev != nullptr && hipEventRecord((hipEvent_t)ev, st) != hipSuccess) return SQ_ERR_HIP;
   return SQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The segmented LoRA call without a caller workspace, for callers that cannot
+// allocate. Its scratch memory is this file-scope device array, one copy per
+// device, held until the process ends. In host code the name `scratch` stands
+// for a host-side shadow, not a device address, so host code never passes it
+// to a kernel or a copy: it uses the address hipGetSymbolAddress returns for
+// the current device, looked up once per device and kept in g_scratch_ptr.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+static int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return SQ_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return SQ_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SQ_OK;
+}
+
+int sq_lora_apply_segmented_noalloc(const void* X, int xt, int64_t M, int64_t K, int64_t ldx,
+                                    int num_segments, const int32_t* seg_start,
+                                    const int32_t* seg_adapter, int num_adapters,
+                                    const void* const* A_ptrs, const void* const* B_ptrs,
+                                    const int32_t* ranks, int max_rank, float scale, void* Y,
+                                    int yt, int64_t N, int64_t ldy, void* stream) {
+  int rc = check_segmented(X, xt, M, K, ldx, num_segments, seg_start, seg_adapter, num_adapters,
+                           A_ptrs, B_ptrs, ranks, max_rank, scale, Y, yt, N, ldy);
+  if (rc != SQ_OK) return rc;
+  if (M == 0 || num_segments == 0) return SQ_OK;
+  SQ_REQUIRE(sq_lora_workspace_bytes(M, K, max_rank) <= kNoAllocScratchBytes, SQ_ERR_WORKSPACE);
+  if ((rc = gate()) != SQ_OK) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_ptr(&ws)) != SQ_OK) return rc;
+  return sq::launch_lora_segmented(X, xt, M, K, ldx, num_segments, seg_start, seg_adapter, A_ptrs,
+                                   B_ptrs, ranks, max_rank, scale, Y, yt, N, ldy, ws,
+                                   as_stream(stream));
 }
 
 int sq_linear_group_run(const sq_linear_group* g, int flags, void* stream,
