@@ -614,6 +614,64 @@ def row_f1(args, torch):
     }
 
 
+def mfma_probe(torch, mode: int, blocks: int = 256, iters: int = 4000, reps: int = 3):
+    """Run the INT8 MFMA-only probe (libsq_probe): returns (TOP/s, mean shader
+    clock in GHz over the blocks' timed loops), the best of `reps` runs."""
+    import ctypes
+    path = os.path.join(ROOT, "w8a8_smoothquant_int8_amd", "libsq_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build with python -m w8a8_smoothquant_int8_amd.build")
+    L = ctypes.CDLL(path)
+    L.sq_probe_mfma_i8.restype = ctypes.c_int
+    L.sq_probe_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    rnd = torch.randint(-2 ** 31, 2 ** 31 - 1, (blocks * 512 * 64,), dtype=torch.int32,
+                        device="cuda", generator=g)
+    clk = torch.zeros(blocks, 2, dtype=torch.int64, device="cuda")
+    sink = torch.empty(blocks * 512, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    best = None
+    for _ in range(reps + 1):                  # the first run warms up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rc = L.sq_probe_mfma_i8(mode, blocks, iters, rnd.data_ptr(), clk.data_ptr(),
+                                sink.data_ptr(), ctypes.c_void_p(st.cuda_stream))
+        e1.record()
+        torch.cuda.synchronize()
+        assert rc == 0, rc
+        ms = e0.elapsed_time(e1)
+        c = clk.cpu().double()
+        ghz = float((c[:, 0] / c[:, 1]).mean()) * 0.1        # reference clock: 100 MHz
+        tops = blocks * 8 * iters * 64 * 65536.0 / (ms * 1e-3) / 1e12
+        if best is None or tops > best[0]:
+            best = (tops, ghz)
+    return best
+
+
+def row_mfma(args, torch):
+    """The practical INT8 matrix-core ceiling: the MFMA-only probe at the
+    GEMM's occupancy with constant and with random operands, and the shader
+    clock each sustains."""
+    const_tops, const_ghz = mfma_probe(torch, 0)
+    rand_tops, rand_ghz = mfma_probe(torch, 1)
+    per_clk = lambda tops, ghz: tops / (INT8_PEAK_TOPS * ghz / 2.4)
+    return {
+        "row": "mfma", "metric": "INT8 MFMA-only rate (probe at the GEMM's occupancy)",
+        "value": round(rand_tops, 1), "unit": "TOPS", "higher_is_better": True, "dtype": "int8",
+        "data": "random operand fragments held in registers",
+        "config": {"blocks": 256, "waves_per_block": 8, "mfma": "V_MFMA_I32_32X32X32_I8",
+                   "accumulators_per_wave": 8},
+        "random_operands": {"tops": round(rand_tops, 1), "shader_clock_ghz": round(rand_ghz, 3),
+                            "frac_of_peak": round(rand_tops / INT8_PEAK_TOPS, 4),
+                            "frac_of_rate_at_clock": round(per_clk(rand_tops, rand_ghz), 4)},
+        "constant_operands": {"tops": round(const_tops, 1), "shader_clock_ghz": round(const_ghz, 3),
+                              "frac_of_peak": round(const_tops / INT8_PEAK_TOPS, 4),
+                              "frac_of_rate_at_clock": round(per_clk(const_tops, const_ghz), 4)},
+        "peak_note": "5.0 POP/s = 256 CUs x 4 SIMDs x 2048 int8 ops/clock x 2.4 GHz",
+    }
+
+
 KERNEL_WORKLOADS = ("tiny_m16_k256_n256", "llama3_8b_proj_m2048", "opt13b_layer_decode_m64",
                     "opt13b_layer_prefill_m4096", "multitenant_lora_m8192", "llama2_70b_mlp_m8192")
 
@@ -759,7 +817,8 @@ def row_kernels(args, torch):
     }
 
 
-ROWS = {"f1": row_f1, "f2": row_f2, "f3": row_f3, "f4": row_f4, "kernels": row_kernels}
+ROWS = {"f1": row_f1, "f2": row_f2, "f3": row_f3, "f4": row_f4, "kernels": row_kernels,
+        "mfma": row_mfma}
 
 
 def main():
@@ -853,6 +912,10 @@ def main():
     traffic = stored_traffic(dom, wl.name)
     lora_epi = any(groups[i][1].fused for i in range(len(groups)) if groups[i][0] in dom_inputs)
 
+    # The measured matrix-core ceiling beside the paper peak: the MFMA-only
+    # probe with random operands, run after the timed region.
+    probe_tops, probe_ghz = mfma_probe(torch, 1)
+
     esz = 4 if wl.dtype == "f32" else 2
     quant_bytes = sum((esz + 1) * wl.M * K + 4 * wl.M for _i, K in wl.inputs)
     line = {
@@ -879,7 +942,10 @@ def main():
                      "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
                      "launches_per_step": launches // args.steps,
                      "ops_per_launch": dom_ops / launches,
-                     "avg_launch_ms": round(avg_launch_ms, 5)},
+                     "avg_launch_ms": round(avg_launch_ms, 5),
+                     "mfma_probe_tops": round(probe_tops, 1),
+                     "mfma_probe_clock_ghz": round(probe_ghz, 3),
+                     "frac_of_mfma_probe": round(achieved / probe_tops, 4)},
         "value_formula": "sum 2MNK / sum (t_gemm incl. dequant and LoRA expand epilogue + "
                          "t_lora_shrink + t_segmented_lora), HIP events in the timed steps",
         "value_pct_of_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2),

@@ -3,7 +3,8 @@
     python -m w8a8_smoothquant_int8_amd.build
 
 Each csrc/*.hip file compiles to an object in parallel; the objects link
-into w8a8_smoothquant_int8_amd/libsq.so, next to this file.
+into w8a8_smoothquant_int8_amd/libsq.so, next to this file. The MFMA rate
+probe that bench.py uses (probe/k_mfma_probe.hip) links into libsq_probe.so.
 """
 from __future__ import annotations
 
@@ -17,6 +18,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsq.so")
+# The measurement probe bench.py prices the GEMM with (not part of libsq).
+PROBE_SRC = os.path.join(PKG, "probe", "k_mfma_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libsq_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -65,8 +69,15 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
     os.replace(tmp, LIB)
+    pobj = _compile(PROBE_SRC)
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, pobj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe link failed:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} from {len(srcs)} sources, and {PROBE_LIB}")
     return LIB
 
 
