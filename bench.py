@@ -672,6 +672,84 @@ def row_mfma(args, torch):
     }
 
 
+def row_lora_window(args, torch):
+    """The GEMM with the stacked-LoRA epilogue, with and without the
+    per-projection rank windows, and without LoRA, on the same group (the
+    workload's data), timed by the group call's own events around the GEMM,
+    alternating the three settings."""
+    from synth.workloads import get_workload
+    import w8a8_smoothquant_int8_amd as sq
+    from w8a8_smoothquant_int8_amd.pipeline import LinearGroup
+    cases = [("llama2_70b_mlp_m8192", "mlp_in"), ("llama3_8b_proj_m2048", "attn_in"),
+             ("llama3_8b_proj_m2048", "mlp_in")]
+    reps = max(min(args.steps, 20), 5)
+    out = {}
+    for name, inp in cases:
+        wl = get_workload(name)
+        rows = wl.group_rows(inp)
+        W = wl.w_group(inp).cuda()
+        X, Xc = wl.x(inp).cuda(), wl.x_cal(inp).cuda()
+        loras = {p: tuple(t.cuda() for t in wl.lora(p)) for p in rows}
+        g = LinearGroup(W, rows, wl.alpha, wl.out_dtype, wl.M, lora=loras)
+        g0 = LinearGroup(W, rows, wl.alpha, wl.out_dtype, wl.M)
+        g.run(X, Xc)
+        g0.run(X, Xc)
+        table = g.lora_parts
+        settings = {"windows": (g, table), "full_rank": (g, None), "no_lora": (g0, None)}
+        ms = {k: [] for k in settings}
+        for _ in range(reps):
+            for k, (grp, parts) in settings.items():
+                if grp is g:
+                    grp.lora_parts = parts
+                    grp._desc_key = None            # rebuild the call's descriptor
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                e1.record()
+                grp.run(X, Xc, sq.SQ_GROUP_FORWARD,
+                        events=sq.sq_group_events(gemm_begin=e0, gemm_end=e1))
+                torch.cuda.synchronize()
+                ms[k].append(e0.elapsed_time(e1))
+        g.lora_parts = table
+        med = {k: sorted(v)[len(v) // 2] for k, v in ms.items()}
+        out[f"{name}/{inp}"] = {
+            "M": wl.M, "N": g.Ntot, "K": g.K, "stacked_rank": g.A_stack.shape[0],
+            "parts": table, "gemm_us": {k: round(v * 1e3, 1) for k, v in med.items()},
+            "lora_epilogue_us": {"windows": round((med["windows"] - med["no_lora"]) * 1e3, 1),
+                                 "full_rank": round((med["full_rank"] - med["no_lora"]) * 1e3, 1)}}
+        del g, g0, W, X, Xc
+        torch.cuda.empty_cache()
+    first = out[f"{cases[0][0]}/{cases[0][1]}"]
+    return {"row": "lora_window", "metric": "GEMM time with the stacked LoRA epilogue, "
+            "per-projection rank windows vs the full stacked rank (median of alternated launches)",
+            "value": first["lora_epilogue_us"]["windows"], "unit": "us of LoRA epilogue",
+            "higher_is_better": False, "data": "synthetic (the workloads' tensors)",
+            "config": {"reps": reps}, "cases": out}
+
+
+def row_oracle(args, torch):
+    """The CPU oracle, stage by stage, on every configuration (the bounded
+    sample of cpu_baseline), and once more on a single core for the
+    Llama-3-8B projections. No GPU work."""
+    from threadpoolctl import threadpool_limits
+    from synth.workloads import get_workload
+    out = {}
+    for name in KERNEL_WORKLOADS:
+        cb = cpu_baseline(get_workload(name), args.cpu_rows, args.cpu_wrows)
+        out[name] = {k: cb[k] for k in ("value", "stages_s", "full_step_s", "full_step_tops",
+                                        "cores")}
+    with threadpool_limits(limits=1):
+        cb1 = cpu_baseline(get_workload("llama3_8b_proj_m2048"), args.cpu_rows, args.cpu_wrows)
+    nproc, model = host_info()
+    return {"row": "oracle", "metric": "CPU oracle GEMM+LoRA TOPS per configuration",
+            "value": out[DEFAULT_WORKLOAD]["value"], "unit": "TOPS", "higher_is_better": True,
+            "data": "synthetic", "nproc": nproc, "cpu_model": model,
+            "sample": f"{args.cpu_rows} activation rows and {args.cpu_wrows} weight rows per input, "
+                      "each stage scaled to the full sizes",
+            "configs": out,
+            "one_core_llama3_8b_proj_m2048": {k: cb1[k] for k in ("value", "stages_s",
+                                                                  "full_step_s", "cores")}}
+
+
 KERNEL_WORKLOADS = ("tiny_m16_k256_n256", "llama3_8b_proj_m2048", "opt13b_layer_decode_m64",
                     "opt13b_layer_prefill_m4096", "multitenant_lora_m8192", "llama2_70b_mlp_m8192")
 
@@ -818,7 +896,7 @@ def row_kernels(args, torch):
 
 
 ROWS = {"f1": row_f1, "f2": row_f2, "f3": row_f3, "f4": row_f4, "kernels": row_kernels,
-        "mfma": row_mfma}
+        "mfma": row_mfma, "lora_window": row_lora_window, "oracle": row_oracle}
 
 
 def main():
@@ -828,6 +906,9 @@ def main():
               "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.row == "oracle":
+        print(json.dumps(ROWS[args.row](args, torch)))
+        return
     if args.row:
         assert torch.cuda.is_available(), "bench.py needs a GPU"
         torch.cuda.set_device(0)

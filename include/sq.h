@@ -31,7 +31,12 @@
  *    not gfx950 gives SQ_ERR_UNSUPPORTED_ARCH (with one warning on stderr per
  *    process). Results are deterministic: two runs on the same inputs give
  *    bitwise identical outputs.
- *  - NaN and Inf inputs are outside the contract.
+ *  - NaN and Inf inputs are outside the contract. Smoothed activations x / s
+ *    below the normal fp32 range (|x / s| < 2^-126) are computed exactly
+ *    except when the quotient lies exactly on a rounding midpoint of the
+ *    subnormal grid; there the result may be one subnormal ulp (2^-149) off
+ *    the IEEE quotient. This can change codes only in a row whose largest
+ *    smoothed value is itself that small.
  */
 #ifndef SQ_H
 #define SQ_H

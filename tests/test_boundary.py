@@ -275,6 +275,33 @@ def test_fp64_reciprocal_division_identity():
     assert np.mean(approx != x3 / d3) > 0.2
 
 
+def test_fp64_reciprocal_division_below_the_normal_range():
+    """Subnormal quotients (|x / d| < 2^-126), the case the normal-range proof
+    leaves out: exact in general, and at most one subnormal ulp off where the
+    quotient is exactly a midpoint of the subnormal grid."""
+    rng = np.random.default_rng(1)
+    F = np.float32
+    n = 500000
+    x = (rng.standard_normal(n) * np.exp(rng.uniform(np.log(1e-45), np.log(1e-30), n))).astype(F)
+    d = np.exp(rng.uniform(np.log(1e-5), np.log(1e5), n)).astype(F)
+    assert np.count_nonzero(np.abs(x / d) < 2.0 ** -126) > n // 3
+    got = (x.astype(np.float64) * (1.0 / d.astype(np.float64))).astype(F)
+    assert np.array_equal(got, x / d)
+    # exact midpoints: x = d (2j + 1) 2^-150, representable when d's odd part is small
+    d = ((rng.integers(1, 2 ** 12, n) * 2 + 1) * 2.0 ** (rng.integers(0, 30, n) - 20)).astype(F)
+    xt = d.astype(np.float64) * (2 * rng.integers(0, 2 ** 10, n) + 1) * 2.0 ** -150
+    keep = xt.astype(F).astype(np.float64) == xt
+    x, d = xt[keep].astype(F), d[keep]
+    ref = x / d
+    got = (x.astype(np.float64) * (1.0 / d.astype(np.float64))).astype(F)
+    ulps = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert ulps.max() == 1 and np.all(np.abs(ref) < 2.0 ** -126)
+    # one fp32 step of x away from each midpoint, the quotient is exact again
+    for toward in (np.inf, -np.inf):
+        xn = np.nextafter(x, F(toward))
+        assert np.array_equal((xn.astype(np.float64) * (1.0 / d.astype(np.float64))).astype(F), xn / d)
+
+
 def test_code_word_rounding():
     """The quantizers' one-add code: clamp to [-127, 127], add 1.5 * 2^23 in
     fp32 (round half to even), take the low byte as int8. Emulated with numpy

@@ -95,6 +95,12 @@ template <int DT> struct DtSize { static constexpr int v = (DT == SQ_F32) ? 4 : 
 // below 2^-52, so it lies strictly between the same two midpoints as x/d and
 // rounds to the same fp32 value. Cost: three VALU ops (widen, multiply,
 // narrow) per element instead of the dozen of an IEEE fp32 division.
+// Below the normal range (|x / d| < 2^-126) the midpoints are coarser and the
+// quotient can sit exactly on one (x = d * (2j + 1) * 2^-150 with d of small
+// odd part); then the two roundings may land one subnormal ulp (2^-149) off
+// the IEEE quotient. Elsewhere in that range the result is still exact. A
+// smoothed value that small changes a code only in a row whose largest
+// smoothed value is itself subnormal.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float div_rn(float x, double rd) {
   return (float)((double)x * rd);
