@@ -241,10 +241,11 @@ def _tile_score(M, N, bm, bn, resident, rate):
     return rate * pad * tiles / (rounds * resident)
 
 
-def gemm_tile(M: int, N: int, K: int) -> str:
+def gemm_tile(M: int, N: int, K: int, lora: bool = False) -> str:
     """The tile configuration libsq picks for an INT8 GEMM of this shape (the
     library's rule: the generic kernel when K is not a multiple of 128 or an
-    operand reaches 4 GiB, the skinny kernel for M <= 64 with fewer than 96
+    operand reaches 4 GiB, the decode kernel for M <= 64 without a LoRA
+    epilogue, the skinny kernel for M <= 64 with one and fewer than 96
     column tiles of 128, else the best of
     256x256 tiles and 256x192 tiles,
     one block per CU, at rates 1 and 0.93, and 128x128 tiles, two blocks per
@@ -252,6 +253,8 @@ def gemm_tile(M: int, N: int, K: int) -> str:
     of blocks that does useful work; ties go to 256x256, then 256x192)."""
     if K % 128 or M * K >= 1 << 32 or N * K >= 1 << 32:
         return "generic"
+    if M <= 64 and not lora:
+        return "decode"
     if M <= 64 and (N + 127) // 128 < 96:
         return "skinny"
     s256 = _tile_score(M, N, 256, 256, 256, 1.0)
@@ -265,7 +268,7 @@ def gemm_tile(M: int, N: int, K: int) -> str:
 def tile_dims(tile: str):
     """(rows, columns) of one output tile of a configuration."""
     return {"256x256": (256, 256), "256x192": (256, 192), "128x128": (128, 128),
-            "generic": (128, 128), "skinny": (64, 32)}[tile]
+            "generic": (128, 128), "skinny": (64, 32), "decode": (64, 64)}[tile]
 
 
 def host_info():
@@ -955,7 +958,7 @@ def main():
         d = rec.stage_ms(inp, g.fused)
         g_ops = 2.0 * wl.M * g.Ntot * K
         lora_ms = d["shrink"] + d["seg_lora"]
-        tile_of[inp] = gemm_tile(wl.M, g.Ntot, K)
+        tile_of[inp] = gemm_tile(wl.M, g.Ntot, K, lora=g.fused)
         per_group[inp] = {
             "projections": list(g.rows), "M": wl.M, "N": g.Ntot, "K": K, "tile": tile_of[inp],
             "lora_rank": (g.A_stack.shape[0] if g.fused else

@@ -45,9 +45,11 @@ def test_gemm_tile_rule_prefers_whole_rounds():
     assert bench.gemm_tile(4096, 6144, 4096) == "256x192"     # 512 tiles instead of 384
     assert bench.gemm_tile(2048, 4096, 14336) == "128x128"
     assert bench.gemm_tile(2048, 4096, 4100) == "generic"
-    assert bench.gemm_tile(64, 5120, 20480) == "skinny"          # decode
+    assert bench.gemm_tile(64, 5120, 20480) == "decode"          # decode, no LoRA epilogue
+    assert bench.gemm_tile(64, 15360, 5120) == "decode"
     assert bench.gemm_tile(65, 5120, 20480) == "128x128"
-    assert bench.gemm_tile(64, 15360, 5120) == "128x128"         # wide: 120 column tiles
+    assert bench.gemm_tile(64, 5120, 20480, lora=True) == "skinny"
+    assert bench.gemm_tile(64, 15360, 5120, lora=True) == "128x128"   # wide: 120 column tiles
 
 
 def test_cpu_baseline_on_the_tiny_workload():
@@ -65,5 +67,5 @@ def test_cpu_baseline_on_segmented_adapters():
 
 
 def test_tile_dims_known_for_every_rule():
-    for t in ("256x256", "256x192", "128x128", "generic", "skinny"):
+    for t in ("256x256", "256x192", "128x128", "generic", "skinny", "decode"):
         assert len(bench.tile_dims(t)) == 2

@@ -142,14 +142,18 @@ def test_static_clipped_validation(L):
 
 def test_gemm_workspace_rules(L):
     wsb = L.sq_w8a8_gemm_workspace_bytes
-    # decode shapes with few 32-column tiles split K: slices x ceil(N/32) x row tiles x 4 KB
+    # decode shapes with fewer than 128 column blocks of 64 split K: slices x
+    # ceil(N/32) 32-column tiles x 2 row tiles x 4 KB; about 256 blocks, each
+    # slice at least 8 K-tiles
     need = wsb(64, 5120, 20480)
-    assert need > 0 and need % (160 * 2 * 4096) == 0
-    assert wsb(32, 5120, 20480) % (160 * 4096) == 0 and wsb(32, 5120, 20480) > 0
+    assert need == 4 * 160 * 2 * 4096                # 80 column blocks: 4 slices
+    assert wsb(32, 5120, 20480) == need              # rows pad to two row tiles
+    assert wsb(64, 5120, 5120) == 4 * 160 * 2 * 4096     # 40 K-tiles: 4 slices of 10
+    assert wsb(64, 1040, 8192) == 8 * 33 * 2 * 4096      # 17 blocks: capped at 64 / 8 slices
     assert wsb(128, 5120, 20480) == 0          # not decode-sized
-    assert wsb(64, 20480, 5120) == 0           # 128x128 tiles already fill the chip
-    assert wsb(64, 5120, 1024) == 0            # too few K-tiles to split
-    assert wsb(64, 5120, 5120) == 0            # fewer than 4 slices of 16 K-tiles
+    assert wsb(64, 8192, 8192) == 0            # 128 column blocks: no split
+    assert wsb(64, 20480, 5120) == 0
+    assert wsb(64, 5120, 1024) == 0            # 8 K-tiles: too few for two slices
     assert wsb(64, 5120, 8192) > 0
     assert wsb(64, 5120, 1000) == 0            # K not a multiple of 128
     assert wsb(0, 5120, 20480) == 0 and wsb(-1, 64, 64) == 0

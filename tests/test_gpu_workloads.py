@@ -84,12 +84,12 @@ def per_tile(n, t, salt):
     return out
 
 
-def tile_samples(M, Ntot, K, rows, extra_rows=()):
+def tile_samples(M, Ntot, K, rows, lora, extra_rows=()):
     """Sampled rows and columns of a group output: every tile row and tile
     column of the library's tile configuration, plus the edges."""
-    tile = bench.gemm_tile(M, Ntot, K)
+    tile = bench.gemm_tile(M, Ntot, K, lora=lora)
     BM, BN = bench.tile_dims(tile)
-    if tile == "skinny":
+    if tile in ("skinny", "decode"):
         BM = 8            # M <= 64: rows of both 32-row MFMA tiles, 8 apart
     r = set(per_tile(M, BM, 37)) | {0, M - 1} | {int(v) for v in extra_rows if 0 <= v < M}
     c = set(per_tile(Ntot, BN, 53)) | {0, Ntot - 1}
@@ -143,7 +143,7 @@ def check_group(wl, inp, seed=0):
     s_ref = O.smoothing_scale(act_max, O.weight_absmax(Wn), wl.alpha)
     Ntot, K = W.shape
     outlier_rows = np.argsort(-np.abs(Xn).max(axis=1))[:4]
-    m_rows, cols, tile, BN = tile_samples(wl.M, Ntot, K, rows, outlier_rows)
+    m_rows, cols, tile, BN = tile_samples(wl.M, Ntot, K, rows, g.fused, outlier_rows)
     print(f"[{wl.name}/{inp}] tile {tile}: {len(m_rows)} rows x {len(cols)} columns", flush=True)
 
     for mode in wl.act_modes:

@@ -103,6 +103,8 @@ __device__ __forceinline__ bool xcd_tile(int tiles_m, int tiles, int& tm, int& t
 constexpr int kBK = 128;          // K-tile in bytes
 // Word 3 of a raw buffer resource (no stride, no swizzle, 32-bit data format).
 constexpr int kBufferRsrcWord3 = 0x00020000;
+// s_waitcnt immediate for vmcnt(vm) lgkmcnt(0) (vmcnt in bits 3:0 and 15:14).
+constexpr int wait_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 0x0070; }
 
 // Epilogue shared by both kernels. The MFMAs take the B rows as their first
 // operand and the A rows as their second, so acc[i][j] holds the 32x32 tile
@@ -613,17 +615,11 @@ k_gemm_pipe(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyBN = 32;
 
-// SPLITK: block (x, y) takes the K-tiles [y * kps, (y + 1) * kps) only and
-// writes its INT32 sums to part (slice y, column tile x; 1024 words per row
-// tile, in register order: word q * 64 + lane); k_gemm_skinny_finish adds the
-// slices and runs the epilogue. INT32 addition is exact (and wraps the same
-// in any order), so the result is that of the unsplit kernel bit for bit.
-template <int OUT, bool STATIC_A, int LORA, int TM, bool SPLITK = false>
+template <int OUT, bool STATIC_A, int LORA, int TM>
 __global__ void __launch_bounds__(kSkinnyWaves * 64)
 k_gemm_skinny(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
               const float* __restrict__ a_scale, const float* __restrict__ w_scale, int M, int N,
-              int K, void* __restrict__ Y, int64_t ldy, LoraEpi le, int kps = 0,
-              int32_t* __restrict__ part = nullptr) {
+              int K, void* __restrict__ Y, int64_t ldy, LoraEpi le) {
   __shared__ int32_t red[kSkinnyWaves - 1][TM][16][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -640,8 +636,7 @@ k_gemm_skinny(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
     ap[i] = A + (int64_t)mrow * K + 16 * lhalf;
   }
   const int nk = K / kBK;
-  const int t0 = SPLITK ? (int)blockIdx.y * kps : 0;             // this block's K-tiles [t0, t1)
-  const int t1 = SPLITK ? (t0 + kps < nk ? t0 + kps : nk) : nk;
+  const int t0 = 0, t1 = nk;
 
   auto load = [&](int kt, v4i (&fb)[4], v4i (&fa)[4][TM]) {
     const int64_t off = (int64_t)kt * kBK;
@@ -689,19 +684,14 @@ k_gemm_skinny(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][0][q] += red[w][i][q][lane];
-  if constexpr (SPLITK) {
-    int32_t* dst = part + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * (TM * 1024);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) dst[i * 1024 + q * 64 + lane] = acc[i][0][q];
-  } else {
-    epilogue<OUT, STATIC_A, LORA, TM, 1>(acc, 0, n0, M, N, a_scale, w_scale, Y, ldy, le);
-  }
+  epilogue<OUT, STATIC_A, LORA, TM, 1>(acc, 0, n0, M, N, a_scale, w_scale, Y, ldy, le);
 }
 
-// The KS slices of a split skinny GEMM, added in slice order, then the
-// epilogue. One wave per 32-column tile.
+// The KS slices of a split-K decode GEMM (INT32 sums, 1024 words per 32 x 32
+// tile in register order: word q * 64 + lane; TM row tiles per 32-column
+// tile), added in slice order, then the epilogue. INT32 addition is exact
+// (and wraps the same in any order), so the result is that of the unsplit
+// kernel bit for bit. One wave per 32-column tile.
 template <int OUT, bool STATIC_A, int TM>
 __global__ void __launch_bounds__(64)
 k_gemm_skinny_finish(const int32_t* __restrict__ part, int KS, const float* __restrict__ a_scale,
@@ -722,6 +712,148 @@ k_gemm_skinny_finish(const int32_t* __restrict__ part, int KS, const float* __re
   epilogue<OUT, STATIC_A, 0, TM, 1>(acc, 0, blockIdx.x * kSkinnyBN, M, N, a_scale, w_scale, Y, ldy,
                                     none);
 }
+
+// ---------------------------------------------------------------------------
+// Decode kernel (M <= 64, K % 128 == 0, no LoRA). A decode GEMM streams its
+// weights once; its MFMA work per byte is small, so its speed is the weight
+// stream's: bytes in flight per CU over the memory latency. A block owns BN
+// output columns over all (up to 64) rows and a range of K-tiles, and keeps
+// NST - 1 K-tiles of both operands in flight in an LDS ring (direct buffer
+// loads), where the two-stage GEMM tiles keep one K-tile. One barrier per
+// K-tile guards the ring slot that the next loads overwrite.
+// SPLITK: block (x, y) takes K-tiles [y kps, (y + 1) kps) and writes its
+// INT32 sums to `part` in the layout k_gemm_skinny_finish adds up (32-column
+// tile ct = (BN / 32) x + wave % (BN / 32), row tile wave / (BN / 32)).
+// ---------------------------------------------------------------------------
+// s_waitcnt vmcnt(LPW j) lgkmcnt(0) for a wave-uniform j in [0, 6].
+template <int LPW>
+__device__ __forceinline__ void dec_wait(int j) {
+  switch (j) {
+    case 0: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LPW)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * LPW)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(3 * LPW)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(4 * LPW)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(5 * LPW)); break;
+    default: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(6 * LPW)); break;
+  }
+}
+
+// BN output columns per block, NST LDS ring slots; 2 x BN / 32 waves, each
+// owning one 32 x 32 output tile (row tile wave / (BN / 32)).
+template <int OUT, bool STATIC_A, bool SPLITK, int BN, int NST>
+__global__ void __launch_bounds__(2 * BN / 32 * 64)
+k_gemm_decode(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+              const float* __restrict__ a_scale, const float* __restrict__ w_scale, int M, int N,
+              int K, void* __restrict__ Y, int64_t ldy, int kps, int32_t* __restrict__ part) {
+  constexpr int CTB = BN / 32;                   // 32-column tiles per block
+  constexpr int NW = 2 * CTB;                    // waves
+  constexpr int SLOT = (64 + BN) * kBK;          // one K-tile of both operands
+  constexpr int LA = 8 / NW, LB = BN / 8 / NW;   // 1 KB loads per wave per K-tile
+  constexpr int LPW = LA + LB;
+  static_assert(8 % NW == 0 || NW > 8, "activation rows must split over the waves");
+  static_assert(NST >= 2 && NST <= 8, "dec_wait covers up to 6 K-tiles issued ahead");
+  __shared__ __attribute__((aligned(1024))) char smem[NST * SLOT];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * BN;
+  const int nk = K / kBK;
+  const int t0 = SPLITK ? (int)blockIdx.y * kps : 0;
+  const int t1 = SPLITK ? (t0 + kps < nk ? t0 + kps : nk) : nk;
+  const int cnt = t1 - t0;                       // >= 1: the host makes every slice non-empty
+
+  // Load instruction q of wave w moves 8 tile rows (activations: rows
+  // 8 (w + NW q); weights: rows 8 (w + NW q) of the block's columns); lane l
+  // fetches the chunk that belongs at position l & 7 of row l / 8, XOR-
+  // swizzled as in k_gemm_pipe. Rows past M or N read the last valid row;
+  // their sums are never stored.
+  const int lr = lane >> 3, lp = lane & 7;
+  uint32_t offA[LA > 0 ? LA : 1], offB[LB];
+#pragma unroll
+  for (int q = 0; q < LA; ++q) {
+    const int r = 8 * (wave + NW * q) + lr;
+    const int g = r < M ? r : M - 1;
+    offA[q] = (uint32_t)g * (uint32_t)K + (uint32_t)swz(r, lp);
+  }
+#pragma unroll
+  for (int q = 0; q < LB; ++q) {
+    const int r = 8 * (wave + NW * q) + lr;
+    const int g = n0 + r < N ? n0 + r : N - 1;
+    offB[q] = (uint32_t)g * (uint32_t)K + (uint32_t)swz(r, lp);
+  }
+  const __amdgpu_buffer_rsrc_t rsA =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)((uint32_t)M * (uint32_t)K), kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsB =
+      __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)((uint32_t)N * (uint32_t)K), kBufferRsrcWord3);
+  auto issue = [&](int i) {                      // K-tile t0 + i into slot i % NST
+    char* sl = smem + (i % NST) * SLOT;
+    const int koff = (t0 + i) * kBK;
+#pragma unroll
+    for (int q = 0; q < LA; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)(sl + 1024 * (wave + NW * q)), 16,
+                                               (int)offA[q], koff, 0, 0);
+#pragma unroll
+    for (int q = 0; q < LB; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_ptr_t)(sl + 64 * kBK + 1024 * (wave + NW * q)),
+                                               16, (int)offB[q], koff, 0, 0);
+  };
+
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int wm = wave / CTB, wn = wave % CTB;
+  const int rowA = wm * 32 + lrow, rowB = 64 + wn * 32 + lrow;
+  // one accumulator per k-step of the K-tile: the four MFMAs of a K-tile are
+  // independent, and the partial sums meet once at the end (exact)
+  v16i acc4[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc4[u] = v16i{};
+
+  const int pre = cnt < NST - 1 ? cnt : NST - 1;
+  for (int i = 0; i < pre; ++i) issue(i);
+  for (int i = 0; i < cnt; ++i) {
+    // this wave's loads of K-tile i have landed (the later ones may not) and
+    // its fragment reads of K-tile i - 1 are done; then every wave's are
+    const int last = i + NST - 1 < cnt ? i + NST - 1 : cnt;
+    dec_wait<LPW>(last - 1 - i);
+    __builtin_amdgcn_s_barrier();
+    if (i + NST - 1 < cnt) issue(i + NST - 1);   // into the slot of K-tile i - 1
+    const char* sl = smem + (i % NST) * SLOT;
+    v4i fa[4], fb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = ks * 2 + lhalf;
+      fa[ks] = *(const v4i*)(sl + rowA * kBK + swz(rowA, c));
+      fb[ks] = *(const v4i*)(sl + rowB * kBK + swz(rowB, c));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc4[ks] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[ks], fa[ks], acc4[ks], 0, 0, 0);
+  }
+  v16i acc[1][1];
+  acc[0][0] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+
+  if constexpr (SPLITK) {
+    const int ct = blockIdx.x * CTB + wn;         // 32-column tile
+    const int CT = (N + 31) / 32;
+    if (ct < CT) {
+      int32_t* dst = part + ((int64_t)blockIdx.y * CT + ct) * 2048 + wm * 1024;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) dst[q * 64 + lane] = acc[0][0][q];
+    }
+  } else {
+    const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f, 0, {}, {}};
+    epilogue<OUT, STATIC_A, 0, 1, 1>(acc, wm * 32, n0 + wn * 32, M, N, a_scale, w_scale, Y, ldy,
+                                     none);
+  }
+}
+// 64 columns and 4 slots (64 KB of LDS, two blocks per CU) measured fastest
+// on the OPT-13B decode shapes among 64 / 128 columns and 4 / 6 / 8 slots,
+// weights rotated past the MALL: 64x15360x5120 20.5 us, 64x5120x5120 16.9,
+// 64x20480x5120 36.4, 64x5120x20480 56.7 (38.8 split over 4 K slices),
+// against 38.6 / 22.0 / 39.8 / 67.5 (61.5) for the 128x128 tiles or the
+// skinny kernel used before. One accumulator per k-step instead of one per
+// wave gained 1-3%.
+constexpr int kDecBN = 64;
+constexpr int kDecStages = 4;
 
 // ---------------------------------------------------------------------------
 // Generic kernel: any K % 16 == 0; 128 x 128 tiles staged through registers.
@@ -837,7 +969,9 @@ k_gemm_generic(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
 //                for narrow outputs (N = 4096) and small M;
 //   CFG_SKINNY:  M <= 64 and N < 12288 (decode): 32-column blocks over all
 //                rows, K split over the block's waves.
-enum TileCfg { CFG_GENERIC = 0, CFG_256 = 1, CFG_128 = 2, CFG_256x192 = 3, CFG_SKINNY = 4 };
+//   CFG_DECODE:  M <= 64 without LoRA: 64-column blocks with a deep LDS ring,
+//                K split across blocks when a workspace is given.
+enum TileCfg { CFG_GENERIC = 0, CFG_256 = 1, CFG_128 = 2, CFG_256x192 = 3, CFG_SKINNY = 4, CFG_DECODE = 5 };
 
 // Score of a tile configuration: the share of the launched tile work that is
 // useful (rows and columns padded up to whole tiles, and the last round of
@@ -850,16 +984,23 @@ static double tile_score(int64_t M, int64_t N, int64_t bm, int64_t bn, int64_t r
   return rate * pad * (double)tiles / (double)(rounds * resident);
 }
 
-static int pick_cfg(int64_t M, int64_t N, int64_t K) {
-  if (K % kBK != 0 || M * K >= (1LL << 32) || N * K >= (1LL << 32)) return CFG_GENERIC;
-  // Tuning override: SQ_GEMM_TILE=0|1|2|3|4 forces a configuration (read once
-  // per process; 4, the skinny kernel, only where M <= 64).
+// Tuning override: SQ_GEMM_TILE=0..5 forces a configuration (read once per
+// process; 4, the skinny kernel, and 5, the decode kernel, only where M <= 64).
+static int forced_cfg() {
   static const int forced = [] {
     const char* e = std::getenv("SQ_GEMM_TILE");
     const int o = (e && *e) ? std::atoi(e) : -1;
-    return (o >= 0 && o <= 4) ? o : -1;
+    return (o >= 0 && o <= 5) ? o : -1;
   }();
-  if (forced >= 0 && (forced != CFG_SKINNY || M <= 64)) return forced;
+  return forced;
+}
+
+// Tile configuration of the LoRA-capable kernels (the decode kernel, chosen
+// before this for M <= 64 without LoRA, is not one of them).
+static int pick_cfg(int64_t M, int64_t N, int64_t K) {
+  if (K % kBK != 0 || M * K >= (1LL << 32) || N * K >= (1LL << 32)) return CFG_GENERIC;
+  const int forced = forced_cfg();
+  if (forced >= 0 && forced != CFG_DECODE && (forced != CFG_SKINNY || M <= 64)) return forced;
   // M <= 64 with fewer than 96 column tiles of 128: the skinny kernel (measured
   // 1.7-3.6x faster at N = 5120); with more, 128x128 tiles already spread the
   // weight stream over the chip and win (by 8-34% at N = 15360 ... 28672).
@@ -889,45 +1030,60 @@ static int launch_pipe(const int8_t* Xq, const int8_t* Wq, const float* a_scale,
   return SQ_OK;
 }
 
-// K split of the skinny kernel across blocks, given a workspace: slices of
-// whole K-tiles so that about 512 blocks run (the column tiles alone give
-// N / 32), each slice at least 16 K-tiles (two per wave), and only where at
-// least 4 slices are wanted and fit (K >= 8192). Measured at M = 64, N = 5120 with the
-// weights rotated past the MALL: K = 20480 69 -> 61 us in 4 slices; K = 5120
-// in 2 slices was slower (22 -> 26 us: the partial sums and the second
-// launch cost more than the wider grid gains). 1: no split.
-static int skinny_splits(int64_t M, int64_t N, int64_t K) {
-  if (M > 64 || pick_cfg(M, N, K) != CFG_SKINNY) return 1;
-  const int64_t ct = (N + kSkinnyBN - 1) / kSkinnyBN;
-  const int64_t kmax = (K / kBK) / 16;
-  if (kmax < 4) return 1;
-  int64_t ks = (512 + ct - 1) / ct;
+// The decode kernel for M <= 64 (no LoRA epilogue): K a multiple of 128 and
+// operands below 4 GiB, unless SQ_GEMM_TILE forces another configuration.
+static bool decode_ok(int64_t M, int64_t N, int64_t K) {
+  if (M > 64 || K % kBK != 0 || M * K >= (1LL << 32) || N * K >= (1LL << 32)) return false;
+  const int f = forced_cfg();
+  return f < 0 || f == CFG_DECODE;
+}
+
+// K split of the decode kernel across blocks, given a workspace, where the
+// column blocks alone leave most CUs idle: slices of whole K-tiles so that
+// about 256 blocks stream, each slice at least 8 K-tiles, so that the INT32
+// partial sums (KS x 64 x N x 4 bytes) stay at most a quarter of the weight
+// bytes. 1: no split.
+static int decode_splits(int64_t M, int64_t N, int64_t K) {
+  if (!decode_ok(M, N, K)) return 1;
+  const int64_t ct = (N + kDecBN - 1) / kDecBN;
+  // with 128 or more column blocks the split was slower (64x15360x5120:
+  // 20.5 -> 26.5 us); below that it pays (64x5120x20480: 56.7 -> 38.8 us)
+  if (ct >= 128) return 1;
+  const int64_t kmax = (K / kBK) / 8;
+  int64_t ks = (256 + ct - 1) / ct;
   if (ks > kmax) ks = kmax;
-  return ks >= 4 ? (int)ks : 1;   // 2 or 3 slices: not measured faster than one
+  return ks > 1 ? (int)ks : 1;
 }
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  const int ks = skinny_splits(M, N, K);
+  const int ks = decode_splits(M, N, K);
   if (ks <= 1) return 0;
-  const int64_t ct = (N + kSkinnyBN - 1) / kSkinnyBN;
-  const int64_t tm = M <= 32 ? 1 : 2;
-  return (size_t)ks * (size_t)ct * (size_t)tm * 1024 * sizeof(int32_t);
+  const int64_t ct = (N + 31) / 32;            // 32-column tiles, two row tiles each
+  return (size_t)ks * (size_t)ct * 2048 * sizeof(int32_t);
 }
 
-template <int OUT, bool STATIC_A, int TM>
-static int launch_skinny_split(const int8_t* Xq, const int8_t* Wq, const float* a_scale,
-                               const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y,
-                               int64_t ldy, int ks, int32_t* part, hipStream_t st) {
-  const unsigned ct = (unsigned)((N + kSkinnyBN - 1) / kSkinnyBN);
+template <int OUT, bool STATIC_A>
+static int launch_decode(const int8_t* Xq, const int8_t* Wq, const float* a_scale,
+                         const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y, int64_t ldy,
+                         int32_t* part, hipStream_t st) {
+  const unsigned bn = (unsigned)((N + kDecBN - 1) / kDecBN);
+  const int ks = part != nullptr ? decode_splits(M, N, K) : 1;
+  if (ks <= 1) {
+    k_gemm_decode<OUT, STATIC_A, false, kDecBN, kDecStages><<<bn, kDecBN / 16 * 64, 0, st>>>(
+        Xq, Wq, a_scale, w_scale, (int)M, (int)N, (int)K, Y, ldy, 0, nullptr);
+    SQ_LAUNCH_CHECK();
+    return SQ_OK;
+  }
   const int nk = (int)(K / kBK);
   const int kps = (nk + ks - 1) / ks;
   const int slices = (nk + kps - 1) / kps;   // every slice non-empty
-  const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f, 0, {}, {}};
-  k_gemm_skinny<OUT, STATIC_A, 0, TM, true><<<dim3(ct, (unsigned)slices), kSkinnyWaves * 64, 0, st>>>(
-      Xq, Wq, a_scale, w_scale, (int)M, (int)N, (int)K, Y, ldy, none, kps, part);
+  k_gemm_decode<OUT, STATIC_A, true, kDecBN, kDecStages><<<dim3(bn, (unsigned)slices), kDecBN / 16 * 64, 0,
+                                                           st>>>(
+      Xq, Wq, a_scale, w_scale, (int)M, (int)N, (int)K, Y, ldy, kps, part);
   SQ_LAUNCH_CHECK();
-  k_gemm_skinny_finish<OUT, STATIC_A, TM><<<ct, 64, 0, st>>>(part, slices, a_scale, w_scale, (int)M,
-                                                            (int)N, Y, ldy);
+  const unsigned ct = (unsigned)((N + 31) / 32);
+  k_gemm_skinny_finish<OUT, STATIC_A, 2><<<ct, 64, 0, st>>>(part, slices, a_scale, w_scale, (int)M,
+                                                           (int)N, Y, ldy);
   SQ_LAUNCH_CHECK();
   return SQ_OK;
 }
@@ -936,13 +1092,9 @@ template <int OUT, bool STATIC_A, int LORA>
 static int launch_gemm_t(const int8_t* Xq, const int8_t* Wq, const float* a_scale,
                          const float* w_scale, int64_t M, int64_t N, int64_t K, void* Y,
                          int64_t ldy, const LoraEpi& le, hipStream_t st, int32_t* part = nullptr) {
-  if constexpr (LORA == 0 && OUT != OUT_I32) {
-    const int ks = part != nullptr ? skinny_splits(M, N, K) : 1;
-    if (ks > 1)
-      return M <= 32 ? launch_skinny_split<OUT, STATIC_A, 1>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy,
-                                                               ks, part, st)
-                     : launch_skinny_split<OUT, STATIC_A, 2>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy,
-                                                               ks, part, st);
+  if constexpr (LORA == 0) {
+    if (decode_ok(M, N, K))
+      return launch_decode<OUT, STATIC_A>(Xq, Wq, a_scale, w_scale, M, N, K, Y, ldy, part, st);
   }
   switch (pick_cfg(M, N, K)) {
     case CFG_256:
