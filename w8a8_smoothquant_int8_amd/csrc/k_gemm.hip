@@ -8,9 +8,10 @@
 // two 16-byte halves of a 32-byte k step.
 //
 // Main kernel (K a multiple of 128): block tile BM x BN, K-tile 128 bytes,
-// 2-stage LDS ring filled straight from global memory by
-// GLOBAL_LOAD_LDS_DWORDX4 (no register staging). One wave instruction moves
-// 1 KB = 8 tile rows into consecutive LDS; each lane picks which 16-byte chunk
+// 2-stage LDS ring filled straight from global memory by buffer loads into
+// LDS (no register staging; a 32-bit per-lane offset and a scalar K-tile
+// offset, so no 64-bit address arithmetic per load). One wave instruction
+// moves 1 KB = 8 tile rows into consecutive LDS; each lane picks which 16-byte chunk
 // of its row to fetch so that the tile lands XOR-swizzled (swz below) and the
 // MFMA operand reads are free of bank conflicts. Tiles are assigned XCD by
 // XCD: the hardware deals workgroups round-robin to the 8 XCDs, so block b
@@ -18,8 +19,13 @@
 // walks patches of 8 tile rows column by column, so the blocks an XCD runs at
 // once share operand panels in its L2.
 //
-// Skinny kernel (M <= 64, narrow N): 32-column blocks over all rows, K split
-// across the block's waves, fragments straight from global memory.
+// Decode kernel (M <= 64, no LoRA): 64-column blocks over all rows with a
+// 4-slot LDS ring (three K-tiles in flight), K split across blocks through a
+// workspace where the column blocks alone are too few.
+//
+// Skinny kernel (M <= 64 with the LoRA epilogue, narrow N): 32-column blocks
+// over all rows, K split across the block's waves, fragments straight from
+// global memory.
 //
 // Generic kernel (any K multiple of 16): 128 x 128 tiles staged through
 // registers, zero-filling the K tail.
