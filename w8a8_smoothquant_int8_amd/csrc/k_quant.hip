@@ -17,6 +17,13 @@
 // the fp64 reciprocals 1/s that make the divisions exact for the others, see
 // div_rn and rcp_rn64) are computed once per block, after its first loads are
 // issued, and reused for all its rows.
+//
+// Two more shapes of the same arithmetic: k_quant_wave (one to four waves per
+// row, K <= 16384 for 16-bit inputs) and k_quant_long (one block per row and
+// the next row in flight, 16384 < K <= 32768 for 16-bit inputs); the kernel
+// above serves fp32 inputs beyond K = 4096.
+#include <cstdlib>
+
 #include "sq_internal.h"
 
 namespace sq {
@@ -451,6 +458,189 @@ static void launch_wave(const char* p, int64_t rows, int64_t K, int64_t ldb, con
   f<<<(unsigned)grid, kWaveRowThreads, 0, st>>>(p, rows, (int)K, ldb, s, scale_io, out, clip);
 }
 
+// ---------------------------------------------------------------------------
+// Long-row quantizer (16-bit inputs, 16384 < K <= 32768): one 512-thread
+// block per row, lane chunks CPT = ceil(K / 4096) (5 at K = 20480, 7 at
+// K = 28672), persistent over the rows. The raw row is double-buffered in
+// registers: row i + 1's loads are issued before row i's first pass, so a
+// whole row of compute (both passes and the block reduction) covers their
+// latency; v is recomputed from the raw row in the second pass (the fp32
+// factors, or the fp64 reciprocals, and two raw rows leave no room for it).
+// For the divided kinds the first pass takes the row max over the fp64
+// products, before their rounding to fp32: RN32 is monotonic, so the max of
+// the rounded values is the rounded max. Chunks past the row end (K not a
+// multiple of 4096) re-read the last chunk, are left out of the max and are
+// not stored.
+// ---------------------------------------------------------------------------
+template <int DT, int CPT, int KIND, int NB>
+__global__ void __launch_bounds__(kQuantMaxThreads)
+k_quant_long(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_bytes,
+             const float* __restrict__ s, float* __restrict__ scale_io, int8_t* __restrict__ out,
+             unsigned long long* __restrict__ clip) {
+  static_assert(DT != SQ_F32, "16-bit inputs: one 16-byte word per chunk");
+  constexpr int T = kQuantMaxThreads;
+  constexpr int NW = T / 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nch = K / 8;
+  const int64_t step = gridDim.x;
+  auto chunk = [&](int j) { return tid + T * j < nch ? tid + T * j : nch - 1; };
+  auto load = [&](uint4 (&r)[CPT], int64_t row) {
+    const char* p = in + row * in_ld_bytes;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) r[j] = *(const uint4*)(p + (int64_t)chunk(j) * 16);
+  };
+  // NB raw rows: the one being quantized and the next NB - 1 in flight
+  uint4 rbuf[NB][CPT];
+  int64_t m = blockIdx.x;
+#pragma unroll
+  for (int b = 0; b < NB - 1; ++b)
+    if (m + b * step < rows) load(rbuf[b], m + b * step);
+
+  // per-channel factors of this thread's chunks, once per block
+  float sm[KIND == Q_FOLD ? CPT : 1][8];
+  double rs[KIND == Q_FOLD ? 1 : CPT][8];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int c = chunk(j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float sv = s != nullptr ? s[c * 8 + e] : 1.0f;
+      if constexpr (KIND == Q_FOLD) sm[j][e] = sv;
+      else rs[j][e] = rcp_rn64(sv);                // RN64(1/s)
+    }
+  }
+  constexpr bool counting = KIND == Q_STATIC_CLIP;
+  int nclip = 0;
+  float a_static = 0.0f;
+  double r_static = 0.0;
+  if constexpr (kStaticKind<KIND>) {
+    a_static = scale_io[0];
+    r_static = a_static != 0.0f ? rcp_rn64(a_static) : 0.0;
+  }
+  __shared__ float red[2][NW];
+
+  auto smooth = [&](const float x, int j, int e) -> float {
+    if constexpr (KIND == Q_FOLD) return x * sm[j][e];   // fp32 multiply
+    else return div_rn(x, rs[j % CPT][e]);               // fp32(x / s), exact
+  };
+  auto process = [&](const uint4 (&cur)[CPT], uint4 (&nxt)[CPT], int64_t row, int par) {
+    if (row + (NB - 1) * step < rows) load(nxt, row + (NB - 1) * step);
+    // pass 1: the row max
+    float amax;
+    if constexpr (KIND == Q_FOLD) {
+      float a = 0.0f;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        float x[8];
+        widen8<DT>(&cur[j], x);
+        float cm = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cm = __builtin_fmaxf(cm, __builtin_fabsf(x[e] * sm[j][e]));
+        a = __builtin_fmaxf(a, tid + T * j < nch ? cm : 0.0f);
+      }
+      amax = a;
+    } else {
+      double a = 0.0;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        float x[8];
+        widen8<DT>(&cur[j], x);
+        double cm = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          cm = __builtin_fmax(cm, __builtin_fabs((double)x[e] * rs[j][e]));
+        a = __builtin_fmax(a, tid + T * j < nch ? cm : 0.0);
+      }
+      amax = (float)a;
+    }
+    float scale;
+    double rscale;
+    if constexpr (kStaticKind<KIND>) {
+      scale = a_static;
+      rscale = r_static;
+    } else {
+      amax = wave_max(amax);
+      if (lane == 0) red[par][wave] = amax;
+      __syncthreads();
+      amax = red[par][0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) amax = __builtin_fmaxf(amax, red[par][w]);
+      scale = amax / 127.0f;                                   // IEEE fp32 division
+      rscale = scale != 0.0f ? rcp_rn64(scale) : 0.0;
+      if (tid == 0) scale_io[row] = scale;
+    }
+    // pass 2: codes (scale == 0: every code is 0)
+    const uint32_t keep = scale != 0.0f ? 0xFFFFFFFFu : 0u;
+    int8_t* orow = out + row * K;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      // the raw words pass through an opaque copy that depends on the scale:
+      // otherwise the compiler recomputes every chunk's v ahead of the row
+      // reduction and holds it there (a register per element, and spills)
+      uint4 w = cur[j];
+      asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w) : "v"(keep));
+      float y[8];
+      widen8<DT>(&w, y);
+      uint32_t q[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = code_word(div_rn(smooth(y[e], j, e), rscale));
+      uint2 pk;
+      pk.x = pack4_codes(q[0], q[1], q[2], q[3]) & keep;
+      pk.y = pack4_codes(q[4], q[5], q[6], q[7]) & keep;
+      const int c = tid + T * j;
+      if (c < nch) *(uint2*)(orow + c * 8) = pk;
+    }
+    // the rare count (see k_quant_rows)
+    if (counting && div_rn(amax, rscale) >= 127.5f) {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        if (tid + T * j < nch) {
+          uint4 w = cur[j];
+          asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w) : "v"(nclip));
+          float y[8];
+          widen8<DT>(&w, y);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) nclip += clips(div_rn(smooth(y[e], j, e), rscale));
+        }
+      }
+    }
+  };
+  // the k-th row of the block uses LDS reduction slot k & 1
+  int par = 0;
+  for (; m < rows; m += NB * step) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int64_t row = m + b * step;
+      if (row < rows) process(rbuf[b], rbuf[(b + NB - 1) % NB], row, (par + b) & 1);
+    }
+    par ^= NB & 1;
+  }
+  if constexpr (counting) {
+    const int n = wave_sum(nclip);
+    if (lane == 0 && n != 0) atomicAdd(clip, (unsigned long long)n);
+  }
+}
+
+template <int DT, int CPT, int KIND>
+struct LongTag {};
+
+// Rows in registers: the one being quantized and the next. A third (two in
+// flight, where the registers allow it: the fold, or up to 6 chunks per lane)
+// measured no faster at K = 20480 and 28672.
+constexpr int kLongRowsBuffered = 2;
+
+template <int DT, int CPT, int KIND>
+static void launch_long(const char* p, int64_t rows, int64_t K, int64_t ldb, const float* s,
+                        float* scale_io, int8_t* out, unsigned long long* clip, hipStream_t st) {
+  auto f = k_quant_long<DT, CPT, KIND, kLongRowsBuffered>;
+  int64_t grid = rows;
+  const int64_t cap = resident_blocks<LongTag<DT, CPT, KIND>>((const void*)f, kQuantMaxThreads);
+  if (grid > cap) grid = cap;
+  f<<<(unsigned)grid, kQuantMaxThreads, 0, st>>>(p, rows, (int)K, ldb, s, scale_io, out, clip);
+}
+
 // Block-per-row-group shape: chunks per thread CPT in {1, 2, 4, 8}, the
 // smallest that lets at most 512 threads cover the row; T = threads, a
 // multiple of 256 (the same number of waves on each of the CU's 4 SIMDs);
@@ -483,6 +673,14 @@ static void launch_shape(const char* p, int64_t rows, int64_t K, int64_t ldb, co
   f<<<(unsigned)grid, T, 0, st>>>(p, rows, K, ldb, s, scale_io, out, clip);
 }
 
+// SQ_QUANT_LONG=0 selects the block-per-row-group kernel for long rows too
+// (both kernels give the same codes and scales; the switch exists to time and
+// test one against the other).
+static bool long_rows_off() {
+  const char* e = std::getenv("SQ_QUANT_LONG");
+  return e != nullptr && e[0] == '0';
+}
+
 template <int DT, int KIND>
 static int launch_rows_dt(const void* in, int64_t rows, int64_t K, int64_t ld, const float* s,
                           float* scale_io, int8_t* out, unsigned long long* clip, hipStream_t st) {
@@ -511,6 +709,17 @@ static int launch_rows_dt(const void* in, int64_t rows, int64_t K, int64_t ld, c
   }
       if (wpr == 2) { SQ_WAVE_CPL(2) } else { SQ_WAVE_CPL(4) }
 #undef SQ_WAVE_CPL
+      SQ_LAUNCH_CHECK();
+      return SQ_OK;
+    }
+    if (!long_rows_off()) {
+      // 16384 < K <= 32768: one block per row, chunks per lane 5 .. 8
+      switch ((K / 8 + kQuantMaxThreads - 1) / kQuantMaxThreads) {
+        case 5: launch_long<DT, 5, KIND>(p, rows, K, ldb, s, scale_io, out, clip, st); break;
+        case 6: launch_long<DT, 6, KIND>(p, rows, K, ldb, s, scale_io, out, clip, st); break;
+        case 7: launch_long<DT, 7, KIND>(p, rows, K, ldb, s, scale_io, out, clip, st); break;
+        default: launch_long<DT, 8, KIND>(p, rows, K, ldb, s, scale_io, out, clip, st); break;
+      }
       SQ_LAUNCH_CHECK();
       return SQ_OK;
     }
