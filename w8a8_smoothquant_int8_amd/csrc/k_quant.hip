@@ -461,18 +461,15 @@ static void launch_wave(const char* p, int64_t rows, int64_t K, int64_t ldb, con
 // ---------------------------------------------------------------------------
 // Long-row quantizer (16-bit inputs, 16384 < K <= 32768): one 512-thread
 // block per row, lane chunks CPT = ceil(K / 4096) (5 at K = 20480, 7 at
-// K = 28672), persistent over the rows. The raw row is double-buffered in
-// registers: row i + 1's loads are issued before row i's first pass, so a
-// whole row of compute (both passes and the block reduction) covers their
-// latency; v is recomputed from the raw row in the second pass (the fp32
-// factors, or the fp64 reciprocals, and two raw rows leave no room for it).
-// For the divided kinds the first pass takes the row max over the fp64
-// products, before their rounding to fp32: RN32 is monotonic, so the max of
-// the rounded values is the rounded max. Chunks past the row end (K not a
+// K = 28672), persistent over the rows. Two raw rows live in registers next
+// to the per-channel factors: pass 1 turns the current row into v (kept in
+// LDS, as per-thread storage) and its row max, and its registers then take
+// the row after next, so two rows stay in flight through the block reduction
+// and pass 2, which quantizes v from LDS. Chunks past the row end (K not a
 // multiple of 4096) re-read the last chunk, are left out of the max and are
 // not stored.
 // ---------------------------------------------------------------------------
-template <int DT, int CPT, int KIND, int NB>
+template <int DT, int CPT, int KIND>
 __global__ void __launch_bounds__(kQuantMaxThreads)
 k_quant_long(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_bytes,
              const float* __restrict__ s, float* __restrict__ scale_io, int8_t* __restrict__ out,
@@ -491,12 +488,14 @@ k_quant_long(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
 #pragma unroll
     for (int j = 0; j < CPT; ++j) r[j] = *(const uint4*)(p + (int64_t)chunk(j) * 16);
   };
-  // NB raw rows: the one being quantized and the next NB - 1 in flight
-  uint4 rbuf[NB][CPT];
+  // Two raw rows in registers: the one being quantized and the next, in
+  // flight. Pass 1 turns the row into v, so its registers are free at once and
+  // take the row after next: two rows stay in flight through the row
+  // reduction and pass 2.
+  uint4 ra[CPT], rb[CPT];
   int64_t m = blockIdx.x;
-#pragma unroll
-  for (int b = 0; b < NB - 1; ++b)
-    if (m + b * step < rows) load(rbuf[b], m + b * step);
+  if (m < rows) load(ra, m);
+  if (m + step < rows) load(rb, m + step);
 
   // per-channel factors of this thread's chunks, once per block
   float sm[KIND == Q_FOLD ? CPT : 1][8];
@@ -520,40 +519,49 @@ k_quant_long(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
     r_static = a_static != 0.0f ? rcp_rn64(a_static) : 0.0;
   }
   __shared__ float red[2][NW];
+  // v of this thread's chunks, kept in LDS between the passes (the registers
+  // hold the factors and two raw rows): half h of chunk j at vst[h][j T + tid],
+  // so consecutive lanes touch consecutive 16-byte words. Each thread reads
+  // back only what it wrote itself, so no barrier guards it.
+  __shared__ float4 vst[2][CPT * T];
 
   auto smooth = [&](const float x, int j, int e) -> float {
     if constexpr (KIND == Q_FOLD) return x * sm[j][e];   // fp32 multiply
-    else return div_rn(x, rs[j % CPT][e]);               // fp32(x / s), exact
+    else return div_rn(x, rs[j][e]);                     // fp32(x / s), exact
   };
-  auto process = [&](const uint4 (&cur)[CPT], uint4 (&nxt)[CPT], int64_t row, int par) {
-    if (row + (NB - 1) * step < rows) load(nxt, row + (NB - 1) * step);
-    // pass 1: the row max
-    float amax;
-    if constexpr (KIND == Q_FOLD) {
-      float a = 0.0f;
+  // (the index passes through an opaque copy that depends on `dep`, a value
+  // known only after pass 1 (and the row reduction): otherwise the compiler
+  // hoists every read above it and holds all of v in registers, and spills)
+  auto read_v = [&](int j, float* y, uint32_t dep) {
+    int i = j * T + tid;
+    asm volatile("" : "+v"(i) : "v"(dep));
+    const float4 v0 = vst[0][i], v1 = vst[1][i];
+    y[0] = v0.x; y[1] = v0.y; y[2] = v0.z; y[3] = v0.w;
+    y[4] = v1.x; y[5] = v1.y; y[6] = v1.z; y[7] = v1.w;
+  };
+  auto process = [&](uint4 (&cur)[CPT], int64_t row, int par) {
+    // pass 1: v and the row max
+    float amax = 0.0f;
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        float x[8];
-        widen8<DT>(&cur[j], x);
-        float cm = 0.0f;
+    for (int j = 0; j < CPT; ++j) {
+      float x[8];
+      widen8<DT>(&cur[j], x);
+      float cm = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cm = __builtin_fmaxf(cm, __builtin_fabsf(x[e] * sm[j][e]));
-        a = __builtin_fmaxf(a, tid + T * j < nch ? cm : 0.0f);
+      for (int e = 0; e < 8; ++e) {
+        x[e] = smooth(x[e], j, e);
+        cm = __builtin_fmaxf(cm, __builtin_fabsf(x[e]));
       }
-      amax = a;
-    } else {
-      double a = 0.0;
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        float x[8];
-        widen8<DT>(&cur[j], x);
-        double cm = 0.0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          cm = __builtin_fmax(cm, __builtin_fabs((double)x[e] * rs[j][e]));
-        a = __builtin_fmax(a, tid + T * j < nch ? cm : 0.0);
-      }
-      amax = (float)a;
+      vst[0][j * T + tid] = make_float4(x[0], x[1], x[2], x[3]);
+      vst[1][j * T + tid] = make_float4(x[4], x[5], x[6], x[7]);
+      amax = __builtin_fmaxf(amax, tid + T * j < nch ? cm : 0.0f);
+    }
+    if (row + 2 * step < rows) {
+      // an opaque zero that depends on the row max: the loads may not move
+      // above pass 1, whose registers they reuse
+      int zero;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(zero) : "v"(amax));
+      load(cur, row + 2 * step + zero);
     }
     float scale;
     double rscale;
@@ -571,21 +579,16 @@ k_quant_long(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
       rscale = scale != 0.0f ? rcp_rn64(scale) : 0.0;
       if (tid == 0) scale_io[row] = scale;
     }
-    // pass 2: codes (scale == 0: every code is 0)
+    // pass 2: codes from v (scale == 0: every code is 0)
     const uint32_t keep = scale != 0.0f ? 0xFFFFFFFFu : 0u;
     int8_t* orow = out + row * K;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-      // the raw words pass through an opaque copy that depends on the scale:
-      // otherwise the compiler recomputes every chunk's v ahead of the row
-      // reduction and holds it there (a register per element, and spills)
-      uint4 w = cur[j];
-      asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w) : "v"(keep));
       float y[8];
-      widen8<DT>(&w, y);
+      read_v(j, y, __float_as_uint(amax));
       uint32_t q[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = code_word(div_rn(smooth(y[e], j, e), rscale));
+      for (int e = 0; e < 8; ++e) q[e] = code_word(div_rn(y[e], rscale));
       uint2 pk;
       pk.x = pack4_codes(q[0], q[1], q[2], q[3]) & keep;
       pk.y = pack4_codes(q[4], q[5], q[6], q[7]) & keep;
@@ -597,25 +600,18 @@ k_quant_long(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         if (tid + T * j < nch) {
-          uint4 w = cur[j];
-          asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w) : "v"(nclip));
           float y[8];
-          widen8<DT>(&w, y);
+          read_v(j, y, (uint32_t)nclip);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) nclip += clips(div_rn(smooth(y[e], j, e), rscale));
+          for (int e = 0; e < 8; ++e) nclip += clips(div_rn(y[e], rscale));
         }
       }
     }
   };
   // the k-th row of the block uses LDS reduction slot k & 1
-  int par = 0;
-  for (; m < rows; m += NB * step) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int64_t row = m + b * step;
-      if (row < rows) process(rbuf[b], rbuf[(b + NB - 1) % NB], row, (par + b) & 1);
-    }
-    par ^= NB & 1;
+  for (; m < rows; m += 2 * step) {
+    process(ra, m, 0);
+    if (m + step < rows) process(rb, m + step, 1);
   }
   if constexpr (counting) {
     const int n = wave_sum(nclip);
@@ -626,15 +622,10 @@ k_quant_long(const char* __restrict__ in, int64_t rows, int K, int64_t in_ld_byt
 template <int DT, int CPT, int KIND>
 struct LongTag {};
 
-// Rows in registers: the one being quantized and the next. A third (two in
-// flight, where the registers allow it: the fold, or up to 6 chunks per lane)
-// measured no faster at K = 20480 and 28672.
-constexpr int kLongRowsBuffered = 2;
-
 template <int DT, int CPT, int KIND>
 static void launch_long(const char* p, int64_t rows, int64_t K, int64_t ldb, const float* s,
                         float* scale_io, int8_t* out, unsigned long long* clip, hipStream_t st) {
-  auto f = k_quant_long<DT, CPT, KIND, kLongRowsBuffered>;
+  auto f = k_quant_long<DT, CPT, KIND>;
   int64_t grid = rows;
   const int64_t cap = resident_blocks<LongTag<DT, CPT, KIND>>((const void*)f, kQuantMaxThreads);
   if (grid > cap) grid = cap;
