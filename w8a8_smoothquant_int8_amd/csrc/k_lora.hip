@@ -609,149 +609,197 @@ k_lora_shrink_seg_pipe(const char* __restrict__ X, int64_t ldx_bytes, int M, int
 template <int YT, bool SEG, int KSM>
 __global__ void __launch_bounds__(kLoraThreads, 2)
 k_lora_expand(const unsigned short* __restrict__ T, int M, int N, LoraArgs la, float scale,
-              void* __restrict__ Y, int64_t ldy) {
+              void* __restrict__ Y, int64_t ldy, int row_tiles, int col_tiles) {
   constexpr int BM = 64, BN = 256;
   __shared__ __attribute__((aligned(16))) float dl[BM * BN];   // 64 KB
   constexpr int VPT = YT == SQ_F32 ? 4 : 8;   // Y values per 16-byte access
   constexpr int TPR = BN / VPT;               // threads per tile row
   constexpr int RPP = 256 / TPR;              // tile rows per pass
   constexpr int NP = BM / RPP;                // passes
+  // The next tile's Y loads are issued before this tile's product where the
+  // registers allow a second Y tile next to the B and T fragments: 16-bit Y
+  // (8 words a thread) and ranks up to 64.
+  constexpr bool PF = KSM <= 2 && YT != SQ_F32;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 15, kg = lane >> 4;
-
-  // The block's rows [m0, mend) and their adapter.
-  int m0, mend, r;
-  const unsigned short* Bm;
-  if constexpr (SEG) {
-    int g, tile;
-    if (!seg_tile_of_block(la, blockIdx.x, &g, &tile)) return;
-    m0 = la.seg_start[g] + tile * BM;
-    const int s1 = la.seg_start[g + 1];
-    mend = m0 + BM < s1 ? m0 + BM : s1;
-    const int ad = la.seg_adapter[g];
-    Bm = (const unsigned short*)la.B_ptrs[ad];
-    r = la.ranks[ad];
-  } else {
-    m0 = blockIdx.x * BM;
-    mend = m0 + BM < M ? m0 + BM : M;
-    Bm = la.B;
-    r = la.r;
-  }
-  const int n0 = blockIdx.y * BN;
   const int pr = tid / TPR, pc = (tid % TPR) * VPT;
-  const bool col_ok = n0 + pc < N;
 
-  // Every load below is unconditional, with out-of-range addresses clamped to
+  // Tile `it` (column tiles fastest): rows [m0, mend), their adapter, and
+  // columns from n0. False when it holds no rows (past the last (request,
+  // tile) pair; every later tile is then empty too). Block-uniform.
+  struct Tile {
+    int m0, mend, r, n0;
+    const unsigned short* Bm;
+  };
+  auto tile_of = [&](int it, Tile& t) -> bool {
+    if (it >= row_tiles * col_tiles) return false;
+    const int tm = it / col_tiles;
+    t.n0 = (it % col_tiles) * BN;
+    if constexpr (SEG) {
+      // every thread has read the previous lookup's result from LDS
+      __syncthreads();
+      int g, tl;
+      if (!seg_tile_of_block(la, tm, &g, &tl)) return false;
+      t.m0 = la.seg_start[g] + tl * BM;
+      const int s1 = la.seg_start[g + 1];
+      t.mend = t.m0 + BM < s1 ? t.m0 + BM : s1;
+      const int ad = la.seg_adapter[g];
+      t.Bm = (const unsigned short*)la.B_ptrs[ad];
+      t.r = la.ranks[ad];
+    } else {
+      t.m0 = tm * BM;
+      t.mend = t.m0 + BM < M ? t.m0 + BM : M;
+      t.Bm = la.B;
+      t.r = la.r;
+    }
+    return true;
+  };
+  // The Y tile, coalesced (rows past mend and columns past N read the tile's
+  // first row and column, and are not stored).
+  auto load_y = [&](const Tile& t, uint4 (&yv)[NP]) {
+    const bool col_ok = t.n0 + pc < N;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int m = t.m0 + p * RPP + pr;
+      const int64_t off = (int64_t)(m < t.mend ? m : t.m0) * ldy + (col_ok ? t.n0 + pc : t.n0);
+      yv[p] = YT == SQ_F32 ? *(const uint4*)((const float*)Y + off)
+                           : *(const uint4*)((const unsigned short*)Y + off);
+    }
+  };
+
+  // One tile: Y (its values in yc, loaded earlier with PF) += scale * T B^T.
+  // Every load is unconditional, with out-of-range addresses clamped to
   // valid ones, and no value needs masking: T rows are zero from the
   // adapter's rank up to Rp (its B columns past r, clamped, meet zeros),
   // clamped T rows stay inside the block's request (finite values whose D
   // rows are not stored), and D columns past N are not stored either.
   // (A select between a loaded value and 0, or a load skipped by a branch,
-  // would end in a wait for all loads in flight, the Y tile's included.)
-  const int nw = n0 + 64 * wave;   // this wave's 64 columns of the tile
-  constexpr int Rp = 32 * KSM;     // T's row stride (R rounded up to 32)
-  // The B and T fragments of rank step ks: B rows nw + 16 t + lane % 16,
-  // T rows m0 + 16 rt + lane % 16, ranks 32 ks + 8 (lane / 16) .. + 7.
-  auto load_bt = [&](int ks, uint4 (&bu)[4], uint4 (&tu)[4]) {
-    const int k = ks * 32 + kg * 8;
-    const int kb = k < r ? k : r - 8;
+  // would end in a wait for all loads in flight, the Y tiles' included.)
+  auto process = [&](const Tile& t, uint4 (&yc)[NP], const Tile* nxt, uint4 (&yn)[NP]) {
+    const int nw = t.n0 + 64 * wave;   // this wave's 64 columns of the tile
+    constexpr int Rp = 32 * KSM;       // T's row stride (R rounded up to 32)
+    const int r = t.r, m0 = t.m0, mend = t.mend;
+    const unsigned short* Bm = t.Bm;
+    // The B and T fragments of rank step ks: B rows nw + 16 u + lane % 16,
+    // T rows m0 + 16 rt + lane % 16, ranks 32 ks + 8 (lane / 16) .. + 7.
+    auto load_bt = [&](int ks, uint4 (&bu)[4], uint4 (&tu)[4]) {
+      const int k = ks * 32 + kg * 8;
+      const int kb = k < r ? k : r - 8;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int n = nw + t * 16 + lrow;
-      bu[t] = *(const uint4*)(Bm + (int64_t)(n < N ? n : N - 1) * r + kb);
+      for (int u = 0; u < 4; ++u) {
+        const int n = nw + u * 16 + lrow;
+        bu[u] = *(const uint4*)(Bm + (int64_t)(n < N ? n : N - 1) * r + kb);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int m = m0 + rt * 16 + lrow;
+        tu[rt] = *(const uint4*)(T + (int64_t)(m < mend ? m : mend - 1) * Rp + k);
+      }
+    };
+    // The fragments of the first PRE rank steps load first (the scheduling
+    // barriers keep the order), so the MFMAs wait only for them while the Y
+    // loads stay in flight through the product.
+    constexpr int PRE = YT == SQ_F32 && KSM > 2 ? 2 : KSM;
+    uint4 bf[KSM][4], tf[KSM][4];
+#pragma unroll
+    for (int ks = 0; ks < PRE; ++ks) load_bt(ks, bf[ks], tf[ks]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (PF) {
+      if (nxt != nullptr) load_y(*nxt, yn);
+    } else {
+      load_y(t, yc);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int m = m0 + rt * 16 + lrow;
-      tu[rt] = *(const uint4*)(T + (int64_t)(m < mend ? m : mend - 1) * Rp + k);
-    }
-  };
-  // The fragments of the first PRE rank steps load before the Y tile (the
-  // scheduling barrier keeps that order), so the MFMAs wait only for them
-  // and the Y loads stay in flight through the product.
-  constexpr int PRE = YT == SQ_F32 && KSM > 2 ? 2 : KSM;
-  uint4 bf[KSM][4], tf[KSM][4];
-#pragma unroll
-  for (int ks = 0; ks < PRE; ++ks) load_bt(ks, bf[ks], tf[ks]);
-  __builtin_amdgcn_sched_barrier(0);
+    for (int ks = PRE; ks < KSM; ++ks) load_bt(ks, bf[ks], tf[ks]);
 
-  // 1. The Y tile, coalesced.
-  uint4 yv[NP];
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const int m = m0 + p * RPP + pr;
-    const int64_t off = (int64_t)(m < mend ? m : m0) * ldy + (col_ok ? n0 + pc : n0);
-    yv[p] = YT == SQ_F32 ? *(const uint4*)((const float*)Y + off)
-                         : *(const uint4*)((const unsigned short*)Y + off);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int ks = PRE; ks < KSM; ++ks) load_bt(ks, bf[ks], tf[ks]);
-
-  // 2. D for rows m0 .. m0 + 63, columns nw .. nw + 63: per rank step 16
-  //    MFMAs (4 row tiles x 4 column tiles of 16 x 16).
-  v4f acc[4][4];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) acc[rt][t] = v4f{0, 0, 0, 0};
-#pragma unroll
-  for (int ks = 0; ks < KSM; ++ks)
+    // D for rows m0 .. m0 + 63, columns nw .. nw + 63: per rank step 16
+    // MFMAs (4 row tiles x 4 column tiles of 16 x 16).
+    v4f acc[4][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_v8bf(bf[ks][t]), bits_to_v8bf(tf[ks][rt]),
-                                                             acc[rt][t], 0, 0, 0);
+      for (int u = 0; u < 4; ++u) acc[rt][u] = v4f{0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < KSM; ++ks)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc[rt][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_v8bf(bf[ks][u]), bits_to_v8bf(tf[ks][rt]),
+                                                               acc[rt][u], 0, 0, 0);
 
-  // 3. Register j of tile (rt, t): row 16 rt + lane % 16, column 64 w + 16 t + 4 kg + j.
+    // D through LDS (float4 slot c of row i stored at c ^ (i & 15)): register
+    // j of tile (rt, u) is row 16 rt + lane % 16, column 64 w + 16 u + 4 kg + j.
+    __syncthreads();   // every thread is done reading the previous tile's D
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int i = rt * 16 + lrow;
+    for (int rt = 0; rt < 4; ++rt) {
+      const int i = rt * 16 + lrow;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int c4 = 16 * wave + 4 * t + kg;
-      *(float4*)(dl + i * BN + ((c4 ^ (i & 15)) << 2)) =
-          make_float4(acc[rt][t][0], acc[rt][t][1], acc[rt][t][2], acc[rt][t][3]);
-    }
-  }
-  __syncthreads();
-
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const int i = p * RPP + pr;
-    const int m = m0 + i;
-    if (m >= mend || !col_ok) continue;
-    const int64_t off = (int64_t)m * ldy + n0 + pc;
-    const int c4 = pc >> 2;
-    const float4 d0 = *(const float4*)(dl + i * BN + ((c4 ^ (i & 15)) << 2));
-    if constexpr (YT == SQ_F32) {
-      float4 y = make_float4(__uint_as_float(yv[p].x), __uint_as_float(yv[p].y),
-                             __uint_as_float(yv[p].z), __uint_as_float(yv[p].w));
-      y.x = y.x + scale * d0.x; y.y = y.y + scale * d0.y;
-      y.z = y.z + scale * d0.z; y.w = y.w + scale * d0.w;
-      *(float4*)((float*)Y + off) = y;
-    } else {
-      const float4 d1 = *(const float4*)(dl + i * BN + (((c4 + 1) ^ (i & 15)) << 2));
-      const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-      const uint32_t w[4] = {yv[p].x, yv[p].y, yv[p].z, yv[p].w};
-      uint32_t o[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t h[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const uint32_t b = e ? w[q] >> 16 : w[q] & 0xFFFFu;
-          float y = YT == SQ_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
-          y = y + scale * d[2 * q + e];
-          h[e] = YT == SQ_BF16 ? f32_to_bf16_bits(y) : f32_to_f16_bits(y);
-        }
-        o[q] = h[0] | (h[1] << 16);
+      for (int u = 0; u < 4; ++u) {
+        const int c4 = 16 * wave + 4 * u + kg;
+        *(float4*)(dl + i * BN + ((c4 ^ (i & 15)) << 2)) =
+            make_float4(acc[rt][u][0], acc[rt][u][1], acc[rt][u][2], acc[rt][u][3]);
       }
-      *(uint4*)((unsigned short*)Y + off) = make_uint4(o[0], o[1], o[2], o[3]);
     }
+    __syncthreads();
+
+    const bool col_ok = t.n0 + pc < N;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int i = p * RPP + pr;
+      const int m = m0 + i;
+      if (m >= mend || !col_ok) continue;
+      const int64_t off = (int64_t)m * ldy + t.n0 + pc;
+      const int c4 = pc >> 2;
+      const float4 d0 = *(const float4*)(dl + i * BN + ((c4 ^ (i & 15)) << 2));
+      if constexpr (YT == SQ_F32) {
+        float4 y = make_float4(__uint_as_float(yc[p].x), __uint_as_float(yc[p].y),
+                               __uint_as_float(yc[p].z), __uint_as_float(yc[p].w));
+        y.x = y.x + scale * d0.x; y.y = y.y + scale * d0.y;
+        y.z = y.z + scale * d0.z; y.w = y.w + scale * d0.w;
+        *(float4*)((float*)Y + off) = y;
+      } else {
+        const float4 d1 = *(const float4*)(dl + i * BN + (((c4 + 1) ^ (i & 15)) << 2));
+        const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        const uint32_t w[4] = {yc[p].x, yc[p].y, yc[p].z, yc[p].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t h[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const uint32_t bb = e ? w[q] >> 16 : w[q] & 0xFFFFu;
+            float y = YT == SQ_BF16 ? bf16_bits_to_f32(bb) : f16_bits_to_f32(bb);
+            y = y + scale * d[2 * q + e];
+            h[e] = YT == SQ_BF16 ? f32_to_bf16_bits(y) : f32_to_f16_bits(y);
+          }
+          o[q] = h[0] | (h[1] << 16);
+        }
+        *(uint4*)((unsigned short*)Y + off) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  };
+
+  // Persistent over the tiles (blockIdx.x, + gridDim.x, ...), two Y register
+  // sets taking turns. A tile's Y rows are read and written only by its own
+  // block, so the prefetch of the next tile never meets a store of another.
+  Tile ta, tb;
+  uint4 ya[NP], yb[NP];
+  int it = blockIdx.x;
+  if (!tile_of(it, ta)) return;
+  if constexpr (PF) load_y(ta, ya);
+  for (;;) {
+    const bool hb = tile_of(it + (int)gridDim.x, tb);
+    process(ta, ya, hb ? &tb : nullptr, yb);
+    if (!hb) break;
+    it += gridDim.x;
+    const bool ha = tile_of(it + (int)gridDim.x, ta);
+    process(tb, yb, ha ? &ta : nullptr, ya);
+    if (!ha) break;
+    it += gridDim.x;
   }
 }
 
@@ -942,6 +990,9 @@ static int launch_shrink_seg_p(const void* X, int64_t M, int64_t K, int64_t ldx,
   return S;
 }
 
+template <int YT, bool SEG>
+struct ExpandTag {};
+
 template <int XT, int YT, bool SEG>
 static int launch_lora_t(const void* X, int64_t M, int64_t K, int64_t ldx, const LoraArgs& la, int R,
                          float scale, void* Y, int64_t N, int64_t ldy, void* ws, hipStream_t st) {
@@ -957,14 +1008,24 @@ static int launch_lora_t(const void* X, int64_t M, int64_t K, int64_t ldx, const
   const int64_t rthreads = M * (Rp / 4);
   k_lora_reduce<<<(unsigned)((rthreads + 63) / 64), 64, 0, st>>>(P, S, R, Rp, (int)M, Tw, Rp);
   SQ_LAUNCH_CHECK();
-  const int64_t row_blocks = (M + 63) / 64 + (SEG ? (la.nseg < M ? la.nseg : M) : 0);
-  const dim3 g2((unsigned)row_blocks, (unsigned)((N + 255) / 256));
+  // Row tiles of 64 (with segments: at most one more per request, tiles
+  // past the last (request, tile) pair are empty) times column tiles of 256;
+  // a persistent grid of two blocks per CU walks them.
+  const int64_t row_tiles = (M + 63) / 64 + (SEG ? (la.nseg < M ? la.nseg : M) : 0);
+  const int64_t col_tiles = (N + 255) / 256;
+  int64_t grid = row_tiles * col_tiles;
+  const int64_t cap = resident_blocks<ExpandTag<YT, SEG>>((const void*)k_lora_expand<YT, SEG, 1>, kLoraThreads);
+  if (grid > cap) grid = cap;
+#define SQ_EXPAND(KSM_)                                                                      \
+  k_lora_expand<YT, SEG, KSM_><<<(unsigned)grid, kLoraThreads, 0, st>>>(                     \
+      Tw, (int)M, (int)N, la, scale, Y, ldy, (int)row_tiles, (int)col_tiles)
   switch (Rp / 32) {
-    case 1: k_lora_expand<YT, SEG, 1><<<g2, kLoraThreads, 0, st>>>(Tw, (int)M, (int)N, la, scale, Y, ldy); break;
-    case 2: k_lora_expand<YT, SEG, 2><<<g2, kLoraThreads, 0, st>>>(Tw, (int)M, (int)N, la, scale, Y, ldy); break;
-    case 3: k_lora_expand<YT, SEG, 3><<<g2, kLoraThreads, 0, st>>>(Tw, (int)M, (int)N, la, scale, Y, ldy); break;
-    default: k_lora_expand<YT, SEG, 4><<<g2, kLoraThreads, 0, st>>>(Tw, (int)M, (int)N, la, scale, Y, ldy); break;
+    case 1: SQ_EXPAND(1); break;
+    case 2: SQ_EXPAND(2); break;
+    case 3: SQ_EXPAND(3); break;
+    default: SQ_EXPAND(4); break;
   }
+#undef SQ_EXPAND
   SQ_LAUNCH_CHECK();
   return SQ_OK;
 }
