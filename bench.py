@@ -761,6 +761,55 @@ def row_oracle(args, torch):
                                                                   "full_step_s", "cores")}}
 
 
+def row_vendor(args, torch):
+    """The INT8 GEMM of this library against the vendor library's (torch._int_mm,
+    which runs hipBLASLt on ROCm: int32 output, no epilogue) on the Llama-2-70B
+    MLP shapes, seeded uniform int8 operands; this library's int32 entry point
+    is checked bit for bit against it. Context for the GEMM's rate, not a
+    stage of the path."""
+    import w8a8_smoothquant_int8_amd as sq
+    torch.manual_seed(0)
+    reps = max(args.steps, 10)
+
+    def timed(f):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {}
+    for (M, N, K) in [(8192, 57344, 8192), (8192, 8192, 28672), (8192, 28672, 8192)]:
+        X = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda")
+        W = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda")
+        a = torch.rand(M, device="cuda") * 1e-3
+        w = torch.rand(N, device="cuda") * 1e-3
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        ops = 2.0 * M * N * K
+        rec = {}
+        ms = timed(lambda: torch._int_mm(X, W.t()))
+        rec["vendor_int32_tops"] = round(ops / ms / 1e9, 1)
+        ms = timed(lambda: sq.sq_w8a8_gemm(X, W, a, w, Y))
+        rec["sq_bf16_tops"] = round(ops / ms / 1e9, 1)
+        if M * N <= 8192 * 28672:
+            acc = torch.empty(M, N, dtype=torch.int32, device="cuda")
+            ms = timed(lambda: sq.sq_w8a8_gemm_i32(X, W, acc))
+            rec["sq_int32_tops"] = round(ops / ms / 1e9, 1)
+            rec["int32_equal"] = bool(torch.equal(acc, torch._int_mm(X, W.t())))
+            del acc
+        out[f"{M}x{N}x{K}"] = rec
+        print(f"vendor {M}x{N}x{K}: {rec}", file=sys.stderr, flush=True)
+        del X, W, Y
+        torch.cuda.empty_cache()
+    return {"row": "vendor", "metric": "INT8 GEMM TOPS, this library against torch._int_mm (hipBLASLt)",
+            "value": out["8192x57344x8192"]["sq_bf16_tops"], "unit": "TOPS", "higher_is_better": True,
+            "data": "seeded uniform int8 operands", "shapes": out}
+
+
 KERNEL_WORKLOADS = ("tiny_m16_k256_n256", "llama3_8b_proj_m2048", "opt13b_layer_decode_m64",
                     "opt13b_layer_prefill_m4096", "multitenant_lora_m8192", "llama2_70b_mlp_m8192")
 
@@ -907,7 +956,8 @@ def row_kernels(args, torch):
 
 
 ROWS = {"f1": row_f1, "f2": row_f2, "f3": row_f3, "f4": row_f4, "kernels": row_kernels,
-        "mfma": row_mfma, "lora_window": row_lora_window, "oracle": row_oracle}
+        "mfma": row_mfma, "lora_window": row_lora_window, "oracle": row_oracle,
+        "vendor": row_vendor}
 
 
 def main():
