@@ -155,6 +155,8 @@ def test_gemm_workspace_rules(L):
     assert wsb(64, 20480, 5120) == 0
     assert wsb(64, 5120, 1024) == 0            # 8 K-tiles: too few for two slices
     assert wsb(64, 5120, 8192) > 0
+    assert wsb(64, 5120, 2048) == 2 * 160 * 2 * 4096     # 16 K-tiles: 2 slices of 8
+    assert wsb(33, 6144, 3072) == 3 * 192 * 2 * 4096     # 96 column blocks: 3 slices
     assert wsb(64, 5120, 1000) == 0            # K not a multiple of 128
     assert wsb(0, 5120, 20480) == 0 and wsb(-1, 64, 64) == 0
     f = L.sq_w8a8_gemm_ws

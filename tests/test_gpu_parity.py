@@ -256,8 +256,11 @@ def test_gemm_i32_extreme_magnitude():
 @pytest.mark.parametrize("M,N,K,split", [(64, 5120, 20480, True), (17, 1040, 8192, True),
                                          (40, 208, 20352, True), (64, 20480, 5120, False),
                                          (64, 5120, 5120, True), (64, 8192, 8192, False),
-                                         (64, 2048, 1920, False), (1, 16400, 2048, False)])
+                                         (64, 2048, 1920, False), (1, 16400, 2048, False),
+                                         (64, 5120, 2048, True), (33, 6144, 3072, True)])
 def test_gemm_ws_split_k(out, mode, M, N, K, split):
+    """Workspace GEMM against the plain one and the oracle, bit for bit; the
+    split shapes take 2 (64x5120x2048), 3 (33x6144x3072), 4, 8 and 19 K slices."""
     rng = np.random.default_rng(M + N + K)
     xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
     wq = rng.integers(-127, 128, (N, K)).astype(np.int8)
