@@ -963,7 +963,7 @@ ROWS = {"f1": row_f1, "f2": row_f2, "f3": row_f3, "f4": row_f4, "kernels": row_k
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
               "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.cpu_baseline_only:
