@@ -143,12 +143,12 @@ def test_static_clipped_validation(L):
 def test_gemm_workspace_rules(L):
     wsb = L.sq_w8a8_gemm_workspace_bytes
     # decode shapes with fewer than 128 column blocks of 64 split K: slices x
-    # ceil(N/32) 32-column tiles x 2 row tiles x 4 KB; about 256 blocks, each
+    # ceil(N/32) 32-column tiles x 2 row tiles x 4 KB; at most 256 blocks, each
     # slice at least 8 K-tiles
     need = wsb(64, 5120, 20480)
-    assert need == 4 * 160 * 2 * 4096                # 80 column blocks: 4 slices
+    assert need == 3 * 160 * 2 * 4096                # 80 column blocks: 3 slices
     assert wsb(32, 5120, 20480) == need              # rows pad to two row tiles
-    assert wsb(64, 5120, 5120) == 4 * 160 * 2 * 4096     # 40 K-tiles: 4 slices of 10
+    assert wsb(64, 5120, 5120) == 3 * 160 * 2 * 4096     # 40 K-tiles: 3 slices of 14, 14, 12
     assert wsb(64, 1040, 8192) == 8 * 33 * 2 * 4096      # 17 blocks: capped at 64 / 8 slices
     assert wsb(128, 5120, 20480) == 0          # not decode-sized
     assert wsb(64, 8192, 8192) == 0            # 128 column blocks: no split
@@ -156,7 +156,8 @@ def test_gemm_workspace_rules(L):
     assert wsb(64, 5120, 1024) == 0            # 8 K-tiles: too few for two slices
     assert wsb(64, 5120, 8192) > 0
     assert wsb(64, 5120, 2048) == 2 * 160 * 2 * 4096     # 16 K-tiles: 2 slices of 8
-    assert wsb(33, 6144, 3072) == 3 * 192 * 2 * 4096     # 96 column blocks: 3 slices
+    assert wsb(33, 6144, 3072) == 2 * 192 * 2 * 4096     # 96 column blocks: 2 slices
+    assert wsb(48, 4096, 8192) == 4 * 128 * 2 * 4096     # 64 column blocks: 4 slices
     assert wsb(64, 5120, 1000) == 0            # K not a multiple of 128
     assert wsb(0, 5120, 20480) == 0 and wsb(-1, 64, 64) == 0
     f = L.sq_w8a8_gemm_ws

@@ -245,22 +245,25 @@ def test_gemm_i32_extreme_magnitude():
     assert np.array_equal(acc.cpu().numpy(), ref)
 
 
-# Decode shapes whose K is split across blocks with a workspace (M = 64, 17
-# and 40; 4, 8 and 19 slices; a ragged last 64-column block at N = 1040 and
-# N = 208, whose second 32-column tile lies past N; the last slice shorter than
-# the others at K = 20352), plus shapes that take no workspace (128 or more
-# column blocks of 64; K too short for two slices of 8 K-tiles): bit-exact
-# against the oracle and the unsplit call.
+# Decode shapes whose K is split across blocks with a workspace (M = 64, 48,
+# 40, 33 and 17; 2, 3, 4, 8 and 19 slices; a ragged last 64-column block at
+# N = 1040 and N = 208, whose second 32-column tile lies past N; the last slice
+# shorter than the others at K = 20480, 5120, 20352), plus shapes that take no
+# workspace (128 or more column blocks of 64; K too short for two slices of
+# 8 K-tiles): bit-exact against the oracle and the unsplit call.
 @pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("mode", ["dynamic", "static"])
 @pytest.mark.parametrize("M,N,K,split", [(64, 5120, 20480, True), (17, 1040, 8192, True),
                                          (40, 208, 20352, True), (64, 20480, 5120, False),
                                          (64, 5120, 5120, True), (64, 8192, 8192, False),
                                          (64, 2048, 1920, False), (1, 16400, 2048, False),
-                                         (64, 5120, 2048, True), (33, 6144, 3072, True)])
+                                         (64, 5120, 2048, True), (33, 6144, 3072, True),
+                                         (48, 4096, 8192, True)])
 def test_gemm_ws_split_k(out, mode, M, N, K, split):
     """Workspace GEMM against the plain one and the oracle, bit for bit; the
-    split shapes take 2 (64x5120x2048), 3 (33x6144x3072), 4, 8 and 19 K slices."""
+    split shapes take 2 (64x5120x2048, 33x6144x3072), 3 (64x5120x20480,
+    64x5120x5120), 4 (48x4096x8192), 8 (17x1040x8192) and 19 (40x208x20352)
+    K slices."""
     rng = np.random.default_rng(M + N + K)
     xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
     wq = rng.integers(-127, 128, (N, K)).astype(np.int8)

@@ -900,7 +900,7 @@ k_gemm_decode(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
 // 64 columns and 4 slots (64 KB of LDS, two blocks per CU) measured fastest
 // on the OPT-13B decode shapes among 64 / 128 columns and 4 / 6 / 8 slots,
 // weights rotated past the MALL: 64x15360x5120 20.5 us, 64x5120x5120 16.9,
-// 64x20480x5120 36.4, 64x5120x20480 56.7 (38.8 split over 4 K slices),
+// 64x20480x5120 36.4, 64x5120x20480 56.7 (30.4 split over 3 K slices),
 // against 38.6 / 22.0 / 39.8 / 67.5 (61.5) for the 128x128 tiles or the
 // skinny kernel used before. One accumulator per k-step instead of one per
 // wave gained 1-3%.
@@ -1092,17 +1092,20 @@ static bool decode_ok(int64_t M, int64_t N, int64_t K) {
 
 // K split of the decode kernel across blocks, given a workspace, where the
 // column blocks alone leave most CUs idle: slices of whole K-tiles so that
-// about 256 blocks stream, each slice at least 8 K-tiles, so that the INT32
-// partial sums (KS x 64 x N x 4 bytes) stay at most a quarter of the weight
-// bytes. 1: no split.
+// at most 256 blocks stream (one per CU), each slice at least 8 K-tiles, so
+// that the INT32 partial sums (KS x 64 x N x 4 bytes) stay at most a quarter
+// of the weight bytes. 1: no split.
 static int decode_splits(int64_t M, int64_t N, int64_t K) {
   if (!decode_ok(M, N, K)) return 1;
   const int64_t ct = (N + kDecBN - 1) / kDecBN;
-  // with 128 or more column blocks the split was slower (64x15360x5120:
-  // 20.5 -> 26.5 us); below that it pays (64x5120x20480: 56.7 -> 38.8 us)
+  // A CU streams about as fast with one decode block as with two, so the
+  // split stops at one block per CU (64x5120x20480: 56.7 us unsplit, 30.4 us
+  // in 3 slices = 240 blocks, 38.6 us in 4 = 320 blocks; 64x5120x5120: 17.1,
+  // 14.3 and 16.5 us); with 128 or more column blocks it does not pay
+  // (64x15360x5120: 20.4 us unsplit, 26.3 us in 2 slices).
   if (ct >= 128) return 1;
   const int64_t kmax = (K / kBK) / 8;
-  int64_t ks = (256 + ct - 1) / ct;
+  int64_t ks = 256 / ct;
   if (ks > kmax) ks = kmax;
   return ks > 1 ? (int)ks : 1;
 }
