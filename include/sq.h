@@ -222,7 +222,8 @@ int sq_w8a8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t M, int64_t N, i
 /* Bytes of device workspace the LoRA calls need for M rows of K channels and
  * ranks up to max_rank (fp32 partial sums of the rank-r intermediate, and the
  * intermediate itself in bf16 for the expand, its rows zero-padded to a
- * multiple of 32 ranks). */
+ * multiple of 32 ranks), plus 16 * (ceil(M / 64) + M) bytes for the table of
+ * (request, 64-row tile) pairs a segmented call writes once per call. */
 size_t sq_lora_workspace_bytes(int64_t M, int64_t K, int max_rank);
 
 /* [LoRA] Pitch, first half: the rank-r intermediate of the LoRA path,

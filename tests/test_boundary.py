@@ -236,12 +236,15 @@ def test_lora_validation(L):
 
 
 def test_lora_workspace_grows_with_rank(L):
-    # partial sums (S slices of M x r fp32) plus T (M rows of r rounded up to 32 ranks, bf16)
+    # partial sums (S slices of M x r fp32) plus T (M rows of r rounded up to 32
+    # ranks, bf16) plus the segmented pair table (16 bytes x (ceil(M / 64) + M))
+    tab = 16 * (2048 // 64 + 2048)
     w16 = L.sq_lora_workspace_bytes(2048, 4096, 16)
     w64 = L.sq_lora_workspace_bytes(2048, 4096, 64)
-    assert w64 > w16 >= 2048 * 16 * 4 + 2048 * 32 * 2
-    assert (w16 - 2048 * 32 * 2) % (2048 * 16 * 4) == 0
-    assert (w64 - 2048 * 64 * 2) % (2048 * 64 * 4) == 0
+    assert w64 > w16 >= 2048 * 16 * 4 + 2048 * 32 * 2 + tab
+    assert (w16 - 2048 * 32 * 2 - tab) % (2048 * 16 * 4) == 0
+    assert (w64 - 2048 * 64 * 2 - tab) % (2048 * 64 * 4) == 0
+    assert (L.sq_lora_workspace_bytes(65, 256, 8) - 16 * (2 + 65)) % 16 == 0
     assert L.sq_lora_workspace_bytes(0, 4096, 16) == 0
 
 

@@ -424,7 +424,44 @@ def test_lora_segmented_short_and_empty_requests(xdt, ranks):
         assert torch.equal(Y[r0:r1].cpu(), y[r0:r1])
 
 
+@pytest.mark.parametrize("ydt", ["bf16", "f32"])
+def test_lora_segmented_many_requests(ydt):
+    """2300 requests (the pair table is written in 9 rounds of 256 requests),
+    most of them 0-2 rows long, a few long ones, some without adapter: every
+    pair's rows and adapter must come out of the table right."""
+    rng = np.random.default_rng(2200)
+    K, N, ranks = 272, 144, [8, 16, 64]
+    lens = [int(rng.integers(0, 3)) if rng.random() < 0.97 else int(rng.integers(60, 200))
+            for _ in range(2300)]
+    M = int(sum(lens))
+    seg_start = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    nseg = len(lens)
+    seg_adapter = rng.integers(0, len(ranks), nseg).astype(np.int32)
+    seg_adapter[rng.random(nseg) < 0.1] = -1
+    x, xn = acts(rng, M, K, "bf16", factor=20.0)
+    As = [cast_to(rng.normal(0, 0.01, (r, K)).astype(F32), "bf16") for r in ranks]
+    Bs = [cast_to(rng.normal(0, 0.01, (N, r)).astype(F32), "bf16") for r in ranks]
+    y = cast_to(rng.normal(0, 0.5, (M, N)).astype(F32), ydt)
+    Ad = [t.cuda() for t in As]
+    Bd = [t.cuda() for t in Bs]
+    Y = y.cuda()
+    ws = torch.empty(sq.sq_lora_workspace_bytes(M, K, 64), dtype=torch.uint8, device="cuda")
+    sq.sq_lora_apply_segmented(x, dev(seg_start), dev(seg_adapter), sq.pointer_table(Ad, "cuda"),
+                               sq.pointer_table(Bd, "cuda"), dev(np.array(ranks, np.int32)), 64, Y, ws)
+    ref = O.lora_apply_segmented(y.float().numpy(), xn, "bf16", seg_start, seg_adapter,
+                                 [t.float().numpy() for t in As], [t.float().numpy() for t in Bs],
+                                 1.0, ydt)
+    ok, rel = lora_close(Y.cpu().float().numpy(), ref)
+    assert ok, rel
+    none = np.zeros(M, bool)
+    for g in np.nonzero(seg_adapter < 0)[0]:
+        none[seg_start[g]:seg_start[g + 1]] = True
+    assert torch.equal(Y.cpu()[torch.from_numpy(none)], y[torch.from_numpy(none)])
+
+
 def test_lora_segmented_single_adapter_equals_single():
+    # both calls split K into the same 4 slices at this shape (300 rows, 4
+    # requests), so one adapter over all rows gives the same result bit for bit
     rng = np.random.default_rng(9)
     M, K, N, r = 300, 1024, 256, 16
     x, xn, a, b, y = lora_inputs(rng, M, K, N, r, "bf16", "bf16")

@@ -57,6 +57,12 @@ __device__ __forceinline__ int find_segment(const int32_t* seg_start, int nseg, 
   return lo;
 }
 
+// One (request, 64-row tile) pair of a segmented call: rows [m0, mend) of
+// one request and its adapter; ad = -1 past the last pair.
+struct SegPair {
+  int m0, mend, ad, pad;
+};
+
 struct LoraArgs {
   // single adapter
   const unsigned short* A;   // [r, K] bf16
@@ -69,6 +75,7 @@ struct LoraArgs {
   const void* const* A_ptrs;
   const void* const* B_ptrs;
   const int32_t* ranks;
+  const SegPair* pairs;      // the call's pair table (k_seg_pairs), in the workspace
 };
 
 // Single-adapter shrink, written as partial sums P[s] over groups of k-chunks.
@@ -419,24 +426,31 @@ k_lora_shrink_seg(const char* __restrict__ X, int64_t ldx_bytes, int M, int K, L
   }
 }
 
-// Block b of a segmented launch takes the b-th (request, 64-row tile) pair,
-// counting, in request order, ceil(len / 64) tiles for every non-empty
-// request with an adapter. The block's 256 threads scan the request table
-// 256 requests at a time (wave prefix sums with lane shifts, then the four
-// wave totals). Returns false (for the whole block) when b is past the last
-// tile. Contains barriers: call it from block-uniform control flow only.
-__device__ bool seg_tile_of_block(const LoraArgs& la, int b, int* g_out, int* tile_out) {
-  __shared__ int s_wsum[4];
-  __shared__ int s_hit[2];
+// The (request, 64-row tile) pairs of a segmented call, in request order:
+// ceil(len / 64) of them for every non-empty request with an adapter. One
+// block scans the request table once per call, kSegScan requests per round
+// (wave prefix sums with lane shifts, then the wave totals), and writes entry
+// b of the table for every pair b; the entries from the pair count up to
+// n_entries get ad = -1. The shrink and expand blocks then find their pair
+// with one load instead of each scanning the table (they read the adapter's
+// rank next to its A or B pointer). n_entries = ceil(M / 64) +
+// min(requests, M) bounds the pair count of well-formed tables (rows within
+// [0, M)); writes past it are dropped.
+constexpr int kSegScan = 256;
+__global__ void __launch_bounds__(kSegScan) k_seg_pairs(LoraArgs la, SegPair* __restrict__ tab,
+                                                        int n_entries) {
+  constexpr int NW = kSegScan / 64;
+  __shared__ int s_wsum[NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) s_hit[0] = -1;
   int base = 0;
-  for (int c0 = 0; c0 < la.nseg; c0 += 256) {
+  for (int c0 = 0; c0 < la.nseg; c0 += kSegScan) {
     const int g = c0 + tid;
-    int tiles = 0;
-    if (g < la.nseg && la.seg_adapter[g] >= 0) {
-      const int len = la.seg_start[g + 1] - la.seg_start[g];
-      tiles = len > 0 ? (len + 63) >> 6 : 0;
+    int tiles = 0, s0 = 0, s1 = 0, ad = -1;
+    if (g < la.nseg) {
+      ad = la.seg_adapter[g];
+      s0 = la.seg_start[g];
+      s1 = la.seg_start[g + 1];
+      if (ad >= 0 && s1 > s0) tiles = (s1 - s0 + 63) >> 6;
     }
     int incl = tiles;
 #pragma unroll
@@ -446,27 +460,26 @@ __device__ bool seg_tile_of_block(const LoraArgs& la, int b, int* g_out, int* ti
     }
     if (lane == 63) s_wsum[wave] = incl;
     __syncthreads();
-    int before = base;
-    for (int w = 0; w < wave; ++w) before += s_wsum[w];
-    const int total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
-    const int excl = before + incl - tiles;
-    if (tiles > 0 && b >= excl && b < excl + tiles) {
-      s_hit[0] = g;
-      s_hit[1] = b - excl;
+    int before = base, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      before += w < wave ? s_wsum[w] : 0;
+      total += s_wsum[w];
+    }
+    const int e = before + incl - tiles;   // this request's first pair
+    for (int q = 0; q < tiles && e + q < n_entries; ++q) {
+      const int m0 = s0 + 64 * q;
+      tab[e + q] = SegPair{m0, m0 + 64 < s1 ? m0 + 64 : s1, ad, 0};
     }
     base += total;
-    __syncthreads();   // s_wsum is rewritten by the next round; s_hit is complete
-    if (base > b) break;
+    __syncthreads();   // s_wsum is rewritten by the next round
   }
-  const int g = s_hit[0];
-  *g_out = g;
-  *tile_out = s_hit[1];
-  return g >= 0;
+  for (int b = base + tid; b < n_entries; b += blockDim.x) tab[b] = SegPair{0, 0, -1, 0};
 }
 
 // Pipelined segmented shrink for 16-bit X: k_lora_shrink_pipe with one
-// adapter per block. Block (b, s) takes the b-th (request, 64-row tile) pair
-// (seg_tile_of_block), so every row of the block uses one adapter: its
+// adapter per block. Block (b, s) takes pair b of the call's pair table, so
+// every row of the block uses one adapter: its
 // A[0:r, chunk] is staged in the two-slot LDS ring (r rounded up to 16; rows
 // past r re-read row r - 1) and multiplied over the adapter's rank tiles
 // only; ranks r .. R - 1 of the partial sums are stored as 0. Rows past the request's end read its last
@@ -486,21 +499,20 @@ k_lora_shrink_seg_pipe(const char* __restrict__ X, int64_t ldx_bytes, int M, int
   constexpr int NA = ROWS / RPI / 4;
   constexpr int SLOT = ROWS * KC * 2;
   static_assert(ROWS % (RPI * 4) == 0, "staged rows must split over the 4 waves");
-  int g, tile;
-  if (!seg_tile_of_block(la, blockIdx.x, &g, &tile)) return;
+  const SegPair pr = la.pairs[blockIdx.x];
+  if (pr.ad < 0) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lrow = lane & 15, kg = lane >> 4;
   const int nchunks = (K + KC - 1) / KC;
-  const int s_end = la.seg_start[g + 1];
-  const int w0 = la.seg_start[g] + tile * 64 + wave * 16;
+  const int s_end = pr.mend;
+  const int w0 = pr.m0 + wave * 16;
   const int my_m = w0 + lrow;
   const bool wave_rows = w0 < s_end;   // the wave holds rows of the request
   const char* xrow = X + (int64_t)(my_m < s_end ? my_m : s_end - 1) * ldx_bytes;
-  const int ad = la.seg_adapter[g];
-  const int ra = la.ranks[ad];
+  const int ra = la.ranks[pr.ad];
   const int ntg = (ra + 15) >> 4;
-  const unsigned short* Ag = (const unsigned short*)la.A_ptrs[ad];
+  const unsigned short* Ag = (const unsigned short*)la.A_ptrs[pr.ad];
 
   auto stage = [&](int c, int slot) {
     const int kc0 = c * KC;
@@ -564,8 +576,8 @@ k_lora_shrink_seg_pipe(const char* __restrict__ X, int64_t ldx_bytes, int M, int
   uint4 xa[KS], xb[KS];
   int c = blockIdx.y;
   if (c < nchunks) {
+    load_x(c, xa);   // needs only the pair; the staging waits for the adapter pointer
     stage(c, 0);
-    load_x(c, xa);
   }
 #pragma unroll 1
   for (; c < nchunks; c += 2 * S) {
@@ -596,9 +608,9 @@ k_lora_shrink_seg_pipe(const char* __restrict__ X, int64_t ldx_bytes, int M, int
 //      16-bit Y or 1024 of fp32).
 //   2. Wave w computes D = T[rows] . B[cols 64 w .. 64 w + 63]^T for all 64
 //      rows (4 x 4 tiles of 16 x 16), so every B fragment it loads serves 64
-//      rows. With segments, block x takes the x-th (request, 64-row tile)
-//      pair (seg_tile_of_block): all its rows use one adapter, and rows past
-//      the request's end are neither read nor written.
+//      rows. With segments, row tile x is pair x of the call's pair table:
+//      all its rows use one adapter, and rows past the request's end are
+//      neither read nor written.
 //   3. D goes to LDS as fp32 (float4 slot c of row i stored at c ^ (i & 15):
 //      the 16 rows of an MFMA tile land on all 64 banks); after a barrier each
 //      thread reads the D values of its Y elements and writes
@@ -638,16 +650,12 @@ k_lora_expand(const unsigned short* __restrict__ T, int M, int N, LoraArgs la, f
     const int tm = it / col_tiles;
     t.n0 = (it % col_tiles) * BN;
     if constexpr (SEG) {
-      // every thread has read the previous lookup's result from LDS
-      __syncthreads();
-      int g, tl;
-      if (!seg_tile_of_block(la, tm, &g, &tl)) return false;
-      t.m0 = la.seg_start[g] + tl * BM;
-      const int s1 = la.seg_start[g + 1];
-      t.mend = t.m0 + BM < s1 ? t.m0 + BM : s1;
-      const int ad = la.seg_adapter[g];
-      t.Bm = (const unsigned short*)la.B_ptrs[ad];
-      t.r = la.ranks[ad];
+      const SegPair pr = la.pairs[tm];
+      if (pr.ad < 0) return false;
+      t.m0 = pr.m0;
+      t.mend = pr.mend;
+      t.Bm = (const unsigned short*)la.B_ptrs[pr.ad];
+      t.r = la.ranks[pr.ad];
     } else {
       t.m0 = tm * BM;
       t.mend = t.m0 + BM < M ? t.m0 + BM : M;
@@ -907,8 +915,9 @@ static void seg_split(int64_t M, int64_t K, int* S, int* kchunk) {
   *S = (int)((K + kc - 1) / kc);
 }
 
-// Workspace for any rank up to R, single-adapter or segmented.
-size_t lora_ws_bytes(int64_t M, int64_t K, int R) {
+// Partial sums and T for any rank up to R, single-adapter or segmented: the
+// offset of the segmented pair table in the workspace.
+static size_t lora_ws_base(int64_t M, int64_t K, int R) {
   int S, kc;
   seg_split(M, K, &S, &kc);
   int64_t smax = S;
@@ -923,6 +932,18 @@ size_t lora_ws_bytes(int64_t M, int64_t K, int R) {
   // (rows zero-padded to Rp = 32 * ceil(R / 32) ranks)
   const int64_t Rp = (R + 31) / 32 * 32;
   return (size_t)smax * (size_t)M * (size_t)R * sizeof(float) + (size_t)M * (size_t)Rp * 2;
+}
+
+// Entries of a segmented call's pair table: ceil(M / 64) + min(requests, M).
+static int64_t seg_pair_entries(int64_t M, int nseg) {
+  return (M + 63) / 64 + (nseg < M ? nseg : M);
+}
+
+// The whole workspace: partial sums, T, then room for the pair table of a
+// segmented call with any number of requests.
+size_t lora_ws_bytes(int64_t M, int64_t K, int R) {
+  return lora_ws_base(M, K, R) + (size_t)seg_pair_entries(M, (int)(M < INT32_MAX ? M : INT32_MAX)) *
+                                     sizeof(SegPair);
 }
 
 // Single-adapter shrink into P; returns the number of slices written.
@@ -967,9 +988,12 @@ template <int XT>
 static int launch_shrink_seg_p(const void* X, int64_t M, int64_t K, int64_t ldx, const LoraArgs& la,
                                int R, float* P, hipStream_t st) {
   if constexpr (XT != SQ_F32) {
-    // the single-adapter plan's slices; one block per (request, 64-row tile)
-    const ShrinkPlan p = plan_shrink_pipe(M, K, R);
-    const int64_t tiles_max = (M + 63) / 64 + (la.nseg < M ? la.nseg : M);
+    // one block per (request, 64-row tile) pair; the slices are those of the
+    // single-adapter rule for as many 64-row blocks as the grid has (the
+    // pairs outnumber the 64-row tiles: 8192 x 4096 in 64 requests, r 64:
+    // 3 slices, whole call 68.6 -> 63.4 us, where M / 64 rows would give 4)
+    const int64_t tiles_max = seg_pair_entries(M, la.nseg);
+    const ShrinkPlan p = plan_shrink_pipe(tiles_max * 64, K, R);
     const dim3 grid((unsigned)tiles_max, (unsigned)p.S);
     const size_t lds = 2 * (size_t)p.nt * 16 * 32 * p.ks * 2;
     const char* x = (const char*)X;
@@ -997,7 +1021,15 @@ template <int XT, int YT, bool SEG>
 static int launch_lora_t(const void* X, int64_t M, int64_t K, int64_t ldx, const LoraArgs& la, int R,
                          float scale, void* Y, int64_t N, int64_t ldy, void* ws, hipStream_t st) {
   float* P = (float*)ws;
-  const int S = SEG ? launch_shrink_seg_p<XT>(X, M, K, ldx, la, R, P, st)
+  LoraArgs lp = la;
+  if constexpr (SEG) {
+    // the pair table after the partial sums and T
+    SegPair* tab = (SegPair*)((char*)ws + lora_ws_base(M, K, R));
+    k_seg_pairs<<<1, kSegScan, 0, st>>>(la, tab, (int)seg_pair_entries(M, la.nseg));
+    SQ_LAUNCH_CHECK();
+    lp.pairs = tab;
+  }
+  const int S = SEG ? launch_shrink_seg_p<XT>(X, M, K, ldx, lp, R, P, st)
                     : launch_shrink_p<XT>(X, M, K, ldx, la.A, R, P, st);
   SQ_LAUNCH_CHECK();
   // T = bf16(sum of the S partials) once, after the partials in the workspace;
@@ -1011,14 +1043,14 @@ static int launch_lora_t(const void* X, int64_t M, int64_t K, int64_t ldx, const
   // Row tiles of 64 (with segments: at most one more per request, tiles
   // past the last (request, tile) pair are empty) times column tiles of 256;
   // a persistent grid of two blocks per CU walks them.
-  const int64_t row_tiles = (M + 63) / 64 + (SEG ? (la.nseg < M ? la.nseg : M) : 0);
+  const int64_t row_tiles = SEG ? seg_pair_entries(M, la.nseg) : (M + 63) / 64;
   const int64_t col_tiles = (N + 255) / 256;
   int64_t grid = row_tiles * col_tiles;
   const int64_t cap = resident_blocks<ExpandTag<YT, SEG>>((const void*)k_lora_expand<YT, SEG, 1>, kLoraThreads);
   if (grid > cap) grid = cap;
 #define SQ_EXPAND(KSM_)                                                                      \
   k_lora_expand<YT, SEG, KSM_><<<(unsigned)grid, kLoraThreads, 0, st>>>(                     \
-      Tw, (int)M, (int)N, la, scale, Y, ldy, (int)row_tiles, (int)col_tiles)
+      Tw, (int)M, (int)N, lp, scale, Y, ldy, (int)row_tiles, (int)col_tiles)
   switch (Rp / 32) {
     case 1: SQ_EXPAND(1); break;
     case 2: SQ_EXPAND(2); break;
