@@ -248,7 +248,8 @@ def gemm_tile(M: int, N: int, K: int, lora: bool = False) -> str:
     """The tile configuration libsq picks for an INT8 GEMM of this shape (the
     library's rule: the generic kernel when K is not a multiple of 128 or an
     operand reaches 4 GiB, the decode kernel for M <= 64 without a LoRA
-    epilogue, the skinny kernel for M <= 64 with one and fewer than 96
+    epilogue (128-column blocks where 64-column ones would outnumber 256 CUs),
+    the skinny kernel for M <= 64 with one and fewer than 96
     column tiles of 128, else the best of
     256x256 tiles and 256x192 tiles,
     one block per CU, at rates 1 and 0.93, and 128x128 tiles, two blocks per
@@ -257,7 +258,7 @@ def gemm_tile(M: int, N: int, K: int, lora: bool = False) -> str:
     if K % 128 or M * K >= 1 << 32 or N * K >= 1 << 32:
         return "generic"
     if M <= 64 and not lora:
-        return "decode"
+        return "decode" if (N + 63) // 64 <= 256 else "decode128"
     if M <= 64 and (N + 127) // 128 < 96:
         return "skinny"
     s256 = _tile_score(M, N, 256, 256, 256, 1.0)
@@ -271,7 +272,8 @@ def gemm_tile(M: int, N: int, K: int, lora: bool = False) -> str:
 def tile_dims(tile: str):
     """(rows, columns) of one output tile of a configuration."""
     return {"256x256": (256, 256), "256x192": (256, 192), "128x128": (128, 128),
-            "generic": (128, 128), "skinny": (64, 32), "decode": (64, 64)}[tile]
+            "generic": (128, 128), "skinny": (64, 32), "decode": (64, 64),
+            "decode128": (64, 128)}[tile]
 
 
 def host_info():

@@ -46,7 +46,8 @@ def test_gemm_tile_rule_prefers_whole_rounds():
     assert bench.gemm_tile(2048, 4096, 14336) == "128x128"
     assert bench.gemm_tile(2048, 4096, 4100) == "generic"
     assert bench.gemm_tile(64, 5120, 20480) == "decode"          # decode, no LoRA epilogue
-    assert bench.gemm_tile(64, 15360, 5120) == "decode"
+    assert bench.gemm_tile(64, 15360, 5120) == "decode"          # 240 blocks of 64 columns
+    assert bench.gemm_tile(64, 20480, 5120) == "decode128"       # 320 of 64: 160 of 128
     assert bench.gemm_tile(65, 5120, 20480) == "128x128"
     assert bench.gemm_tile(64, 5120, 20480, lora=True) == "skinny"
     assert bench.gemm_tile(64, 15360, 5120, lora=True) == "128x128"   # wide: 120 column tiles
@@ -67,5 +68,5 @@ def test_cpu_baseline_on_segmented_adapters():
 
 
 def test_tile_dims_known_for_every_rule():
-    for t in ("256x256", "256x192", "128x128", "generic", "skinny", "decode"):
+    for t in ("256x256", "256x192", "128x128", "generic", "skinny", "decode", "decode128"):
         assert len(bench.tile_dims(t)) == 2

@@ -287,7 +287,10 @@ def test_gemm_ws_split_k(out, mode, M, N, K, split):
 
 @pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("mode", ["dynamic", "static"])
-@pytest.mark.parametrize("M,N,K", [(33, 48, 272), (300, 1024, 4096), (64, 20480, 5120)])
+# (64, 20480, 5120) and (33, 16448, 1024): decode shapes with more 64-column
+# blocks than CUs, run in 128-column blocks (the second with a half-empty last one)
+@pytest.mark.parametrize("M,N,K", [(33, 48, 272), (300, 1024, 4096), (64, 20480, 5120),
+                                   (33, 16448, 1024)])
 def test_gemm_dequant(out, mode, M, N, K):
     rng = np.random.default_rng(M * N + K)
     xq = rng.integers(-127, 128, (M, K)).astype(np.int8)

@@ -89,10 +89,12 @@ def tile_samples(M, Ntot, K, rows, lora, extra_rows=()):
     column of the library's tile configuration, plus the edges."""
     tile = bench.gemm_tile(M, Ntot, K, lora=lora)
     BM, BN = bench.tile_dims(tile)
-    if tile in ("skinny", "decode"):
+    if tile in ("skinny", "decode", "decode128"):
         BM = 8            # M <= 64: rows of both 32-row MFMA tiles, 8 apart
+    # decode blocks: a column in every wave's 32-column MFMA tile
+    cstep = 32 if tile in ("decode", "decode128") else BN
     r = set(per_tile(M, BM, 37)) | {0, M - 1} | {int(v) for v in extra_rows if 0 <= v < M}
-    c = set(per_tile(Ntot, BN, 53)) | {0, Ntot - 1}
+    c = set(per_tile(Ntot, cstep, 53)) | {0, Ntot - 1}
     for r0, r1 in rows.values():
         c |= {r0, r1 - 1}
     return np.array(sorted(r), np.int64), np.array(sorted(c), np.int64), tile, BN
