@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--row", choices=sorted(ROWS), default=None,
                     help="measure one of the widened rows instead of the whole step "
                          "(one JSON line of its own)")
+    ap.add_argument("--kernel-workloads", default=None,
+                    help="with --row kernels: a comma-separated subset of the configurations "
+                         "(default: all of them)")
     ap.add_argument("--cpu-baseline-only", action="store_true",
                     help="print the CPU-oracle baseline of --workload as JSON and exit (no GPU; "
                          "bench.py runs this in a child process of its own)")
@@ -865,7 +868,13 @@ def row_kernels(args, torch):
             r.update(tops=round(tops, 1), frac_int8=round(tops / INT8_PEAK_TOPS, 3))
         return r
 
-    for name in KERNEL_WORKLOADS:
+    names = KERNEL_WORKLOADS
+    if args.kernel_workloads:
+        names = tuple(args.kernel_workloads.split(","))
+        unknown = [n for n in names if n not in KERNEL_WORKLOADS]
+        if unknown:
+            raise SystemExit(f"--kernel-workloads: unknown {unknown}; choose from {KERNEL_WORKLOADS}")
+    for name in names:
         wl = get_workload(name)
         dt, esz = dt_of[wl.dtype], (4 if wl.dtype == "f32" else 2)
         odt = dt_of[wl.out_dtype]
@@ -953,13 +962,26 @@ def row_kernels(args, torch):
                                     "HBM fraction of the memory-bound kernels at M >= 4096)",
         "value": round(med, 3) if med is not None else None, "unit": "fraction of 8 TB/s",
         "higher_is_better": True, "data": "synthetic (device-random tensors of each configuration's shapes)",
-        "config": {"workloads": list(KERNEL_WORKLOADS), "reps": reps}, "kernels": out,
+        "config": {"workloads": list(names), "reps": reps}, "kernels": out,
     }
 
 
 ROWS = {"f1": row_f1, "f2": row_f2, "f3": row_f3, "f4": row_f4, "kernels": row_kernels,
         "mfma": row_mfma, "lora_window": row_lora_window, "oracle": row_oracle,
         "vendor": row_vendor}
+
+
+def copy_calibration(args, torch):
+    """With --copy-calibration-mib: one device copy of that many MiB, whose
+    FETCH_SIZE / WRITE_SIZE counters (known bytes each way) scale the other
+    dispatches' counters to bytes."""
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
 
 def main():
@@ -993,6 +1015,7 @@ def main():
     if args.row:
         assert torch.cuda.is_available(), "bench.py needs a GPU"
         torch.cuda.set_device(0)
+        copy_calibration(args, torch)
         print(json.dumps(ROWS[args.row](args, torch)))
         return
     from synth.workloads import get_workload
@@ -1004,13 +1027,7 @@ def main():
         raise SystemExit("device 0 is not gfx950")
     wl = get_workload(args.workload)
     groups = setup(wl, torch)
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(args, torch)
     st = Streams(torch, groups, max(1, args.streams))
     for _ in range(args.warmup):
         run_step_streams(groups, st, join=False)
