@@ -394,18 +394,56 @@ def cpu_baseline(wl, rows_per_input: int, wrows_per_input: int):
     }
 
 
-def time_launches(torch, fn, reps: int, warm: int = 3) -> float:
-    """Average ms of fn() over reps launches on the current stream (HIP events)."""
-    for _ in range(warm):
-        fn()
+_SLEEP_PER_S = None
+
+
+def gpu_head_start(torch, seconds: float) -> None:
+    """Keep the current stream busy for about `seconds` (a spin kernel), so that
+    the launches enqueued next are all queued before the first of them runs:
+    they then run back to back, and HIP events around them time the GPU work
+    alone, not the host's launch overhead (two Python binding calls can take
+    longer to issue than small kernels take to run)."""
+    global _SLEEP_PER_S
+    if seconds <= 0:
+        return
+    if _SLEEP_PER_S is None:                     # spin cycles per second, measured once
+        n = 1 << 20
+        torch.cuda._sleep(n)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(n)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP_PER_S = n / max(e0.elapsed_time(e1) / 1e3, 1e-6)
+    torch.cuda._sleep(int(min(seconds, 0.5) * _SLEEP_PER_S))
+
+
+def time_calls(torch, fns, reps: int) -> float:
+    """Average ms per call over reps calls cycling through fns, after one warm
+    call each, timed with HIP events around GPU work that runs back to back
+    (gpu_head_start covers three times the host time the warm calls took to
+    issue, plus 0.2 ms)."""
+    t0 = time.perf_counter()
+    for f in fns:
+        f()
+    host = (time.perf_counter() - t0) / len(fns)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    gpu_head_start(torch, 3.0 * host * reps + 2e-4)
     e0.record()
-    for _ in range(reps):
-        fn()
+    for i in range(reps):
+        fns[i % len(fns)]()
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps
+
+
+def time_launches(torch, fn, reps: int, warm: int = 3) -> float:
+    """Average ms of fn() over reps launches on the current stream (HIP events,
+    back to back: see time_calls)."""
+    for _ in range(warm - 1):
+        fn()
+    return time_calls(torch, [fn], reps)
 
 
 def row_f3(args, torch):
@@ -822,17 +860,8 @@ KERNEL_WORKLOADS = ("tiny_m16_k256_n256", "llama3_8b_proj_m2048", "opt13b_layer_
 def time_rotated(torch, fns, reps):
     """Average ms per call over reps calls cycling through fns (one per input
     copy), after one warm call each: with enough copies the inputs do not stay
-    in the 256 MB MALL between their calls."""
-    for f in fns:
-        f()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(reps):
-        fns[i % len(fns)]()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    in the 256 MB MALL between their calls (back to back: see time_calls)."""
+    return time_calls(torch, fns, reps)
 
 
 def row_kernels(args, torch):
