@@ -462,6 +462,30 @@ def test_lora_segmented_many_requests(ydt):
     assert torch.equal(Y.cpu()[torch.from_numpy(none)], y[torch.from_numpy(none)])
 
 
+@pytest.mark.parametrize("case", ["no_adapter", "empty"])
+def test_lora_segmented_no_pairs_leaves_y(case):
+    """Requests that are all without an adapter, or all empty but one row
+    span without adapter: the pair table holds no pair, every shrink block and
+    expand tile exits, and Y is left as it was, bit for bit."""
+    rng = np.random.default_rng(77)
+    M, K, N, ranks = 200, 272, 144, [8, 16]
+    if case == "no_adapter":
+        seg_start = np.array([0, 10, 90, 200], np.int32)
+        seg_adapter = np.array([-1, -1, -1], np.int32)
+    else:
+        seg_start = np.array([0, 0, 0, 200, 200], np.int32)
+        seg_adapter = np.array([0, 1, -1, 1], np.int32)
+    x, _ = acts(rng, M, K, "bf16", factor=20.0)
+    As = [cast_to(rng.normal(0, 0.01, (r, K)).astype(F32), "bf16").cuda() for r in ranks]
+    Bs = [cast_to(rng.normal(0, 0.01, (N, r)).astype(F32), "bf16").cuda() for r in ranks]
+    y = cast_to(rng.normal(0, 0.5, (M, N)).astype(F32), "bf16")
+    Y = y.cuda()
+    ws = torch.empty(sq.sq_lora_workspace_bytes(M, K, 16), dtype=torch.uint8, device="cuda")
+    sq.sq_lora_apply_segmented(x, dev(seg_start), dev(seg_adapter), sq.pointer_table(As, "cuda"),
+                               sq.pointer_table(Bs, "cuda"), dev(np.array(ranks, np.int32)), 16, Y, ws)
+    assert torch.equal(Y.cpu(), y)
+
+
 def test_lora_segmented_single_adapter_equals_single():
     # both calls split K into the same 4 slices at this shape (300 rows, 4
     # requests), so one adapter over all rows gives the same result bit for bit
