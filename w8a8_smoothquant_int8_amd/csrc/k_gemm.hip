@@ -740,29 +740,42 @@ k_gemm_skinny(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
 }
 
 // The KS slices of a split-K decode GEMM (INT32 sums, 1024 words per 32 x 32
-// tile in register order: word q * 64 + lane; TM row tiles per 32-column
-// tile), added in slice order, then the epilogue. INT32 addition is exact
-// (and wraps the same in any order), so the result is that of the unsplit
-// kernel bit for bit. One wave per 32-column tile.
-template <int OUT, bool STATIC_A, int TM>
+// tile in register order: word q * 64 + lane; two row tiles per 32-column
+// tile), added up, then the epilogue. INT32 addition is exact (and wraps the
+// same in any order), so the result is that of the unsplit kernel bit for
+// bit. One wave per (32-column tile, row tile): block (x, y) takes column
+// tile x and row tile y. The slices are read in groups of four whose 64
+// loads are all issued before the first add (a group past the last slice
+// re-reads that slice and adds nothing), so the wave waits for memory once
+// per group rather than once per slice.
+template <int OUT, bool STATIC_A>
 __global__ void __launch_bounds__(64)
 k_gemm_skinny_finish(const int32_t* __restrict__ part, int KS, const float* __restrict__ a_scale,
                      const float* __restrict__ w_scale, int M, int N, void* __restrict__ Y,
                      int64_t ldy) {
   const int lane = threadIdx.x;
-  v16i acc[TM][1];
+  const int64_t tile_words = (int64_t)gridDim.x * 2048;     // one slice of every column tile
+  const int32_t* src = part + (int64_t)blockIdx.x * 2048 + blockIdx.y * 1024 + lane;
+  v16i acc[1][1];
+  acc[0][0] = v16i{};
+  for (int sl = 0; sl < KS; sl += 4) {
+    int32_t v[4][16];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) acc[i][0] = v16i{};
-  for (int sl = 0; sl < KS; ++sl) {
-    const int32_t* src = part + ((int64_t)sl * gridDim.x + blockIdx.x) * (TM * 1024);
+    for (int u = 0; u < 4; ++u) {
+      const int64_t o = (int64_t)(sl + u < KS ? sl + u : KS - 1) * tile_words;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int q = 0; q < 16; ++q) v[u][q] = src[o + q * 64];
+    }
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][0][q] += src[i * 1024 + q * 64 + lane];
+    for (int u = 0; u < 4; ++u) {
+      const int keep = sl + u < KS ? -1 : 0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[0][0][q] += v[u][q] & keep;
+    }
   }
   const LoraEpi none{nullptr, 0, nullptr, 0, 0.0f, 0, {}, {}};
-  epilogue<OUT, STATIC_A, 0, TM, 1>(acc, 0, blockIdx.x * kSkinnyBN, M, N, a_scale, w_scale, Y, ldy,
-                                    none);
+  epilogue<OUT, STATIC_A, 0, 1, 1>(acc, 32 * blockIdx.y, blockIdx.x * kSkinnyBN, M, N, a_scale,
+                                   w_scale, Y, ldy, none);
 }
 
 // ---------------------------------------------------------------------------
@@ -1147,8 +1160,8 @@ static int launch_decode(const int8_t* Xq, const int8_t* Wq, const float* a_scal
       Xq, Wq, a_scale, w_scale, (int)M, (int)N, (int)K, Y, ldy, kps, part);
   SQ_LAUNCH_CHECK();
   const unsigned ct = (unsigned)((N + 31) / 32);
-  k_gemm_skinny_finish<OUT, STATIC_A, 2><<<ct, 64, 0, st>>>(part, slices, a_scale, w_scale, (int)M,
-                                                           (int)N, Y, ldy);
+  k_gemm_skinny_finish<OUT, STATIC_A><<<dim3(ct, M > 32 ? 2u : 1u), 64, 0, st>>>(
+      part, slices, a_scale, w_scale, (int)M, (int)N, Y, ldy);
   SQ_LAUNCH_CHECK();
   return SQ_OK;
 }
